@@ -1,0 +1,366 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the decode hot path.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline timing).
+ * Independent of the HIP library: no shared code, headers or tables.
+ *
+ * Each function states the definition it writes out and where the pages give
+ * it; the readings taken where the pages are silent are stated in place.
+ * Loops run in the index order of the definition; OpenMP only splits
+ * independent outputs (rows, heads), never a sum.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Normal: (1 + f/1024) * 2^(e-15); subnormal (e = 0): f * 2^-24.
+ * [GEM] Native Metal diagnostic: block scales are binary16. */
+double orc_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp(1024.0 + (double)f, e - 25);
+    return sign ? -v : v;
+}
+
+static double read_scale(const uint8_t *p) {
+    /* little-endian byte order (the GGUF blocks are stored little-endian) */
+    return orc_half_to_double((uint16_t)(p[0] | (p[1] << 8)));
+}
+
+/* Q4_0 block of 32 weights, 18 bytes ([GEM] Native Metal diagnostic: 18-byte
+ * blocks, binary16 scale plus 16 payload bytes, weight = (quant - 8) * scale).
+ * Code order inside the payload (the pages do not print it; reading taken
+ * from the workload statement): byte j holds element j in its low nibble and
+ * element j + 16 in its high nibble. */
+static void q4_0_block(const uint8_t *blk, double *w32) {
+    double d = read_scale(blk);
+    const uint8_t *qs = blk + 2;
+    for (int j = 0; j < 16; ++j) {
+        int lo = qs[j] & 0x0F;
+        int hi = qs[j] >> 4;
+        w32[j] = d * (double)(lo - 8);
+        w32[j + 16] = d * (double)(hi - 8);
+    }
+}
+
+/* Q8_0 block of 32 weights, 34 bytes: binary16 scale then 32 int8 codes,
+ * weight = code * scale ([GEM] Verified model facts: the token table is Q8_0;
+ * the byte layout is the reading used throughout). */
+static void q8_0_block(const uint8_t *blk, double *w32) {
+    double d = read_scale(blk);
+    for (int j = 0; j < 32; ++j)
+        w32[j] = d * (double)(int8_t)blk[2 + j];
+}
+
+typedef void (*block_fn)(const uint8_t *, double *);
+
+static void dequant_rows(block_fn fn, int block_bytes, const uint8_t *w, int64_t n_rows,
+                         int64_t k, double *out) {
+    int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_rows; ++n)
+        for (int64_t b = 0; b < nb; ++b)
+            fn(w + (n * nb + b) * block_bytes, out + n * k + b * 32);
+}
+
+void orc_q4_0_dequant(const uint8_t *w, int64_t n_rows, int64_t k, double *out) {
+    dequant_rows(q4_0_block, 18, w, n_rows, k, out);
+}
+
+void orc_q8_0_dequant(const uint8_t *w, int64_t n_rows, int64_t k, double *out) {
+    dequant_rows(q8_0_block, 34, w, n_rows, k, out);
+}
+
+/* y[b][n] = sum_k W[n][k] x[b][k] (+ res[b][n]), sum in increasing k. */
+static void matvec(block_fn fn, int block_bytes, const uint8_t *w, int64_t n_rows, int64_t k,
+                   const double *x, int64_t batch, const double *res, double *y,
+                   double *terms) {
+    int64_t nb = k / 32;
+#pragma omp parallel
+    {
+        double *row = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            for (int64_t b = 0; b < nb; ++b)
+                fn(w + (n * nb + b) * block_bytes, row + b * 32);
+            for (int64_t bi = 0; bi < batch; ++bi) {
+                const double *xb = x + bi * k;
+                double s = 0.0, a = 0.0;
+                for (int64_t i = 0; i < k; ++i) {
+                    double t = row[i] * xb[i];
+                    s += t;
+                    a += fabs(t);
+                }
+                if (res) {
+                    s += res[bi * n_rows + n];
+                    a += fabs(res[bi * n_rows + n]);
+                }
+                y[bi * n_rows + n] = s;
+                if (terms)
+                    terms[bi * n_rows + n] = a;
+            }
+        }
+        free(row);
+    }
+}
+
+void orc_q4_0_matvec(const uint8_t *w, int64_t n_rows, int64_t k, const double *x,
+                     int64_t batch, const double *res, double *y, double *terms) {
+    matvec(q4_0_block, 18, w, n_rows, k, x, batch, res, y, terms);
+}
+
+void orc_q8_0_matvec(const uint8_t *w, int64_t n_rows, int64_t k, const double *x,
+                     int64_t batch, const double *res, double *y, double *terms) {
+    matvec(q8_0_block, 34, w, n_rows, k, x, batch, res, y, terms);
+}
+
+/* Embedding lookup of the tied Q8_0 table ([GELO] 04: tied input/output
+ * embeddings; [GEM] Verified model facts: Q8_0 token embeddings). */
+void orc_q8_0_gather(const uint8_t *table, int64_t vocab, int64_t k, const int32_t *tok,
+                     int64_t batch, double *x) {
+    int64_t nb = k / 32;
+    (void)vocab;
+    for (int64_t bi = 0; bi < batch; ++bi)
+        for (int64_t b = 0; b < nb; ++b)
+            q8_0_block(table + ((int64_t)tok[bi] * nb + b) * 34, x + bi * k + b * 32);
+}
+
+/* RMSNorm ([GELO] 05 Components: decoder rms_norm; 02 glossary: QK-norm is
+ * the same per-head RMSNorm): y_i = w_i * x_i / sqrt((1/D) sum x^2 + eps).
+ * Reading: the gain is w itself (not 1 + w). */
+void orc_rmsnorm(const double *x, const double *w, int64_t rows, int64_t dim, double eps,
+                 double *y) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * dim;
+        double ss = 0.0;
+        for (int64_t i = 0; i < dim; ++i)
+            ss += xr[i] * xr[i];
+        double inv = 1.0 / sqrt(ss / (double)dim + eps);
+        for (int64_t i = 0; i < dim; ++i)
+            y[r * dim + i] = xr[i] * inv * (w ? w[i] : 1.0);
+    }
+}
+
+/* NeoX rotary embedding ([GEM] Native Metal diagnostic: NeoX RoPE): element
+ * i is paired with element i + hd/2 and rotated by pos * theta^(-2i/hd). */
+void orc_rope_neox(double *x, int64_t hd, int64_t pos, double theta) {
+    int64_t half = hd / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double inv_freq = pow(theta, -(2.0 * (double)i) / (double)hd);
+        double ang = (double)pos * inv_freq;
+        double c = cos(ang), s = sin(ang);
+        double a = x[i], b = x[i + half];
+        x[i] = a * c - b * s;
+        x[i + half] = b * c + a * s;
+    }
+}
+
+/* SwiGLU ([GELO] 04: SwiGLU FFN): h = silu(g) * u, silu(z) = z / (1 + e^-z). */
+void orc_swiglu(const double *g, const double *u, int64_t n, double *h) {
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* Greedy choice ([GELO] 05: greedy sampler; [GEM] Native Metal diagnostic:
+ * equal logits resolve deterministically by token id -> lowest id wins). */
+int64_t orc_argmax(const double *v, int64_t n, double *margin) {
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; ++i)
+        if (v[i] > v[best])
+            best = i;
+    if (margin) {
+        double second = -INFINITY;
+        for (int64_t i = 0; i < n; ++i)
+            if (i != best && v[i] > second)
+                second = v[i];
+        *margin = n > 1 ? v[best] - second : INFINITY;
+    }
+    return best;
+}
+
+/* Decode attention ([GELO] 05: causal_gqa_attention_cached with one query
+ * row attending every cached position plus the new one; 02 glossary: GQA
+ * shares one K/V head among several query heads; sliding-window layers see
+ * only the last W tokens).  Readings: head h reads kv head floor(h / G);
+ * the window counts the current token; softmax is exact (max-subtracted). */
+void orc_gqa_attention(const double *q, int64_t n_q_heads, int64_t n_kv_heads, int64_t hd,
+                       const double *keys, const double *values, int64_t n_pos,
+                       int64_t window, double scale, double *o, double *bound) {
+    int64_t group = n_q_heads / n_kv_heads;
+    int64_t lo = (window > 0 && n_pos > window) ? n_pos - window : 0;
+    int64_t cnt = n_pos - lo;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)cnt);
+        double *sa = (double *)malloc(sizeof(double) * (size_t)cnt);
+#pragma omp for schedule(static)
+        for (int64_t h = 0; h < n_q_heads; ++h) {
+            int64_t g = h / group;
+            const double *qh = q + h * hd;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < cnt; ++j) {
+                const double *kj = keys + ((lo + j) * n_kv_heads + g) * hd;
+                double dot = 0.0, adot = 0.0;
+                for (int64_t i = 0; i < hd; ++i) {
+                    dot += qh[i] * kj[i];
+                    adot += fabs(qh[i] * kj[i]);
+                }
+                s[j] = scale * dot;
+                sa[j] = fabs(scale) * adot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            double z = 0.0;
+            for (int64_t j = 0; j < cnt; ++j) {
+                s[j] = exp(s[j] - m);
+                z += s[j];
+            }
+            for (int64_t j = 0; j < cnt; ++j)
+                s[j] /= z; /* s now holds the softmax weights p_j */
+            for (int64_t d = 0; d < hd; ++d) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < cnt; ++j)
+                    acc += s[j] * values[((lo + j) * n_kv_heads + g) * hd + d];
+                o[h * hd + d] = acc;
+            }
+            if (bound) {
+                for (int64_t d = 0; d < hd; ++d) {
+                    double a = 0.0, b = 0.0;
+                    for (int64_t j = 0; j < cnt; ++j) {
+                        double v = values[((lo + j) * n_kv_heads + g) * hd + d];
+                        a += s[j] * fabs(v);
+                        b += s[j] * fabs(v - o[h * hd + d]) * sa[j];
+                    }
+                    bound[h * hd + d] = a + b;
+                }
+            }
+        }
+        free(s);
+        free(sa);
+    }
+}
+
+/* One decode step.  Block topology ([GELO] 06 Compute flow: pre-LN block,
+ * QKV projection, per-head QK-norm before RoPE, GQA attention over the cache
+ * plus the new row, O projection with residual, pre-FFN norm, gate/up,
+ * SwiGLU, down projection with residual; tied LM head; greedy choice).
+ * Gemma-4 full-attention layers take V from the K projection: the cached V
+ * row is the unit-gain RMSNorm of the raw K row ([GEM] Verified model facts). */
+void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_t *next,
+                     double *logits, double *margins) {
+    int64_t B = m->batch, D = m->d_model, Hq = m->n_q_heads, F = m->ffn;
+    double *x = (double *)malloc(sizeof(double) * (size_t)(B * D));
+    double *xn = (double *)malloc(sizeof(double) * (size_t)(B * D));
+    orc_q8_0_gather(m->embed, m->vocab, D, tok, B, x);
+
+    for (int64_t l = 0; l < m->n_layers; ++l) {
+        const orc_layer *L = &m->layers[l];
+        int64_t hd = L->head_dim, Hkv = L->n_kv_heads;
+        int64_t nq = Hq * hd, nk = Hkv * hd, nv = L->v_from_k ? 0 : nk;
+        int64_t nqkv = nq + nk + nv;
+        double *qkv = (double *)malloc(sizeof(double) * (size_t)(B * nqkv));
+        double *att = (double *)malloc(sizeof(double) * (size_t)(B * nq));
+
+        orc_rmsnorm(x, L->attn_norm, B, D, m->eps, xn);
+        orc_q4_0_matvec(L->wqkv, nqkv, D, xn, B, NULL, qkv, NULL);
+
+        int64_t n_pos = pos + 1;
+        int64_t lo = (L->window > 0 && n_pos > L->window) ? n_pos - L->window : 0;
+        double *keys = (double *)malloc(sizeof(double) * (size_t)(n_pos * nk));
+        double *vals = (double *)malloc(sizeof(double) * (size_t)(n_pos * nk));
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)hd);
+        double *vrow = (double *)malloc(sizeof(double) * (size_t)hd);
+        for (int64_t bi = 0; bi < B; ++bi) {
+            double *q = qkv + bi * nqkv;
+            double *kr = q + nq;
+            double *vr = L->v_from_k ? NULL : kr + nk;
+            for (int64_t h = 0; h < Hq; ++h) {
+                orc_rmsnorm(q + h * hd, L->q_norm, 1, hd, m->eps, tmp);
+                orc_rope_neox(tmp, hd, pos, L->rope_theta);
+                memcpy(q + h * hd, tmp, sizeof(double) * (size_t)hd);
+            }
+            for (int64_t g = 0; g < Hkv; ++g) {
+                if (L->v_from_k)
+                    orc_rmsnorm(kr + g * hd, NULL, 1, hd, m->eps, vrow);
+                else
+                    memcpy(vrow, vr + g * hd, sizeof(double) * (size_t)hd);
+                orc_rmsnorm(kr + g * hd, L->k_norm, 1, hd, m->eps, tmp);
+                orc_rope_neox(tmp, hd, pos, L->rope_theta);
+                /* the cache is F32: the appended row is stored rounded */
+                int64_t slot = pos % L->cap;
+                float *kc = L->k_cache + ((bi * Hkv + g) * L->cap + slot) * hd;
+                float *vc = L->v_cache + ((bi * Hkv + g) * L->cap + slot) * hd;
+                for (int64_t i = 0; i < hd; ++i) {
+                    kc[i] = (float)tmp[i];
+                    vc[i] = (float)vrow[i];
+                }
+            }
+            for (int64_t p = lo; p < n_pos; ++p) {
+                int64_t slot = p % L->cap;
+                for (int64_t g = 0; g < Hkv; ++g)
+                    for (int64_t i = 0; i < hd; ++i) {
+                        keys[(p * Hkv + g) * hd + i] =
+                            L->k_cache[((bi * Hkv + g) * L->cap + slot) * hd + i];
+                        vals[(p * Hkv + g) * hd + i] =
+                            L->v_cache[((bi * Hkv + g) * L->cap + slot) * hd + i];
+                    }
+            }
+            orc_gqa_attention(q, Hq, Hkv, hd, keys, vals, n_pos, L->window, L->attn_scale,
+                              att + bi * nq, NULL);
+        }
+        free(keys);
+        free(vals);
+        free(tmp);
+        free(vrow);
+
+        orc_q4_0_matvec(L->wo, D, nq, att, B, x, xn, NULL);
+        memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+
+        double *gu = (double *)malloc(sizeof(double) * (size_t)(B * 2 * F));
+        double *hh = (double *)malloc(sizeof(double) * (size_t)(B * F));
+        orc_rmsnorm(x, L->ffn_norm, B, D, m->eps, xn);
+        orc_q4_0_matvec(L->wgu, 2 * F, D, xn, B, NULL, gu, NULL);
+        for (int64_t bi = 0; bi < B; ++bi)
+            orc_swiglu(gu + bi * 2 * F, gu + bi * 2 * F + F, F, hh + bi * F);
+        orc_q4_0_matvec(L->wd, D, F, hh, B, x, xn, NULL);
+        memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+        free(gu);
+        free(hh);
+        free(qkv);
+        free(att);
+    }
+
+    orc_rmsnorm(x, m->final_norm, B, D, m->eps, xn);
+    double *lg = logits ? logits : (double *)malloc(sizeof(double) * (size_t)(B * m->vocab));
+    orc_q8_0_matvec(m->embed, m->vocab, D, xn, B, NULL, lg, NULL);
+    for (int64_t bi = 0; bi < B; ++bi) {
+        double mg;
+        next[bi] = (int32_t)orc_argmax(lg + bi * m->vocab, m->vocab, &mg);
+        if (margins)
+            margins[bi] = mg;
+    }
+    if (!logits)
+        free(lg);
+    free(x);
+    free(xn);
+}

@@ -1,0 +1,348 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each test is chosen so that a plausible slip in the oracle (dropped term, wrong
+sign, swapped nibbles, transposed operand, wrong head mapping, wrong RoPE
+pairing, wrong window edge) fails at least one of them.  Nothing here compares
+the oracle with a copy of its own formula or with the HIP path.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hand_block():
+    with open(os.path.join(GOLDEN, "q4_0_hand_block.json")) as f:
+        g = json.load(f)
+    blk = bytes.fromhex(g["block_hex"]) + bytes.fromhex(g["payload_hex"])
+    assert len(blk) == 18
+    return np.frombuffer(blk, dtype=np.uint8).copy(), g
+
+
+# ----------------------------------------------------------------- binary16
+def test_half_every_bit_pattern():
+    """All 65,536 binary16 patterns against numpy's IEEE conversion."""
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # and the sign of zero
+    assert math.copysign(1.0, oracle.half_to_double(0x8000)) == -1.0
+
+
+# ----------------------------------------------------------------- Q4_0
+def test_q4_0_hand_block_weights():
+    blk, g = _hand_block()
+    w = oracle.q4_0_dequant(blk, 1, 32)[0]
+    assert w.tolist() == g["weights"]
+
+
+def test_q4_0_hand_block_matvec_cases():
+    blk, g = _hand_block()
+    k = np.arange(32, dtype=np.float64)
+    xs = {"ones": np.ones(32), "k_squared": k * k}
+    for case in g["cases"]:
+        y, _ = oracle.q4_0_matvec(blk, 1, 32, xs[case["x"]])
+        assert y[0, 0] == case["y"], case
+    # unit vectors recover each weight exactly; e_0 and e_16 tell the nibbles apart
+    eye = np.eye(32)
+    y, _ = oracle.q4_0_matvec(blk, 1, 32, eye)
+    assert y[:, 0].tolist() == g["weights"]
+    assert y[0, 0] == -0.5 and y[16, 0] == 0.4375
+
+
+def test_q4_0_code_eight_is_zero_and_scale_little_endian():
+    blk = np.zeros(18, dtype=np.uint8)
+    blk[0:2] = [0x00, 0x3C]          # 0x3C00 = 1.0 little-endian
+    blk[2:] = 0x88                   # every code 8 -> weight 0
+    assert np.all(oracle.q4_0_dequant(blk, 1, 32) == 0.0)
+    blk[2:] = 0xFF                   # every code 15 -> weight 7 * d
+    assert np.all(oracle.q4_0_dequant(blk, 1, 32) == 7.0)
+    blk[2:] = 0x00                   # every code 0 -> weight -8 * d
+    assert np.all(oracle.q4_0_dequant(blk, 1, 32) == -8.0)
+
+
+def _expand_codes_q4(w_bytes, n_rows, k):
+    """Integer codes of a Q4_0 matrix, element order per the format statement."""
+    blocks = w_bytes.reshape(n_rows, k // 32, 18)
+    qs = blocks[:, :, 2:]
+    codes = np.concatenate([qs & 0x0F, qs >> 4], axis=2)      # elements 0..15, 16..31
+    return codes.reshape(n_rows, k).astype(np.int64)
+
+
+def test_q4_0_matvec_integer_exact():
+    """Power-of-two scale and integer x: the result is exact in int64 arithmetic."""
+    rng = np.random.default_rng(7)
+    n_rows, k = 13, 96
+    w = synth.q4_0_matrix(11, "int-exact", n_rows, k)
+    blocks = w.reshape(n_rows, k // 32, 18)
+    blocks[:, :, 0] = 0x00
+    blocks[:, :, 1] = 0x30            # 0x3000 = 0.125
+    x = rng.integers(-50, 51, size=(3, k))
+    codes = _expand_codes_q4(w, n_rows, k)
+    exact = (x @ (codes - 8).T)       # int64, exact
+    y, terms = oracle.q4_0_matvec(w, n_rows, k, x.astype(np.float64))
+    assert np.array_equal(y, exact * 0.125)
+    assert np.array_equal(terms, np.abs(x)[:, None, :].__mul__(np.abs(codes - 8)[None]).sum(-1) * 0.125)
+
+
+def test_q4_0_vs_q8_0_cross_encoding():
+    """A Q4_0 matrix re-encoded as Q8_0 (same scale, code - 8 per element) gives
+    bit-identical products: catches a nibble-order or offset slip in either path."""
+    n_rows, k = 9, 256
+    w4 = synth.q4_0_matrix(3, "cross", n_rows, k)
+    codes = _expand_codes_q4(w4, n_rows, k) - 8
+    b4 = w4.reshape(n_rows, k // 32, 18)
+    w8 = np.empty((n_rows, k // 32, 34), dtype=np.uint8)
+    w8[:, :, 0:2] = b4[:, :, 0:2]
+    w8[:, :, 2:] = codes.reshape(n_rows, k // 32, 32).astype(np.int8).view(np.uint8)
+    x = synth.normal_f32(3, "cross-x", (4, k))
+    y4, t4 = oracle.q4_0_matvec(w4, n_rows, k, x)
+    y8, t8 = oracle.q8_0_matvec(w8.reshape(n_rows, -1), n_rows, k, x)
+    assert np.array_equal(y4, y8) and np.array_equal(t4, t8)
+
+
+@pytest.mark.parametrize("n_rows,k,batch", [(67, 32, 1), (67, 64, 3), (33, 256, 8), (5, 288, 2)])
+def test_q4_0_matvec_matches_dense_product(n_rows, k, batch):
+    """Brute force on tiny shapes (with non-multiple row tails): the blocked
+    matvec equals a dense fp64 product of the dequantised matrix."""
+    w = synth.q4_0_matrix(5, f"dense-{n_rows}-{k}", n_rows, k)
+    x = synth.normal_f32(5, f"dense-x-{n_rows}-{k}", (batch, k)).astype(np.float64)
+    r = synth.normal_f32(5, f"dense-r-{n_rows}-{k}", (batch, n_rows)).astype(np.float64)
+    dense = oracle.q4_0_dequant(w, n_rows, k)
+    y, terms = oracle.q4_0_matvec(w, n_rows, k, x, res=r)
+    ref = x @ dense.T + r
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+    assert np.allclose(terms, np.abs(x) @ np.abs(dense).T + np.abs(r), rtol=1e-13)
+    # transposed-operand slip: the dense product with W (not W^T) has another shape
+    assert dense.shape == (n_rows, k)
+
+
+def test_q4_0_byte_count_fact():
+    """Research record, buffer-ownership section: 5376 x 21504 Q4_0 = 65,028,096 bytes."""
+    w = synth.q4_0_matrix(1, "fact", 4, 5376)
+    assert w.shape[1] * 21504 == 65_028_096
+
+
+# ----------------------------------------------------------------- Q8_0
+def test_q8_0_hand_block():
+    blk = np.zeros(34, dtype=np.uint8)
+    blk[0:2] = [0x00, 0x38]                      # 0x3800 = 0.5
+    codes = np.array([(-1) ** j * j for j in range(32)], dtype=np.int8)
+    codes[31] = -127
+    blk[2:] = codes.view(np.uint8)
+    w = oracle.q8_0_dequant(blk, 1, 32)[0]
+    assert w.tolist() == [0.5 * float(c) for c in codes]
+    assert w[31] == -63.5 and w[2] == 1.0 and w[3] == -1.5
+
+
+def test_q8_0_gather_is_row_of_table():
+    v, k = 50, 64
+    t = synth.q8_0_matrix(2, "gather", v, k)
+    tok = np.array([0, 49, 7, 7], dtype=np.int32)
+    x = oracle.q8_0_gather(t, v, k, tok)
+    dense = oracle.q8_0_dequant(t, v, k)
+    assert np.array_equal(x, dense[tok])
+    # and equals the product with a unit vector on the output side
+    y, _ = oracle.q8_0_matvec(t, v, k, np.eye(k))
+    assert np.array_equal(y.T[tok], x)
+
+
+# ----------------------------------------------------------------- RMSNorm
+def test_rmsnorm_unit_gain_invariant():
+    x = synth.normal_f32(4, "rms", (5, 300)).astype(np.float64) * 3.0
+    eps = 1e-6
+    y = oracle.rmsnorm(x, None, eps)
+    ms = (x * x).mean(axis=1)
+    assert np.allclose(np.sqrt((y * y).mean(axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-14)
+
+
+def test_rmsnorm_constant_row_and_hand_case():
+    w = np.array([0.5, 1.0, 2.0, -1.0])
+    c, eps = 3.0, 1e-6
+    y = oracle.rmsnorm(np.full(4, c), w, eps)
+    assert np.allclose(y, w * c / math.sqrt(c * c + eps), rtol=1e-15)
+    y = oracle.rmsnorm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.0)
+    r = math.sqrt(12.5)
+    assert np.allclose(y, [3.0 / r, 8.0 / r], rtol=1e-15)
+
+
+def test_rmsnorm_scale_invariance_without_eps():
+    x = synth.normal_f32(4, "rms2", (300,)).astype(np.float64)
+    w = synth.uniform_f32(4, "rms2w", (300,), 0.8, 1.2)
+    a = oracle.rmsnorm(x, w, 0.0)
+    assert np.allclose(oracle.rmsnorm(x * 1e3, w, 0.0), a, rtol=1e-13)
+    assert np.allclose(oracle.rmsnorm(-x * 0.25, w, 0.0), -a, rtol=1e-13)
+
+
+# ----------------------------------------------------------------- RoPE
+def test_rope_position_zero_is_identity():
+    x = synth.normal_f32(6, "rope0", (3, 128)).astype(np.float64)
+    assert np.array_equal(oracle.rope_neox(x, 0, 1e6), x)
+
+
+def test_rope_one_pair_closed_form():
+    """hd = 2: the single pair rotates by exactly pos radians."""
+    for pos in (1, 7, 4096, 8200):
+        y = oracle.rope_neox(np.array([1.0, 0.0]), pos, 1e6)
+        assert y[0] == math.cos(pos) and y[1] == math.sin(pos)
+
+
+def test_rope_neox_pairing_and_frequency():
+    """hd = 4: element 1 pairs with element 3 (NeoX half split, not adjacent
+    pairs) and turns at theta^(-2/4) per position."""
+    theta, pos = 10000.0, 3
+    y = oracle.rope_neox(np.array([0.0, 1.0, 0.0, 0.0]), pos, theta)
+    a = pos * theta ** (-0.5)
+    assert abs(y[1] - math.cos(a)) < 1e-15 and abs(y[3] - math.sin(a)) < 1e-15
+    assert y[0] == 0.0 and y[2] == 0.0
+
+
+def test_rope_norm_and_relative_position():
+    hd = 128
+    q = synth.normal_f32(6, "rq", (hd,)).astype(np.float64)
+    k = synth.normal_f32(6, "rk", (hd,)).astype(np.float64)
+    rq = oracle.rope_neox(q, 4096, 1e6)
+    h = hd // 2
+    assert np.allclose(rq[:h] ** 2 + rq[h:] ** 2, q[:h] ** 2 + q[h:] ** 2, rtol=1e-13)
+    d1 = oracle.rope_neox(q, 900, 1e6) @ oracle.rope_neox(k, 700, 1e6)
+    d2 = oracle.rope_neox(q, 250, 1e6) @ oracle.rope_neox(k, 50, 1e6)
+    assert abs(d1 - d2) < 1e-11 * (np.abs(q) @ np.abs(k))
+
+
+# ----------------------------------------------------------------- SwiGLU
+def test_swiglu_values():
+    g = np.array([0.0, 1.0, 40.0, -40.0, -1.0])
+    u = np.array([5.0, 1.0, 1.0, 1.0, 2.0])
+    h = oracle.swiglu(g, u)
+    assert h[0] == 0.0
+    assert abs(h[1] - 0.7310585786300049) < 1e-16
+    assert abs(h[2] - 40.0) < 1e-15
+    assert abs(h[3]) < 1e-15 and h[3] < 0
+    assert abs(h[4] - 2.0 * (-1.0 / (1.0 + math.e))) < 1e-15
+
+
+# ----------------------------------------------------------------- argmax
+def test_argmax_ties_and_margin():
+    i, m = oracle.argmax(np.array([1.0, 3.0, 3.0, 2.0]))
+    assert i == 1 and m == 0.0
+    i, m = oracle.argmax(np.array([-5.0, -1.0, -2.0]))
+    assert i == 1 and m == 1.0
+    v = synth.normal_f32(8, "am", (10000,)).astype(np.float64)
+    i, m = oracle.argmax(v)
+    assert i == max(range(v.size), key=lambda j: (v[j], -j))
+    s = sorted(v.tolist())
+    assert m == s[-1] - s[-2]
+
+
+# ----------------------------------------------------------------- attention
+def _attn_inputs(seed, hq, hkv, hd, n):
+    q = synth.normal_f32(seed, "aq", (hq, hd)).astype(np.float64)
+    k = synth.normal_f32(seed, "ak", (n, hkv, hd)).astype(np.float64)
+    v = synth.normal_f32(seed, "av", (n, hkv, hd)).astype(np.float64)
+    return q, k, v
+
+
+def _attn_brute(q, k, v, window, scale):
+    """Pure-Python loops over a tiny case, straight from the softmax definition."""
+    hq, hd = q.shape
+    n, hkv, _ = k.shape
+    group = hq // hkv
+    lo = max(0, n - window) if window else 0
+    out = np.zeros((hq, hd))
+    for h in range(hq):
+        g = h // group
+        s = [scale * sum(q[h, i] * k[j, g, i] for i in range(hd)) for j in range(lo, n)]
+        mx = max(s)
+        e = [math.exp(t - mx) for t in s]
+        z = sum(e)
+        for d in range(hd):
+            out[h, d] = sum(e[j - lo] / z * v[j, g, d] for j in range(lo, n))
+    return out
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 8])
+def test_attention_brute_force_small(window):
+    q, k, v = _attn_inputs(1, 4, 2, 8, 6)
+    o, _ = oracle.gqa_attention(q, k, v, window, 0.3)
+    assert np.allclose(o, _attn_brute(q, k, v, window, 0.3), rtol=1e-13, atol=1e-14)
+
+
+def test_attention_special_cases():
+    q, k, v = _attn_inputs(2, 8, 2, 16, 9)
+    # one key: the output is that key's value row
+    o, _ = oracle.gqa_attention(q, k[:1], v[:1], 0, 1.0)
+    assert np.allclose(o, np.repeat(v[0], 4, axis=0), rtol=1e-15)
+    # window 1: only the newest position is seen
+    o, _ = oracle.gqa_attention(q, k, v, 1, 1.0)
+    assert np.allclose(o, np.repeat(v[-1], 4, axis=0), rtol=1e-15)
+    # equal keys: uniform weights, output = mean of the values in the window
+    ke = np.repeat(k[:1], 9, axis=0)
+    o, _ = oracle.gqa_attention(q, ke, v, 0, 1.0)
+    assert np.allclose(o, np.repeat(v.mean(axis=0), 4, axis=0), rtol=1e-13)
+    o, _ = oracle.gqa_attention(q, ke, v, 4, 1.0)
+    assert np.allclose(o, np.repeat(v[-4:].mean(axis=0), 4, axis=0), rtol=1e-13)
+    # constant values: weights sum to one
+    vc = np.full_like(v, 2.5)
+    o, _ = oracle.gqa_attention(q, k, vc, 0, 0.7)
+    assert np.allclose(o, 2.5, rtol=1e-15)
+    # window >= n equals the full cache
+    a, _ = oracle.gqa_attention(q, k, v, 9, 0.7)
+    b, _ = oracle.gqa_attention(q, k, v, 0, 0.7)
+    assert np.array_equal(a, b)
+
+
+def test_attention_head_group_mapping():
+    """Query head h reads kv head h // (Hq / Hkv)."""
+    hq, hkv, hd, n = 8, 4, 4, 5
+    q, k, _ = _attn_inputs(3, hq, hkv, hd, n)
+    v = np.zeros((n, hkv, hd))
+    for g in range(hkv):
+        v[:, g, :] = g
+    o, _ = oracle.gqa_attention(q, k, v, 0, 1.0)
+    assert np.allclose(o[:, 0], [h // 2 for h in range(hq)], rtol=1e-15)
+
+
+def test_attention_mha_equals_per_head():
+    q, k, v = _attn_inputs(4, 3, 3, 8, 7)
+    o, _ = oracle.gqa_attention(q, k, v, 0, 0.5)
+    for h in range(3):
+        oh, _ = oracle.gqa_attention(q[h:h + 1], k[:, h:h + 1], v[:, h:h + 1], 0, 0.5)
+        assert np.array_equal(oh[0], o[h])
+
+
+def test_attention_two_key_closed_form():
+    q = np.array([[1.0, 2.0]])
+    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    v = np.array([[[10.0, 0.0]], [[0.0, 4.0]]])
+    o, _ = oracle.gqa_attention(q, k, v, 0, 0.5)
+    e1, e2 = math.exp(0.5), math.exp(1.0)
+    assert np.allclose(o[0], [10.0 * e1 / (e1 + e2), 4.0 * e2 / (e1 + e2)], rtol=1e-15)
+
+
+def test_attention_chunk_merge_composition():
+    """Attention over all keys equals the merge of attention over disjoint chunks,
+    each weighted by its share of the softmax mass (the split-K identity)."""
+    q, k, v = _attn_inputs(5, 2, 1, 16, 40)
+    scale = 0.25
+    full, _ = oracle.gqa_attention(q, k, v, 0, scale)
+    cuts = [0, 7, 8, 25, 40]
+    for h in range(2):
+        num = np.zeros(16)
+        den = 0.0
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            oc, _ = oracle.gqa_attention(q[h:h + 1], k[a:b], v[a:b], 0, scale)
+            s = scale * (k[a:b, 0] @ q[h])
+            mass = np.exp(s).sum()
+            num += mass * oc[0]
+            den += mass
+        assert np.allclose(num / den, full[h], rtol=1e-12)
