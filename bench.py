@@ -1,0 +1,156 @@
+"""Benchmark of the Q4_0 decode hot path on one MI355X.
+
+Default workload: the Q4_0 matvec at the 31B FFN projection shape,
+K=5376 -> N=21504 (65,028,096 weight bytes), B=1.  One step = one matvec
+dispatch over one activation batch; dispatches rotate over 16 independently
+drawn weight copies (1.04 GB, larger than the 256 MB last-level cache) so every
+step streams its weights from HBM.  Inputs are resident in HBM before timing.
+
+Prints one JSON line (rank 0, N=1 only):
+  value      = algorithmic bytes per dispatch / mean dispatch time (GB/s)
+  roofline   = the matvec kernel against the 8 TB/s HBM3E peak
+  cpu_baseline = the fp64 oracle timed on a bounded sample on the host cores
+Extra keys report B=8 at the same shape and the decode workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def matvec_bytes(n, k, b):
+    return n * (k // 32) * 18 + 4 * b * k + 4 * b * n
+
+
+def time_matvec(q, torch, Ws, x, y, steps, warmup):
+    """Mean time per dispatch (ms) over `steps` back-to-back launches, HIP events
+    on the stream the kernels are launched on."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        q.q4_0_matvec(Ws[i % len(Ws)], x, y=y)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        q.q4_0_matvec(Ws[i % len(Ws)], x, y=y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline_matvec(w, budget_s=12.0):
+    import numpy as np
+
+    import oracle
+    from synth import workloads as wl
+    W, x = wl.matvec_inputs(w, 1)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.q4_0_matvec(W, w.n, w.k, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    per = el / reps
+    return {"value": round(matvec_bytes(w.n, w.k, 1) / per / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full {w.k}x{w.n} B=1 fp64 matvecs ({el:.1f} s), "
+                      f"{per * 1e3:.1f} ms each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-matvec", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import q4_quantized_matvec_amd as q
+    from synth import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.MATVEC_5376x21504
+    log(f"generating {args.copies} weight copies of {w.k}x{w.n}")
+    Ws = []
+    for c in range(args.copies):
+        W, _ = wl.matvec_inputs(w, 1, copy=c)
+        Ws.append(torch.from_numpy(W).to(dev))
+    _, x1 = wl.matvec_inputs(w, 1)
+    _, x8 = wl.matvec_inputs(w, 8)
+    x1 = torch.from_numpy(x1).to(dev)
+    x8 = torch.from_numpy(x8).to(dev)
+    y1 = torch.empty((1, w.n), dtype=torch.float32, device=dev)
+    y8 = torch.empty((8, w.n), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    log("timing B=1")
+    ms1 = time_matvec(q, torch, Ws, x1, y1, args.steps, args.warmup)
+    log("timing B=8")
+    ms8 = time_matvec(q, torch, Ws, x8, y8, args.steps, args.warmup)
+    log("timing B=1 cache-resident (one copy)")
+    ms1r = time_matvec(q, torch, Ws[:1], x1, y1, args.steps, args.warmup)
+
+    bytes1 = matvec_bytes(w.n, w.k, 1)
+    bytes8 = matvec_bytes(w.n, w.k, 8)
+    gbs1 = bytes1 / (ms1 * 1e-3) / 1e9
+    gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            traffic = json.load(f).get("q4_0_matvec_5376x21504_B1")
+
+    out = {
+        "metric": "Q4_0 matvec GB/s (% of HBM peak) at 5376x21504; decode tok/s at B=1 and B=8",
+        "value": round(gbs1, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms1, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox; Q4_0 codes uniform, binary16 scales U[0.005,0.02], x N(0,1))",
+        "config": {"workload": w.name, "N": w.n, "K": w.k, "B": 1, "weight_copies": args.copies,
+                   "weight_bytes": w.n * (w.k // 32) * 18},
+        "roofline": {"bound": "hbm", "achieved": round(gbs1, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs1 / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "matvec_B8": {"GB/s": round(gbs8, 2), "ms": round(ms8, 6),
+                      "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4)},
+        "matvec_B1_cache_resident": {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
+                                     "ms": round(ms1r, 6)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline_matvec(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

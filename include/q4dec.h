@@ -1,0 +1,255 @@
+/*
+ * q4dec.h -- C ABI of the MI355X (gfx950) decode hot path for Q4_0-weight
+ * decoders: Q4_0/Q8_0 dequant-matvec, embedding gather, RMSNorm, per-head
+ * QK-norm + NeoX RoPE with KV-cache append, split-K grouped-query decode
+ * attention, SwiGLU, greedy argmax, and a decode scheduler that replays one
+ * whole decode step as a HIP graph.
+ *
+ * Pages cited (by title and section):
+ *   [GEM]  "Research record" (gem engine research record): "Verified model
+ *          facts"; "Native Metal diagnostic: buffer ownership".
+ *   [GELO] "GELO LLM" (generation): 02 "Definitions & glossary", 04
+ *          "Supported workloads & architectures", 05 "Components", 06
+ *          "Compute flow & trust boundaries".
+ *
+ * Conventions for every call:
+ *   - Pointers named *_dev or documented as device memory must point to
+ *     device memory of the current HIP device; the caller owns all memory.
+ *     The library never allocates, frees or keeps device memory of its own.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; nothing synchronises the
+ *     device except decode_model_create.
+ *   - Activations are fp32, row-major, batch-major ([B][dim]).
+ *   - Arguments are validated on the host before any HIP call; a call that
+ *     returns an error has enqueued nothing.  The message of the last error
+ *     of the calling thread is returned by q4dec_last_error().
+ *   - Q4_0 / Q8_0 matrices are row-major block rows: row n (output feature n)
+ *     holds K/32 consecutive blocks.
+ */
+#ifndef Q4DEC_H
+#define Q4DEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad flag */
+    Q4_ERR_SHAPE = 2,       /* sizes inconsistent (K % 32, Hq % Hkv, odd head_dim, ...) */
+    Q4_ERR_ALIGNMENT = 3,   /* pointer not aligned as the call requires */
+    Q4_ERR_CAPACITY = 4,    /* a position does not fit the KV cache */
+    Q4_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+    Q4_ERR_UNSUPPORTED = 6, /* valid but outside what the kernels implement */
+    Q4_ERR_HIP = 7          /* the HIP runtime reported an error */
+} q4_status;
+
+/* Message of the calling thread's most recent error ("" if none). */
+const char *q4dec_last_error(void);
+/* Library version string. */
+const char *q4dec_version(void);
+
+/* ------------------------------------------------------------------ matvec
+ * q4_0_matvec: y[b][n] = sum_k W[n][k] * x[b][k]  (+ residual[b][n])
+ *   with W[n][k] = d * (q - 8) for the Q4_0 block holding element k of row n:
+ *   18 bytes = little-endian binary16 scale d, then 16 code bytes; byte j
+ *   holds element j (low nibble) and element j + 16 (high nibble).
+ *   ([GEM] Native Metal diagnostic: 18-byte blocks, binary16 scale, 16
+ *   payload bytes, (quant - 8) * scale.)
+ *
+ *   W         device, N * (K/32) * 18 bytes, 2-byte aligned
+ *   N, K      output / input features; K % 32 == 0; N >= 1; 1 <= B <= 8
+ *   x         device fp32 [B][K], 4-byte aligned
+ *   y         device fp32 [B][N]; may alias residual (in-place residual add)
+ *   residual  device fp32 [B][N] or NULL
+ * Accumulation is fp32; every weight-activation product is formed exactly.
+ * Errors: Q4_ERR_INVALID_ARG (null / sizes), Q4_ERR_SHAPE (K % 32),
+ *         Q4_ERR_ALIGNMENT, Q4_ERR_UNSUPPORTED (B > 8), Q4_ERR_HIP.
+ */
+q4_status q4_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
+                      float *y, const float *residual, void *stream);
+
+/* q8_0_matvec: as q4_0_matvec for Q8_0 blocks: 34 bytes = little-endian
+ * binary16 scale d then 32 int8 codes q; W[n][k] = d * q.  Used for the tied
+ * logit projection ([GEM] Verified model facts: Q8_0 token table; [GELO] 04:
+ * tied input/output embeddings).  Same arguments and errors. */
+q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
+                      float *y, const float *residual, void *stream);
+
+/* q8_0_gather: x[b][:] = dequantised row tokens[b] of the Q8_0 table E
+ * (embedding lookup of the tied table; [GELO] 05 generation loop embeds the
+ * previous token).
+ *   E       device, V * (K/32) * 34 bytes;  tokens device int32 [B]
+ *   x       device fp32 [B][K]
+ * A token id outside [0, V) yields a row of NaN (no out-of-range read).
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE (K % 32), Q4_ERR_HIP. */
+q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens, int64_t B,
+                      float *x, void *stream);
+
+/* ------------------------------------------------------------------ norms
+ * rmsnorm: y[r][i] = w[i] * x[r][i] / sqrt(mean_i(x[r][i]^2) + eps)
+ *   ([GELO] 05 Components: decoder RMSNorm.)  x, y device fp32 [rows][dim]
+ *   (y may alias x); w device fp32 [dim] or NULL for unit gain; eps >= 0.
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_HIP. */
+q4_status rmsnorm(const float *x, const float *w, int64_t rows, int64_t dim, float eps,
+                  float *y, void *stream);
+
+/* swiglu: h[r][i] = g[r][i] / (1 + exp(-g[r][i])) * u[r][i], 0 <= i < n.
+ *   ([GELO] 04: SwiGLU FFN.)  g and u are read with row stride ld (ld >= n;
+ *   a merged gate|up projection output passes g = gu, u = gu + n, ld = 2n);
+ *   h is [rows][n].  Device fp32.
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_HIP. */
+q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld, float *h,
+                 void *stream);
+
+/* KV-cache layout: element strides of a [batch][n_kv_heads][cap][head_dim]
+ * style cache; the head_dim axis is contiguous.  Position p of a sequence
+ * lives in slot p % cap (a cache with cap >= the positions it must hold is
+ * linear; a sliding-window layer may use a ring with cap == window). */
+typedef struct {
+    int64_t batch, n_kv_heads, head_dim, cap;
+    int64_t stride_b, stride_h, stride_t;
+} q4_kv_layout;
+
+/* qk_norm_rope: for the new token of each sequence b at device position
+ * *pos_dev:
+ *   q_h <- RoPE(rmsnorm(q_h, q_norm))  for each query head (in place in q);
+ *   k_g <- RoPE(rmsnorm(k_g, k_norm)), appended to k_cache at slot pos % cap;
+ *   v_g appended to v_cache; with v_from_k the V row is the unit-gain
+ *   rmsnorm of the raw (pre-norm) k_g and v must be NULL.
+ * RoPE is NeoX style: element i pairs with i + hd/2, angle
+ * pos * theta^(-2i/hd), computed in fp64 and reduced before the sine/cosine.
+ * ([GELO] 02 glossary and 05 Components: per-head QK-norm before RoPE with a
+ * shared head_dim gain; [GEM] Native Metal diagnostic: NeoX RoPE; [GEM]
+ * Verified model facts: full-attention layers take V from the K projection
+ * with an unweighted RMS normalisation.)
+ *   q        device fp32, row b at q + b*ldq, n_q_heads * head_dim values
+ *   k, v     device fp32, row b at k + b*ldkv (same for v)
+ *   q_norm, k_norm  device fp32 [head_dim]
+ *   kv       cache layout (host struct); head_dim even, <= 512
+ *   pos_dev  device int64 [1]; the kernel writes nothing outside the cache
+ *            (a position whose slot would be out of range is not written).
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE (n_q_heads % n_kv_heads, odd hd),
+ *         Q4_ERR_UNSUPPORTED (hd > 512), Q4_ERR_HIP. */
+q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
+                       const float *q_norm, const float *k_norm, int64_t n_q_heads,
+                       const q4_kv_layout *kv, const int64_t *pos_dev, double theta,
+                       float eps, int v_from_k, float *k_cache, float *v_cache,
+                       void *stream);
+
+/* ------------------------------------------------------------------ attention
+ * gqa_decode_attn: one query row per sequence attends the cached positions
+ *   [lo, n) with n = *n_dev and lo = max(0, n - window) (window 0 = all):
+ *   out_h = sum_j softmax_j(scale * q_h . k_j) v_j, query head h reading kv
+ *   head h / (n_q_heads / n_kv_heads).
+ *   ([GELO] 05: cached GQA attention, decode attends n_cache + 1 keys; 02:
+ *   GQA, sliding window over the last W tokens.)
+ * Split-K: the key range is cut into fixed chunks processed in parallel, each
+ * producing (max, sum, weighted V); a second pass merges the chunks in
+ * ascending order, so results are bitwise reproducible.
+ *   q        device fp32, row b at q + b*ldq ([n_q_heads][head_dim])
+ *   k_cache, v_cache  device fp32 with layout kv (slot = position % cap)
+ *   n_dev    device int64 [1]; positions outside the last cap are never read
+ *   out      device fp32, row b at out + b*ldo ([n_q_heads][head_dim])
+ *   ws       device workspace of at least gqa_decode_attn_workspace() bytes,
+ *            256-byte aligned; contents need no initialisation
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE, Q4_ERR_UNSUPPORTED (hd > 512 or
+ *         hd % 4, group > 16), Q4_ERR_WORKSPACE, Q4_ERR_HIP. */
+q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads, const float *k_cache,
+                          const float *v_cache, const q4_kv_layout *kv, const int64_t *n_dev,
+                          int64_t window, float scale, float *out, int64_t ldo, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Workspace bytes gqa_decode_attn needs for this layout / window (0 on bad
+ * arguments). */
+size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_heads, int64_t window);
+
+/* ------------------------------------------------------------------ sampling
+ * argmax_rows: out[b] = index of the largest logits[b][v], lowest index on
+ *   ties ([GELO] 05: greedy sampler; [GEM] Native Metal diagnostic: equal
+ *   logits resolve deterministically by token id).  NaN never wins.
+ *   logits device fp32 [B][V]; out device int32 [B].
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_HIP. */
+q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int32_t *out, void *stream);
+
+/* ------------------------------------------------------------------ decode step
+ * One autoregressive decode step of a pre-norm decoder ([GELO] 06 Compute
+ * flow: per block RMSNorm -> merged QKV projection -> per-head QK-norm +
+ * RoPE -> cached GQA attention -> O projection + residual -> RMSNorm ->
+ * merged gate|up -> SwiGLU -> down projection + residual; tied Q8_0 logits;
+ * greedy choice), with the whole step captured once and replayed as a HIP
+ * graph ([GEM] Native Metal diagnostic: persistent buffers and whole-token
+ * command spans).  All weights and caches stay resident; the position lives
+ * in device memory so the same graph serves every step. */
+typedef struct {
+    const void *wqkv;        /* Q4_0 [(Hq + Hkv + (v_from_k ? 0 : Hkv)) * hd][d_model] */
+    const void *wo;          /* Q4_0 [d_model][Hq * hd] */
+    const void *wgu;         /* Q4_0 [2 * ffn][d_model]: gate rows, then up rows */
+    const void *wd;          /* Q4_0 [d_model][ffn] */
+    const float *attn_norm;  /* [d_model] */
+    const float *ffn_norm;   /* [d_model] */
+    const float *q_norm;     /* [hd] */
+    const float *k_norm;     /* [hd] */
+    float *k_cache;          /* [batch][Hkv][cap][hd], contiguous */
+    float *v_cache;          /* same layout */
+    int64_t n_kv_heads, head_dim, cap, window; /* window 0 = full attention */
+    double rope_theta;
+    float attn_scale;
+    int32_t v_from_k;        /* 1: no V rows in wqkv; V = unit-gain rmsnorm(raw K) */
+} q4_layer_desc;
+
+typedef struct {
+    int64_t n_layers, d_model, n_q_heads, ffn, vocab, batch; /* batch 1..8 */
+    float eps;
+    const void *embed;        /* Q8_0 [vocab][d_model], tied input/output table */
+    const float *final_norm;  /* [d_model] */
+    const q4_layer_desc *layers; /* host array [n_layers], copied at create */
+} q4_model_desc;
+
+typedef struct q4_decode_model q4_decode_model;
+
+/* Device workspace bytes decode_model_create needs (activations, attention
+ * partials, position counter). */
+q4_status decode_model_workspace(const q4_model_desc *desc, size_t *bytes);
+
+/* Validates the description, binds the caller's workspace (256-byte aligned,
+ * at least decode_model_workspace() bytes) and returns a host handle.  The
+ * position starts at 0.  Synchronises the device.
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE, Q4_ERR_ALIGNMENT,
+ *         Q4_ERR_UNSUPPORTED, Q4_ERR_WORKSPACE, Q4_ERR_HIP. */
+q4_status decode_model_create(const q4_model_desc *desc, void *ws, size_t ws_bytes,
+                              q4_decode_model **out);
+
+/* Sets the position of the next token (all sequences advance in lockstep).
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_CAPACITY (pos does not fit a linear
+ * cache), Q4_ERR_HIP. */
+q4_status decode_model_set_position(q4_decode_model *m, int64_t pos, void *stream);
+
+/* Current host-side view of the position of the next token. */
+int64_t decode_model_position(const q4_decode_model *m);
+
+/* Runs one step: tokens_dev (device int32 [batch]) are the current tokens;
+ * writes the greedy next tokens to next_tokens_dev (device int32 [batch],
+ * may equal tokens_dev) and, if logits_dev is not NULL, the logits (device
+ * fp32 [batch][vocab]); then advances the position by one.  The first call
+ * with a given (tokens, next, logits) pointer triple captures the graph;
+ * later calls replay it.
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_CAPACITY, Q4_ERR_HIP. */
+q4_status decode_step(q4_decode_model *m, const int32_t *tokens_dev, int32_t *next_tokens_dev,
+                      float *logits_dev, void *stream);
+
+/* Same step, launched kernel by kernel instead of through the graph (for
+ * debugging and for comparing the two).  Same arguments and errors. */
+q4_status decode_step_eager(q4_decode_model *m, const int32_t *tokens_dev,
+                            int32_t *next_tokens_dev, float *logits_dev, void *stream);
+
+/* Releases the host handle and its graphs (caller memory is untouched). */
+q4_status decode_model_destroy(q4_decode_model *m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4DEC_H */

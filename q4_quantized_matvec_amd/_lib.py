@@ -1,0 +1,289 @@
+"""ctypes view of libq4dec.so.  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4dec.so")
+
+STATUS = {
+    0: "Q4_OK", 1: "Q4_ERR_INVALID_ARG", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGNMENT",
+    4: "Q4_ERR_CAPACITY", 5: "Q4_ERR_WORKSPACE", 6: "Q4_ERR_UNSUPPORTED", 7: "Q4_ERR_HIP",
+}
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, name, status, msg):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{name}: {self.status_name}: {msg}")
+
+
+class KVLayout(C.Structure):
+    _fields_ = [("batch", C.c_int64), ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64),
+                ("cap", C.c_int64), ("stride_b", C.c_int64), ("stride_h", C.c_int64),
+                ("stride_t", C.c_int64)]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("wqkv", C.c_void_p), ("wo", C.c_void_p), ("wgu", C.c_void_p), ("wd", C.c_void_p),
+                ("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
+                ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64), ("cap", C.c_int64),
+                ("window", C.c_int64), ("rope_theta", C.c_double), ("attn_scale", C.c_float),
+                ("v_from_k", C.c_int32)]
+
+
+class ModelDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int64), ("d_model", C.c_int64), ("n_q_heads", C.c_int64),
+                ("ffn", C.c_int64), ("vocab", C.c_int64), ("batch", C.c_int64),
+                ("eps", C.c_float), ("embed", C.c_void_p), ("final_norm", C.c_void_p),
+                ("layers", C.POINTER(LayerDesc))]
+
+
+_P, _I64, _F, _D, _SZ = C.c_void_p, C.c_int64, C.c_float, C.c_double, C.c_size_t
+_SIGS = {
+    "q4dec_last_error": ([], C.c_char_p),
+    "q4dec_version": ([], C.c_char_p),
+    "q4_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
+    "q8_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
+    "q8_0_gather": ([_P, _I64, _I64, _P, _I64, _P, _P], C.c_int),
+    "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
+    "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
+    "qk_norm_rope": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D, _F,
+                      C.c_int, _P, _P, _P], C.c_int),
+    "gqa_decode_attn": ([_P, _I64, _I64, _P, _P, C.POINTER(KVLayout), _P, _I64, _F, _P, _I64,
+                         _P, _SZ, _P], C.c_int),
+    "gqa_decode_attn_workspace": ([C.POINTER(KVLayout), _I64, _I64], _SZ),
+    "argmax_rows": ([_P, _I64, _I64, _P, _P], C.c_int),
+    "decode_model_workspace": ([C.POINTER(ModelDesc), C.POINTER(_SZ)], C.c_int),
+    "decode_model_create": ([C.POINTER(ModelDesc), _P, _SZ, C.POINTER(_P)], C.c_int),
+    "decode_model_set_position": ([_P, _I64, _P], C.c_int),
+    "decode_model_position": ([_P], _I64),
+    "decode_step": ([_P, _P, _P, _P, _P], C.c_int),
+    "decode_step_eager": ([_P, _P, _P, _P, _P], C.c_int),
+    "decode_model_destroy": ([_P], C.c_int),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m q4_quantized_matvec_amd.build` (no CPU fallback exists)")
+        _lib = _Bound(C.CDLL(LIB_PATH))
+    return _lib
+
+
+class _Bound:
+    """Library wrapper that attaches the C signature to each symbol on first use."""
+
+    def __init__(self, cdll):
+        self._cdll = cdll
+
+    def __getattr__(self, name):
+        fn = getattr(self._cdll, name)  # AttributeError if the symbol is not exported
+        if name in _SIGS:
+            fn.argtypes, fn.restype = _SIGS[name]
+        setattr(self, name, fn)
+        return fn
+
+
+def version() -> str:
+    return lib().q4dec_version().decode()
+
+
+def _check(name, status):
+    if status != 0:
+        raise Q4Error(name, status, lib().q4dec_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _cuda_f32(t, name):
+    if t is None:
+        return
+    if not t.is_cuda or str(t.dtype) != "torch.float32":
+        raise TypeError(f"{name} must be a float32 CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _qmatrix_dims(W, K, bpb):
+    if not W.is_cuda or str(W.dtype) != "torch.uint8" or not W.is_contiguous():
+        raise TypeError("W must be a contiguous uint8 CUDA tensor")
+    row_bytes = K // 32 * bpb
+    if row_bytes == 0 or W.numel() % row_bytes:
+        raise ValueError("W size is not a whole number of rows")
+    return W.numel() // row_bytes
+
+
+def _matvec(name, bpb, W, x, y, residual, stream, n):
+    import torch
+    _cuda_f32(x, "x")
+    B, K = (1, x.numel()) if x.dim() == 1 else x.shape
+    N = n if n is not None else _qmatrix_dims(W, K, bpb)
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _cuda_f32(y, "y")
+    _cuda_f32(residual, "residual")
+    _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), B, _ptr(y), _ptr(residual),
+                                      _stream(stream)))
+    return y
+
+
+def q4_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
+    """y[B,N] = dequant(W) @ x[B,K] (+ residual).  W: uint8 [N, K/32*18] on device."""
+    return _matvec("q4_0_matvec", 18, W, x, y, residual, stream, n)
+
+
+def q8_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
+    """y[B,N] = dequant(W) @ x[B,K] (+ residual).  W: uint8 [N, K/32*34] on device."""
+    return _matvec("q8_0_matvec", 34, W, x, y, residual, stream, n)
+
+
+def q8_0_gather(E, tokens, K, x=None, stream=None):
+    import torch
+    V = _qmatrix_dims(E, K, 34)
+    B = tokens.numel()
+    if x is None:
+        x = torch.empty((B, K), dtype=torch.float32, device=tokens.device)
+    _check("q8_0_gather", lib().q8_0_gather(_ptr(E), V, K, _ptr(tokens), B, _ptr(x),
+                                            _stream(stream)))
+    return x
+
+
+def rmsnorm(x, w, eps, y=None, stream=None):
+    import torch
+    _cuda_f32(x, "x")
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    if y is None:
+        y = torch.empty_like(x)
+    _check("rmsnorm", lib().rmsnorm(_ptr(x), _ptr(w), rows, dim, eps, _ptr(y), _stream(stream)))
+    return y
+
+
+def swiglu(g, u, rows, n, ld, h=None, stream=None):
+    """h[rows, n] = silu(g) * u, g/u read with row stride ld (elements)."""
+    import torch
+    if h is None:
+        h = torch.empty((rows, n), dtype=torch.float32, device=g.device)
+    _check("swiglu", lib().swiglu(_ptr(g), _ptr(u), rows, n, ld, _ptr(h), _stream(stream)))
+    return h
+
+
+def kv_layout_of(cache):
+    """Layout of a contiguous fp32 cache tensor [B, Hkv, cap, hd]."""
+    B, H, cap, hd = cache.shape
+    s = cache.stride()
+    return KVLayout(B, H, hd, cap, s[0], s[1], s[2])
+
+
+def qk_norm_rope(q, ldq, k, v, ldkv, q_norm, k_norm, n_q_heads, kv, pos_dev, theta, eps,
+                 v_from_k, k_cache, v_cache, stream=None):
+    _check("qk_norm_rope", lib().qk_norm_rope(
+        _ptr(q), ldq, _ptr(k), _ptr(v), ldkv, _ptr(q_norm), _ptr(k_norm), n_q_heads,
+        C.byref(kv), _ptr(pos_dev), float(theta), float(eps), int(bool(v_from_k)),
+        _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+
+
+def gqa_decode_attn_workspace(kv, n_q_heads, window):
+    return lib().gqa_decode_attn_workspace(C.byref(kv), n_q_heads, window)
+
+
+def gqa_decode_attn(q, ldq, n_q_heads, k_cache, v_cache, kv, n_dev, window, scale, out, ldo,
+                    ws, stream=None):
+    _check("gqa_decode_attn", lib().gqa_decode_attn(
+        _ptr(q), ldq, n_q_heads, _ptr(k_cache), _ptr(v_cache), C.byref(kv), _ptr(n_dev),
+        int(window), float(scale), _ptr(out), ldo, _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def argmax_rows(logits, out=None, stream=None):
+    import torch
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check("argmax_rows", lib().argmax_rows(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+    return out
+
+
+class DecodeModel:
+    """Host handle of a resident decode model (weights/caches stay caller-owned).
+
+    ``layers``: list of dicts with device tensors wqkv, wo, wgu, wd, attn_norm,
+    ffn_norm, q_norm, k_norm, k_cache, v_cache and ints/floats n_kv_heads,
+    head_dim, window, rope_theta, attn_scale, v_from_k.
+    """
+
+    def __init__(self, *, d_model, n_q_heads, ffn, vocab, batch, eps, embed, final_norm,
+                 layers, device=None):
+        import torch
+        self._keep = [embed, final_norm]
+        arr = (LayerDesc * len(layers))()
+        for i, L in enumerate(layers):
+            d = arr[i]
+            for key in ("wqkv", "wo", "wgu", "wd", "attn_norm", "ffn_norm", "q_norm", "k_norm",
+                        "k_cache", "v_cache"):
+                setattr(d, key, _ptr(L[key]))
+                self._keep.append(L[key])
+            d.n_kv_heads = L["n_kv_heads"]
+            d.head_dim = L["head_dim"]
+            d.cap = L["k_cache"].shape[2]
+            d.window = L["window"]
+            d.rope_theta = L["rope_theta"]
+            d.attn_scale = L["attn_scale"]
+            d.v_from_k = 1 if L["v_from_k"] else 0
+        self._layers = arr
+        desc = ModelDesc(len(layers), d_model, n_q_heads, ffn, vocab, batch, eps, _ptr(embed),
+                         _ptr(final_norm), C.cast(arr, C.POINTER(LayerDesc)))
+        self._desc = desc
+        nbytes = C.c_size_t()
+        _check("decode_model_workspace", lib().decode_model_workspace(C.byref(desc),
+                                                                      C.byref(nbytes)))
+        dev = device or embed.device
+        self.workspace = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+        h = C.c_void_p()
+        _check("decode_model_create", lib().decode_model_create(
+            C.byref(desc), _ptr(self.workspace), nbytes.value, C.byref(h)))
+        self._h = h
+        self.batch, self.vocab = batch, vocab
+
+    def set_position(self, pos, stream=None):
+        _check("decode_model_set_position",
+               lib().decode_model_set_position(self._h, int(pos), _stream(stream)))
+
+    @property
+    def position(self):
+        return lib().decode_model_position(self._h)
+
+    def step(self, tokens, next_tokens, logits=None, stream=None, eager=False):
+        fn = lib().decode_step_eager if eager else lib().decode_step
+        _check("decode_step", fn(self._h, _ptr(tokens), _ptr(next_tokens), _ptr(logits),
+                                 _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().decode_model_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

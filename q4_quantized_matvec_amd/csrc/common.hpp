@@ -1,0 +1,99 @@
+// Internal helpers shared by the HIP sources of libq4dec (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+
+#include "q4dec.h"
+
+namespace q4 {
+
+// Records the message for q4dec_last_error() and returns the status.
+q4_status fail(q4_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+// Checks hipGetLastError() after a launch.
+q4_status launch_status(const char *what);
+// Compute units of the current device (cached per device).
+int device_cus();
+// Host validation of a KV-cache layout shared by the attention-side calls.
+q4_status check_kv_layout(const char *name, const q4_kv_layout *kv);
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace q4
+
+#define Q4_CHECK(cond, status, ...)                                                   \
+    do {                                                                              \
+        if (!(cond)) return ::q4::fail((status), __VA_ARGS__);                        \
+    } while (0)
+
+#define Q4_HIP_CHECK(call)                                                            \
+    do {                                                                              \
+        hipError_t e_ = (call);                                                       \
+        if (e_ != hipSuccess)                                                         \
+            return ::q4::fail(Q4_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// ------------------------------------------------------------------ device side
+namespace q4dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// 16 bytes with only 2-byte alignment: gfx950 serves these as one dwordx4.
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// acc + (low / high binary16 half of t) * x, the half widened exactly to fp32
+// (folds into v_fma_mix_f32).
+__device__ __forceinline__ float fma_lo(uint32_t t, float x, float acc) {
+    return __builtin_fmaf(static_cast<float>(__builtin_bit_cast(half2_t, t).x), x, acc);
+}
+__device__ __forceinline__ float fma_hi(uint32_t t, float x, float acc) {
+    return __builtin_fmaf(static_cast<float>(__builtin_bit_cast(half2_t, t).y), x, acc);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+// DPP quad permutes, half-row / row mirrors, then row broadcasts 15 and 31.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);        // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);       // row_half_mirror
+    v += dpp<0x140>(v);       // row_mirror: every lane holds its 16-lane row sum
+    v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// DPP move whose lanes without a valid source keep their own value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_keep(float v) {
+    int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the 64 lanes (all lanes must be active); every lane receives it.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_keep<0xB1>(v));
+    v = fmaxf(v, dpp_keep<0x4E>(v));
+    v = fmaxf(v, dpp_keep<0x141>(v));
+    v = fmaxf(v, dpp_keep<0x140>(v));
+    float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+    t = fmaxf(t, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31)));
+    t = fmaxf(t, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47)));
+    t = fmaxf(t, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63)));
+    return t;
+}
+
+}  // namespace q4dev

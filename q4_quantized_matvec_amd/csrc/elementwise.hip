@@ -1,0 +1,249 @@
+// RMSNorm, SwiGLU, per-head QK-norm + NeoX RoPE with KV-cache append, and the
+// greedy argmax, for gfx950.
+//
+// Definitions ("GELO LLM" page, 02 "Definitions & glossary" and 05
+// "Components"; "Research record" page, "Native Metal diagnostic"):
+//   rmsnorm  y = w * x / sqrt(mean(x^2) + eps)
+//   QK-norm  the same RMSNorm per head_dim slice with one shared gain, before RoPE
+//   RoPE     NeoX pairing (i, i + hd/2), angle pos * theta^(-2i/hd)
+//   SwiGLU   silu(g) * u
+//   argmax   greedy choice, lowest token id on equal logits
+#include "common.hpp"
+
+namespace {
+using namespace q4dev;
+
+constexpr int kWG = 256;
+
+// Sum over a 256-thread workgroup; every thread receives the total.
+__device__ __forceinline__ float block_sum(float v, float *lds4) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const float t = lds4[0] + lds4[1] + lds4[2] + lds4[3];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(kWG) void rmsnorm_kernel(const float *x, const float *__restrict__ w,
+                                                      float *y, int dim, float eps) {
+    __shared__ float red[4];
+    const float *xr = x + static_cast<size_t>(blockIdx.x) * dim;
+    float *yr = y + static_cast<size_t>(blockIdx.x) * dim;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < dim; i += kWG) ss = __builtin_fmaf(xr[i], xr[i], ss);
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(dim) + eps);
+    for (int i = threadIdx.x; i < dim; i += kWG) yr[i] = xr[i] * inv * (w ? w[i] : 1.0f);
+}
+
+__global__ __launch_bounds__(kWG) void swiglu_kernel(const float *g, const float *u, float *h,
+                                                     int64_t rows, int64_t n, int64_t ld) {
+    const int64_t total = rows * n;
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWG + threadIdx.x; t < total;
+         t += static_cast<int64_t>(gridDim.x) * kWG) {
+        const int64_t r = t / n, i = t % n;
+        const float gv = g[r * ld + i];
+        h[t] = gv / (1.0f + expf(-gv)) * u[r * ld + i];
+    }
+}
+
+// One wavefront per (sequence, head).  Heads [0, Hq) are query heads (written
+// back in place); heads [Hq, Hq + Hkv) are key heads whose rotated row (and the
+// value row) are appended to the caches at slot pos % cap.
+constexpr int kMaxPairsPerLane = 4;  // head_dim <= 512
+
+__global__ __launch_bounds__(64) void qk_norm_rope_kernel(
+    float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
+    const float *__restrict__ qn, const float *__restrict__ kn, int Hq, int hd,
+    const int64_t *__restrict__ pos_dev, double theta, float eps, int v_from_k,
+    float *kc, float *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st) {
+    const int b = blockIdx.y;
+    const int head = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int half = hd >> 1;
+    const bool is_q = head < Hq;
+    const int g = head - Hq;
+    const float *src = is_q ? q + b * ldq + static_cast<int64_t>(head) * hd
+                            : k + b * ldkv + static_cast<int64_t>(g) * hd;
+    const float *gain = is_q ? qn : kn;
+
+    float a[kMaxPairsPerLane], c[kMaxPairsPerLane];
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < kMaxPairsPerLane; ++p) {
+        const int i = lane + 64 * p;
+        a[p] = 0.f;
+        c[p] = 0.f;
+        if (i < half) {
+            a[p] = src[i];
+            c[p] = src[i + half];
+            ss = __builtin_fmaf(a[p], a[p], __builtin_fmaf(c[p], c[p], ss));
+        }
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(hd) + eps);
+    const int64_t pos = *pos_dev;
+
+    float *dst = nullptr;
+    float *vdst = nullptr;
+    if (is_q) {
+        dst = q + b * ldq + static_cast<int64_t>(head) * hd;
+    } else if (pos >= 0) {
+        const int64_t base = b * sb + g * sh + (pos % cap) * st;
+        dst = kc + base;
+        vdst = vc + base;
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxPairsPerLane; ++p) {
+        const int i = lane + 64 * p;
+        if (i < half) {
+            // angle in fp64, reduced by 2*pi before the sine and cosine
+            const double inv_freq = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(hd));
+            double ang = static_cast<double>(pos) * inv_freq;
+            const double two_pi = 6.283185307179586;
+            ang -= two_pi * rint(ang / two_pi);
+            double sd, cd;
+            sincos(ang, &sd, &cd);
+            const float sn = static_cast<float>(sd), cs = static_cast<float>(cd);
+            const float x0 = a[p] * inv * gain[i];
+            const float x1 = c[p] * inv * gain[i + half];
+            if (dst) {
+                dst[i] = x0 * cs - x1 * sn;
+                dst[i + half] = x1 * cs + x0 * sn;
+            }
+            if (vdst) {
+                if (v_from_k) {
+                    vdst[i] = a[p] * inv;
+                    vdst[i + half] = c[p] * inv;
+                } else {
+                    const float *vs = v + b * ldkv + static_cast<int64_t>(g) * hd;
+                    vdst[i] = vs[i];
+                    vdst[i + half] = vs[i + half];
+                }
+            }
+        }
+    }
+}
+
+// One workgroup per row; (value, index) with the lowest index among equal
+// maxima.  NaN never compares greater, so it never wins.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ logits,
+                                                      int32_t *out, int64_t V) {
+    __shared__ float sv[1024];
+    __shared__ int si[1024];
+    const float *row = logits + static_cast<int64_t>(blockIdx.x) * V;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int64_t i = threadIdx.x; i < V; i += 1024) {
+        const float v = row[i];
+        if (v > best || (v == best && i < bi)) {
+            best = v;
+            bi = static_cast<int>(i);
+        }
+    }
+    sv[threadIdx.x] = best;
+    si[threadIdx.x] = bi;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if (threadIdx.x < s) {
+            const float ov = sv[threadIdx.x + s];
+            const int oi = si[threadIdx.x + s];
+            if (ov > sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
+                sv[threadIdx.x] = ov;
+                si[threadIdx.x] = oi;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = si[0] == 0x7fffffff ? 0 : si[0];
+}
+
+}  // namespace
+
+extern "C" q4_status rmsnorm(const float *x, const float *w, int64_t rows, int64_t dim, float eps,
+                             float *y, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(x && y, Q4_ERR_INVALID_ARG, "rmsnorm: x and y must not be NULL");
+    Q4_CHECK(rows >= 1 && dim >= 1 && eps >= 0.f, Q4_ERR_INVALID_ARG,
+             "rmsnorm: rows, dim must be >= 1 and eps >= 0");
+    Q4_CHECK(rows <= (1 << 30) && dim <= (1 << 26), Q4_ERR_UNSUPPORTED, "rmsnorm: sizes too large");
+    Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!w || q4::aligned(w, 4)), Q4_ERR_ALIGNMENT,
+             "rmsnorm: x, w, y must be 4-byte aligned");
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(rows)), dim3(kWG), 0,
+                       q4::as_stream(stream), x, w, y, static_cast<int>(dim), eps);
+    return q4::launch_status("rmsnorm");
+}
+
+extern "C" q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld,
+                            float *h, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(g && u && h, Q4_ERR_INVALID_ARG, "swiglu: g, u and h must not be NULL");
+    Q4_CHECK(rows >= 1 && n >= 1 && ld >= n, Q4_ERR_INVALID_ARG,
+             "swiglu: rows, n must be >= 1 and ld >= n");
+    Q4_CHECK(q4::aligned(g, 4) && q4::aligned(u, 4) && q4::aligned(h, 4), Q4_ERR_ALIGNMENT,
+             "swiglu: g, u, h must be 4-byte aligned");
+    const int64_t total = rows * n;
+    const int64_t want = (total + kWG - 1) / kWG;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(want, 4096));
+    hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(kWG), 0, q4::as_stream(stream), g, u, h,
+                       rows, n, ld);
+    return q4::launch_status("swiglu");
+}
+
+namespace q4 {
+q4_status check_kv_layout(const char *name, const q4_kv_layout *kv) {
+    Q4_CHECK(kv, Q4_ERR_INVALID_ARG, "%s: kv layout must not be NULL", name);
+    Q4_CHECK(kv->batch >= 1 && kv->n_kv_heads >= 1 && kv->head_dim >= 2 && kv->cap >= 1,
+             Q4_ERR_INVALID_ARG, "%s: kv layout sizes must be positive", name);
+    Q4_CHECK(kv->stride_b >= 0 && kv->stride_h >= 0 && kv->stride_t >= kv->head_dim,
+             Q4_ERR_SHAPE, "%s: kv strides must be >= 0 and stride_t >= head_dim", name);
+    Q4_CHECK(kv->head_dim % 2 == 0, Q4_ERR_SHAPE, "%s: head_dim %lld is odd", name,
+             (long long)kv->head_dim);
+    Q4_CHECK(kv->head_dim <= 512, Q4_ERR_UNSUPPORTED, "%s: head_dim %lld > 512", name,
+             (long long)kv->head_dim);
+    Q4_CHECK(kv->batch <= 65535 && kv->n_kv_heads <= 4096, Q4_ERR_UNSUPPORTED,
+             "%s: batch or kv heads too large", name);
+    return Q4_OK;
+}
+}  // namespace q4
+
+extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v,
+                                  int64_t ldkv, const float *q_norm, const float *k_norm,
+                                  int64_t n_q_heads, const q4_kv_layout *kv,
+                                  const int64_t *pos_dev, double theta, float eps, int v_from_k,
+                                  float *k_cache, float *v_cache, void *stream) {
+    q4::clear_error();
+    q4_status st = q4::check_kv_layout("qk_norm_rope", kv);
+    if (st != Q4_OK) return st;
+    Q4_CHECK(q && k && q_norm && k_norm && pos_dev && k_cache && v_cache, Q4_ERR_INVALID_ARG,
+             "qk_norm_rope: q, k, q_norm, k_norm, pos_dev and the caches must not be NULL");
+    Q4_CHECK(v_from_k ? v == nullptr : v != nullptr, Q4_ERR_INVALID_ARG,
+             "qk_norm_rope: v must be NULL exactly when v_from_k is set");
+    Q4_CHECK(n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0, Q4_ERR_SHAPE,
+             "qk_norm_rope: n_q_heads %lld is not a multiple of n_kv_heads %lld",
+             (long long)n_q_heads, (long long)kv->n_kv_heads);
+    Q4_CHECK(ldq >= n_q_heads * kv->head_dim && ldkv >= kv->n_kv_heads * kv->head_dim,
+             Q4_ERR_SHAPE, "qk_norm_rope: row strides smaller than the rows");
+    Q4_CHECK(theta > 0.0 && eps >= 0.f, Q4_ERR_INVALID_ARG, "qk_norm_rope: theta > 0, eps >= 0");
+    Q4_CHECK(n_q_heads + kv->n_kv_heads <= 65535, Q4_ERR_UNSUPPORTED, "qk_norm_rope: too many heads");
+    dim3 grid(static_cast<unsigned>(n_q_heads + kv->n_kv_heads), static_cast<unsigned>(kv->batch));
+    hipLaunchKernelGGL(qk_norm_rope_kernel, grid, dim3(64), 0, q4::as_stream(stream), q, ldq, k, v,
+                       ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
+                       static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
+                       k_cache, v_cache, kv->cap, kv->stride_b, kv->stride_h, kv->stride_t);
+    return q4::launch_status("qk_norm_rope");
+}
+
+extern "C" q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int32_t *out,
+                                 void *stream) {
+    q4::clear_error();
+    Q4_CHECK(logits && out, Q4_ERR_INVALID_ARG, "argmax_rows: logits and out must not be NULL");
+    Q4_CHECK(B >= 1 && V >= 1, Q4_ERR_INVALID_ARG, "argmax_rows: B and V must be >= 1");
+    Q4_CHECK(V <= 0x7ffffffe && B <= (1 << 30), Q4_ERR_UNSUPPORTED, "argmax_rows: sizes too large");
+    Q4_CHECK(q4::aligned(logits, 4) && q4::aligned(out, 4), Q4_ERR_ALIGNMENT,
+             "argmax_rows: logits and out must be 4-byte aligned");
+    hipLaunchKernelGGL(argmax_kernel, dim3(static_cast<unsigned>(B)), dim3(1024), 0,
+                       q4::as_stream(stream), logits, out, V);
+    return q4::launch_status("argmax_rows");
+}

@@ -1,0 +1,473 @@
+// Q4_0 / Q8_0 dequant-matvec and the Q8_0 embedding gather for gfx950.
+//
+// Block formats (Research record, "Native Metal diagnostic: buffer ownership":
+// 18-byte Q4_0 blocks = binary16 scale + 16 payload bytes, weight =
+// (quant - 8) * scale; "Verified model facts": Q8_0 token table):
+//   Q4_0: [d:f16][16 code bytes]; byte j = element j (low) | element j+16 (high)
+//   Q8_0: [d:f16][32 int8 codes]
+//
+// Fast path (B = 1, K % 256 == 0): one wavefront walks a contiguous range of
+// output rows.  Lane l owns block columns l, l+64, ... of its K range and keeps
+// their 32 activations in VGPRs for the whole kernel, so activations are read
+// from memory once per wavefront and the weight bytes are the only stream.
+// Per row every lane issues one 16-byte load of its block's codes (the 2-byte
+// alignment is served by the hardware as a single dwordx4) plus the 2-byte
+// scale, one row ahead of the arithmetic.  Adjacent lanes read adjacent
+// blocks, so a wavefront's loads of one row cover 1152 contiguous bytes.
+//
+// Q4_0 arithmetic: each 4-bit code is moved into the low bits of a 16-bit lane
+// with a mask, which makes it the binary16 subnormal q * 2^-24.  v_fma_mix_f32
+// widens that half exactly and multiplies it with the fp32 activation, so
+// every product q * x is formed exactly in one FMA and no convert is needed:
+//   s = sum_j q_j x_j * 2^-24 ;  y += d * (s * 2^24 - 8 * sum_j x_j)
+// (the per-block sum of activations is computed once, at load time).
+//
+// Large K is split over the four wavefronts of a workgroup (2 or 4 parts)
+// whose partial sums meet in LDS and are added in a fixed order.
+#include "common.hpp"
+
+namespace {
+using namespace q4dev;
+
+constexpr int kWG = 256;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<0> {  // Q4_0
+    static constexpr int kBytes = 18;
+    static constexpr int kDwords = 4;
+};
+template <>
+struct Fmt<1> {  // Q8_0
+    static constexpr int kBytes = 34;
+    static constexpr int kDwords = 8;
+};
+
+// One row's raw words per owned column: the 4-byte-aligned window holding
+// the block (kDwords + 1 words) and the row's residual.
+template <int FMT, int JX>
+struct RowRegs {
+    uint32_t w[JX][Fmt<FMT>::kDwords + 1];
+    float res;  // residual of the row (read from a valid dummy address when there is none)
+};
+
+// Loads one row's blocks for the lane's columns.  Every load is issued
+// unconditionally (columns past the end are clamped to a real block and their
+// activations are zero), so the compiler can count outstanding loads exactly
+// and never has to drain the queue with vmcnt(0).
+//
+// A block starts at byte 18c (34c for Q8_0), i.e. at 0 or 2 mod 4.  Loads are
+// issued from the 4-byte-aligned address at or below the block start (2-byte
+// aligned 16-byte loads stream far slower than 4-byte aligned ones); the
+// words are re-aligned in registers by selectors that depend only on the
+// parity of the column, which is fixed per lane.
+template <int FMT, int JX>
+__device__ __forceinline__ void load_row(const uint8_t *wrow, const int (&col)[JX],
+                                         const float *resp, RowRegs<FMT, JX> &r) {
+    r.res = *resp;
+#pragma unroll
+    for (int j = 0; j < JX; ++j) {
+        const uint8_t *b = wrow + ((static_cast<size_t>(col[j]) * Fmt<FMT>::kBytes) & ~size_t(3));
+#pragma unroll
+        for (int h = 0; h < Fmt<FMT>::kDwords / 4; ++h) {
+            const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(b + 16 * h);
+            r.w[j][4 * h + 0] = v.x;
+            r.w[j][4 * h + 1] = v.y;
+            r.w[j][4 * h + 2] = v.z;
+            r.w[j][4 * h + 3] = v.w;
+        }
+        r.w[j][Fmt<FMT>::kDwords] = *reinterpret_cast<const uint32_t *>(b + 4 * Fmt<FMT>::kDwords);
+    }
+}
+
+// Blocks per K part when KS wavefronts split a row: rounded up to a multiple
+// of 8 so every part starts on an even column.
+__host__ __device__ inline int ks_part_blocks(int nb, int ks) { return ((nb + ks - 1) / ks + 7) / 8 * 8; }
+
+// Tunables of the B = 1 path (compile-time).
+#ifndef Q4_MV_PREFETCH
+#define Q4_MV_PREFETCH 2  // rows of loads in flight ahead of the row being reduced
+#endif
+#ifndef Q4_MV_PREFETCH_Q8
+#define Q4_MV_PREFETCH_Q8 1
+#endif
+#ifndef Q4_MV_X_LDS
+#define Q4_MV_X_LDS 1     // stage the activations through LDS once per workgroup
+#endif
+#ifndef Q4_MV_WG_PER_CU
+#define Q4_MV_WG_PER_CU 0 // 0: chosen from the register footprint
+#endif
+#ifndef Q4_MV_MIN_WAVES
+#define Q4_MV_MIN_WAVES 1 // occupancy hint (waves per SIMD) for the register allocator
+#endif
+
+constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
+
+// B = 1 fast path.  KS wavefronts of a workgroup split K; 4 / KS row groups;
+// PF rows of loads in flight per wavefront.
+template <int FMT, int JX, int KS, int PF>
+__global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
+                                                    const float *__restrict__ x, float *y,
+                                                    const float *res, int N, int K) {
+    constexpr int RG = 4 / KS;
+    constexpr int NBUF = PF + 1;
+    constexpr bool kXLds = Q4_MV_X_LDS && KS == 1;
+    __shared__ float red[4];
+    __shared__ float xs[kXLds ? kXLdsFloats : 1];
+    const int lane = threadIdx.x & 63;
+    // wave-uniform: keeps row addressing in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wave % KS;
+    const int rg = wave / KS;
+    const int nb = K >> 5;
+    const int nbw = ks_part_blocks(nb, KS);
+    const int c0 = ks * nbw;
+    const int c1 = min(nb, c0 + nbw);
+    const size_t row_bytes = static_cast<size_t>(nb) * Fmt<FMT>::kBytes;
+
+    // Contiguous row range of this row group (sizes differ by at most one).
+    const int G = gridDim.x * RG;
+    const int g = blockIdx.x * RG + rg;
+    const int q = N / G, r = N % G;
+    const int cnt = q + (g < r ? 1 : 0);
+    const int row0 = g * q + min(g, r);
+    const int iters = q + (r > 0 ? 1 : 0);  // same for every wavefront of the grid
+
+    bool valid[JX];
+    int col[JX];
+#pragma unroll
+    for (int j = 0; j < JX; ++j) {
+        const int c = c0 + lane + 64 * j;
+        valid[j] = c < c1;
+        col[j] = min(c, nb - 1);
+    }
+    // Byte offset of the block inside its aligned window: 0 for even columns,
+    // 2 for odd ones (c0 is a multiple of 8 and the clamp target nb - 1 is odd,
+    // so the parity of every owned column is the lane's parity).  v_perm_b32
+    // selectors: code word i = window bytes [off+2+4i, off+6+4i) out of the
+    // pair (w[i+1]:w[i]); scale = window bytes [off, off+2) zero-extended.
+    const bool odd = lane & 1;
+    const uint32_t sel_q = odd ? 0x07060504u : 0x05040302u;
+    const uint32_t sel_d = odd ? 0x0C0C0302u : 0x0C0C0100u;
+    // Q4_0: code bytes 4i, 4i+2 (sel_e) or 4i+1, 4i+3 (sel_o) of word i, each
+    // zero-extended into a 16-bit lane.
+    const uint32_t sel_e = odd ? 0x0C060C04u : 0x0C040C02u;
+    const uint32_t sel_o = odd ? 0x0C070C05u : 0x0C050C03u;
+
+    // Activations of the lane's block columns stay in registers.  With the
+    // whole K in one wavefront the workgroup stages x through LDS once.
+    if constexpr (kXLds) {
+        const float4 *xg = reinterpret_cast<const float4 *>(x);
+        float4 *xl = reinterpret_cast<float4 *>(xs);
+        for (int i = threadIdx.x; i < (K >> 2); i += kWG) xl[i] = xg[i];
+        __syncthreads();
+    }
+    float xr[JX][32];
+    float xc[JX];
+#pragma unroll
+    for (int j = 0; j < JX; ++j) {
+        const int c = c0 + lane + 64 * j;
+        float s = 0.f;
+        if (valid[j]) {
+            const float4 *xp = kXLds ? reinterpret_cast<const float4 *>(xs + c * 32)
+                                     : reinterpret_cast<const float4 *>(x + static_cast<size_t>(c) * 32);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = xp[i];
+                xr[j][4 * i + 0] = v.x;
+                xr[j][4 * i + 1] = v.y;
+                xr[j][4 * i + 2] = v.z;
+                xr[j][4 * i + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 32; ++i) s += xr[j][i];
+            if constexpr (FMT == 0) {
+#pragma unroll
+                for (int i = 16; i < 32; ++i) xr[j][i] *= 0.0625f;  // exact power-of-two scaling
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xr[j][i] = 0.f;
+        }
+        xc[j] = -8.f * s;
+    }
+
+    // Rows past this group's range are clamped to a real row (loaded, unused).
+    // Without a residual the residual slot reads x[0] and is ignored.
+    const bool has_res = res != nullptr;
+    auto fetch = [&](int it, RowRegs<FMT, JX> &r) {
+        const int row = min(row0 + it, N - 1);
+        load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
+    };
+    RowRegs<FMT, JX> buf[NBUF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
+
+    auto process = [&](int it, const RowRegs<FMT, JX> &cur) {
+        const bool act = it < cnt;
+        float acc = 0.f;
+        if (act) {
+            // 2*JX independent FMA chains (blocks interleaved, low/high code
+            // halves apart) so dependent-issue latency stays hidden.
+            float sa[JX], sb[JX];
+#pragma unroll
+            for (int j = 0; j < JX; ++j) sa[j] = sb[j] = 0.f;
+            if constexpr (FMT == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int j = 0; j < JX; ++j) {
+                        // e = code bytes (4i, 4i+2), o = (4i+1, 4i+3), one per 16-bit
+                        // lane.  Low nibbles -> binary16 subnormals q * 2^-24; high
+                        // nibbles stay in bits 4..7 (16 q * 2^-24) and meet
+                        // activations pre-scaled by 1/16 (exact).
+                        const uint32_t e = __builtin_amdgcn_perm(cur.w[j][i + 1], cur.w[j][i], sel_e);
+                        const uint32_t o = __builtin_amdgcn_perm(cur.w[j][i + 1], cur.w[j][i], sel_o);
+                        const uint32_t le = e & 0x000F000Fu, he = e & 0x00F000F0u;
+                        const uint32_t lo = o & 0x000F000Fu, ho = o & 0x00F000F0u;
+                        sa[j] = fma_lo(le, xr[j][4 * i + 0], sa[j]);
+                        sb[j] = fma_lo(he, xr[j][16 + 4 * i + 0], sb[j]);
+                        sa[j] = fma_lo(lo, xr[j][4 * i + 1], sa[j]);
+                        sb[j] = fma_lo(ho, xr[j][16 + 4 * i + 1], sb[j]);
+                        sa[j] = fma_hi(le, xr[j][4 * i + 2], sa[j]);
+                        sb[j] = fma_hi(he, xr[j][16 + 4 * i + 2], sb[j]);
+                        sa[j] = fma_hi(lo, xr[j][4 * i + 3], sa[j]);
+                        sb[j] = fma_hi(ho, xr[j][16 + 4 * i + 3], sb[j]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < JX; ++j) {
+                    const float d = half_bits_to_float(__builtin_amdgcn_perm(0u, cur.w[j][0], sel_d));
+                    const float t = __builtin_fmaf(d, __builtin_fmaf(sa[j] + sb[j], 16777216.f, xc[j]), acc);
+                    acc = valid[j] ? t : acc;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                    for (int j = 0; j < JX; ++j) {
+                        const uint32_t w = __builtin_amdgcn_perm(cur.w[j][i + 1], cur.w[j][i], sel_q);
+                        sa[j] = __builtin_fmaf(static_cast<float>(static_cast<int8_t>(w)), xr[j][4 * i + 0], sa[j]);
+                        sb[j] = __builtin_fmaf(static_cast<float>(static_cast<int8_t>(w >> 8)), xr[j][4 * i + 1], sb[j]);
+                        sa[j] = __builtin_fmaf(static_cast<float>(static_cast<int8_t>(w >> 16)), xr[j][4 * i + 2], sa[j]);
+                        sb[j] = __builtin_fmaf(static_cast<float>(static_cast<int8_t>(w >> 24)), xr[j][4 * i + 3], sb[j]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < JX; ++j) {
+                    const float d = half_bits_to_float(__builtin_amdgcn_perm(0u, cur.w[j][0], sel_d));
+                    const float t = __builtin_fmaf(d, sa[j] + sb[j], acc);
+                    acc = valid[j] ? t : acc;
+                }
+            }
+        }
+        acc = wave_sum(acc);
+        const int row = row0 + it;
+        if constexpr (KS == 1) {
+            if (act && lane == 0) y[row] = has_res ? acc + cur.res : acc;
+        } else {
+            if (lane == 0) red[wave] = acc;
+            __syncthreads();
+            if (ks == 0 && act && lane == 0) {
+                float s = red[rg * KS];
+#pragma unroll
+                for (int k = 1; k < KS; ++k) s += red[rg * KS + k];
+                y[row] = has_res ? s + cur.res : s;
+            }
+            __syncthreads();
+        }
+    };
+
+    // Ring of NBUF register sets: row it lives in buf[it % NBUF]; the loads of
+    // row it + PF are issued before row it is reduced.  The unrolled body keeps
+    // every buffer index a compile-time constant and has no branch around a
+    // load; the tail issues no loads.
+    int it0 = 0;
+    for (; it0 + NBUF <= iters; it0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            fetch(it0 + u + PF, buf[(u + PF) % NBUF]);
+            process(it0 + u, buf[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u)
+        if (it0 + u < iters) process(it0 + u, buf[u]);
+}
+
+// Generic path: any K % 32 == 0, 1 <= B <= 8, scale/codes read as 16-bit words.
+template <int FMT, int B>
+__global__ __launch_bounds__(kWG) void mv_generic_kernel(const uint8_t *__restrict__ W,
+                                                         const float *__restrict__ x, float *y,
+                                                         const float *res, int N, int K) {
+    const int lane = threadIdx.x & 63;
+    const int nb = K >> 5;
+    const size_t row_bytes = static_cast<size_t>(nb) * Fmt<FMT>::kBytes;
+    const int waves = gridDim.x * (kWG / 64);
+    for (int row = blockIdx.x * (kWG / 64) + (threadIdx.x >> 6); row < N; row += waves) {
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+        for (int c = lane; c < nb; c += 64) {
+            const uint16_t *h = reinterpret_cast<const uint16_t *>(W + row * row_bytes +
+                                                                   static_cast<size_t>(c) * Fmt<FMT>::kBytes);
+            const float d = half_bits_to_float(h[0]);
+            float w[32];
+            if constexpr (FMT == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t v = h[1 + j];  // code bytes 2j (low 8 bits) and 2j+1
+                    w[2 * j] = static_cast<float>(static_cast<int>(v & 15u) - 8);
+                    w[2 * j + 16] = static_cast<float>(static_cast<int>((v >> 4) & 15u) - 8);
+                    w[2 * j + 1] = static_cast<float>(static_cast<int>((v >> 8) & 15u) - 8);
+                    w[2 * j + 17] = static_cast<float>(static_cast<int>((v >> 12) & 15u) - 8);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t v = h[1 + j];
+                    w[2 * j] = static_cast<float>(static_cast<int8_t>(v & 0xFFu));
+                    w[2 * j + 1] = static_cast<float>(static_cast<int8_t>(v >> 8));
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float *xb = x + static_cast<size_t>(b) * K + static_cast<size_t>(c) * 32;
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) s = __builtin_fmaf(w[i], xb[i], s);
+                acc[b] = __builtin_fmaf(d, s, acc[b]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float t = wave_sum(acc[b]);
+            if (lane == 0) {
+                const size_t o = static_cast<size_t>(b) * N + row;
+                y[o] = t + (res ? res[o] : 0.f);
+            }
+        }
+    }
+}
+
+// x[b][:] = dequantised row tokens[b] of a Q8_0 table; one thread per block.
+__global__ __launch_bounds__(kWG) void q8_gather_kernel(const uint8_t *__restrict__ E,
+                                                        const int32_t *__restrict__ tok,
+                                                        float *__restrict__ x, int V, int K,
+                                                        int B) {
+    const int nb = K >> 5;
+    const int t = blockIdx.x * kWG + threadIdx.x;
+    if (t >= B * nb) return;
+    const int b = t / nb, c = t % nb;
+    const int id = tok[b];
+    float *out = x + static_cast<size_t>(b) * K + static_cast<size_t>(c) * 32;
+    if (id < 0 || id >= V) {
+        for (int i = 0; i < 32; ++i) out[i] = __builtin_nanf("");
+        return;
+    }
+    const uint8_t *blk = E + (static_cast<size_t>(id) * nb + c) * 34;
+    const float d = half_bits_to_float(*reinterpret_cast<const uint16_t *>(blk));
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(blk + 2);
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t v = h[j];
+        out[2 * j] = d * static_cast<float>(static_cast<int8_t>(v & 0xFFu));
+        out[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(v >> 8));
+    }
+}
+
+template <int FMT, int JX, int KS>
+void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int N, int K,
+               hipStream_t s) {
+    constexpr int PF = FMT == 0 ? Q4_MV_PREFETCH : Q4_MV_PREFETCH_Q8;
+    constexpr int RG = 4 / KS;
+    const int want = (N + RG - 1) / RG;
+    const int per_cu = Q4_MV_WG_PER_CU ? Q4_MV_WG_PER_CU : (JX <= 2 ? 3 : 2);
+    const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
+    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF>), dim3(nwg), dim3(kWG), 0, s, W, x, y, res, N, K);
+}
+
+template <int FMT, int KS>
+void launch_b1_jx(int jx, const uint8_t *W, const float *x, float *y, const float *res, int N,
+                  int K, hipStream_t s) {
+    switch (jx) {
+        case 1: launch_b1<FMT, 1, KS>(W, x, y, res, N, K, s); break;
+        case 2: launch_b1<FMT, 2, KS>(W, x, y, res, N, K, s); break;
+        case 3: launch_b1<FMT, 3, KS>(W, x, y, res, N, K, s); break;
+        default: launch_b1<FMT, 4, KS>(W, x, y, res, N, K, s); break;
+    }
+}
+
+template <int FMT>
+void launch_generic(int B, const uint8_t *W, const float *x, float *y, const float *res, int N,
+                    int K, hipStream_t s) {
+    const int nwg = std::max(1, std::min((N + 3) / 4, 4 * q4::device_cus()));
+    switch (B) {
+#define Q4_CASE(BB) \
+    case BB: hipLaunchKernelGGL((mv_generic_kernel<FMT, BB>), dim3(nwg), dim3(kWG), 0, s, W, x, y, res, N, K); break;
+        Q4_CASE(1) Q4_CASE(2) Q4_CASE(3) Q4_CASE(4) Q4_CASE(5) Q4_CASE(6) Q4_CASE(7) Q4_CASE(8)
+#undef Q4_CASE
+    }
+}
+
+template <int FMT>
+q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
+                       int64_t B, float *y, const float *res, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
+    Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
+             name, (long long)N, (long long)K, (long long)B);
+    Q4_CHECK(K % 32 == 0, Q4_ERR_SHAPE, "%s: K=%lld is not a multiple of 32", name, (long long)K);
+    Q4_CHECK(B <= 8, Q4_ERR_UNSUPPORTED, "%s: B=%lld > 8", name, (long long)B);
+    Q4_CHECK(N <= (1 << 30) && K <= (1 << 24), Q4_ERR_UNSUPPORTED, "%s: N or K too large", name);
+    Q4_CHECK(q4::aligned(Wv, 2), Q4_ERR_ALIGNMENT, "%s: W must be 2-byte aligned", name);
+    Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!res || q4::aligned(res, 4)),
+             Q4_ERR_ALIGNMENT, "%s: x, y and residual must be 4-byte aligned", name);
+    const uint8_t *W = static_cast<const uint8_t *>(Wv);
+    hipStream_t s = q4::as_stream(stream);
+    const int n = static_cast<int>(N), k = static_cast<int>(K);
+    const int nb = k / 32;
+    int ks = 0;
+    if (B == 1 && K % 256 == 0 && q4::aligned(x, 16)) {
+        for (int cand : {1, 2, 4})
+            if (ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
+    }
+    if (ks) {
+        const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
+        if (ks == 1) launch_b1_jx<FMT, 1>(jx, W, x, y, res, n, k, s);
+        else if (ks == 2) launch_b1_jx<FMT, 2>(jx, W, x, y, res, n, k, s);
+        else launch_b1_jx<FMT, 4>(jx, W, x, y, res, n, k, s);
+    } else {
+        launch_generic<FMT>(static_cast<int>(B), W, x, y, res, n, k, s);
+    }
+    return q4::launch_status(name);
+}
+
+}  // namespace
+
+extern "C" q4_status q4_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
+                                 float *y, const float *residual, void *stream) {
+    return matvec_entry<0>("q4_0_matvec", W, N, K, x, B, y, residual, stream);
+}
+
+extern "C" q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
+                                 float *y, const float *residual, void *stream) {
+    return matvec_entry<1>("q8_0_matvec", W, N, K, x, B, y, residual, stream);
+}
+
+extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens,
+                                 int64_t B, float *x, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(E && tokens && x, Q4_ERR_INVALID_ARG, "q8_0_gather: E, tokens and x must not be NULL");
+    Q4_CHECK(V >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "q8_0_gather: V, K, B must be >= 1");
+    Q4_CHECK(K % 32 == 0, Q4_ERR_SHAPE, "q8_0_gather: K=%lld is not a multiple of 32", (long long)K);
+    Q4_CHECK(V <= (1 << 30) && K <= (1 << 24) && B <= (1 << 20), Q4_ERR_UNSUPPORTED,
+             "q8_0_gather: sizes too large");
+    Q4_CHECK(q4::aligned(E, 2) && q4::aligned(tokens, 4) && q4::aligned(x, 4), Q4_ERR_ALIGNMENT,
+             "q8_0_gather: E must be 2-byte, tokens and x 4-byte aligned");
+    const int total = static_cast<int>(B) * static_cast<int>(K / 32);
+    hipLaunchKernelGGL(q8_gather_kernel, dim3((total + kWG - 1) / kWG), dim3(kWG), 0,
+                       q4::as_stream(stream), static_cast<const uint8_t *>(E), tokens, x,
+                       static_cast<int>(V), static_cast<int>(K), static_cast<int>(B));
+    return q4::launch_status("q8_0_gather");
+}

@@ -1,0 +1,57 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import q4_quantized_matvec_amd as q
+from q4_quantized_matvec_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "q4dec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_parsed():
+    names = declared_functions()
+    for must in ("q4_0_matvec", "q8_0_matvec", "rmsnorm", "qk_norm_rope", "gqa_decode_attn",
+                 "swiglu", "decode_step", "argmax_rows", "q8_0_gather"):
+        assert must in names
+
+
+def test_exports_every_declared_symbol():
+    cdll = C.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(cdll, n)]
+    assert not missing, f"not exported: {missing}"
+    assert set(declared_functions()) <= set(_lib._SIGS)
+
+
+def test_version_string():
+    assert "gfx950" in q.version()
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return _lib.STATUS[st], q.lib().q4dec_last_error().decode()
+
+
+def test_matvec_rejects_bad_arguments_on_host():
+    L = q.lib()
+    fake = 0x1000  # never dereferenced: validation fails first
+    assert _status(L.q4_0_matvec, None, 4, 32, fake, 1, fake, None, None)[0] == "Q4_ERR_INVALID_ARG"
+    assert _status(L.q4_0_matvec, fake, 0, 32, fake, 1, fake, None, None)[0] == "Q4_ERR_INVALID_ARG"
+    assert _status(L.q4_0_matvec, fake, 4, 48, fake, 1, fake, None, None)[0] == "Q4_ERR_SHAPE"
+    assert _status(L.q4_0_matvec, fake, 4, 32, fake, 9, fake, None, None)[0] == "Q4_ERR_UNSUPPORTED"
+    assert _status(L.q4_0_matvec, fake + 1, 4, 32, fake, 1, fake, None, None)[0] == "Q4_ERR_ALIGNMENT"
+    st, msg = _status(L.q8_0_matvec, fake, 4, 32, fake + 2, 1, fake, None, None)
+    assert st == "Q4_ERR_ALIGNMENT" and "aligned" in msg
+    assert _status(L.q8_0_gather, fake, 10, 33, fake, 1, fake, None)[0] == "Q4_ERR_SHAPE"
+    assert _status(L.q8_0_gather, None, 10, 32, fake, 1, fake, None)[0] == "Q4_ERR_INVALID_ARG"

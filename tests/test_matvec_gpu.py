@@ -1,0 +1,129 @@
+"""GPU parity of the Q4_0 / Q8_0 matvec and the Q8_0 gather against the oracle.
+
+Bar: |gpu - oracle| <= 2e-4 * sum_k |w_k x_k| (+ |residual|) + 1e-6 per output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q4_quantized_matvec_amd as q
+import synth
+from synth import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check(y, ref, terms, what):
+    y = y.detach().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    err = np.abs(y - ref)
+    tol = 2e-4 * terms + 1e-6
+    ratio = float((err / tol).max())
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    assert ratio <= 1.0, f"{what}: max err/tol {ratio:.3e}"
+    return ratio
+
+
+CASES_Q4 = [
+    # (N, K, B): fast path (B=1, K%256==0) incl. every register/K-split variant,
+    # ragged row tails, and the generic path (K%256 != 0 or B > 1)
+    (67, 256, 1), (1, 256, 1), (5, 2048, 1), (1000, 2048, 1), (777, 5376, 1), (300, 8192, 1),
+    (200, 16384, 1), (130, 21504, 1), (257, 2560, 1), (99, 9728, 1),
+    (67, 32, 1), (67, 288, 3), (33, 256, 8), (100, 2560, 8), (64, 5376, 2), (50, 9728, 4),
+]
+
+
+@pytest.mark.parametrize("n,k,b", CASES_Q4)
+def test_q4_0_matvec_parity(dev, n, k, b):
+    _say(f"q4_0_matvec N={n} K={k} B={b}")
+    W = synth.q4_0_matrix(101, f"t.q4.{n}.{k}", n, k)
+    x = synth.normal_f32(101, f"t.q4x.{n}.{k}.{b}", (b, k))
+    ref, terms = oracle.q4_0_matvec(W, n, k, x)
+    y = q.q4_0_matvec(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev))
+    torch.cuda.synchronize()
+    _check(y, ref, terms, f"q4 {n}x{k} B={b}")
+
+
+@pytest.mark.parametrize("n,k,b", [(67, 256, 1), (1000, 2560, 1), (500, 5376, 1),
+                                   (100, 2560, 8), (31, 32, 1), (300, 21504, 1), (40, 288, 5)])
+def test_q8_0_matvec_parity(dev, n, k, b):
+    _say(f"q8_0_matvec N={n} K={k} B={b}")
+    W = synth.q8_0_matrix(102, f"t.q8.{n}.{k}", n, k)
+    x = synth.normal_f32(102, f"t.q8x.{n}.{k}.{b}", (b, k))
+    ref, terms = oracle.q8_0_matvec(W, n, k, x)
+    y = q.q8_0_matvec(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev))
+    torch.cuda.synchronize()
+    _check(y, ref, terms, f"q8 {n}x{k} B={b}")
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("b", [1, 3])
+def test_matvec_residual_in_place(dev, fmt, b):
+    _say(f"{fmt} residual in place B={b}")
+    n, k = 513, 2048
+    gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
+    orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
+    fn = q.q4_0_matvec if fmt == "q4" else q.q8_0_matvec
+    W = gen(103, f"t.res.{fmt}", n, k)
+    x = synth.normal_f32(103, f"t.resx.{b}", (b, k))
+    r = synth.normal_f32(103, f"t.resr.{b}", (b, n))
+    ref, terms = orc(W, n, k, x, res=r)
+    yr = torch.from_numpy(r).to(dev)
+    fn(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev), y=yr, residual=yr)
+    torch.cuda.synchronize()
+    _check(yr, ref, terms, f"{fmt} residual alias")
+
+
+@pytest.mark.parametrize("b", [1, 8])
+def test_matvec_5376x21504_full(dev, b):
+    """The 31B FFN-shape workload, every output, in the launch configuration the
+    benchmark times."""
+    _say(f"q4_0_matvec 5376x21504 B={b} full")
+    w = wl.MATVEC_5376x21504
+    W, x = wl.matvec_inputs(w, b)
+    ref, terms = oracle.q4_0_matvec(W, w.n, w.k, x)
+    Wd = torch.from_numpy(W).to(dev)
+    xd = torch.from_numpy(x).to(dev)
+    y1 = q.q4_0_matvec(Wd, xd)
+    y2 = q.q4_0_matvec(Wd, xd)
+    torch.cuda.synchronize()
+    _check(y1, ref, terms, f"5376x21504 B={b}")
+    assert torch.equal(y1, y2), "repeated launches differ bitwise"
+
+
+def test_matvec_2048x6144_full(dev):
+    _say("q4_0_matvec 2048x6144 B=1 full")
+    w = wl.MATVEC_2048x6144
+    W, x = wl.matvec_inputs(w, 1)
+    ref, terms = oracle.q4_0_matvec(W, w.n, w.k, x)
+    y = q.q4_0_matvec(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev))
+    torch.cuda.synchronize()
+    _check(y, ref, terms, "2048x6144")
+
+
+def test_q8_0_gather_parity(dev):
+    _say("q8_0_gather")
+    v, k = 1000, 2560
+    E = synth.q8_0_matrix(104, "t.gather", v, k)
+    tok = np.array([0, 999, 17, 17, 512], dtype=np.int32)
+    ref = oracle.q8_0_gather(E, v, k, tok)
+    x = q.q8_0_gather(torch.from_numpy(E).to(dev), torch.from_numpy(tok).to(dev), k)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().astype(np.float64)
+    # d * q is exact in fp32 (11-bit scale times 8-bit code)
+    assert np.array_equal(got, ref)
+
+
+def test_q8_0_gather_out_of_range_token_gives_nan(dev):
+    _say("q8_0_gather out-of-range")
+    v, k = 50, 64
+    E = synth.q8_0_matrix(105, "t.gather2", v, k)
+    tok = torch.tensor([3, -1, 50], dtype=torch.int32, device=dev)
+    x = q.q8_0_gather(torch.from_numpy(E).to(dev), tok, k)
+    torch.cuda.synchronize()
+    x = x.cpu().numpy()
+    assert np.all(np.isfinite(x[0])) and np.all(np.isnan(x[1])) and np.all(np.isnan(x[2]))
