@@ -1,0 +1,314 @@
+// Split-K grouped-query decode attention over an fp32 KV cache, gfx950.
+//
+// Definition ("GELO LLM" page, 05 "Components": cached GQA attention where a
+// decode step's single query row attends every cached position plus the new
+// one; 02 "Definitions & glossary": several query heads share one K/V head; a
+// sliding-window layer attends only the last W tokens):
+//   o_h = sum_j softmax_j(scale * q_h . k_j) v_j ,  j in [lo, n),
+//   lo = max(0, n - W) (W = 0: lo = 0), kv head of query head h = h / G.
+//
+// Pass 1 (one workgroup per (chunk, kv head, sequence)): the G query heads
+// that share the kv head are held in VGPRs (pre-scaled), the chunk's keys are
+// read once for all of them, an exact softmax over the chunk gives (m, l) and
+// the un-normalised sum_j e^(s_j - m) v_j is formed with the same weights for
+// every query head.  Pass 2 merges the chunks of each query head in ascending
+// chunk order: o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the
+// non-empty chunks, M = max m_c, so the result does not depend on scheduling.
+#include "common.hpp"
+
+namespace {
+using namespace q4dev;
+
+constexpr int kWG = 256;
+constexpr int kMaxChunk = 256;
+
+struct AttnGeom {
+    int G;      // query heads per kv head
+    int chunk;  // positions per chunk
+    int nch;    // chunks per (sequence, kv head)
+};
+
+// Chunking depends only on the layout and window (never on n), so the
+// workspace size and the captured launch stay valid as n grows.
+AttnGeom attn_geom(const q4_kv_layout &kv, int64_t n_q_heads, int64_t window) {
+    AttnGeom g;
+    g.G = static_cast<int>(n_q_heads / kv.n_kv_heads);
+    const int64_t maxvis = window > 0 ? std::min<int64_t>(window, kv.cap) : kv.cap;
+    const int64_t per_head = std::max<int64_t>(1, 2048 / (kv.batch * kv.n_kv_heads));
+    int64_t ch = (maxvis + per_head - 1) / per_head;
+    ch = (ch + 31) / 32 * 32;
+    ch = std::max<int64_t>(64, std::min<int64_t>(kMaxChunk, ch));
+    g.chunk = static_cast<int>(ch);
+    g.nch = static_cast<int>((maxvis + ch - 1) / ch);
+    return g;
+}
+
+size_t attn_ws_bytes(const q4_kv_layout &kv, const AttnGeom &g) {
+    const size_t units = static_cast<size_t>(kv.batch) * kv.n_kv_heads * g.nch * g.G;
+    return units * (static_cast<size_t>(kv.head_dim) + 2) * sizeof(float);
+}
+
+// Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
+// group receives its group's total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<0xB1>(v);   // xor 1
+    v += dpp<0x4E>(v);   // xor 2
+    v += dpp<0x141>(v);  // half-row mirror: groups of 8
+    if constexpr (L >= 16) v += dpp<0x140>(v);  // row mirror: groups of 16
+    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int HD, int GM>
+__global__ __launch_bounds__(kWG) void attn_split_kernel(
+    const float *__restrict__ q, int64_t ldq, int G, const float *__restrict__ kc,
+    const float *__restrict__ vc, int64_t cap, int64_t sb, int64_t sh, int64_t st,
+    const int64_t *__restrict__ n_dev, int64_t window, float scale, int chunk, int nch,
+    float *__restrict__ part) {
+    constexpr int LPK = HD / 8;         // lanes per key in the score pass
+    constexpr int KPW = 64 / LPK;       // keys per wavefront per step
+    constexpr int DPT = HD > kWG ? HD / kWG : 1;  // dims per thread in the value pass
+    constexpr int KG = HD < kWG ? kWG / HD : 1;   // key groups in the value pass
+    __shared__ float sc[kMaxChunk * GM];          // scores, then weights: [pos][g]
+    __shared__ float red[KG > 1 ? kWG * GM : 1];  // value-pass partials of extra key groups
+
+    const int c = blockIdx.x, g0 = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n = *n_dev;
+    int64_t lo = window > 0 ? n - window : 0;
+    lo = max(lo, n - cap);
+    lo = max(lo, int64_t(0));
+    const int64_t p0 = lo + static_cast<int64_t>(c) * chunk;
+    const int cnt = static_cast<int>(max(int64_t(0), min(int64_t(chunk), n - p0)));
+
+    const size_t unit = ((static_cast<size_t>(b) * gridDim.y + g0) * nch + c) * GM;
+    float *po = part + unit * HD;                                   // [G][HD] (unit stride GM rows)
+    float *pml = part + static_cast<size_t>(gridDim.z) * gridDim.y * nch * GM * HD + unit * 2;
+    if (cnt == 0) {
+        if (threadIdx.x < G) {
+            pml[2 * threadIdx.x] = -INFINITY;
+            pml[2 * threadIdx.x + 1] = 0.f;
+        }
+        return;
+    }
+    const float *kb = kc + b * sb + g0 * sh;
+    const float *vb = vc + b * sb + g0 * sh;
+
+    // ---- scores: LPK lanes per key, 8 consecutive elements per lane
+    const int sub = lane % LPK, kgl = lane / LPK;
+    float qv[GM][8];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        const float *qh = q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][e] = g < G ? qh[e] * scale : 0.f;
+    }
+    for (int base = 0; base < cnt; base += 4 * KPW) {
+        const int jj = base + wave * KPW + kgl;
+        float kr[8];
+        if (jj < cnt) {
+            const float4 *kp = reinterpret_cast<const float4 *>(kb + ((p0 + jj) % cap) * st + sub * 8);
+            const float4 a = kp[0], bq = kp[1];
+            kr[0] = a.x; kr[1] = a.y; kr[2] = a.z; kr[3] = a.w;
+            kr[4] = bq.x; kr[5] = bq.y; kr[6] = bq.z; kr[7] = bq.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kr[e] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[g][e], kr[e], s);
+            s = group_sum<LPK>(s);
+            if (sub == 0 && jj < cnt && g < G) sc[jj * GM + g] = s;
+        }
+    }
+    __syncthreads();
+
+    // ---- exact softmax over the chunk: one wavefront per query head
+    for (int g = wave; g < G; g += 4) {
+        float m = -INFINITY;
+        for (int j = lane; j < cnt; j += 64) m = fmaxf(m, sc[j * GM + g]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int j = lane; j < cnt; j += 64) {
+            const float e = __expf(sc[j * GM + g] - m);
+            sc[j * GM + g] = e;
+            l += e;
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            pml[2 * g] = m;
+            pml[2 * g + 1] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- weighted values: threads over head dims, KG key groups
+    const int kg = threadIdx.x / (KG > 1 ? HD : kWG);
+    const int d0 = threadIdx.x % (KG > 1 ? HD : kWG);
+    float acc[GM][DPT];
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int t = 0; t < DPT; ++t) acc[g][t] = 0.f;
+    for (int j = kg; j < cnt; j += KG) {
+        const float *vr = vb + ((p0 + j) % cap) * st;
+        float vv[DPT];
+#pragma unroll
+        for (int t = 0; t < DPT; ++t) vv[t] = vr[d0 + t * kWG];
+        float w[GM];
+        if constexpr (GM % 4 == 0) {
+#pragma unroll
+            for (int g = 0; g < GM; g += 4) {
+                const float4 p4 = *reinterpret_cast<const float4 *>(&sc[j * GM + g]);
+                w[g] = p4.x; w[g + 1] = p4.y; w[g + 2] = p4.z; w[g + 3] = p4.w;
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) w[g] = sc[j * GM + g];
+        }
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int t = 0; t < DPT; ++t) acc[g][t] = __builtin_fmaf(w[g], vv[t], acc[g][t]);
+    }
+    if constexpr (KG > 1) {
+        if (kg > 0) {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) red[(kg * GM + g) * HD + d0] = acc[g][0];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                float s = acc[g][0];
+                for (int k = 1; k < KG; ++k) s += red[(k * GM + g) * HD + d0];  // fixed order
+                if (g < G) po[g * HD + d0] = s;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int t = 0; t < DPT; ++t)
+                if (g < G) po[g * HD + d0 + t * kWG] = acc[g][t];
+    }
+}
+
+// One workgroup per (query head, sequence): merges the chunks in order.
+__global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict__ part, int G,
+                                                         int Hkv, int nch, int GM, int hd,
+                                                         float *__restrict__ out, int64_t ldo,
+                                                         int B) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int g0 = h / G, g = h % G;
+    const size_t units_total = static_cast<size_t>(B) * Hkv * nch * GM;
+    const float *pml = part + units_total * hd;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) {
+        const size_t u = ((static_cast<size_t>(b) * Hkv + g0) * nch + c) * GM + g;
+        if (pml[2 * u + 1] > 0.f) M = fmaxf(M, pml[2 * u]);
+    }
+    for (int d = threadIdx.x; d < hd; d += kWG) {
+        float num = 0.f, den = 0.f;
+        for (int c = 0; c < nch; ++c) {
+            const size_t u = ((static_cast<size_t>(b) * Hkv + g0) * nch + c) * GM + g;
+            const float l = pml[2 * u + 1];
+            if (l > 0.f) {
+                const float w = __expf(pml[2 * u] - M);
+                num = __builtin_fmaf(w, part[u * hd + d], num);
+                den = __builtin_fmaf(w, l, den);
+            }
+        }
+        out[b * ldo + static_cast<int64_t>(h) * hd + d] = den > 0.f ? num / den : 0.f;
+    }
+}
+
+template <int HD>
+void launch_split_hd(int GM, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
+                     const float *kc, const float *vc, const q4_kv_layout &kv,
+                     const int64_t *n_dev, int64_t window, float scale, int chunk, int nch,
+                     float *part) {
+#define Q4_ATTN_CASE(GG)                                                                         \
+    case GG:                                                                                     \
+        hipLaunchKernelGGL((attn_split_kernel<HD, GG>), grid, dim3(kWG), 0, s, q, ldq, G, kc, vc, \
+                           kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale,  \
+                           chunk, nch, part);                                                    \
+        break;
+    switch (GM) { Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(8) Q4_ATTN_CASE(16) }
+#undef Q4_ATTN_CASE
+}
+
+int round_group(int G) {
+    int gm = 1;
+    while (gm < G) gm *= 2;
+    return gm;
+}
+
+}  // namespace
+
+extern "C" size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_heads,
+                                            int64_t window) {
+    if (!kv || kv->n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || kv->cap < 1 ||
+        kv->batch < 1 || kv->head_dim < 1 || window < 0)
+        return 0;
+    AttnGeom g = attn_geom(*kv, n_q_heads, window);
+    q4_kv_layout k2 = *kv;
+    // partial rows are stored padded to the kernel's group size
+    const int gm = round_group(g.G);
+    const size_t units = static_cast<size_t>(k2.batch) * k2.n_kv_heads * g.nch * gm;
+    return units * (static_cast<size_t>(k2.head_dim) + 2) * sizeof(float);
+}
+
+extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads,
+                                     const float *k_cache, const float *v_cache,
+                                     const q4_kv_layout *kv, const int64_t *n_dev, int64_t window,
+                                     float scale, float *out, int64_t ldo, void *ws,
+                                     size_t ws_bytes, void *stream) {
+    q4::clear_error();
+    q4_status st = q4::check_kv_layout("gqa_decode_attn", kv);
+    if (st != Q4_OK) return st;
+    Q4_CHECK(q && k_cache && v_cache && n_dev && out, Q4_ERR_INVALID_ARG,
+             "gqa_decode_attn: q, caches, n_dev and out must not be NULL");
+    Q4_CHECK(window >= 0, Q4_ERR_INVALID_ARG, "gqa_decode_attn: window must be >= 0");
+    Q4_CHECK(n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0, Q4_ERR_SHAPE,
+             "gqa_decode_attn: n_q_heads %lld is not a multiple of n_kv_heads %lld",
+             (long long)n_q_heads, (long long)kv->n_kv_heads);
+    const int64_t hd = kv->head_dim;
+    Q4_CHECK(hd == 64 || hd == 128 || hd == 256 || hd == 512, Q4_ERR_UNSUPPORTED,
+             "gqa_decode_attn: head_dim %lld not in {64, 128, 256, 512}", (long long)hd);
+    const int G = static_cast<int>(n_q_heads / kv->n_kv_heads);
+    Q4_CHECK(G <= 16, Q4_ERR_UNSUPPORTED, "gqa_decode_attn: %d query heads per kv head > 16", G);
+    Q4_CHECK(ldq >= n_q_heads * hd && ldo >= n_q_heads * hd, Q4_ERR_SHAPE,
+             "gqa_decode_attn: row strides smaller than the rows");
+    Q4_CHECK(kv->stride_t % 4 == 0 && kv->stride_h % 4 == 0 && kv->stride_b % 4 == 0 && ldq % 4 == 0,
+             Q4_ERR_ALIGNMENT, "gqa_decode_attn: cache strides and ldq must be multiples of 4");
+    Q4_CHECK(q4::aligned(q, 16) && q4::aligned(k_cache, 16) && q4::aligned(v_cache, 16) &&
+                 q4::aligned(out, 4) && q4::aligned(n_dev, 8),
+             Q4_ERR_ALIGNMENT, "gqa_decode_attn: q and caches must be 16-byte aligned");
+    const size_t need = gqa_decode_attn_workspace(kv, n_q_heads, window);
+    Q4_CHECK(ws && ws_bytes >= need && q4::aligned(ws, 256), Q4_ERR_WORKSPACE,
+             "gqa_decode_attn: workspace of %zu bytes (256-byte aligned) needed, got %zu", need,
+             ws_bytes);
+    AttnGeom g = attn_geom(*kv, n_q_heads, window);
+    const int gm = round_group(G);
+    hipStream_t s = q4::as_stream(stream);
+    float *part = static_cast<float *>(ws);
+    dim3 grid(g.nch, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
+    switch (hd) {
+        case 64: launch_split_hd<64>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
+        case 128: launch_split_hd<128>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
+        case 256: launch_split_hd<256>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
+        default: launch_split_hd<512>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
+    }
+    q4_status ls = q4::launch_status("gqa_decode_attn (split)");
+    if (ls != Q4_OK) return ls;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(kv->batch)),
+                       dim3(kWG), 0, s, part, G, static_cast<int>(kv->n_kv_heads), g.nch, gm,
+                       static_cast<int>(hd), out, ldo, static_cast<int>(kv->batch));
+    return q4::launch_status("gqa_decode_attn (merge)");
+}

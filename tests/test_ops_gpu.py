@@ -1,0 +1,201 @@
+"""GPU parity of RMSNorm, SwiGLU, QK-norm + RoPE + KV append, GQA decode
+attention and argmax against the fp64 oracle (element by element)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q4_quantized_matvec_amd as q
+import synth
+from q4_quantized_matvec_amd._lib import KVLayout, kv_layout_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("rows,dim,gain", [(1, 2560, True), (8, 5376, True), (3, 100, False),
+                                           (5, 21504, True), (1, 1, True)])
+def test_rmsnorm_parity(dev, rows, dim, gain):
+    _say(f"rmsnorm {rows}x{dim} gain={gain}")
+    x = synth.normal_f32(201, f"rms.x.{rows}.{dim}", (rows, dim)) * 3.0
+    w = synth.uniform_f32(201, f"rms.w.{dim}", (dim,), 0.8, 1.2) if gain else None
+    ref = oracle.rmsnorm(x, w, 1e-6)
+    y = q.rmsnorm(torch.from_numpy(x).to(dev), None if w is None else torch.from_numpy(w).to(dev), 1e-6)
+    torch.cuda.synchronize()
+    err = np.abs(_np(y) - ref)
+    assert np.all(err <= 2e-4 * np.abs(ref) + 1e-6)
+
+
+def test_rmsnorm_in_place(dev):
+    x = synth.normal_f32(202, "rms.inplace", (4, 2048))
+    w = synth.uniform_f32(202, "rms.inplace.w", (2048,), 0.8, 1.2)
+    ref = oracle.rmsnorm(x, w, 1e-6)
+    xt = torch.from_numpy(x).to(dev)
+    q.rmsnorm(xt, torch.from_numpy(w).to(dev), 1e-6, y=xt)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(_np(xt) - ref) <= 2e-4 * np.abs(ref) + 1e-6)
+
+
+@pytest.mark.parametrize("rows,n", [(1, 9728), (8, 9728), (3, 21504), (2, 7)])
+def test_swiglu_parity_merged_rows(dev, rows, n):
+    _say(f"swiglu {rows}x{n}")
+    gu = synth.normal_f32(203, f"swiglu.{rows}.{n}", (rows, 2 * n)) * 4.0
+    ref = np.stack([oracle.swiglu(gu[r, :n], gu[r, n:]) for r in range(rows)])
+    g = torch.from_numpy(gu).to(dev)
+    h = q.swiglu(g, g[:, n:], rows, n, 2 * n)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(_np(h) - ref) <= 2e-4 * np.abs(ref) + 1e-6)
+
+
+def _qk_case(dev, B, hq, hkv, hd, cap, pos, theta, v_from_k, seed):
+    nq, nk = hq * hd, hkv * hd
+    ld = nq + nk + (0 if v_from_k else nk)
+    rows = synth.normal_f32(seed, f"qk.rows.{hd}.{pos}", (B, ld)) * 2.0
+    qn = synth.uniform_f32(seed, f"qk.qn.{hd}", (hd,), 0.8, 1.2)
+    kn = synth.uniform_f32(seed, f"qk.kn.{hd}", (hd,), 0.8, 1.2)
+    kc = synth.normal_f32(seed, f"qk.kc.{hd}", (B, hkv, cap, hd))
+    vc = synth.normal_f32(seed, f"qk.vc.{hd}", (B, hkv, cap, hd))
+    rows_d = torch.from_numpy(rows).to(dev)
+    kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
+    q.qk_norm_rope(rows_d, ld, rows_d[:, nq:], None if v_from_k else rows_d[:, nq + nk:], ld,
+                   torch.from_numpy(qn).to(dev), torch.from_numpy(kn).to(dev), hq,
+                   kv_layout_of(kc_d), pos_d, theta, 1e-6, v_from_k, kc_d, vc_d)
+    torch.cuda.synchronize()
+    return rows, qn, kn, kc, vc, _np(rows_d), _np(kc_d), _np(vc_d)
+
+
+def _rope_tol(normed, pos, theta):
+    """2e-4 * (|x_i cos| + |x_{i+h} sin|) + 1e-6 per output element."""
+    hd = normed.shape[-1]
+    h = hd // 2
+    i = np.arange(h)
+    ang = pos * theta ** (-(2.0 * i) / hd)
+    c, s = np.abs(np.cos(ang)), np.abs(np.sin(ang))
+    a, b = np.abs(normed[..., :h]), np.abs(normed[..., h:])
+    t0 = a * c + b * s
+    t1 = b * c + a * s
+    return 2e-4 * np.concatenate([t0, t1], axis=-1) + 1e-6
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256, 512])
+@pytest.mark.parametrize("pos,theta", [(0, 1e6), (7, 1e4), (4096, 1e6), (8200, 1e6)])
+@pytest.mark.parametrize("v_from_k", [False, True])
+def test_qk_norm_rope_parity(dev, hd, pos, theta, v_from_k):
+    _say(f"qk_norm_rope hd={hd} pos={pos} theta={theta} v_from_k={v_from_k}")
+    B, hq, hkv, cap = 2, 4, 2, 16
+    rows, qn, kn, kc0, vc0, got, kc, vc = _qk_case(dev, B, hq, hkv, hd, cap, pos, theta,
+                                                    v_from_k, 204)
+    nq, nk = hq * hd, hkv * hd
+    slot = pos % cap
+    for b in range(B):
+        qh = rows[b, :nq].reshape(hq, hd)
+        kr = rows[b, nq:nq + nk].reshape(hkv, hd)
+        qnorm = oracle.rmsnorm(qh, qn, 1e-6)
+        qref = oracle.rope_neox(qnorm, pos, theta)
+        assert np.all(np.abs(got[b, :nq].reshape(hq, hd) - qref) <= _rope_tol(qnorm, pos, theta))
+        knorm = oracle.rmsnorm(kr, kn, 1e-6)
+        kref = oracle.rope_neox(knorm, pos, theta)
+        assert np.all(np.abs(kc[b, :, slot] - kref) <= _rope_tol(knorm, pos, theta))
+        vref = (oracle.rmsnorm(kr, None, 1e-6) if v_from_k
+                else rows[b, nq + nk:].reshape(hkv, hd).astype(np.float64))
+        assert np.all(np.abs(vc[b, :, slot] - vref) <= 2e-4 * np.abs(vref) + 1e-6)
+    # every other slot is untouched
+    others = [s for s in range(cap) if s != slot]
+    assert np.array_equal(kc[:, :, others], kc0[:, :, others])
+    assert np.array_equal(vc[:, :, others], vc0[:, :, others])
+
+
+def _attn_oracle(qh, kc, vc, n, window, scale, cap):
+    """Visible positions of one sequence gathered in position order for the oracle."""
+    hkv, _, hd = kc.shape
+    keys = np.zeros((n, hkv, hd))
+    vals = np.zeros((n, hkv, hd))
+    lo = max(0, n - window) if window else 0
+    lo = max(lo, n - cap)
+    for p in range(lo, n):
+        keys[p] = kc[:, p % cap]
+        vals[p] = vc[:, p % cap]
+    # positions below lo are never seen: the oracle window expresses the same set
+    w = n - lo if (window or lo > 0) else 0
+    return oracle.gqa_attention(qh, keys, vals, w, scale)
+
+
+ATTN_CASES = [
+    # (B, Hq, Hkv, hd, cap, n, window)
+    (1, 16, 8, 128, 4097, 4097, 0),      # the 1.7B-shaped layer, full cache
+    (3, 16, 8, 128, 300, 257, 0),        # ragged chunk tail
+    (2, 32, 8, 128, 64, 1, 0),           # one key
+    (1, 32, 16, 256, 1024, 1024, 1024),  # sliding window, full ring
+    (1, 32, 16, 256, 1024, 3000, 1024),  # ring wrapped past capacity
+    (1, 32, 4, 512, 600, 555, 0),        # 8:1 groups, head_dim 512
+    (2, 16, 1, 64, 100, 77, 16),         # 16:1 groups, window smaller than n
+    (1, 6, 6, 128, 50, 33, 0),           # multi-head (G = 1)
+    (8, 32, 8, 128, 2064, 2049, 0),      # Qwen3-4B-shaped, B = 8
+]
+
+
+@pytest.mark.parametrize("B,hq,hkv,hd,cap,n,window", ATTN_CASES)
+def test_gqa_decode_attn_parity(dev, B, hq, hkv, hd, cap, n, window):
+    _say(f"gqa_decode_attn B={B} Hq={hq} Hkv={hkv} hd={hd} cap={cap} n={n} window={window}")
+    seed = 205
+    qv = synth.normal_f32(seed, f"att.q.{hd}.{hq}", (B, hq * hd))
+    kc = synth.normal_f32(seed, f"att.k.{hd}.{cap}", (B, hkv, cap, hd))
+    vc = synth.normal_f32(seed, f"att.v.{hd}.{cap}", (B, hkv, cap, hd))
+    scale = 1.0 / math.sqrt(hd) if window == 0 else 1.0
+    kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    kv = kv_layout_of(kc_d)
+    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, hq * hd), dtype=torch.float32, device=dev)
+    n_d = torch.tensor([n], dtype=torch.int64, device=dev)
+    q.gqa_decode_attn(torch.from_numpy(qv).to(dev), hq * hd, hq, kc_d, vc_d, kv, n_d, window, scale,
+                      out, hq * hd, ws)
+    torch.cuda.synchronize()
+    got = _np(out)
+    worst = 0.0
+    for b in range(B):
+        o, bound = _attn_oracle(qv[b].reshape(hq, hd).astype(np.float64), kc[b].astype(np.float64),
+                                vc[b].astype(np.float64), n, window, scale, cap)
+        err = np.abs(got[b].reshape(hq, hd) - o)
+        tol = 2e-4 * bound + 1e-6
+        worst = max(worst, float((err / tol).max()))
+    assert worst <= 1.0, f"max err/tol {worst:.3e}"
+
+
+def test_gqa_decode_attn_deterministic(dev):
+    B, hq, hkv, hd, cap = 2, 16, 8, 128, 3000
+    qv = torch.randn(B, hq * hd, device=dev)
+    kc = torch.randn(B, hkv, cap, hd, device=dev)
+    vc = torch.randn(B, hkv, cap, hd, device=dev)
+    kv = kv_layout_of(kc)
+    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
+    n_d = torch.tensor([2999], dtype=torch.int64, device=dev)
+    outs = []
+    for _ in range(3):
+        out = torch.empty((B, hq * hd), device=dev)
+        q.gqa_decode_attn(qv, hq * hd, hq, kc, vc, kv, n_d, 0, 0.088, out, hq * hd, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_argmax_rows_ties_and_parity(dev):
+    _say("argmax_rows")
+    V = 262144
+    lg = synth.normal_f32(206, "argmax", (4, V)) * 10.0
+    lg[1, 100] = lg[1, 7] = lg[1].max() + 1.0   # tie: lowest id wins
+    lg[2, :] = -np.inf
+    lg[3, 5] = np.nan
+    lg[3, 9] = 1e30
+    got = q.argmax_rows(torch.from_numpy(lg).to(dev)).cpu().numpy()
+    exp = [oracle.argmax(lg[0])[0], 7, 0, 9]
+    assert got.tolist() == exp
