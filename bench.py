@@ -52,6 +52,71 @@ def time_matvec(q, torch, Ws, x, y, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def decode_algorithmic_bytes(m, step):
+    """Bytes one decode step must move: every weight byte (Q4_0 matrices, the
+    Q8_0 logit table, the gathered embedding rows, norm gains), every visible
+    KV-cache byte, the appended KV rows and the logits."""
+    from synth import workloads as wl
+    d, F, V, B = m.d_model, m.ffn, m.vocab, m.batch
+    q4 = lambda n, k: n * (k // 32) * 18
+    total = V * (d // 32) * 34 + B * (d // 32) * 34 + 4 * d + 4 * B * V
+    n = m.start_pos + step + 1
+    for ly in m.layers:
+        nq, nk, nv = wl.layer_rows(m, ly)
+        total += q4(nq + nk + nv, d) + q4(d, nq) + q4(2 * F, d) + q4(d, F)
+        total += 4 * (2 * d + 2 * ly.head_dim)
+        vis = min(n, ly.window) if ly.window else n
+        total += B * ly.n_kv_heads * ly.head_dim * 4 * (2 * vis + 2)
+    return total
+
+
+def bench_decode(q, torch, m, reps=3, warmup=2):
+    """Times 16-step greedy decode runs from the prefilled position (HIP graph
+    replay, two graphs ping-ponging the token buffers)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from decode_util import gpu_model, upload_model
+    from synth import workloads as wl
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    weights = wl.model_weights(m)
+    dmod = upload_model(m, weights, dev)
+    del weights
+    log(f"{m.name}: generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    dm = gpu_model(q, m, dmod)
+    a = torch.from_numpy(wl.start_tokens(m)).to(dev)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+
+    def run(steps):
+        dm.set_position(m.start_pos)
+        for s_ in range(steps):
+            src, dst = (a, b) if s_ % 2 == 0 else (b, a)
+            dm.step(src, dst)
+
+    for _ in range(warmup):
+        run(m.steps)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(m.steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / m.steps)
+    ms = sorted(times)[len(times) // 2]
+    nbytes = sum(decode_algorithmic_bytes(m, s_) for s_ in range(m.steps)) / m.steps
+    dm.close()
+    del dmod
+    torch.cuda.empty_cache()
+    return {"tok/s": round(m.batch * 1e3 / ms, 2), "ms_per_step": round(ms, 4), "batch": m.batch,
+            "steps": m.steps, "start_pos": m.start_pos,
+            "algorithmic_GB_per_step": round(nbytes / 1e9, 4),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline_matvec(w, budget_s=12.0):
     import numpy as np
 
@@ -80,6 +145,8 @@ def main():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-matvec", action="store_true")
+    ap.add_argument("--decode", default="qwen3_4b,gemma4_31b",
+                    help="decode workloads to time (comma list, empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -146,6 +213,14 @@ def main():
         "matvec_B1_cache_resident": {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
                                      "ms": round(ms1r, 6)},
     }
+    if not args.only_matvec and args.decode:
+        del Ws
+        torch.cuda.empty_cache()
+        shapes = {"qwen3_4b": wl.QWEN3_4B, "gemma4_31b": wl.GEMMA4_31B}
+        out["decode"] = {}
+        for key in [k for k in args.decode.split(",") if k]:
+            log(f"timing decode {key}")
+            out["decode"][shapes[key].name] = bench_decode(q, torch, shapes[key])
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline_matvec(w)

@@ -79,6 +79,29 @@ q4_status q4_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64
 q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
                       float *y, const float *residual, void *stream);
 
+/* Input transforms a matvec can apply to its activation rows as it reads
+ * them, fusing the producer of the input into the matvec:
+ *   Q4_IN_PLAIN    x
+ *   Q4_IN_RMSNORM  norm_w * x / sqrt(mean(x^2) + eps)  (norm_w NULL: unit gain)
+ *                  ([GELO] 05 Components: decoder RMSNorm)
+ *   Q4_IN_SWIGLU   x / (1 + exp(-x)) * x2               ([GELO] 04: SwiGLU FFN) */
+typedef enum { Q4_IN_PLAIN = 0, Q4_IN_RMSNORM = 1, Q4_IN_SWIGLU = 2 } q4_input_op;
+
+/* q4_0_matvec_fused / q8_0_matvec_fused: y[b] = W op(x[b]) (+ residual[b]),
+ * where row b of x (and of x2 for SwiGLU) starts at element b * ld_x
+ * (ld_x >= K; a merged gate|up output passes x = gu, x2 = gu + F, ld_x = 2F).
+ * The transform is computed in fp32 exactly as rmsnorm() / swiglu() define
+ * it (the RMSNorm sum of squares may be added in a different order).
+ * Other arguments, layouts and errors as q4_0_matvec / q8_0_matvec, plus
+ * Q4_ERR_INVALID_ARG for an unknown op, a missing x2 or eps < 0 and
+ * Q4_ERR_SHAPE for ld_x < K. */
+q4_status q4_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x, const float *x2,
+                            int64_t ld_x, int64_t B, q4_input_op op, const float *norm_w, float eps,
+                            float *y, const float *residual, void *stream);
+q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x, const float *x2,
+                            int64_t ld_x, int64_t B, q4_input_op op, const float *norm_w, float eps,
+                            float *y, const float *residual, void *stream);
+
 /* q8_0_gather: x[b][:] = dequantised row tokens[b] of the Q8_0 table E
  * (embedding lookup of the tied table; [GELO] 05 generation loop embeds the
  * previous token).

@@ -49,6 +49,8 @@ _SIGS = {
     "q4_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_gather": ([_P, _I64, _I64, _P, _I64, _P, _P], C.c_int),
+    "q4_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
+    "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
     "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
     "qk_norm_rope": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D, _F,
@@ -154,6 +156,33 @@ def q4_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
 def q8_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
     """y[B,N] = dequant(W) @ x[B,K] (+ residual).  W: uint8 [N, K/32*34] on device."""
     return _matvec("q8_0_matvec", 34, W, x, y, residual, stream, n)
+
+
+IN_PLAIN, IN_RMSNORM, IN_SWIGLU = 0, 1, 2
+
+
+def _matvec_fused(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, stream, n):
+    import torch
+    N = n if n is not None else _qmatrix_dims(W, K, bpb)
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op),
+                                      _ptr(norm_w), float(eps), _ptr(y), _ptr(residual),
+                                      _stream(stream)))
+    return y
+
+
+def q4_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None, residual=None,
+                      stream=None, n=None):
+    """y[B,N] = dequant(W) @ op(x rows) (+ residual); rows of x (and x2) at stride ld."""
+    return _matvec_fused("q4_0_matvec_fused", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,
+                         residual, stream, n)
+
+
+def q8_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None, residual=None,
+                      stream=None, n=None):
+    return _matvec_fused("q8_0_matvec_fused", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
+                         residual, stream, n)
 
 
 def q8_0_gather(E, tokens, K, x=None, stream=None):

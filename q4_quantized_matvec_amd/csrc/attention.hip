@@ -20,12 +20,11 @@ namespace {
 using namespace q4dev;
 
 constexpr int kWG = 256;
-constexpr int kMaxChunk = 256;
+constexpr int kChunk = 64;  // positions per chunk (one per lane in the softmax pass)
 
 struct AttnGeom {
-    int G;      // query heads per kv head
-    int chunk;  // positions per chunk
-    int nch;    // chunks per (sequence, kv head)
+    int G;    // query heads per kv head
+    int nch;  // chunks per (sequence, kv head)
 };
 
 // Chunking depends only on the layout and window (never on n), so the
@@ -34,18 +33,8 @@ AttnGeom attn_geom(const q4_kv_layout &kv, int64_t n_q_heads, int64_t window) {
     AttnGeom g;
     g.G = static_cast<int>(n_q_heads / kv.n_kv_heads);
     const int64_t maxvis = window > 0 ? std::min<int64_t>(window, kv.cap) : kv.cap;
-    const int64_t per_head = std::max<int64_t>(1, 2048 / (kv.batch * kv.n_kv_heads));
-    int64_t ch = (maxvis + per_head - 1) / per_head;
-    ch = (ch + 31) / 32 * 32;
-    ch = std::max<int64_t>(64, std::min<int64_t>(kMaxChunk, ch));
-    g.chunk = static_cast<int>(ch);
-    g.nch = static_cast<int>((maxvis + ch - 1) / ch);
+    g.nch = static_cast<int>((maxvis + kChunk - 1) / kChunk);
     return g;
-}
-
-size_t attn_ws_bytes(const q4_kv_layout &kv, const AttnGeom &g) {
-    const size_t units = static_cast<size_t>(kv.batch) * kv.n_kv_heads * g.nch * g.G;
-    return units * (static_cast<size_t>(kv.head_dim) + 2) * sizeof(float);
 }
 
 // Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
@@ -61,18 +50,22 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// One workgroup per (chunk, kv head, sequence).  Loads are issued in batches
+// ahead of their use so the wavefronts keep many rows in flight.
 template <int HD, int GM>
 __global__ __launch_bounds__(kWG) void attn_split_kernel(
     const float *__restrict__ q, int64_t ldq, int G, const float *__restrict__ kc,
     const float *__restrict__ vc, int64_t cap, int64_t sb, int64_t sh, int64_t st,
-    const int64_t *__restrict__ n_dev, int64_t window, float scale, int chunk, int nch,
+    const int64_t *__restrict__ n_dev, int64_t window, float scale, int nch,
     float *__restrict__ part) {
-    constexpr int LPK = HD / 8;         // lanes per key in the score pass
-    constexpr int KPW = 64 / LPK;       // keys per wavefront per step
-    constexpr int DPT = HD > kWG ? HD / kWG : 1;  // dims per thread in the value pass
-    constexpr int KG = HD < kWG ? kWG / HD : 1;   // key groups in the value pass
-    __shared__ float sc[kMaxChunk * GM];          // scores, then weights: [pos][g]
-    __shared__ float red[KG > 1 ? kWG * GM : 1];  // value-pass partials of extra key groups
+    constexpr int LPK = HD / 8;              // score pass: lanes per key, 8 elements per lane
+    constexpr int KPW = 64 / LPK;            // keys per wavefront per step
+    constexpr int SIT = kChunk / (4 * KPW);  // score steps per wavefront
+    constexpr int TPK = HD / 4;              // value pass: threads per key (float4 each)
+    constexpr int KG = kWG / TPK;            // value pass: key groups
+    constexpr int VIT = kChunk / KG;         // value pass: keys per thread
+    __shared__ __align__(16) float sc[kChunk * GM];  // scores, then weights: [pos][g]
+    __shared__ __align__(16) float4 red[KG > 1 ? (KG - 1) * GM * TPK : 1];
 
     const int c = blockIdx.x, g0 = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -80,11 +73,11 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     int64_t lo = window > 0 ? n - window : 0;
     lo = max(lo, n - cap);
     lo = max(lo, int64_t(0));
-    const int64_t p0 = lo + static_cast<int64_t>(c) * chunk;
-    const int cnt = static_cast<int>(max(int64_t(0), min(int64_t(chunk), n - p0)));
+    const int64_t p0 = lo + static_cast<int64_t>(c) * kChunk;
+    const int cnt = static_cast<int>(max(int64_t(0), min(int64_t(kChunk), n - p0)));
 
     const size_t unit = ((static_cast<size_t>(b) * gridDim.y + g0) * nch + c) * GM;
-    float *po = part + unit * HD;                                   // [G][HD] (unit stride GM rows)
+    float *po = part + unit * HD;  // [GM][HD]
     float *pml = part + static_cast<size_t>(gridDim.z) * gridDim.y * nch * GM * HD + unit * 2;
     if (cnt == 0) {
         if (threadIdx.x < G) {
@@ -95,51 +88,50 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     }
     const float *kb = kc + b * sb + g0 * sh;
     const float *vb = vc + b * sb + g0 * sh;
+    // slot of chunk position j (positions past the chunk end re-read its first row)
+    auto slot = [&](int j) { return ((p0 + (j < cnt ? j : 0)) % cap) * st; };
 
-    // ---- scores: LPK lanes per key, 8 consecutive elements per lane
+    // ---- scores
     const int sub = lane % LPK, kgl = lane / LPK;
+    float kr[SIT][8];
+#pragma unroll
+    for (int it = 0; it < SIT; ++it) {
+        const int jj = it * 4 * KPW + wave * KPW + kgl;
+        const float4 *kp = reinterpret_cast<const float4 *>(kb + slot(jj) + sub * 8);
+        const float4 a = kp[0], bq = kp[1];
+        kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
+        kr[it][4] = bq.x; kr[it][5] = bq.y; kr[it][6] = bq.z; kr[it][7] = bq.w;
+    }
     float qv[GM][8];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        const float *qh = q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[g][e] = g < G ? qh[e] * scale : 0.f;
+        const float4 *qh = reinterpret_cast<const float4 *>(
+            q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 8);
+        const float4 a = qh[0], bq = qh[1];
+        qv[g][0] = a.x * scale; qv[g][1] = a.y * scale; qv[g][2] = a.z * scale; qv[g][3] = a.w * scale;
+        qv[g][4] = bq.x * scale; qv[g][5] = bq.y * scale; qv[g][6] = bq.z * scale; qv[g][7] = bq.w * scale;
     }
-    for (int base = 0; base < cnt; base += 4 * KPW) {
-        const int jj = base + wave * KPW + kgl;
-        float kr[8];
-        if (jj < cnt) {
-            const float4 *kp = reinterpret_cast<const float4 *>(kb + ((p0 + jj) % cap) * st + sub * 8);
-            const float4 a = kp[0], bq = kp[1];
-            kr[0] = a.x; kr[1] = a.y; kr[2] = a.z; kr[3] = a.w;
-            kr[4] = bq.x; kr[5] = bq.y; kr[6] = bq.z; kr[7] = bq.w;
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kr[e] = 0.f;
-        }
+    for (int it = 0; it < SIT; ++it) {
+        const int jj = it * 4 * KPW + wave * KPW + kgl;
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
             float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[g][e], kr[e], s);
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[g][e], kr[it][e], s);
             s = group_sum<LPK>(s);
-            if (sub == 0 && jj < cnt && g < G) sc[jj * GM + g] = s;
+            if (sub == 0 && g < G) sc[jj * GM + g] = jj < cnt ? s : -INFINITY;
         }
     }
     __syncthreads();
 
-    // ---- exact softmax over the chunk: one wavefront per query head
+    // ---- exact softmax over the chunk: one wavefront per query head, one lane per position
     for (int g = wave; g < G; g += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < cnt; j += 64) m = fmaxf(m, sc[j * GM + g]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < cnt; j += 64) {
-            const float e = __expf(sc[j * GM + g] - m);
-            sc[j * GM + g] = e;
-            l += e;
-        }
-        l = wave_sum(l);
+        const float s = sc[lane * GM + g];
+        const float m = wave_max(s);
+        const float e = lane < cnt ? __expf(s - m) : 0.f;
+        const float l = wave_sum(e);
+        sc[lane * GM + g] = e;
         if (lane == 0) {
             pml[2 * g] = m;
             pml[2 * g + 1] = l;
@@ -147,82 +139,90 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     }
     __syncthreads();
 
-    // ---- weighted values: threads over head dims, KG key groups
-    const int kg = threadIdx.x / (KG > 1 ? HD : kWG);
-    const int d0 = threadIdx.x % (KG > 1 ? HD : kWG);
-    float acc[GM][DPT];
+    // ---- weighted values: TPK threads per key (4 dims each), KG key groups
+    const int kg = threadIdx.x / TPK, d4 = threadIdx.x % TPK;
+    float4 vv[VIT];
 #pragma unroll
-    for (int g = 0; g < GM; ++g)
+    for (int it = 0; it < VIT; ++it)
+        vv[it] = reinterpret_cast<const float4 *>(vb + slot(kg + it * KG))[d4];
+    float4 acc[GM];
 #pragma unroll
-        for (int t = 0; t < DPT; ++t) acc[g][t] = 0.f;
-    for (int j = kg; j < cnt; j += KG) {
-        const float *vr = vb + ((p0 + j) % cap) * st;
-        float vv[DPT];
+    for (int g = 0; g < GM; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int t = 0; t < DPT; ++t) vv[t] = vr[d0 + t * kWG];
-        float w[GM];
-        if constexpr (GM % 4 == 0) {
+    for (int it = 0; it < VIT; ++it) {
+        const int j = kg + it * KG;  // weights of positions past cnt are 0
 #pragma unroll
-            for (int g = 0; g < GM; g += 4) {
-                const float4 p4 = *reinterpret_cast<const float4 *>(&sc[j * GM + g]);
-                w[g] = p4.x; w[g + 1] = p4.y; w[g + 2] = p4.z; w[g + 3] = p4.w;
-            }
-        } else {
-#pragma unroll
-            for (int g = 0; g < GM; ++g) w[g] = sc[j * GM + g];
+        for (int g = 0; g < GM; ++g) {
+            const float w = sc[j * GM + g];
+            acc[g].x = __builtin_fmaf(w, vv[it].x, acc[g].x);
+            acc[g].y = __builtin_fmaf(w, vv[it].y, acc[g].y);
+            acc[g].z = __builtin_fmaf(w, vv[it].z, acc[g].z);
+            acc[g].w = __builtin_fmaf(w, vv[it].w, acc[g].w);
         }
-#pragma unroll
-        for (int g = 0; g < GM; ++g)
-#pragma unroll
-            for (int t = 0; t < DPT; ++t) acc[g][t] = __builtin_fmaf(w[g], vv[t], acc[g][t]);
     }
     if constexpr (KG > 1) {
         if (kg > 0) {
 #pragma unroll
-            for (int g = 0; g < GM; ++g) red[(kg * GM + g) * HD + d0] = acc[g][0];
+            for (int g = 0; g < GM; ++g) red[((kg - 1) * GM + g) * TPK + d4] = acc[g];
         }
         __syncthreads();
         if (kg == 0) {
 #pragma unroll
             for (int g = 0; g < GM; ++g) {
-                float s = acc[g][0];
-                for (int k = 1; k < KG; ++k) s += red[(k * GM + g) * HD + d0];  // fixed order
-                if (g < G) po[g * HD + d0] = s;
+                float4 s4 = acc[g];
+                for (int k = 1; k < KG; ++k) {  // fixed order
+                    const float4 r = red[((k - 1) * GM + g) * TPK + d4];
+                    s4.x += r.x; s4.y += r.y; s4.z += r.z; s4.w += r.w;
+                }
+                if (g < G) reinterpret_cast<float4 *>(po + g * HD)[d4] = s4;
             }
         }
     } else {
 #pragma unroll
         for (int g = 0; g < GM; ++g)
-#pragma unroll
-            for (int t = 0; t < DPT; ++t)
-                if (g < G) po[g * HD + d0 + t * kWG] = acc[g][t];
+            if (g < G) reinterpret_cast<float4 *>(po + g * HD)[d4] = acc[g];
     }
 }
 
-// One workgroup per (query head, sequence): merges the chunks in order.
+// Merge: one workgroup per (query head, sequence, 64-dimension slice); four
+// chunk groups accumulate interleaved chunks and are added in a fixed order.
 __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict__ part, int G,
                                                          int Hkv, int nch, int GM, int hd,
                                                          float *__restrict__ out, int64_t ldo,
                                                          int B) {
+    __shared__ float rn[3][64], rd[3][64];
     const int h = blockIdx.x, b = blockIdx.y;
     const int g0 = h / G, g = h % G;
+    const int cg = threadIdx.x >> 6, dl = threadIdx.x & 63;
+    const int d = blockIdx.z * 64 + dl;
     const size_t units_total = static_cast<size_t>(B) * Hkv * nch * GM;
     const float *pml = part + units_total * hd;
+    const size_t u0 = (static_cast<size_t>(b) * Hkv + g0) * nch * GM + g;
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) {
-        const size_t u = ((static_cast<size_t>(b) * Hkv + g0) * nch + c) * GM + g;
+    for (int c = dl; c < nch; c += 64) {
+        const size_t u = u0 + static_cast<size_t>(c) * GM;
         if (pml[2 * u + 1] > 0.f) M = fmaxf(M, pml[2 * u]);
     }
-    for (int d = threadIdx.x; d < hd; d += kWG) {
-        float num = 0.f, den = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const size_t u = ((static_cast<size_t>(b) * Hkv + g0) * nch + c) * GM + g;
-            const float l = pml[2 * u + 1];
-            if (l > 0.f) {
-                const float w = __expf(pml[2 * u] - M);
-                num = __builtin_fmaf(w, part[u * hd + d], num);
-                den = __builtin_fmaf(w, l, den);
-            }
+    M = wave_max(M);
+    float num = 0.f, den = 0.f;
+    for (int c = cg; c < nch; c += 4) {
+        const size_t u = u0 + static_cast<size_t>(c) * GM;
+        const float l = pml[2 * u + 1];
+        if (l > 0.f) {
+            const float w = __expf(pml[2 * u] - M);
+            if (d < hd) num = __builtin_fmaf(w, part[u * hd + d], num);
+            den = __builtin_fmaf(w, l, den);
+        }
+    }
+    if (cg > 0) {
+        rn[cg - 1][dl] = num;
+        rd[cg - 1][dl] = den;
+    }
+    __syncthreads();
+    if (cg == 0 && d < hd) {
+        for (int k = 0; k < 3; ++k) {
+            num += rn[k][dl];
+            den += rd[k][dl];
         }
         out[b * ldo + static_cast<int64_t>(h) * hd + d] = den > 0.f ? num / den : 0.f;
     }
@@ -231,13 +231,12 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
 template <int HD>
 void launch_split_hd(int GM, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
                      const float *kc, const float *vc, const q4_kv_layout &kv,
-                     const int64_t *n_dev, int64_t window, float scale, int chunk, int nch,
-                     float *part) {
+                     const int64_t *n_dev, int64_t window, float scale, int nch, float *part) {
 #define Q4_ATTN_CASE(GG)                                                                         \
     case GG:                                                                                     \
         hipLaunchKernelGGL((attn_split_kernel<HD, GG>), grid, dim3(kWG), 0, s, q, ldq, G, kc, vc, \
                            kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale,  \
-                           chunk, nch, part);                                                    \
+                           nch, part);                                                    \
         break;
     switch (GM) { Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(8) Q4_ATTN_CASE(16) }
 #undef Q4_ATTN_CASE
@@ -300,14 +299,16 @@ extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_he
     float *part = static_cast<float *>(ws);
     dim3 grid(g.nch, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
     switch (hd) {
-        case 64: launch_split_hd<64>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
-        case 128: launch_split_hd<128>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
-        case 256: launch_split_hd<256>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
-        default: launch_split_hd<512>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.chunk, g.nch, part); break;
+        case 64: launch_split_hd<64>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
+        case 128: launch_split_hd<128>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
+        case 256: launch_split_hd<256>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
+        default: launch_split_hd<512>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
     }
     q4_status ls = q4::launch_status("gqa_decode_attn (split)");
     if (ls != Q4_OK) return ls;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(kv->batch)),
+    hipLaunchKernelGGL(attn_merge_kernel,
+                       dim3(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(kv->batch),
+                            static_cast<unsigned>((hd + 63) / 64)),
                        dim3(kWG), 0, s, part, G, static_cast<int>(kv->n_kv_heads), g.nch, gm,
                        static_cast<int>(hd), out, ldo, static_cast<int>(kv->batch));
     return q4::launch_status("gqa_decode_attn (merge)");

@@ -21,7 +21,7 @@ struct q4_decode_model {
     std::vector<q4_layer_desc> layers;
     std::vector<q4_kv_layout> kv;
     int64_t *pos_dev = nullptr;  // [0] = position of the next token, [1] = n = position + 1
-    float *x = nullptr, *xn = nullptr, *qkv = nullptr, *att = nullptr, *gu = nullptr, *h = nullptr;
+    float *x = nullptr, *qkv = nullptr, *att = nullptr, *gu = nullptr;
     float *logits = nullptr;
     void *attn_ws = nullptr;
     size_t attn_ws_bytes = 0;
@@ -55,7 +55,7 @@ __global__ void advance_position_kernel(int64_t *pos) {
 }
 
 struct Layout {
-    size_t pos, x, xn, qkv, att, gu, h, logits, attn, total;
+    size_t pos, x, qkv, att, gu, logits, attn, total;
 };
 
 int64_t layer_qkv_rows(const q4_model_desc &d, const q4_layer_desc &l) {
@@ -95,11 +95,9 @@ Layout plan(const q4_model_desc &d) {
     };
     L.pos = take(2 * sizeof(int64_t));
     L.x = take(sizeof(float) * B * d.d_model);
-    L.xn = take(sizeof(float) * B * d.d_model);
     L.qkv = take(sizeof(float) * B * qkv);
     L.att = take(sizeof(float) * B * att);
     L.gu = take(sizeof(float) * B * 2 * d.ffn);
-    L.h = take(sizeof(float) * B * d.ffn);
     L.logits = take(sizeof(float) * B * d.vocab);
     L.attn = take(attn);
     L.total = o;
@@ -166,8 +164,9 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         const q4_layer_desc &l = m->layers[i];
         const int64_t hd = l.head_dim, nq = d.n_q_heads * hd, nk = l.n_kv_heads * hd;
         const int64_t nqkv = layer_qkv_rows(d, l);
-        Q4_TRY(rmsnorm(m->x, l.attn_norm, B, D, d.eps, m->xn, sv));
-        Q4_TRY(q4_0_matvec(l.wqkv, nqkv, D, m->xn, B, m->qkv, nullptr, sv));
+        // attention RMSNorm fused into the QKV projection's input
+        Q4_TRY(q4_0_matvec_fused(l.wqkv, nqkv, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, l.attn_norm,
+                                 d.eps, m->qkv, nullptr, sv));
         Q4_TRY(qk_norm_rope(m->qkv, nqkv, m->qkv + nq, l.v_from_k ? nullptr : m->qkv + nq + nk, nqkv,
                             l.q_norm, l.k_norm, d.n_q_heads, &m->kv[i], m->pos_dev, l.rope_theta,
                             d.eps, l.v_from_k, l.k_cache, l.v_cache, sv));
@@ -175,14 +174,15 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
                                m->pos_dev + 1, l.window, l.attn_scale, m->att, nq, m->attn_ws,
                                m->attn_ws_bytes, sv));
         Q4_TRY(q4_0_matvec(l.wo, D, nq, m->att, B, m->x, m->x, sv));
-        Q4_TRY(rmsnorm(m->x, l.ffn_norm, B, D, d.eps, m->xn, sv));
-        Q4_TRY(q4_0_matvec(l.wgu, 2 * F, D, m->xn, B, m->gu, nullptr, sv));
-        Q4_TRY(swiglu(m->gu, m->gu + F, B, F, 2 * F, m->h, sv));
-        Q4_TRY(q4_0_matvec(l.wd, D, F, m->h, B, m->x, m->x, sv));
+        // FFN RMSNorm fused into gate|up; SwiGLU fused into the down projection
+        Q4_TRY(q4_0_matvec_fused(l.wgu, 2 * F, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, l.ffn_norm,
+                                 d.eps, m->gu, nullptr, sv));
+        Q4_TRY(q4_0_matvec_fused(l.wd, D, F, m->gu, m->gu + F, 2 * F, B, Q4_IN_SWIGLU, nullptr, 0.f,
+                                 m->x, m->x, sv));
     }
     float *lg = logits ? logits : m->logits;
-    Q4_TRY(rmsnorm(m->x, d.final_norm, B, D, d.eps, m->xn, sv));
-    Q4_TRY(q8_0_matvec(d.embed, d.vocab, D, m->xn, B, lg, nullptr, sv));
+    Q4_TRY(q8_0_matvec_fused(d.embed, d.vocab, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, d.final_norm,
+                             d.eps, lg, nullptr, sv));
     Q4_TRY(argmax_rows(lg, B, d.vocab, next, sv));
     hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, s, m->pos_dev);
     return q4::launch_status("decode_step (advance)");
@@ -229,11 +229,9 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     char *base = static_cast<char *>(ws);
     m->pos_dev = reinterpret_cast<int64_t *>(base + L.pos);
     m->x = reinterpret_cast<float *>(base + L.x);
-    m->xn = reinterpret_cast<float *>(base + L.xn);
     m->qkv = reinterpret_cast<float *>(base + L.qkv);
     m->att = reinterpret_cast<float *>(base + L.att);
     m->gu = reinterpret_cast<float *>(base + L.gu);
-    m->h = reinterpret_cast<float *>(base + L.h);
     m->logits = reinterpret_cast<float *>(base + L.logits);
     m->attn_ws = base + L.attn;
     m->attn_ws_bytes = L.total - L.attn;

@@ -46,6 +46,21 @@ struct Fmt<1> {  // Q8_0
 
 // One row's raw words per owned column: the 4-byte-aligned window holding
 // the block (kDwords + 1 words) and the row's residual.
+// Transform applied to the activation rows as they are read (fuses the
+// producer of the matvec input into its prologue):
+//   kind 0: x
+//   kind 1: rmsnorm(x) = w * x / sqrt(mean(x^2) + eps)   (w NULL: unit gain)
+//   kind 2: swiglu(x, u) = x / (1 + exp(-x)) * u
+struct InOp {
+    int kind;
+    const float *u;  // kind 2: second operand, same row stride as x
+    const float *w;  // kind 1: gain
+    float eps;
+    int64_t ld;      // row stride of x (and u) in elements
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 template <int FMT, int JX>
 struct RowRegs {
     uint32_t w[JX][Fmt<FMT>::kDwords + 1];
@@ -108,10 +123,19 @@ constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
 // PF rows of loads in flight per wavefront.
 template <int FMT, int JX, int KS, int PF>
 __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
-                                                    const float *__restrict__ x, float *y,
-                                                    const float *res, int N, int K) {
+                                                    const float *x, float *y, const float *res,
+                                                    int N, int K, InOp op) {
     constexpr int RG = 4 / KS;
     constexpr int NBUF = PF + 1;
+    // batch row of this workgroup (each batch row streams the matrix itself;
+    // repeated passes are mostly served by the last-level cache)
+    {
+        const int64_t b = blockIdx.y;
+        x += b * op.ld;
+        if (op.u) op.u += b * op.ld;
+        y += b * static_cast<int64_t>(N);
+        if (res) res += b * static_cast<int64_t>(N);
+    }
     constexpr bool kXLds = Q4_MV_X_LDS && KS == 1;
     __shared__ float red[4];
     __shared__ float xs[kXLds ? kXLdsFloats : 1];
@@ -156,12 +180,44 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     const uint32_t sel_o = odd ? 0x0C070C05u : 0x0C050C03u;
 
     // Activations of the lane's block columns stay in registers.  With the
-    // whole K in one wavefront the workgroup stages x through LDS once.
+    // whole K in one wavefront the workgroup stages x through LDS once; the
+    // input transform is applied on the way (sum of squares reduced in LDS).
+    float inv = 1.f;
     if constexpr (kXLds) {
         const float4 *xg = reinterpret_cast<const float4 *>(x);
+        const float4 *ug = reinterpret_cast<const float4 *>(op.u);
         float4 *xl = reinterpret_cast<float4 *>(xs);
-        for (int i = threadIdx.x; i < (K >> 2); i += kWG) xl[i] = xg[i];
+        float ss = 0.f;
+        for (int i = threadIdx.x; i < (K >> 2); i += kWG) {
+            float4 v = xg[i];
+            if (op.kind == 2) {
+                const float4 u = ug[i];
+                v.x = silu_mul(v.x, u.x);
+                v.y = silu_mul(v.y, u.y);
+                v.z = silu_mul(v.z, u.z);
+                v.w = silu_mul(v.w, u.w);
+            }
+            ss = __builtin_fmaf(v.x, v.x, __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.z, v.z, __builtin_fmaf(v.w, v.w, ss))));
+            xl[i] = v;
+        }
+        if (op.kind == 1) {
+            ss = wave_sum(ss);
+            if (lane == 0) red[wave] = ss;
+        }
         __syncthreads();
+        if (op.kind == 1) {
+            inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / static_cast<float>(K) + op.eps);
+            __syncthreads();  // red[] is reused by the row reductions of split-K shapes
+        }
+    } else if (op.kind == 1) {
+        // every wavefront reduces the whole row itself
+        float ss = 0.f;
+        const float4 *xg = reinterpret_cast<const float4 *>(x);
+        for (int i = lane; i < (K >> 2); i += 64) {
+            const float4 v = xg[i];
+            ss = __builtin_fmaf(v.x, v.x, __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.z, v.z, __builtin_fmaf(v.w, v.w, ss))));
+        }
+        inv = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(K) + op.eps);
     }
     float xr[JX][32];
     float xc[JX];
@@ -174,11 +230,23 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                                      : reinterpret_cast<const float4 *>(x + static_cast<size_t>(c) * 32);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float4 v = xp[i];
+                float4 v = xp[i];
+                if (!kXLds && op.kind == 2) {
+                    const float4 u = reinterpret_cast<const float4 *>(op.u + static_cast<size_t>(c) * 32)[i];
+                    v.x = silu_mul(v.x, u.x);
+                    v.y = silu_mul(v.y, u.y);
+                    v.z = silu_mul(v.z, u.z);
+                    v.w = silu_mul(v.w, u.w);
+                }
                 xr[j][4 * i + 0] = v.x;
                 xr[j][4 * i + 1] = v.y;
                 xr[j][4 * i + 2] = v.z;
                 xr[j][4 * i + 3] = v.w;
+            }
+            if (op.kind == 1) {
+                const float *wg = op.w ? op.w + static_cast<size_t>(c) * 32 : nullptr;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xr[j][i] = xr[j][i] * inv * (wg ? wg[i] : 1.0f);
             }
 #pragma unroll
             for (int i = 0; i < 32; ++i) s += xr[j][i];
@@ -297,14 +365,24 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
 }
 
 // Generic path: any K % 32 == 0, 1 <= B <= 8, scale/codes read as 16-bit words.
-template <int FMT, int B>
+template <int FMT, int B, int KIND>
 __global__ __launch_bounds__(kWG) void mv_generic_kernel(const uint8_t *__restrict__ W,
                                                          const float *__restrict__ x, float *y,
-                                                         const float *res, int N, int K) {
+                                                         const float *res, int N, int K, InOp op) {
     const int lane = threadIdx.x & 63;
     const int nb = K >> 5;
     const size_t row_bytes = static_cast<size_t>(nb) * Fmt<FMT>::kBytes;
     const int waves = gridDim.x * (kWG / 64);
+    float inv[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        inv[b] = 1.f;
+        if constexpr (KIND == 1) {
+            float ss = 0.f;
+            for (int i = lane; i < K; i += 64) ss = __builtin_fmaf(x[b * op.ld + i], x[b * op.ld + i], ss);
+            inv[b] = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(K) + op.eps);
+        }
+    }
     for (int row = blockIdx.x * (kWG / 64) + (threadIdx.x >> 6); row < N; row += waves) {
         float acc[B];
 #pragma unroll
@@ -333,10 +411,16 @@ __global__ __launch_bounds__(kWG) void mv_generic_kernel(const uint8_t *__restri
             }
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float *xb = x + static_cast<size_t>(b) * K + static_cast<size_t>(c) * 32;
+                const size_t off = static_cast<size_t>(b) * op.ld + static_cast<size_t>(c) * 32;
+                const float *xb = x + off;
                 float s = 0.f;
 #pragma unroll
-                for (int i = 0; i < 32; ++i) s = __builtin_fmaf(w[i], xb[i], s);
+                for (int i = 0; i < 32; ++i) {
+                    float xv = xb[i];
+                    if constexpr (KIND == 1) xv = xv * inv[b] * (op.w ? op.w[c * 32 + i] : 1.0f);
+                    else if constexpr (KIND == 2) xv = silu_mul(xv, op.u[off + i]);
+                    s = __builtin_fmaf(w[i], xv, s);
+                }
                 acc[b] = __builtin_fmaf(d, s, acc[b]);
             }
         }
@@ -378,67 +462,81 @@ __global__ __launch_bounds__(kWG) void q8_gather_kernel(const uint8_t *__restric
 
 template <int FMT, int JX, int KS>
 void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int N, int K,
-               hipStream_t s) {
+               int B, const InOp &op, hipStream_t s) {
     constexpr int PF = FMT == 0 ? Q4_MV_PREFETCH : Q4_MV_PREFETCH_Q8;
     constexpr int RG = 4 / KS;
     const int want = (N + RG - 1) / RG;
     const int per_cu = Q4_MV_WG_PER_CU ? Q4_MV_WG_PER_CU : (JX <= 2 ? 3 : 2);
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
-    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF>), dim3(nwg), dim3(kWG), 0, s, W, x, y, res, N, K);
+    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF>), dim3(nwg, B), dim3(kWG), 0, s, W, x, y, res, N, K, op);
 }
 
 template <int FMT, int KS>
 void launch_b1_jx(int jx, const uint8_t *W, const float *x, float *y, const float *res, int N,
-                  int K, hipStream_t s) {
+                  int K, int B, const InOp &op, hipStream_t s) {
     switch (jx) {
-        case 1: launch_b1<FMT, 1, KS>(W, x, y, res, N, K, s); break;
-        case 2: launch_b1<FMT, 2, KS>(W, x, y, res, N, K, s); break;
-        case 3: launch_b1<FMT, 3, KS>(W, x, y, res, N, K, s); break;
-        default: launch_b1<FMT, 4, KS>(W, x, y, res, N, K, s); break;
+        case 1: launch_b1<FMT, 1, KS>(W, x, y, res, N, K, B, op, s); break;
+        case 2: launch_b1<FMT, 2, KS>(W, x, y, res, N, K, B, op, s); break;
+        case 3: launch_b1<FMT, 3, KS>(W, x, y, res, N, K, B, op, s); break;
+        default: launch_b1<FMT, 4, KS>(W, x, y, res, N, K, B, op, s); break;
     }
 }
 
 template <int FMT>
 void launch_generic(int B, const uint8_t *W, const float *x, float *y, const float *res, int N,
-                    int K, hipStream_t s) {
+                    int K, const InOp &op, hipStream_t s) {
     const int nwg = std::max(1, std::min((N + 3) / 4, 4 * q4::device_cus()));
-    switch (B) {
-#define Q4_CASE(BB) \
-    case BB: hipLaunchKernelGGL((mv_generic_kernel<FMT, BB>), dim3(nwg), dim3(kWG), 0, s, W, x, y, res, N, K); break;
-        Q4_CASE(1) Q4_CASE(2) Q4_CASE(3) Q4_CASE(4) Q4_CASE(5) Q4_CASE(6) Q4_CASE(7) Q4_CASE(8)
+#define Q4_CASE(BB, KK) \
+    case BB: hipLaunchKernelGGL((mv_generic_kernel<FMT, BB, KK>), dim3(nwg), dim3(kWG), 0, s, W, x, y, res, N, K, op); break;
+#define Q4_SWITCH(KK) \
+    switch (B) { Q4_CASE(1, KK) Q4_CASE(2, KK) Q4_CASE(3, KK) Q4_CASE(4, KK) Q4_CASE(5, KK) Q4_CASE(6, KK) Q4_CASE(7, KK) Q4_CASE(8, KK) }
+    if (op.kind == 1) { Q4_SWITCH(1) }
+    else if (op.kind == 2) { Q4_SWITCH(2) }
+    else { Q4_SWITCH(0) }
+#undef Q4_SWITCH
 #undef Q4_CASE
-    }
 }
 
 template <int FMT>
 q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
-                       int64_t B, float *y, const float *res, void *stream) {
+                       const float *x2, int64_t ldx, int64_t B, int op_kind, const float *norm_w,
+                       float eps, float *y, const float *res, void *stream) {
     q4::clear_error();
     Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
     Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
              name, (long long)N, (long long)K, (long long)B);
+    Q4_CHECK(op_kind >= Q4_IN_PLAIN && op_kind <= Q4_IN_SWIGLU, Q4_ERR_INVALID_ARG,
+             "%s: unknown input transform %d", name, op_kind);
+    Q4_CHECK(op_kind != Q4_IN_SWIGLU || x2, Q4_ERR_INVALID_ARG, "%s: SwiGLU needs x2", name);
+    Q4_CHECK(op_kind != Q4_IN_RMSNORM || eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
+    Q4_CHECK(ldx >= K, Q4_ERR_SHAPE, "%s: ld_x=%lld < K=%lld", name, (long long)ldx, (long long)K);
     Q4_CHECK(K % 32 == 0, Q4_ERR_SHAPE, "%s: K=%lld is not a multiple of 32", name, (long long)K);
     Q4_CHECK(B <= 8, Q4_ERR_UNSUPPORTED, "%s: B=%lld > 8", name, (long long)B);
-    Q4_CHECK(N <= (1 << 30) && K <= (1 << 24), Q4_ERR_UNSUPPORTED, "%s: N or K too large", name);
+    Q4_CHECK(N <= (1 << 30) && K <= (1 << 24) && ldx <= (1 << 26), Q4_ERR_UNSUPPORTED,
+             "%s: N or K too large", name);
     Q4_CHECK(q4::aligned(Wv, 2), Q4_ERR_ALIGNMENT, "%s: W must be 2-byte aligned", name);
-    Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!res || q4::aligned(res, 4)),
-             Q4_ERR_ALIGNMENT, "%s: x, y and residual must be 4-byte aligned", name);
+    Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!res || q4::aligned(res, 4)) &&
+                 (!x2 || q4::aligned(x2, 4)) && (!norm_w || q4::aligned(norm_w, 4)),
+             Q4_ERR_ALIGNMENT, "%s: x, x2, norm_w, y and residual must be 4-byte aligned", name);
     const uint8_t *W = static_cast<const uint8_t *>(Wv);
     hipStream_t s = q4::as_stream(stream);
     const int n = static_cast<int>(N), k = static_cast<int>(K);
     const int nb = k / 32;
+    InOp op{op_kind, op_kind == Q4_IN_SWIGLU ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
+            eps, ldx};
     int ks = 0;
-    if (B == 1 && K % 256 == 0 && q4::aligned(x, 16)) {
+    if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) && ldx % 4 == 0) {
         for (int cand : {1, 2, 4})
             if (ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
     }
     if (ks) {
         const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
-        if (ks == 1) launch_b1_jx<FMT, 1>(jx, W, x, y, res, n, k, s);
-        else if (ks == 2) launch_b1_jx<FMT, 2>(jx, W, x, y, res, n, k, s);
-        else launch_b1_jx<FMT, 4>(jx, W, x, y, res, n, k, s);
+        const int b = static_cast<int>(B);
+        if (ks == 1) launch_b1_jx<FMT, 1>(jx, W, x, y, res, n, k, b, op, s);
+        else if (ks == 2) launch_b1_jx<FMT, 2>(jx, W, x, y, res, n, k, b, op, s);
+        else launch_b1_jx<FMT, 4>(jx, W, x, y, res, n, k, b, op, s);
     } else {
-        launch_generic<FMT>(static_cast<int>(B), W, x, y, res, n, k, s);
+        launch_generic<FMT>(static_cast<int>(B), W, x, y, res, n, k, op, s);
     }
     return q4::launch_status(name);
 }
@@ -447,12 +545,30 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
 
 extern "C" q4_status q4_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
                                  float *y, const float *residual, void *stream) {
-    return matvec_entry<0>("q4_0_matvec", W, N, K, x, B, y, residual, stream);
+    return matvec_entry<0>("q4_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, nullptr, 0.f, y,
+                           residual, stream);
 }
 
 extern "C" q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
                                  float *y, const float *residual, void *stream) {
-    return matvec_entry<1>("q8_0_matvec", W, N, K, x, B, y, residual, stream);
+    return matvec_entry<1>("q8_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, nullptr, 0.f, y,
+                           residual, stream);
+}
+
+extern "C" q4_status q4_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
+                                       const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
+                                       const float *norm_w, float eps, float *y,
+                                       const float *residual, void *stream) {
+    return matvec_entry<0>("q4_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
+                           residual, stream);
+}
+
+extern "C" q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
+                                       const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
+                                       const float *norm_w, float eps, float *y,
+                                       const float *residual, void *stream) {
+    return matvec_entry<1>("q8_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
+                           residual, stream);
 }
 
 extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens,

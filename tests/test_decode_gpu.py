@@ -84,12 +84,9 @@ def test_decode_lockstep_per_op(dev, shape):
         hd, hkv = ly.head_dim, ly.n_kv_heads
         nq, nk, nv = wl.layer_rows(m, ly)
         nqkv = nq + nk + nv
-        xn = q.rmsnorm(x, L["attn_norm"], eps)
-        r = oracle.rmsnorm(np_(x), W["attn_norm"], eps)
-        _check(xn, r, 2e-4 * np.abs(r) + 1e-6, f"L{l} attn rmsnorm")
-        qkv = q.q4_0_matvec(L["wqkv"], xn)
-        r, t = oracle.q4_0_matvec(W["wqkv"], nqkv, D, np_(xn))
-        _check(qkv, r, 2e-4 * t + 1e-6, f"L{l} qkv matvec")
+        qkv = q.q4_0_matvec_fused(L["wqkv"], x, D, B, D, q.IN_RMSNORM, norm_w=L["attn_norm"], eps=eps)
+        r, t = oracle.q4_0_matvec(W["wqkv"], nqkv, D, oracle.rmsnorm(np_(x), W["attn_norm"], eps))
+        _check(qkv, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + qkv matvec")
         raw = np_(qkv).copy()
         q.qk_norm_rope(qkv, nqkv, qkv[:, nq:], None if ly.v_from_k else qkv[:, nq + nk:], nqkv,
                        L["q_norm"], L["k_norm"], Hq, kv_layout_of(L["k_cache"]), pos_d[0:1],
@@ -120,22 +117,20 @@ def test_decode_lockstep_per_op(dev, shape):
         q.q4_0_matvec(L["wo"], att, y=x, residual=x)
         r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att), res=xo)
         _check(x, r, 2e-4 * t + 1e-6, f"L{l} o-proj + residual")
-        xn = q.rmsnorm(x, L["ffn_norm"], eps)
-        gu = q.q4_0_matvec(L["wgu"], xn)
-        r, t = oracle.q4_0_matvec(W["wgu"], 2 * F, D, np_(xn))
-        _check(gu, r, 2e-4 * t + 1e-6, f"L{l} gate|up")
-        h = q.swiglu(gu, gu[:, F:], B, F, 2 * F)
+        gu = q.q4_0_matvec_fused(L["wgu"], x, D, B, D, q.IN_RMSNORM, norm_w=L["ffn_norm"], eps=eps)
+        r, t = oracle.q4_0_matvec(W["wgu"], 2 * F, D, oracle.rmsnorm(np_(x), W["ffn_norm"], eps))
+        _check(gu, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + gate|up")
         g64 = np_(gu)
-        r = np.stack([oracle.swiglu(g64[b, :F], g64[b, F:]) for b in range(B)])
-        _check(h, r, 2e-4 * np.abs(r) + 1e-6, f"L{l} swiglu")
+        h = np.stack([oracle.swiglu(g64[b, :F], g64[b, F:]) for b in range(B)])
         xo = np_(x)
-        q.q4_0_matvec(L["wd"], h, y=x, residual=x)
-        r, t = oracle.q4_0_matvec(W["wd"], D, F, np_(h), res=xo)
-        _check(x, r, 2e-4 * t + 1e-6, f"L{l} down + residual")
-    xn = q.rmsnorm(x, dmod["final_norm"], eps)
-    logits = q.q8_0_matvec(dmod["embed"], xn)
-    r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D, np_(xn))
-    _check(logits, r, 2e-4 * t + 1e-6, "logits")
+        q.q4_0_matvec_fused(L["wd"], gu, F, B, 2 * F, q.IN_SWIGLU, x2=gu[:, F:], y=x, residual=x)
+        r, t = oracle.q4_0_matvec(W["wd"], D, F, h, res=xo)
+        _check(x, r, 2e-4 * t + 1e-6, f"L{l} swiglu + down + residual")
+    logits = q.q8_0_matvec_fused(dmod["embed"], x, D, B, D, q.IN_RMSNORM,
+                                 norm_w=dmod["final_norm"], eps=eps)
+    r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D,
+                              oracle.rmsnorm(np_(x), weights["final_norm"], eps))
+    _check(logits, r, 2e-4 * t + 1e-6, "final rmsnorm + logits")
     nxt = q.argmax_rows(logits)
     assert nxt.cpu().numpy().tolist() == [oracle.argmax(np_(logits)[b])[0] for b in range(B)]
 

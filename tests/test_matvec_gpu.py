@@ -127,3 +127,36 @@ def test_q8_0_gather_out_of_range_token_gives_nan(dev):
     torch.cuda.synchronize()
     x = x.cpu().numpy()
     assert np.all(np.isfinite(x[0])) and np.all(np.isnan(x[1])) and np.all(np.isnan(x[2]))
+
+
+FUSED_CASES = [
+    # (fmt, N, K, B, op): LDS-staged (K <= 8192), split-K (K = 21504) and B > 1 paths
+    ("q4", 300, 2560, 1, "rms"), ("q4", 257, 5376, 1, "swiglu"), ("q4", 200, 21504, 1, "swiglu"),
+    ("q4", 130, 21504, 1, "rms"), ("q4", 100, 2560, 8, "rms"), ("q4", 64, 9728, 8, "swiglu"),
+    ("q8", 1000, 5376, 1, "rms"), ("q8", 300, 2560, 8, "rms"), ("q4", 77, 2048, 1, "rms_unit"),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,b,op", FUSED_CASES)
+def test_matvec_fused_input_parity(dev, fmt, n, k, b, op):
+    _say(f"{fmt} fused {op} N={n} K={k} B={b}")
+    gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
+    orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
+    fn = q.q4_0_matvec_fused if fmt == "q4" else q.q8_0_matvec_fused
+    W = gen(106, f"t.fused.{fmt}.{n}.{k}", n, k)
+    ld = 2 * k if op == "swiglu" else k
+    xa = synth.normal_f32(106, f"t.fused.x.{k}.{b}", (b, ld)) * 2.0
+    w = synth.uniform_f32(106, f"t.fused.w.{k}", (k,), 0.8, 1.2)
+    r = synth.normal_f32(106, f"t.fused.r.{n}.{b}", (b, n))
+    if op == "swiglu":
+        xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
+    else:
+        xin = oracle.rmsnorm(xa[:, :k], None if op == "rms_unit" else w, 1e-6)
+    ref, terms = orc(W, n, k, xin, res=r)
+    xd = torch.from_numpy(xa).to(dev)
+    yr = torch.from_numpy(r).to(dev)
+    kind = q.IN_SWIGLU if op == "swiglu" else q.IN_RMSNORM
+    fn(torch.from_numpy(W).to(dev), xd, k, b, ld, kind, x2=xd[:, k:] if op == "swiglu" else None,
+       norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6, y=yr, residual=yr)
+    torch.cuda.synchronize()
+    _check(yr, ref, terms, f"{fmt} fused {op} {n}x{k} B={b}")
