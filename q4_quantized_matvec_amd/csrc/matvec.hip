@@ -138,6 +138,9 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     }
     constexpr bool kXLds = Q4_MV_X_LDS && KS == 1;
     __shared__ float red[4];
+    constexpr int kFlush = 32;  // split-K rows reduced per barrier pair
+    __shared__ float kpart[KS > 1 ? 4 * kFlush : 1];
+    __shared__ float kres[KS > 1 ? 4 * kFlush : 1];
     __shared__ float xs[kXLds ? kXLdsFloats : 1];
     const int lane = threadIdx.x & 63;
     // wave-uniform: keeps row addressing in scalar registers
@@ -335,15 +338,26 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         if constexpr (KS == 1) {
             if (act && lane == 0) y[row] = has_res ? acc + cur.res : acc;
         } else {
-            if (lane == 0) red[wave] = acc;
-            __syncthreads();
-            if (ks == 0 && act && lane == 0) {
-                float s = red[rg * KS];
-#pragma unroll
-                for (int k = 1; k < KS; ++k) s += red[rg * KS + k];
-                y[row] = has_res ? s + cur.res : s;
+            // split K: park the partial (and the residual) in LDS; rows are
+            // reduced in batches of kFlush with two barriers per batch
+            const int slot = it % kFlush;
+            if (lane == 0) {
+                kpart[(rg * KS + ks) * kFlush + slot] = acc;
+                if (ks == 0) kres[rg * kFlush + slot] = cur.res;
             }
-            __syncthreads();
+            if (slot == kFlush - 1 || it + 1 == iters) {
+                __syncthreads();
+                if (ks == 0 && lane <= slot) {
+                    const int r = it - slot + lane;
+                    if (r < cnt) {
+                        float v = kpart[(rg * KS) * kFlush + lane];
+#pragma unroll
+                        for (int k = 1; k < KS; ++k) v += kpart[(rg * KS + k) * kFlush + lane];  // fixed order
+                        y[row0 + r] = has_res ? v + kres[rg * kFlush + lane] : v;
+                    }
+                }
+                __syncthreads();
+            }
         }
     };
 
