@@ -117,6 +117,71 @@ def bench_decode(q, torch, m, reps=3, warmup=2):
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def copy_calibration(torch, nbytes=1 << 30, reps=4):
+    """A plain device-to-device copy of a known size, launched after the timed
+    matvecs so that an HBM byte counter (FETCH_SIZE, WRITE_SIZE) can be scaled
+    to bytes: each launch reads and writes exactly `nbytes`."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} launches of {nbytes} bytes")
+
+
+def pmc_traffic(fetch_csv, write_csv, kernel="mv_b1_kernel", copy_bytes=1 << 30):
+    """HBM traffic per matvec launch from two rocprofv3 --pmc passes (FETCH_SIZE,
+    then WRITE_SIZE; both in KiB per dispatch), each scaled by the ratio of the
+    known copy size to what the same counter read for the calibration copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {"mv": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if kernel in name:
+                vals["mv"].append(float(r["Counter_Value"]))
+            elif "copy" in name.lower() or "elementwise" in name.lower():
+                vals["copy"].append(float(r["Counter_Value"]))
+        assert vals["mv"] and vals["copy"], f"{path}: no {counter} rows for both kernels"
+        mv = sorted(vals["mv"])[len(vals["mv"]) // 2]
+        cp = sorted(vals["copy"])[len(vals["copy"]) // 2]
+        return mv, cp
+
+    mv_f, cp_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    mv_w, cp_w = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (cp_f * 1024.0)
+    w_scale = copy_bytes / (cp_w * 1024.0)
+    return {"fetch_kib_raw": mv_f, "write_kib_raw": mv_w,
+            "copy_fetch_kib_raw": cp_f, "copy_write_kib_raw": cp_w,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "bytes_per_launch": round(mv_f * 1024.0 * f_scale + mv_w * 1024.0 * w_scale)}
+
+
+def kernel_source_hash():
+    """Digest of the matvec kernel's sources: stored counter readings are used
+    only while it is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("matvec.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "q4_quantized_matvec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(key):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(key)
+    if not t or t.get("kernel_source") != kernel_source_hash():
+        return None
+    return t["bytes_per_launch"]
+
+
 def cpu_baseline_matvec(w, budget_s=12.0):
     import numpy as np
 
@@ -128,7 +193,7 @@ def cpu_baseline_matvec(w, budget_s=12.0):
         oracle.q4_0_matvec(W, w.n, w.k, x)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 200:
+        if el >= budget_s or reps >= 20000:
             break
     per = el / reps
     return {"value": round(matvec_bytes(w.n, w.k, 1) / per / 1e9, 3), "unit": "GB/s",
@@ -147,7 +212,27 @@ def main():
     ap.add_argument("--only-matvec", action="store_true")
     ap.add_argument("--decode", default="qwen3_4b,gemma4_31b",
                     help="decode workloads to time (comma list, empty for none)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the B=1 HBM-streaming matvec (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a 1 GiB device copy to scale byte counters")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the decode workloads (for profiler runs)")
+    ap.add_argument("--pmc-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc passes and exit")
     args = ap.parse_args()
+    if args.pmc_traffic:
+        t = pmc_traffic(*args.pmc_traffic)
+        t["source"] = ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE over "
+                       "'bench.py --headline-only --copy-calibration --no-cpu-baseline'")
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        data = json.load(open(path)) if os.path.exists(path) else {}
+        t["kernel_source"] = kernel_source_hash()
+        data["q4_0_matvec_5376x21504_B1"] = t
+        with open(path, "w") as f:
+            json.dump(data, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
@@ -159,6 +244,13 @@ def main():
     from synth import workloads as wl
 
     dev = torch.device("cuda:0")
+    shapes = {"qwen3_4b": wl.QWEN3_4B, "gemma4_31b": wl.GEMMA4_31B}
+    decode_keys = [k for k in args.decode.split(",") if k] if not args.only_matvec else []
+    if args.only_decode:
+        res = {shapes[k].name: bench_decode(q, torch, shapes[k]) for k in decode_keys}
+        print(json.dumps({"decode": res}), flush=True)
+        return
+
     w = wl.MATVEC_5376x21504
     log(f"generating {args.copies} weight copies of {w.k}x{w.n}")
     Ws = []
@@ -166,31 +258,15 @@ def main():
         W, _ = wl.matvec_inputs(w, 1, copy=c)
         Ws.append(torch.from_numpy(W).to(dev))
     _, x1 = wl.matvec_inputs(w, 1)
-    _, x8 = wl.matvec_inputs(w, 8)
     x1 = torch.from_numpy(x1).to(dev)
-    x8 = torch.from_numpy(x8).to(dev)
     y1 = torch.empty((1, w.n), dtype=torch.float32, device=dev)
-    y8 = torch.empty((8, w.n), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     log("timing B=1")
     ms1 = time_matvec(q, torch, Ws, x1, y1, args.steps, args.warmup)
-    log("timing B=8")
-    ms8 = time_matvec(q, torch, Ws, x8, y8, args.steps, args.warmup)
-    log("timing B=1 cache-resident (one copy)")
-    ms1r = time_matvec(q, torch, Ws[:1], x1, y1, args.steps, args.warmup)
-
     bytes1 = matvec_bytes(w.n, w.k, 1)
-    bytes8 = matvec_bytes(w.n, w.k, 8)
     gbs1 = bytes1 / (ms1 * 1e-3) / 1e9
-    gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
-
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            traffic = json.load(f).get("q4_0_matvec_5376x21504_B1")
-
+    traffic = stored_traffic("q4_0_matvec_5376x21504_B1")
     out = {
         "metric": "Q4_0 matvec GB/s (% of HBM peak) at 5376x21504; decode tok/s at B=1 and B=8",
         "value": round(gbs1, 2),
@@ -205,23 +281,35 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Philox; Q4_0 codes uniform, binary16 scales U[0.005,0.02], x N(0,1))",
         "config": {"workload": w.name, "N": w.n, "K": w.k, "B": 1, "weight_copies": args.copies,
-                   "weight_bytes": w.n * (w.k // 32) * 18},
+                   "weight_bytes": w.n * (w.k // 32) * 18,
+                   "algorithmic_bytes_per_launch": bytes1},
         "roofline": {"bound": "hbm", "achieved": round(gbs1, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs1 / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "matvec_B8": {"GB/s": round(gbs8, 2), "ms": round(ms8, 6),
-                      "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4)},
-        "matvec_B1_cache_resident": {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
-                                     "ms": round(ms1r, 6)},
+                     "unit": "GB/s", "frac": round(gbs1 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
     }
-    if not args.only_matvec and args.decode:
-        del Ws
-        torch.cuda.empty_cache()
-        shapes = {"qwen3_4b": wl.QWEN3_4B, "gemma4_31b": wl.GEMMA4_31B}
-        out["decode"] = {}
-        for key in [k for k in args.decode.split(",") if k]:
-            log(f"timing decode {key}")
-            out["decode"][shapes[key].name] = bench_decode(q, torch, shapes[key])
-    if not args.no_cpu_baseline:
+    if args.copy_calibration:
+        copy_calibration(torch)
+    if not args.headline_only:
+        _, x8 = wl.matvec_inputs(w, 8)
+        x8 = torch.from_numpy(x8).to(dev)
+        y8 = torch.empty((8, w.n), dtype=torch.float32, device=dev)
+        log("timing B=8")
+        ms8 = time_matvec(q, torch, Ws, x8, y8, args.steps, args.warmup)
+        log("timing B=1 cache-resident (one copy)")
+        ms1r = time_matvec(q, torch, Ws[:1], x1, y1, args.steps, args.warmup)
+        gbs8 = matvec_bytes(w.n, w.k, 8) / (ms8 * 1e-3) / 1e9
+        out["matvec_B8"] = {"GB/s": round(gbs8, 2), "ms": round(ms8, 6),
+                            "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4)}
+        out["matvec_B1_cache_resident"] = {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
+                                           "ms": round(ms1r, 6)}
+        if decode_keys:
+            del Ws
+            torch.cuda.empty_cache()
+            out["decode"] = {}
+            for key in decode_keys:
+                log(f"timing decode {key}")
+                out["decode"][shapes[key].name] = bench_decode(q, torch, shapes[key])
+    if not args.no_cpu_baseline and not args.headline_only:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline_matvec(w)
     print(json.dumps(out), flush=True)
