@@ -52,6 +52,81 @@ def time_matvec(q, torch, Ws, x, y, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
+def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):
+    """As time_matvec for the matrix-core path (prep + main kernel per call)."""
+    stream = torch.cuda.current_stream()
+    N = y.shape[1]
+    ws = torch.empty(q.matvec_batched_workspace(N, K, B), dtype=torch.uint8, device=x.device)
+    for i in range(warmup):
+        q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_attention_stack(q, torch, batch, reps=20, warmup=3):
+    """The 28-layer Qwen3-1.7B-shaped attention stack at n_cache = 4096: per
+    layer QK-norm + RoPE + KV append at position 4096, then split-K attention
+    over the 4097 keys.  Every layer has its own cache, so a pass streams
+    28 * B * 2 * 8 * 4097 * 128 * 4 bytes of K/V."""
+    import numpy as np
+
+    from q4_quantized_matvec_amd._lib import kv_layout_of
+    from synth import workloads as wl
+    w = wl.ATTN_QWEN3_1P7B
+    dev = torch.device("cuda:0")
+    hq, hkv, hd, pos = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_cache
+    pos_d = torch.tensor([pos, pos + 1], dtype=torch.int64, device=dev)
+    layers = []
+    for l in range(w.n_layers):
+        qh, kh, vh, qn, kn, kc, vc = wl.attn_layer_inputs(w, batch, l)
+        kcd = torch.from_numpy(kc).to(dev)
+        layers.append(dict(q=torch.from_numpy(qh.reshape(batch, -1).copy()).to(dev),
+                           k=torch.from_numpy(kh.reshape(batch, -1).copy()).to(dev),
+                           v=torch.from_numpy(vh.reshape(batch, -1).copy()).to(dev),
+                           qn=torch.from_numpy(qn).to(dev), kn=torch.from_numpy(kn).to(dev),
+                           kc=kcd, vc=torch.from_numpy(vc).to(dev), kv=kv_layout_of(kcd)))
+        del kc, vc
+    ws = torch.empty(q.gqa_decode_attn_workspace(layers[0]["kv"], hq, 0), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((batch, hq * hd), dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(hd)
+
+    def one_pass():
+        for L in layers:
+            q.qk_norm_rope(L["q"], hq * hd, L["k"], L["v"], hkv * hd, L["qn"], L["kn"], hq,
+                           L["kv"], pos_d[0:1], w.rope_theta, w.eps, False, L["kc"], L["vc"])
+            q.gqa_decode_attn(L["q"], hq * hd, hq, L["kc"], L["vc"], L["kv"], pos_d[1:2], 0,
+                              scale, out, hq * hd, ws)
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = pos + 1
+    nbytes = w.n_layers * batch * (2 * hkv * hd * n * 4 + 2 * hq * hd * 4 + 4 * hkv * hd * 4)
+    del layers
+    torch.cuda.empty_cache()
+    return {"ms_per_pass": round(ms, 4), "batch": batch, "layers": w.n_layers, "n_keys": n,
+            "algorithmic_GB_per_pass": round(nbytes / 1e9, 4),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def decode_algorithmic_bytes(m, step):
     """Bytes one decode step must move: every weight byte (Q4_0 matrices, the
     Q8_0 logit table, the gathered embedding rows, norm gains), every visible
@@ -216,6 +291,8 @@ def main():
                     help="time only the B=1 HBM-streaming matvec (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a 1 GiB device copy to scale byte counters")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the 28-layer attention-stack timing")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode workloads (for profiler runs)")
     ap.add_argument("--pmc-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -293,18 +370,23 @@ def main():
         _, x8 = wl.matvec_inputs(w, 8)
         x8 = torch.from_numpy(x8).to(dev)
         y8 = torch.empty((8, w.n), dtype=torch.float32, device=dev)
-        log("timing B=8")
-        ms8 = time_matvec(q, torch, Ws, x8, y8, args.steps, args.warmup)
+        log("timing B=8 (matrix cores)")
+        ms8 = time_matvec_batched(q, torch, Ws, x8, y8, w.k, 8, args.steps, args.warmup)
         log("timing B=1 cache-resident (one copy)")
         ms1r = time_matvec(q, torch, Ws[:1], x1, y1, args.steps, args.warmup)
         gbs8 = matvec_bytes(w.n, w.k, 8) / (ms8 * 1e-3) / 1e9
         out["matvec_B8"] = {"GB/s": round(gbs8, 2), "ms": round(ms8, 6),
-                            "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4)}
+                            "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4), "path": "mfma"}
         out["matvec_B1_cache_resident"] = {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
                                            "ms": round(ms1r, 6)}
+        del Ws
+        torch.cuda.empty_cache()
+        if not args.no_attention:
+            out["attn_qwen3_1p7b"] = {}
+            for bb in (1, 8):
+                log(f"timing the 28-layer attention stack, B={bb}")
+                out["attn_qwen3_1p7b"][f"B{bb}"] = bench_attention_stack(q, torch, bb)
         if decode_keys:
-            del Ws
-            torch.cuda.empty_cache()
             out["decode"] = {}
             for key in decode_keys:
                 log(f"timing decode {key}")

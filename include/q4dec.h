@@ -102,6 +102,30 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                             int64_t ld_x, int64_t B, q4_input_op op, const float *norm_w, float eps,
                             float *y, const float *residual, void *stream);
 
+/* q4_0_matvec_batched / q8_0_matvec_batched: the same products as the fused
+ * calls, computed on the matrix cores (binary16 MFMA with every weight and
+ * every activation represented exactly: activations are split into two
+ * halves after a per-row power-of-two scaling), for 1 <= B <= 8 activation
+ * rows; meant for B >= 2, where eight products per weight outrun the vector
+ * units.  Products are formed exactly and summed in fp32.
+ *   W         16-byte aligned; K % 256 == 0 (else Q4_ERR_UNSUPPORTED)
+ *   x, x2     16-byte aligned, ld_x % 4 == 0
+ *   ws        device workspace of at least matvec_batched_workspace(N, K, B)
+ *             bytes, 256-byte aligned, owned by the caller; its contents
+ *             need no initialisation and are overwritten by every call, so
+ *             calls sharing one workspace must be ordered (one stream).
+ * Two kernels are enqueued on `stream`.  Results are bitwise reproducible.
+ * Other arguments and errors as q4_0_matvec_fused, plus Q4_ERR_WORKSPACE. */
+size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B);
+q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
+                              const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
+                              const float *norm_w, float eps, float *y, const float *residual,
+                              void *ws, size_t ws_bytes, void *stream);
+q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
+                              const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
+                              const float *norm_w, float eps, float *y, const float *residual,
+                              void *ws, size_t ws_bytes, void *stream);
+
 /* q8_0_gather: x[b][:] = dequantised row tokens[b] of the Q8_0 table E
  * (embedding lookup of the tied table; [GELO] 05 generation loop embeds the
  * previous token).

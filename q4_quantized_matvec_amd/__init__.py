@@ -13,11 +13,14 @@ from ._lib import (  # noqa: F401
     gqa_decode_attn,
     gqa_decode_attn_workspace,
     lib,
+    matvec_batched_workspace,
     IN_PLAIN,
     IN_RMSNORM,
     IN_SWIGLU,
     q4_0_matvec,
     q4_0_matvec_fused,
+    q4_0_matvec_batched,
+    q8_0_matvec_batched,
     q8_0_matvec_fused,
     q8_0_gather,
     q8_0_matvec,

@@ -51,6 +51,11 @@ _SIGS = {
     "q8_0_gather": ([_P, _I64, _I64, _P, _I64, _P, _P], C.c_int),
     "q4_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
     "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
+    "matvec_batched_workspace": ([_I64, _I64, _I64], _SZ),
+    "q4_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P, _SZ,
+                             _P], C.c_int),
+    "q8_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P, _SZ,
+                             _P], C.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
     "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
     "qk_norm_rope": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D, _F,
@@ -183,6 +188,39 @@ def q8_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None,
                       stream=None, n=None):
     return _matvec_fused("q8_0_matvec_fused", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
                          residual, stream, n)
+
+
+def matvec_batched_workspace(N, K, B):
+    """Bytes of device workspace q4_0/q8_0_matvec_batched need (0: shape unsupported)."""
+    return int(lib().matvec_batched_workspace(N, K, B))
+
+
+def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, ws, stream, n):
+    import torch
+    N = n if n is not None else _qmatrix_dims(W, K, bpb)
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(256, matvec_batched_workspace(N, K, B)), dtype=torch.uint8,
+                         device=x.device)
+    _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op),
+                                      _ptr(norm_w), float(eps), _ptr(y), _ptr(residual),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def q4_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
+                        residual=None, ws=None, stream=None, n=None):
+    """As q4_0_matvec_fused, on the matrix cores (1 <= B <= 8, K % 256 == 0).  ``ws``: a
+    uint8 device tensor of matvec_batched_workspace(N, K, B) bytes (allocated if None)."""
+    return _matvec_batched("q4_0_matvec_batched", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,
+                           residual, ws, stream, n)
+
+
+def q8_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
+                        residual=None, ws=None, stream=None, n=None):
+    return _matvec_batched("q8_0_matvec_batched", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
+                           residual, ws, stream, n)
 
 
 def q8_0_gather(E, tokens, K, x=None, stream=None):

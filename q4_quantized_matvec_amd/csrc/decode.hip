@@ -25,6 +25,8 @@ struct q4_decode_model {
     float *logits = nullptr;
     void *attn_ws = nullptr;
     size_t attn_ws_bytes = 0;
+    void *mv_ws = nullptr;  // matrix-core matvec workspace (batch >= 2), else NULL
+    size_t mv_ws_bytes = 0;
     hipStream_t capture = nullptr;
     struct Graph {
         const int32_t *tok;
@@ -55,7 +57,7 @@ __global__ void advance_position_kernel(int64_t *pos) {
 }
 
 struct Layout {
-    size_t pos, x, qkv, att, gu, logits, attn, total;
+    size_t pos, x, qkv, att, gu, logits, mv, mv_bytes, attn, total;
 };
 
 int64_t layer_qkv_rows(const q4_model_desc &d, const q4_layer_desc &l) {
@@ -75,17 +77,31 @@ q4_kv_layout layer_kv(const q4_model_desc &d, const q4_layer_desc &l) {
     return kv;
 }
 
+// With two or more sequences the projections run on the matrix cores
+// (q4_0_matvec_batched) wherever the shape allows it.
+bool batched_ok(const q4_model_desc &d, const void *W, int64_t K) {
+    return d.batch >= 2 && K % 256 == 0 && q4::aligned(W, 16);
+}
+
 Layout plan(const q4_model_desc &d) {
     const int64_t B = d.batch;
     int64_t qkv = 0, att = 0;
-    size_t attn = 0;
+    size_t attn = 0, mv = 0;
+    auto need_mv = [&](const void *W, int64_t N, int64_t K) {
+        if (batched_ok(d, W, K)) mv = std::max(mv, matvec_batched_workspace(N, K, B));
+    };
     for (int64_t i = 0; i < d.n_layers; ++i) {
         const q4_layer_desc &l = d.layers[i];
         qkv = std::max(qkv, layer_qkv_rows(d, l));
         att = std::max(att, d.n_q_heads * l.head_dim);
         q4_kv_layout kv = layer_kv(d, l);
         attn = std::max(attn, gqa_decode_attn_workspace(&kv, d.n_q_heads, l.window));
+        need_mv(l.wqkv, layer_qkv_rows(d, l), d.d_model);
+        need_mv(l.wo, d.d_model, d.n_q_heads * l.head_dim);
+        need_mv(l.wgu, 2 * d.ffn, d.d_model);
+        need_mv(l.wd, d.d_model, d.ffn);
     }
+    need_mv(d.embed, d.vocab, d.d_model);
     Layout L;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -99,6 +115,8 @@ Layout plan(const q4_model_desc &d) {
     L.att = take(sizeof(float) * B * att);
     L.gu = take(sizeof(float) * B * 2 * d.ffn);
     L.logits = take(sizeof(float) * B * d.vocab);
+    L.mv = take(mv);
+    L.mv_bytes = mv;
     L.attn = take(attn);
     L.total = o;
     return L;
@@ -153,6 +171,19 @@ bool fits(const q4_decode_model *m, int64_t pos) {
         if (s_ != Q4_OK) return s_;           \
     } while (0)
 
+// One projection of the step: matrix cores for two or more sequences,
+// otherwise the vector-unit kernels.
+q4_status project(q4_decode_model *m, int fmt, const void *W, int64_t N, int64_t K, const float *x,
+                  const float *x2, int64_t ldx, q4_input_op op, const float *nw, float *y,
+                  const float *res, void *s) {
+    const q4_model_desc &d = m->desc;
+    if (m->mv_ws && batched_ok(d, W, K))
+        return (fmt == 0 ? q4_0_matvec_batched : q8_0_matvec_batched)(
+            W, N, K, x, x2, ldx, d.batch, op, nw, d.eps, y, res, m->mv_ws, m->mv_ws_bytes, s);
+    return (fmt == 0 ? q4_0_matvec_fused : q8_0_matvec_fused)(W, N, K, x, x2, ldx, d.batch, op, nw,
+                                                              d.eps, y, res, s);
+}
+
 // Enqueues one whole step on s.
 q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, float *logits,
                        hipStream_t s) {
@@ -165,24 +196,24 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         const int64_t hd = l.head_dim, nq = d.n_q_heads * hd, nk = l.n_kv_heads * hd;
         const int64_t nqkv = layer_qkv_rows(d, l);
         // attention RMSNorm fused into the QKV projection's input
-        Q4_TRY(q4_0_matvec_fused(l.wqkv, nqkv, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, l.attn_norm,
-                                 d.eps, m->qkv, nullptr, sv));
+        Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, l.attn_norm, m->qkv,
+                       nullptr, sv));
         Q4_TRY(qk_norm_rope(m->qkv, nqkv, m->qkv + nq, l.v_from_k ? nullptr : m->qkv + nq + nk, nqkv,
                             l.q_norm, l.k_norm, d.n_q_heads, &m->kv[i], m->pos_dev, l.rope_theta,
                             d.eps, l.v_from_k, l.k_cache, l.v_cache, sv));
         Q4_TRY(gqa_decode_attn(m->qkv, nqkv, d.n_q_heads, l.k_cache, l.v_cache, &m->kv[i],
                                m->pos_dev + 1, l.window, l.attn_scale, m->att, nq, m->attn_ws,
                                m->attn_ws_bytes, sv));
-        Q4_TRY(q4_0_matvec(l.wo, D, nq, m->att, B, m->x, m->x, sv));
+        Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, nullptr, m->x, m->x, sv));
         // FFN RMSNorm fused into gate|up; SwiGLU fused into the down projection
-        Q4_TRY(q4_0_matvec_fused(l.wgu, 2 * F, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, l.ffn_norm,
-                                 d.eps, m->gu, nullptr, sv));
-        Q4_TRY(q4_0_matvec_fused(l.wd, D, F, m->gu, m->gu + F, 2 * F, B, Q4_IN_SWIGLU, nullptr, 0.f,
-                                 m->x, m->x, sv));
+        Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, l.ffn_norm, m->gu,
+                       nullptr, sv));
+        Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, Q4_IN_SWIGLU, nullptr, m->x, m->x,
+                       sv));
     }
     float *lg = logits ? logits : m->logits;
-    Q4_TRY(q8_0_matvec_fused(d.embed, d.vocab, D, m->x, nullptr, D, B, Q4_IN_RMSNORM, d.final_norm,
-                             d.eps, lg, nullptr, sv));
+    Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, d.final_norm, lg,
+                   nullptr, sv));
     Q4_TRY(argmax_rows(lg, B, d.vocab, next, sv));
     hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, s, m->pos_dev);
     return q4::launch_status("decode_step (advance)");
@@ -235,6 +266,8 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     m->logits = reinterpret_cast<float *>(base + L.logits);
     m->attn_ws = base + L.attn;
     m->attn_ws_bytes = L.total - L.attn;
+    m->mv_ws = L.mv_bytes ? base + L.mv : nullptr;
+    m->mv_ws_bytes = L.mv_bytes;
     hipError_t e = hipStreamCreateWithFlags(&m->capture, hipStreamNonBlocking);
     if (e != hipSuccess) {
         delete m;

@@ -74,6 +74,15 @@ def test_decode_lockstep_per_op(dev, shape):
     B, D, Hq, F, eps = m.batch, m.d_model, m.n_q_heads, m.ffn, m.eps
     pos = m.start_pos
     tok = torch.from_numpy(wl.start_tokens(m)).to(dev)
+
+    def proj(fmt, W, xx, K, ld, op, **kw):
+        # the step runs its projections on the matrix cores when B >= 2
+        if B >= 2 and K % 256 == 0:
+            fn = q.q4_0_matvec_batched if fmt == 4 else q.q8_0_matvec_batched
+        else:
+            fn = q.q4_0_matvec_fused if fmt == 4 else q.q8_0_matvec_fused
+        return fn(W, xx, K, B, ld, op, eps=eps, **kw)
+
     pos_d = torch.tensor([pos, pos + 1], dtype=torch.int64, device=dev)
     x = q.q8_0_gather(dmod["embed"], tok, D)
     _check(x, oracle.q8_0_gather(weights["embed"], m.vocab, D, tok.cpu().numpy()),
@@ -84,7 +93,7 @@ def test_decode_lockstep_per_op(dev, shape):
         hd, hkv = ly.head_dim, ly.n_kv_heads
         nq, nk, nv = wl.layer_rows(m, ly)
         nqkv = nq + nk + nv
-        qkv = q.q4_0_matvec_fused(L["wqkv"], x, D, B, D, q.IN_RMSNORM, norm_w=L["attn_norm"], eps=eps)
+        qkv = proj(4, L["wqkv"], x, D, D, q.IN_RMSNORM, norm_w=L["attn_norm"])
         r, t = oracle.q4_0_matvec(W["wqkv"], nqkv, D, oracle.rmsnorm(np_(x), W["attn_norm"], eps))
         _check(qkv, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + qkv matvec")
         raw = np_(qkv).copy()
@@ -114,20 +123,19 @@ def test_decode_lockstep_per_op(dev, shape):
                                             ly.attn_scale)
             _check(att[b], o, 2e-4 * bound + 1e-6, f"L{l} attention")
         xo = np_(x)
-        q.q4_0_matvec(L["wo"], att, y=x, residual=x)
+        proj(4, L["wo"], att, nq, nq, q.IN_PLAIN, y=x, residual=x)
         r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att), res=xo)
         _check(x, r, 2e-4 * t + 1e-6, f"L{l} o-proj + residual")
-        gu = q.q4_0_matvec_fused(L["wgu"], x, D, B, D, q.IN_RMSNORM, norm_w=L["ffn_norm"], eps=eps)
+        gu = proj(4, L["wgu"], x, D, D, q.IN_RMSNORM, norm_w=L["ffn_norm"])
         r, t = oracle.q4_0_matvec(W["wgu"], 2 * F, D, oracle.rmsnorm(np_(x), W["ffn_norm"], eps))
         _check(gu, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + gate|up")
         g64 = np_(gu)
         h = np.stack([oracle.swiglu(g64[b, :F], g64[b, F:]) for b in range(B)])
         xo = np_(x)
-        q.q4_0_matvec_fused(L["wd"], gu, F, B, 2 * F, q.IN_SWIGLU, x2=gu[:, F:], y=x, residual=x)
+        proj(4, L["wd"], gu, F, 2 * F, q.IN_SWIGLU, x2=gu[:, F:], y=x, residual=x)
         r, t = oracle.q4_0_matvec(W["wd"], D, F, h, res=xo)
         _check(x, r, 2e-4 * t + 1e-6, f"L{l} swiglu + down + residual")
-    logits = q.q8_0_matvec_fused(dmod["embed"], x, D, B, D, q.IN_RMSNORM,
-                                 norm_w=dmod["final_norm"], eps=eps)
+    logits = proj(8, dmod["embed"], x, D, D, q.IN_RMSNORM, norm_w=dmod["final_norm"])
     r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D,
                               oracle.rmsnorm(np_(x), weights["final_norm"], eps))
     _check(logits, r, 2e-4 * t + 1e-6, "final rmsnorm + logits")

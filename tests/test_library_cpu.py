@@ -55,3 +55,20 @@ def test_matvec_rejects_bad_arguments_on_host():
     assert st == "Q4_ERR_ALIGNMENT" and "aligned" in msg
     assert _status(L.q8_0_gather, fake, 10, 33, fake, 1, fake, None)[0] == "Q4_ERR_SHAPE"
     assert _status(L.q8_0_gather, None, 10, 32, fake, 1, fake, None)[0] == "Q4_ERR_INVALID_ARG"
+
+
+def test_batched_matvec_rejects_bad_arguments_on_host():
+    L = q.lib()
+    fake = 0x10000
+    need = q.matvec_batched_workspace(100, 512, 4)
+    assert need > 0
+    assert q.matvec_batched_workspace(100, 288, 4) == 0    # K % 256 != 0
+    assert q.matvec_batched_workspace(100, 512, 9) == 0    # B > 8
+    args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, None, 0.0, fake, None,
+                                        ws, nbytes, None)
+    assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake, need - 1))[0] == "Q4_ERR_WORKSPACE"
+    assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake + 16, need))[0] == "Q4_ERR_WORKSPACE"
+    assert _status(L.q4_0_matvec_batched, *args(fake, 288, 4, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
+    assert _status(L.q4_0_matvec_batched, *args(fake, 512, 9, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
+    assert _status(L.q8_0_matvec_batched, *args(fake + 2, 512, 4, fake, need))[0] == "Q4_ERR_ALIGNMENT"
+    assert _status(L.q4_0_matvec_batched, *args(None, 512, 4, fake, need))[0] == "Q4_ERR_INVALID_ARG"

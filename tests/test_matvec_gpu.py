@@ -160,3 +160,116 @@ def test_matvec_fused_input_parity(dev, fmt, n, k, b, op):
        norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6, y=yr, residual=yr)
     torch.cuda.synchronize()
     _check(yr, ref, terms, f"{fmt} fused {op} {n}x{k} B={b}")
+
+
+BATCHED_CASES = [
+    # (fmt, N, K, B, op): one split (S = 1) and K split over workgroups (S > 1),
+    # ragged row tails, every batch count, each input transform
+    ("q4", 67, 256, 2, "plain"), ("q4", 16, 256, 1, "plain"), ("q4", 1000, 2560, 8, "rms"),
+    ("q4", 300, 9728, 8, "swiglu"), ("q4", 2560, 4096, 8, "plain"), ("q4", 777, 5376, 3, "plain"),
+    ("q4", 33, 512, 5, "rms_unit"), ("q4", 6144, 2560, 8, "rms"), ("q4", 130, 21504, 7, "swiglu"),
+    ("q8", 500, 2560, 8, "rms"), ("q8", 100, 256, 4, "plain"), ("q8", 3001, 2560, 6, "plain"),
+]
+
+
+def _fused_inputs(fmt, n, k, b, op, seed):
+    gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
+    W = gen(seed, f"t.batched.{fmt}.{n}.{k}", n, k)
+    ld = 2 * k if op == "swiglu" else k
+    xa = synth.normal_f32(seed, f"t.batched.x.{k}.{b}", (b, ld)) * 2.0
+    w = synth.uniform_f32(seed, f"t.batched.w.{k}", (k,), 0.8, 1.2)
+    r = synth.normal_f32(seed, f"t.batched.r.{n}.{b}", (b, n))
+    if op == "swiglu":
+        xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
+    elif op == "plain":
+        xin = xa[:, :k].astype(np.float64)
+    else:
+        xin = oracle.rmsnorm(xa[:, :k], None if op == "rms_unit" else w, 1e-6)
+    return W, xa, w, r, xin, ld
+
+
+_KIND = {"plain": q.IN_PLAIN, "rms": q.IN_RMSNORM, "rms_unit": q.IN_RMSNORM, "swiglu": q.IN_SWIGLU}
+
+
+@pytest.mark.parametrize("fmt,n,k,b,op", BATCHED_CASES)
+def test_matvec_batched_parity(dev, fmt, n, k, b, op):
+    _say(f"{fmt} batched {op} N={n} K={k} B={b}")
+    orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
+    fn = q.q4_0_matvec_batched if fmt == "q4" else q.q8_0_matvec_batched
+    W, xa, w, r, xin, ld = _fused_inputs(fmt, n, k, b, op, 107)
+    ref, terms = orc(W, n, k, xin, res=r)
+    xd = torch.from_numpy(xa).to(dev)
+    yr = torch.from_numpy(r).to(dev)
+    Wd = torch.from_numpy(W).to(dev)
+    kw = dict(x2=xd[:, k:] if op == "swiglu" else None,
+              norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
+    y0 = fn(Wd, xd, k, b, ld, _KIND[op], **kw)
+    fn(Wd, xd, k, b, ld, _KIND[op], y=yr, residual=yr, **kw)
+    torch.cuda.synchronize()
+    _check(yr, ref, terms, f"{fmt} batched {op} {n}x{k} B={b}")
+    # without the residual, and bitwise repeatable
+    y1 = fn(Wd, xd, k, b, ld, _KIND[op], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1), "repeated launches differ bitwise"
+    ref0, terms0 = orc(W, n, k, xin)
+    _check(y0, ref0, terms0, f"{fmt} batched {op} {n}x{k} B={b} no residual")
+
+
+def test_matvec_batched_row_scales(dev):
+    """Rows of very different magnitude (and an all-zero row) keep the
+    relative accuracy: each row is scaled by its own power of two."""
+    _say("q4 batched row scales")
+    n, k, b = 200, 2048, 6
+    W = synth.q4_0_matrix(108, "t.batched.scales", n, k)
+    x = synth.normal_f32(108, "t.batched.scales.x", (b, k))
+    x = x * np.array([1.0, 3e4, 1e-6, 0.0, 7e-3, 1e9], dtype=np.float32)[:, None]
+    ref, terms = oracle.q4_0_matvec(W, n, k, x)
+    y = q.q4_0_matvec_batched(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev), k, b, k)
+    torch.cuda.synchronize()
+    _check(y, ref, terms, "row scales")
+    assert torch.all(y[3] == 0)
+
+
+def test_matvec_batched_matches_fused_path(dev):
+    """The matrix-core path and the vector path agree within the bound on the
+    attention-output shape of the 4B model at B = 8."""
+    _say("batched vs fused, 2560x4096 B=8")
+    n, k, b = 2560, 4096, 8
+    W = torch.from_numpy(synth.q4_0_matrix(109, "t.batched.vs", n, k)).to(dev)
+    x = torch.from_numpy(synth.normal_f32(109, "t.batched.vs.x", (b, k))).to(dev)
+    y1 = q.q4_0_matvec_batched(W, x, k, b, k)
+    y2 = q.q4_0_matvec(W, x)
+    torch.cuda.synchronize()
+    ref, terms = oracle.q4_0_matvec(W.cpu().numpy(), n, k, x.cpu().numpy())
+    _check(y1, ref, terms, "batched")
+    _check(y2, ref, terms, "fused")
+
+
+def test_matvec_batched_5376x21504_B8_full(dev):
+    """The 31B FFN-shape workload at B = 8, every output."""
+    _say("q4_0_matvec_batched 5376x21504 B=8 full")
+    w = wl.MATVEC_5376x21504
+    W, x = wl.matvec_inputs(w, 8)
+    ref, terms = oracle.q4_0_matvec(W, w.n, w.k, x)
+    Wd = torch.from_numpy(W).to(dev)
+    xd = torch.from_numpy(x).to(dev)
+    y1 = q.q4_0_matvec_batched(Wd, xd, w.k, 8, w.k)
+    y2 = q.q4_0_matvec_batched(Wd, xd, w.k, 8, w.k)
+    torch.cuda.synchronize()
+    _check(y1, ref, terms, "5376x21504 B=8 batched")
+    assert torch.equal(y1, y2)
+
+
+def test_matvec_batched_workspace_errors(dev):
+    n, k, b = 100, 512, 4
+    W = torch.from_numpy(synth.q4_0_matrix(110, "t.batched.err", n, k)).to(dev)
+    x = torch.zeros((b, k), dtype=torch.float32, device=dev)
+    need = q.matvec_batched_workspace(n, k, b)
+    small = torch.empty(need - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(q.Q4Error) as e:
+        q.q4_0_matvec_batched(W, x, k, b, k, ws=small)
+    assert e.value.status_name == "Q4_ERR_WORKSPACE"
+    with pytest.raises(q.Q4Error) as e:
+        q.q4_0_matvec_batched(torch.zeros((n, 9 * 18), dtype=torch.uint8, device=dev),
+                              torch.zeros((b, 288), dtype=torch.float32, device=dev), 288, b, 288)
+    assert e.value.status_name == "Q4_ERR_UNSUPPORTED"
