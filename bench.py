@@ -56,7 +56,7 @@ def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):
     """As time_matvec for the matrix-core path (prep + main kernel per call)."""
     stream = torch.cuda.current_stream()
     N = y.shape[1]
-    ws = torch.empty(q.matvec_batched_workspace(N, K, B), dtype=torch.uint8, device=x.device)
+    ws = torch.zeros(q.matvec_batched_workspace(N, K, B), dtype=torch.uint8, device=x.device)
     for i in range(warmup):
         q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws)
     torch.cuda.synchronize()

@@ -103,18 +103,20 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                             float *y, const float *residual, void *stream);
 
 /* q4_0_matvec_batched / q8_0_matvec_batched: the same products as the fused
- * calls, computed on the matrix cores (binary16 MFMA with every weight and
- * every activation represented exactly: activations are split into two
- * halves after a per-row power-of-two scaling), for 1 <= B <= 8 activation
- * rows; meant for B >= 2, where eight products per weight outrun the vector
- * units.  Products are formed exactly and summed in fp32.
+ * calls, computed on the matrix cores for 1 <= B <= 8 activation rows; meant
+ * for B >= 2, where eight products per weight outrun the vector units.
+ * Operands are exact binary16 (codes as integers; activations, after a
+ * power-of-two scaling per row and per 256 k, split into two halves), so
+ * every product is exact and sums are fp32.  RMSNorm's 1/rms is applied to
+ * the finished sums.  One kernel launch; bitwise reproducible.
  *   W         16-byte aligned; K % 256 == 0 (else Q4_ERR_UNSUPPORTED)
- *   x, x2     16-byte aligned, ld_x % 4 == 0
+ *   x, x2     16-byte aligned, ld_x % 4 == 0; norm_w 16-byte aligned
+ *   y         must not overlap x or x2 (Q4_ERR_INVALID_ARG); may alias residual
  *   ws        device workspace of at least matvec_batched_workspace(N, K, B)
- *             bytes, 256-byte aligned, owned by the caller; its contents
- *             need no initialisation and are overwritten by every call, so
- *             calls sharing one workspace must be ordered (one stream).
- * Two kernels are enqueued on `stream`.  Results are bitwise reproducible.
+ *             bytes, 256-byte aligned, owned by the caller.  Its first 16 KiB
+ *             (split tickets) must be zero before the first call that uses
+ *             it; every call leaves them zero.  Calls sharing a workspace
+ *             must be ordered (one stream).
  * Other arguments and errors as q4_0_matvec_fused, plus Q4_ERR_WORKSPACE. */
 size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B);
 q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,

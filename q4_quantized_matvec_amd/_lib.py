@@ -200,8 +200,8 @@ def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual,
     N = n if n is not None else _qmatrix_dims(W, K, bpb)
     if y is None:
         y = torch.empty((B, N), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = torch.empty(max(256, matvec_batched_workspace(N, K, B)), dtype=torch.uint8,
+    if ws is None:  # split tickets must start at zero
+        ws = torch.zeros(max(256, matvec_batched_workspace(N, K, B)), dtype=torch.uint8,
                          device=x.device)
     _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op),
                                       _ptr(norm_w), float(eps), _ptr(y), _ptr(residual),
@@ -212,7 +212,8 @@ def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual,
 def q4_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
                         residual=None, ws=None, stream=None, n=None):
     """As q4_0_matvec_fused, on the matrix cores (1 <= B <= 8, K % 256 == 0).  ``ws``: a
-    uint8 device tensor of matvec_batched_workspace(N, K, B) bytes (allocated if None)."""
+    zero-initialised uint8 device tensor of matvec_batched_workspace(N, K, B) bytes, reusable
+    across calls on one stream (allocated if None)."""
     return _matvec_batched("q4_0_matvec_batched", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,
                            residual, ws, stream, n)
 

@@ -275,6 +275,8 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     }
     hipLaunchKernelGGL(set_position_kernel, dim3(1), dim3(1), 0, m->capture, m->pos_dev, int64_t(0));
     e = hipGetLastError();
+    // the matrix-core matvec's split tickets start at zero (each call leaves them so)
+    if (e == hipSuccess && m->mv_ws) e = hipMemsetAsync(m->mv_ws, 0, m->mv_ws_bytes, m->capture);
     if (e == hipSuccess) e = hipStreamSynchronize(m->capture);
     if (e != hipSuccess) {
         (void)hipStreamDestroy(m->capture);

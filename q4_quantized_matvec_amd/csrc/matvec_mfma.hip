@@ -4,37 +4,40 @@
 // Definition ("Research record" page, "Native Metal diagnostic: buffer
 // ownership": 18-byte Q4_0 blocks, weight = (quant - 8) * scale; "Verified
 // model facts": the Q8_0 token table):
-//   y[b][n] = sum_k d[n][k/32] * c[n][k] * x[b][k]   (+ residual[b][n]),
+//   y[b][n] = sum_k d[n][k/32] * c[n][k] * op(x)[b][k]   (+ residual[b][n]),
 // c = q - 8 (Q4_0) or the int8 code q (Q8_0).
 //
-// With eight activation rows every weight feeds eight products, which is more
-// than the vector ALUs can keep up with at HBM speed; v_mfma_f32_16x16x32_f16
-// takes them instead, one Q4_0 block (32 k) per instruction, so the block
-// scale is applied once per 16x16 result tile:
-//   D[i][n] = sum_{k in block} X[i][k] * c[n][k] ,  y += d[n][block] * D .
-// Operands are exact in binary16: c is an integer of at most 8 bits, and the
-// activations are carried as two halves, X = hi + lo with
-// hi = fp16(s_b x), lo = fp16(s_b x - hi) (22 significant bits), so the 16
-// MFMA rows are 8 batch rows x {hi, lo} and every product is exact.  s_b is a
-// power of two per batch row that puts max |s_b x| in [2^12, 2^13): binary16
-// can neither overflow nor lose the small elements, and dividing by s_b at
-// the end is exact.
+// With eight activation rows every weight feeds eight products, more than the
+// vector ALUs sustain at HBM speed; v_mfma_f32_16x16x32_f16 takes them, one
+// block (32 k) per instruction, so the block scale is applied once per 16 x 16
+// result tile:
+//   D[i][n] = sum_{k in block} X[i][k] * c[n][k] ,   acc += d[n][block] * D .
+// Both operands are exact in binary16.  c is an integer of at most 8 bits
+// (built as 1024 + q with one mask-or, then one packed subtract).  The
+// activations of each step of 256 k are scaled by a power of two s per batch
+// row, chosen so that the largest |s x| lies in [2^11, 2^12), and carried as
+// two halves, hi = fp16(s x) and lo = fp16(s x - hi), 22 significant bits: the
+// 16 MFMA rows are 8 batch rows x {hi, lo}, every product is exact, and 1/s is
+// applied exactly to the step's partial sums.
 //
-// Two launches:
-//  * prep (one workgroup per batch slot): applies the input transform (plain,
-//    RMSNorm, SwiGLU), finds s_b and writes the activations in MFMA operand
-//    order, XF[block][lane] = 8 halves; it also clears the split counters.
-//  * main: a wavefront owns 16 output rows and walks K in steps of 8 blocks.
-//    Lane (n, g) = (lane % 16, lane / 16) loads 2 consecutive blocks of row n
-//    (36 or 68 contiguous bytes, 4-byte aligned); permlane16/32 swaps
-//    transpose the 4 x 4 lane groups so that for every block lane group g
-//    holds its part of the codes (Q4_0: payload bytes 4g..4g+3, i.e. elements
-//    4g..4g+3 in low nibbles and 4g+16..4g+19 in high nibbles, the high ones
-//    kept x16 and paired with activations / 16; Q8_0: payload bytes
-//    8g..8g+7).  Codes become halves with one mask-or (1024 + q) and one
-//    packed subtract.  K is split over S workgroups when the row count alone
-//    cannot fill the chip; their partial sums are added in a fixed order by
-//    whichever workgroup finishes last, so results are bitwise reproducible.
+// One kernel.  A workgroup (4 wavefronts) owns 64 output rows and a range of
+// K steps; per step of 8 blocks:
+//  * operand build: each wavefront converts 2 of the 8 blocks for all batch
+//    rows (applying the input transform: gain multiply for RMSNorm, SiLU(x)*u
+//    for SwiGLU), the step's per-row maxima meet in LDS, and the halves are
+//    written to LDS in MFMA operand order;
+//  * weights: lane (n, g) = (lane % 16, lane / 16) of a wavefront holds 2
+//    consecutive blocks of row n (36 or 68 contiguous bytes, loaded one step
+//    ahead); permlane32/16 swaps transpose the 4 x 4 lane groups so that for
+//    every block lane group g holds its share of the codes (Q4_0: payload
+//    bytes 4g..4g+3, i.e. elements 4g..4g+3 as low nibbles and 4g+16..4g+19 as
+//    high nibbles, the latter kept x16 and paired with activations / 16;
+//    Q8_0: payload bytes 8g..8g+7); 8 MFMAs per wavefront.
+// RMSNorm's 1/rms factor is common to a whole row, so it is applied to the
+// finished sums; the sums of squares are gathered from the same operand
+// build.  K is split over S workgroups when the row count alone cannot fill
+// the chip; the partial sums are added in split order by whichever workgroup
+// of the row range finishes last, so results are bitwise reproducible.
 #include "common.hpp"
 
 namespace {
@@ -46,12 +49,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_al4_t __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4_al16_t __attribute__((ext_vector_type(4), aligned(16)));
 
-constexpr int kWG = 256;          // 4 wavefronts
-constexpr int kRowsWG = 64;       // 16 rows per wavefront
-constexpr int kSeg = 8;           // blocks per wavefront step (one MFMA each)
-constexpr int kTargetWGs = 1024;  // about 4 workgroups per compute unit
-constexpr int kPrepThreads = 256;  // one workgroup converts 64 blocks of one row
+constexpr int kWG = 256;            // 4 wavefronts
+constexpr int kRowsWG = 64;         // 16 rows per wavefront
+constexpr int kSeg = 8;             // blocks per step (one MFMA each per wavefront)
+constexpr int kTargetWGs = 1024;    // about 4 workgroups per compute unit
 constexpr int kMaxB = 8;
+constexpr int kCounters = 4096;     // split tickets: row ranges of a K-split launch
+constexpr size_t kCounterBytes = kCounters * sizeof(int);
 
 template <int FMT>
 struct BF;
@@ -68,115 +72,55 @@ struct BF<1> {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// Offset of element e (0..7) of lane group g inside a block, and its
-// activation factor (high Q4_0 nibbles are kept x16 in the weight operand).
+// Offset inside a block of element e (0..7) of lane group g.
 template <int FMT>
 __device__ __forceinline__ int elem_of(int g, int e) {
     if constexpr (FMT == 0) return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
     else return 8 * g + e;
 }
 
-// ---------------------------------------------------------------- prep kernel
-template <int FMT, int KIND>
-__global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(
-    const float *__restrict__ x, const float *__restrict__ u, const float *__restrict__ nw,
-    float eps, int64_t ld, int K, int B, u32x4_t *__restrict__ xf, float *__restrict__ sinv,
-    int *__restrict__ counters, int n_counters) {
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nb = K / 32;
-    if (b == 0 && blockIdx.y == 0)
-        for (int i = tid; i < n_counters; i += kPrepThreads) counters[i] = 0;
-    const bool live = b < B;
-    float s = 0.f, inv = 1.f;
-    if (live) {
-        const float *xr = x + static_cast<int64_t>(b) * ld;
-        const float *ur = KIND == 2 ? u + static_cast<int64_t>(b) * ld : nullptr;
-        float ss = 0.f, mx = 0.f;
-        for (int k = tid; k < K; k += kPrepThreads) {
-            float v = xr[k];
-            if constexpr (KIND == 1) {
-                ss = fmaf(v, v, ss);
-                v = v * (nw ? nw[k] : 1.0f);
-            } else if constexpr (KIND == 2) {
-                v = silu_mul(v, ur[k]);
-            }
-            mx = fmaxf(mx, fabsf(v));
-        }
-        __shared__ float red_s[kPrepThreads / 64], red_m[kPrepThreads / 64];
-        const float ws = wave_sum(ss), wm = wave_max(mx);
-        if ((tid & 63) == 0) {
-            red_s[tid >> 6] = ws;
-            red_m[tid >> 6] = wm;
-        }
-        __syncthreads();
-        float tss = 0.f, tmx = 0.f;
-        for (int w = 0; w < kPrepThreads / 64; ++w) {
-            tss += red_s[w];
-            tmx = fmaxf(tmx, red_m[w]);
-        }
-        if constexpr (KIND == 1) {
-            inv = 1.0f / sqrtf(tss / static_cast<float>(K) + eps);
-            tmx = tmx * inv;
-        }
-        int e = 0;
-        if (tmx > 0.f && tmx <= 3.4e38f) (void)frexpf(tmx, &e);
-        const int sh = min(max(13 - e, -120), 120);
-        s = (tmx <= 3.4e38f) ? ldexpf(1.0f, sh) : 1.0f;  // inf / nan rows keep scale 1
-        if (tid == 0 && blockIdx.y == 0) sinv[b] = (tmx <= 3.4e38f) ? ldexpf(1.0f, -sh) : 1.0f;
-    } else if (tid == 0 && blockIdx.y == 0) {
-        sinv[b] = 0.f;
-    }
-    const float *xr = x + static_cast<int64_t>(live ? b : 0) * ld;
-    const float *ur = KIND == 2 ? u + static_cast<int64_t>(live ? b : 0) * ld : nullptr;
-    const int it = blockIdx.y * kPrepThreads + tid;  // (block, lane group) item
-    if (it < nb * 4) {
-        const int j = it >> 2, g = it & 3;
-        half8_t hi, lo;
-        if (live) {
-            // Two runs of 4 contiguous elements (x and u are 16-byte aligned).
-            const int k0 = 32 * j + elem_of<FMT>(g, 0);
-            const int k1 = 32 * j + elem_of<FMT>(g, 4);
-            float v[8];
-            const f32x4_al16_t a0 = *reinterpret_cast<const f32x4_al16_t *>(xr + k0);
-            const f32x4_al16_t a1 = *reinterpret_cast<const f32x4_al16_t *>(xr + k1);
-            v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-            v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
-            if constexpr (KIND == 2) {
-                const f32x4_al16_t b0 = *reinterpret_cast<const f32x4_al16_t *>(ur + k0);
-                const f32x4_al16_t b1 = *reinterpret_cast<const f32x4_al16_t *>(ur + k1);
-                v[0] = silu_mul(v[0], b0.x); v[1] = silu_mul(v[1], b0.y);
-                v[2] = silu_mul(v[2], b0.z); v[3] = silu_mul(v[3], b0.w);
-                v[4] = silu_mul(v[4], b1.x); v[5] = silu_mul(v[5], b1.y);
-                v[6] = silu_mul(v[6], b1.z); v[7] = silu_mul(v[7], b1.w);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float t = v[e];
-                if constexpr (KIND == 1) {
-                    const int k = (e < 4 ? k0 + e : k1 + e - 4);
-                    t = t * inv * (nw ? nw[k] : 1.0f);
-                }
-                t *= s;
-                if (FMT == 0 && e >= 4) t *= 0.0625f;
-                const _Float16 h = static_cast<_Float16>(t);
-                hi[e] = h;
-                lo[e] = static_cast<_Float16>(t - static_cast<float>(h));
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                hi[e] = static_cast<_Float16>(0.0f);
-                lo[e] = static_cast<_Float16>(0.0f);
-            }
-        }
-        u32x4_t *dst = xf + static_cast<int64_t>(j) * 64 + 16 * g + 2 * b;
-        dst[0] = __builtin_bit_cast(u32x4_t, hi);
-        dst[1] = __builtin_bit_cast(u32x4_t, lo);
-    }
+// Power-of-two exponent that puts m (the largest magnitude of a step) in
+// [2^11, 2^12); 0 for zero, infinite or NaN maxima (values pass unscaled).
+__device__ __forceinline__ int step_shift(float m) {
+    if (!(m > 0.f) || !(m <= 3.4e38f)) return 0;
+    int e;
+    (void)frexpf(m, &e);
+    return min(max(12 - e, -120), 120);
 }
 
-// ---------------------------------------------------------------- main kernel
+__device__ __forceinline__ float max4(f32x4_t v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+// A copy the compiler cannot see through.  When both results of one
+// permlane swap are reinterpreted as floating point, this compiler has been
+// seen to merge the two reinterpretations into one (computing a[0] + a[0]
+// for a[0] + a[1]); every second result that is used as a float or half is
+// therefore passed through this copy first.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Maximum over the 4 lanes l, l^16, l^32, l^48; every one of them receives it.
+__device__ __forceinline__ float rows_max(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, opaque_copy(a[1])));
+    const uint32_t um = __builtin_bit_cast(uint32_t, m);
+    auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
+    return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, opaque_copy(b[1])));
+}
+// Sum over the 4 lanes l, l^16, l^32, l^48; every one of them receives the
+// same bits (both steps add commutatively).
+__device__ __forceinline__ float rows_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = __builtin_bit_cast(float, a[0]) + __builtin_bit_cast(float, opaque_copy(a[1]));
+    const uint32_t um = __builtin_bit_cast(uint32_t, m);
+    auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
+    return __builtin_bit_cast(float, b[0]) + __builtin_bit_cast(float, opaque_copy(b[1]));
+}
+
 // Lane groups 0..3 hold v_t for t = 0..3; afterwards v_s at lane group g is
 // the old v_g of lane group s (a 4 x 4 transpose across the 16-lane rows).
 __device__ __forceinline__ void transpose4(uint32_t &v0, uint32_t &v1, uint32_t &v2, uint32_t &v3) {
@@ -236,13 +180,53 @@ __device__ __forceinline__ void load_seg(const uint8_t *p, uint32_t (&dw)[DW]) {
     dw[DW - 1] = *reinterpret_cast<const uint32_t *>(p + 4 * (DW - 1));
 }
 
+// The 8 weight operands of one step from a lane's two-block window.
 template <int FMT>
+__device__ __forceinline__ void weight_operands(const uint32_t (&dw)[BF<FMT>::kLaneDw], half8_t (&wf)[kSeg]) {
+    if constexpr (FMT == 0) {
+        // even block: payload at byte 2 of the window; odd block: at byte 20
+        uint32_t e0 = __builtin_amdgcn_alignbyte(dw[1], dw[0], 2);
+        uint32_t e1 = __builtin_amdgcn_alignbyte(dw[2], dw[1], 2);
+        uint32_t e2 = __builtin_amdgcn_alignbyte(dw[3], dw[2], 2);
+        uint32_t e3 = __builtin_amdgcn_alignbyte(dw[4], dw[3], 2);
+        uint32_t o0 = dw[5], o1 = dw[6], o2 = dw[7], o3 = dw[8];
+        transpose4(e0, e1, e2, e3);
+        transpose4(o0, o1, o2, o3);
+        wf[0] = q4_codes(e0); wf[1] = q4_codes(o0);
+        wf[2] = q4_codes(e1); wf[3] = q4_codes(o1);
+        wf[4] = q4_codes(e2); wf[5] = q4_codes(o2);
+        wf[6] = q4_codes(e3); wf[7] = q4_codes(o3);
+    } else {
+        uint32_t e[8], o[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            e[t] = __builtin_amdgcn_alignbyte(dw[t + 1], dw[t], 2);
+            o[t] = dw[9 + t];
+        }
+        transpose4(e[0], e[2], e[4], e[6]);
+        transpose4(e[1], e[3], e[5], e[7]);
+        transpose4(o[0], o[2], o[4], o[6]);
+        transpose4(o[1], o[3], o[5], o[7]);
+        wf[0] = q8_codes(e[0], e[1]); wf[1] = q8_codes(o[0], o[1]);
+        wf[2] = q8_codes(e[2], e[3]); wf[3] = q8_codes(o[2], o[3]);
+        wf[4] = q8_codes(e[4], e[5]); wf[5] = q8_codes(o[4], o[5]);
+        wf[6] = q8_codes(e[6], e[7]); wf[7] = q8_codes(o[6], o[7]);
+    }
+}
+
+template <int FMT, int KIND>
 __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
-    const uint8_t *__restrict__ W, int N, int K, int B, const u32x4_t *__restrict__ xf,
-    const float *__restrict__ sinv, float *y, const float *res, float *__restrict__ part,
-    int *__restrict__ counters, int S, int cps) {
+    const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
+    const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
+    const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
+    float *__restrict__ part, int S, int cps) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
+    __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
+    __shared__ f32x4_t stepmax[2][kMaxB];    // per batch row: the 4 wavefronts' maxima
+    __shared__ float ssq_w[4][kMaxB];
+    __shared__ int ticket;
+
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
@@ -252,92 +236,142 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     const int c0 = blockIdx.y * cps;
     const int c1 = min(kc, c0 + cps);
     const uint8_t *wrow = W + static_cast<int64_t>(nl) * nb * kBytes + g * 2 * kBytes;
+    const int64_t seg = kSeg * kBytes;
+    // operand-build role of this lane: MFMA row 2 * batch + {hi, lo}
+    const int xb = (lane & 15) >> 1, xp = lane & 1;
+    const bool xlive = xb < B;
+    const float *xr = x + static_cast<int64_t>(xlive ? xb : 0) * ld;
+    const float *ur = KIND == 2 ? u + static_cast<int64_t>(xlive ? xb : 0) * ld : nullptr;
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    const int64_t seg = kSeg * kBytes;
+    const f32x4_t one = {1.f, 1.f, 1.f, 1.f};
+    float ssq = 0.f;
     uint32_t dw[kDw], nx[kDw];
     load_seg<kDw>(wrow + c0 * seg, dw);
     for (int c = c0; c < c1; ++c) {
-        // activations of this step first, then the next step's weights, so
-        // waiting for the former never waits for the latter
-        u32x4_t xa[kSeg];
-        const u32x4_t *xp = xf + static_cast<int64_t>(c) * kSeg * 64 + lane;
+        const int buf = c & 1;
+        // ---- activations of this step, blocks 2wv and 2wv+1 (loaded before
+        // the next step's weights, so waiting for them never waits for those)
+        f32x4_t xv[2][2], tv[2][2];
 #pragma unroll
-        for (int jj = 0; jj < kSeg; ++jj) xa[jj] = xp[jj * 64];
+        for (int h = 0; h < 2; ++h) {
+            const int kb = 32 * (kSeg * c + 2 * wv + h);
+            const int k0 = kb + elem_of<FMT>(g, 0), k1 = kb + elem_of<FMT>(g, 4);
+            xv[h][0] = xlive ? *reinterpret_cast<const f32x4_al16_t *>(xr + k0) : zero;
+            xv[h][1] = xlive ? *reinterpret_cast<const f32x4_al16_t *>(xr + k1) : zero;
+            if constexpr (KIND == 1) {
+                tv[h][0] = (xlive && nw) ? *reinterpret_cast<const f32x4_al16_t *>(nw + k0) : one;
+                tv[h][1] = (xlive && nw) ? *reinterpret_cast<const f32x4_al16_t *>(nw + k1) : one;
+            } else if constexpr (KIND == 2) {
+                tv[h][0] = xlive ? *reinterpret_cast<const f32x4_al16_t *>(ur + k0) : zero;
+                tv[h][1] = xlive ? *reinterpret_cast<const f32x4_al16_t *>(ur + k1) : zero;
+            }
+        }
         load_seg<kDw>(wrow + min(c + 1, c1 - 1) * seg, nx);
 
-        // Block scales of this lane's two blocks, then every lane group's.
-        uint32_t dp = __builtin_amdgcn_perm(dw[(kDw - 1) / 2], dw[0], 0x07060100u);
+        float v[2][8];
+        float lm = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = xv[h][e >> 2][e & 3];
+                float t = a;
+                if constexpr (KIND == 1) {
+                    ssq = fmaf(a, a, ssq);
+                    t = a * tv[h][e >> 2][e & 3];
+                } else if constexpr (KIND == 2) {
+                    t = silu_mul(a, tv[h][e >> 2][e & 3]);
+                }
+                v[h][e] = t;
+                lm = fmaxf(lm, fabsf(t));
+            }
+        }
+        lm = rows_max(lm);
+        if (g == 0 && xp == 0) stepmax[buf][xb][wv] = lm;
+        __syncthreads();
+        const float s = ldexpf(1.0f, step_shift(max4(stepmax[buf][xb])));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            half8_t hv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float t = v[h][e] * s;
+                if (FMT == 0 && e >= 4) t *= 0.0625f;
+                const _Float16 hi = static_cast<_Float16>(t);
+                hv[e] = xp == 0 ? hi : static_cast<_Float16>(t - static_cast<float>(hi));
+            }
+            frag[buf][2 * wv + h][lane] = __builtin_bit_cast(u32x4_t, hv);
+        }
+        // 1/s of the two batch rows whose sums this lane accumulates
+        const float fa = ldexpf(1.0f, -step_shift(max4(stepmax[buf][2 * g])));
+        const float fb = ldexpf(1.0f, -step_shift(max4(stepmax[buf][2 * g + 1])));
+        __syncthreads();
+
+        // ---- weights: the block scales of this lane's two blocks, then every
+        // lane group's, then the codes
+        const uint32_t dp = __builtin_amdgcn_perm(dw[(kDw - 1) / 2], dw[0], 0x07060100u);
         uint32_t dps[4];
         {
             auto r = __builtin_amdgcn_permlane32_swap(dp, dp, false, false);
             auto s01 = __builtin_amdgcn_permlane16_swap(r[0], r[0], false, false);
             auto s23 = __builtin_amdgcn_permlane16_swap(r[1], r[1], false, false);
             dps[0] = s01[0];
-            dps[1] = s01[1];
+            dps[1] = opaque_copy(s01[1]);
             dps[2] = s23[0];
-            dps[3] = s23[1];
+            dps[3] = opaque_copy(s23[1]);
         }
         half8_t wf[kSeg];
-        if constexpr (FMT == 0) {
-            // even block: payload at byte 2 of the lane's window; odd block: at byte 20
-            uint32_t e0 = __builtin_amdgcn_alignbyte(dw[1], dw[0], 2);
-            uint32_t e1 = __builtin_amdgcn_alignbyte(dw[2], dw[1], 2);
-            uint32_t e2 = __builtin_amdgcn_alignbyte(dw[3], dw[2], 2);
-            uint32_t e3 = __builtin_amdgcn_alignbyte(dw[4], dw[3], 2);
-            uint32_t o0 = dw[5], o1 = dw[6], o2 = dw[7], o3 = dw[8];
-            transpose4(e0, e1, e2, e3);
-            transpose4(o0, o1, o2, o3);
-            wf[0] = q4_codes(e0); wf[1] = q4_codes(o0);
-            wf[2] = q4_codes(e1); wf[3] = q4_codes(o1);
-            wf[4] = q4_codes(e2); wf[5] = q4_codes(o2);
-            wf[6] = q4_codes(e3); wf[7] = q4_codes(o3);
-        } else {
-            uint32_t e[8], o[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                e[t] = __builtin_amdgcn_alignbyte(dw[t + 1], dw[t], 2);
-                o[t] = dw[9 + t];
-            }
-            transpose4(e[0], e[2], e[4], e[6]);
-            transpose4(e[1], e[3], e[5], e[7]);
-            transpose4(o[0], o[2], o[4], o[6]);
-            transpose4(o[1], o[3], o[5], o[7]);
-            wf[0] = q8_codes(e[0], e[1]); wf[1] = q8_codes(o[0], o[1]);
-            wf[2] = q8_codes(e[2], e[3]); wf[3] = q8_codes(o[2], o[3]);
-            wf[4] = q8_codes(e[4], e[5]); wf[5] = q8_codes(o[4], o[5]);
-            wf[6] = q8_codes(e[6], e[7]); wf[7] = q8_codes(o[6], o[7]);
-        }
+        weight_operands<FMT>(dw, wf);
+        f32x4_t st = zero;
 #pragma unroll
         for (int jj = 0; jj < kSeg; ++jj) {
             const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8_t, xa[jj]), wf[jj], zero, 0, 0, 0);
+                __builtin_bit_cast(half8_t, frag[buf][jj][lane]), wf[jj], zero, 0, 0, 0);
             const uint32_t sc = dps[jj >> 1];
             if (jj & 1) {
-                acc[0] = fma_hi(sc, d[0], acc[0]);
-                acc[1] = fma_hi(sc, d[1], acc[1]);
-                acc[2] = fma_hi(sc, d[2], acc[2]);
-                acc[3] = fma_hi(sc, d[3], acc[3]);
+                st[0] = fma_hi(sc, d[0], st[0]);
+                st[1] = fma_hi(sc, d[1], st[1]);
+                st[2] = fma_hi(sc, d[2], st[2]);
+                st[3] = fma_hi(sc, d[3], st[3]);
             } else {
-                acc[0] = fma_lo(sc, d[0], acc[0]);
-                acc[1] = fma_lo(sc, d[1], acc[1]);
-                acc[2] = fma_lo(sc, d[2], acc[2]);
-                acc[3] = fma_lo(sc, d[3], acc[3]);
+                st[0] = fma_lo(sc, d[0], st[0]);
+                st[1] = fma_lo(sc, d[1], st[1]);
+                st[2] = fma_lo(sc, d[2], st[2]);
+                st[3] = fma_lo(sc, d[3], st[3]);
             }
         }
+        // result rows 4g..4g+3 are (batch 2g: hi, lo), (batch 2g+1: hi, lo)
+        acc[0] = fmaf(fa, st[0], acc[0]);
+        acc[1] = fmaf(fa, st[1], acc[1]);
+        acc[2] = fmaf(fb, st[2], acc[2]);
+        acc[3] = fmaf(fb, st[3], acc[3]);
 #pragma unroll
         for (int t = 0; t < kDw; ++t) dw[t] = nx[t];
     }
-    // Result rows 4g..4g+3 are (batch 2g: hi, lo), (batch 2g+1: hi, lo).
+
+    // RMSNorm: sums of squares of this K range per batch row, in a fixed order
+    // (lanes with xp == 1 hold the same elements and are not counted).
+    if constexpr (KIND == 1) {
+        const float t = rows_sum(xp == 0 ? ssq : 0.f);
+        if (g == 0 && xp == 0) ssq_w[wv][xb] = t;
+        __syncthreads();
+    }
+    auto range_ssq = [&](int b) { return ((ssq_w[0][b] + ssq_w[1][b]) + ssq_w[2][b]) + ssq_w[3][b]; };
     const int ba = 2 * g, bb = 2 * g + 1;
-    const float ya = (acc[0] + acc[1]) * sinv[ba];
-    const float yb = (acc[2] + acc[3]) * sinv[bb];
+    const float ya = acc[0] + acc[1];
+    const float yb = acc[2] + acc[3];
     const int64_t ln = N;
     if (S == 1) {
+        float ia = 1.f, ib = 1.f;
+        if constexpr (KIND == 1) {
+            ia = 1.0f / sqrtf(range_ssq(ba) / static_cast<float>(K) + eps);
+            ib = 1.0f / sqrtf(range_ssq(bb) / static_cast<float>(K) + eps);
+        }
         if (n < N) {
-            if (ba < B) y[ba * ln + n] = res ? ya + res[ba * ln + n] : ya;
-            if (bb < B) y[bb * ln + n] = res ? yb + res[bb * ln + n] : yb;
+            if (ba < B) y[ba * ln + n] = res ? ya * ia + res[ba * ln + n] : ya * ia;
+            if (bb < B) y[bb * ln + n] = res ? yb * ib + res[bb * ln + n] : yb * ib;
         }
         return;
     }
@@ -351,11 +385,16 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
         if (ba < B) __hip_atomic_store(pp + ba * ln + n, ya, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (bb < B) __hip_atomic_store(pp + bb * ln + n, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if constexpr (KIND == 1) {
+        if (threadIdx.x < B)
+            __hip_atomic_store(ssq_part + (static_cast<int64_t>(blockIdx.x) * S + blockIdx.y) * kMaxB +
+                                   threadIdx.x,
+                               range_ssq(threadIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);  // every store of this wavefront has completed
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    __shared__ int ticket;
     if (threadIdx.x == 0)
         ticket = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -371,12 +410,19 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
         for (; sp + 8 <= S; sp += 8) {  // eight loads in flight, added in split order
             float t[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                t[u] = __hip_atomic_load(pb + (sp + u) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q = 0; q < 8; ++q)
+                t[q] = __hip_atomic_load(pb + (sp + q) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v += t[u];
+            for (int q = 0; q < 8; ++q) v += t[q];
         }
         for (; sp < S; ++sp) v += __hip_atomic_load(pb + sp * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (KIND == 1) {
+            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + b;
+            float tot = 0.f;
+            for (int sp2 = 0; sp2 < S; ++sp2)
+                tot += __hip_atomic_load(sq + sp2 * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v *= 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+        }
         y[b * ln + nn] = res ? v + res[b * ln + nn] : v;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -385,7 +431,7 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
 // ---------------------------------------------------------------- host side
 struct Plan {
     int rg, kc, S, cps;
-    size_t off_sinv, off_xf, off_part, bytes;
+    size_t off_ssq, off_part, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -394,24 +440,30 @@ Plan make_plan(int64_t N, int64_t K, int64_t B) {
     Plan p;
     p.rg = static_cast<int>((N + kRowsWG - 1) / kRowsWG);
     p.kc = static_cast<int>(K / (32 * kSeg));
-    const int want = std::max(1, std::min(p.kc, (kTargetWGs + p.rg - 1) / p.rg));
+    int want = std::max(1, std::min(p.kc, (kTargetWGs + p.rg - 1) / p.rg));
+    if (p.rg > kCounters) want = 1;
     p.cps = (p.kc + want - 1) / want;
     p.S = (p.kc + p.cps - 1) / p.cps;
-    p.off_sinv = align256(static_cast<size_t>(p.rg) * sizeof(int));
-    p.off_xf = p.off_sinv + 256;
-    p.off_part = p.off_xf + static_cast<size_t>(K / 32) * 64 * 16;
+    p.off_ssq = kCounterBytes;
+    const size_t ssq = p.S > 1 ? align256(static_cast<size_t>(p.rg) * p.S * kMaxB * sizeof(float)) : 0;
+    p.off_part = p.off_ssq + ssq;
     p.bytes = p.off_part + (p.S > 1 ? align256(static_cast<size_t>(p.S) * B * N * sizeof(float)) : 0);
     return p;
 }
 
 template <int FMT, int KIND>
-void launch_prep(const float *x, const float *u, const float *nw, float eps, int64_t ld, int K,
-                 int B, void *ws, const Plan &p, hipStream_t s) {
+void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
+            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, hipStream_t s) {
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    const int parts = (K / 32 * 4 + kPrepThreads - 1) / kPrepThreads;
-    hipLaunchKernelGGL((mfma_prep_kernel<FMT, KIND>), dim3(kMaxB, parts), dim3(kPrepThreads), 0, s, x, u,
-                       nw, eps, ld, K, B, reinterpret_cast<u32x4_t *>(w8 + p.off_xf),
-                       reinterpret_cast<float *>(w8 + p.off_sinv), reinterpret_cast<int *>(w8), p.rg);
+    hipLaunchKernelGGL((mv_mfma_kernel<FMT, KIND>), dim3(p.rg, p.S), dim3(kWG), 0, s, W, N, K, B, x,
+                       u, nw, ld, eps, y, res, reinterpret_cast<int *>(w8),
+                       reinterpret_cast<float *>(w8 + p.off_ssq),
+                       reinterpret_cast<float *>(w8 + p.off_part), p.S, p.cps);
+}
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
 }
 
 template <int FMT>
@@ -434,27 +486,27 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     Q4_CHECK(N <= (1 << 30) && K <= (1 << 24) && ldx <= (1 << 26), Q4_ERR_UNSUPPORTED,
              "%s: N or K too large", name);
     Q4_CHECK(q4::aligned(Wv, 16), Q4_ERR_ALIGNMENT, "%s: W must be 16-byte aligned", name);
-    Q4_CHECK(q4::aligned(x, 16) && (!x2 || q4::aligned(x2, 16)) && ldx % 4 == 0, Q4_ERR_ALIGNMENT,
-             "%s: x and x2 must be 16-byte aligned with ld_x a multiple of 4", name);
-    Q4_CHECK(q4::aligned(y, 4) && (!res || q4::aligned(res, 4)) && (!norm_w || q4::aligned(norm_w, 4)),
-             Q4_ERR_ALIGNMENT, "%s: y, residual and norm_w must be 4-byte aligned", name);
+    Q4_CHECK(q4::aligned(x, 16) && (!x2 || q4::aligned(x2, 16)) && ldx % 4 == 0 &&
+                 (!norm_w || q4::aligned(norm_w, 16)),
+             Q4_ERR_ALIGNMENT, "%s: x, x2 and norm_w must be 16-byte aligned with ld_x a multiple of 4",
+             name);
+    Q4_CHECK(q4::aligned(y, 4) && (!res || q4::aligned(res, 4)), Q4_ERR_ALIGNMENT,
+             "%s: y and residual must be 4-byte aligned", name);
+    const size_t xbytes = static_cast<size_t>((B - 1) * ldx + K) * sizeof(float);
+    const size_t ybytes = static_cast<size_t>(B * N) * sizeof(float);
+    Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
+             Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
     const Plan p = make_plan(N, K, B);
     Q4_CHECK(ws && q4::aligned(ws, 256), Q4_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
              name);
     Q4_CHECK(ws_bytes >= p.bytes, Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", name,
              ws_bytes, p.bytes);
     hipStream_t s = q4::as_stream(stream);
-    const int k = static_cast<int>(K), b = static_cast<int>(B);
-    if (op_kind == Q4_IN_RMSNORM) launch_prep<FMT, 1>(x, nullptr, norm_w, eps, ldx, k, b, ws, p, s);
-    else if (op_kind == Q4_IN_SWIGLU) launch_prep<FMT, 2>(x, x2, nullptr, eps, ldx, k, b, ws, p, s);
-    else launch_prep<FMT, 0>(x, nullptr, nullptr, eps, ldx, k, b, ws, p, s);
-    uint8_t *w8 = static_cast<uint8_t *>(ws);
-    hipLaunchKernelGGL((mv_mfma_kernel<FMT>), dim3(p.rg, p.S), dim3(kWG), 0, s,
-                       static_cast<const uint8_t *>(Wv), static_cast<int>(N), k, b,
-                       reinterpret_cast<const u32x4_t *>(w8 + p.off_xf),
-                       reinterpret_cast<const float *>(w8 + p.off_sinv), y, res,
-                       reinterpret_cast<float *>(w8 + p.off_part), reinterpret_cast<int *>(w8), p.S,
-                       p.cps);
+    const uint8_t *W = static_cast<const uint8_t *>(Wv);
+    const int n = static_cast<int>(N), k = static_cast<int>(K), b = static_cast<int>(B);
+    if (op_kind == Q4_IN_RMSNORM) launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, s);
+    else if (op_kind == Q4_IN_SWIGLU) launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, s);
+    else launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, s);
     return q4::launch_status(name);
 }
 

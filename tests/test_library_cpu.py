@@ -64,7 +64,8 @@ def test_batched_matvec_rejects_bad_arguments_on_host():
     assert need > 0
     assert q.matvec_batched_workspace(100, 288, 4) == 0    # K % 256 != 0
     assert q.matvec_batched_workspace(100, 512, 9) == 0    # B > 8
-    args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, None, 0.0, fake, None,
+    ybuf = 0x40000000  # does not overlap x
+    args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, None, 0.0, ybuf, None,
                                         ws, nbytes, None)
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake, need - 1))[0] == "Q4_ERR_WORKSPACE"
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake + 16, need))[0] == "Q4_ERR_WORKSPACE"

@@ -273,3 +273,22 @@ def test_matvec_batched_workspace_errors(dev):
         q.q4_0_matvec_batched(torch.zeros((n, 9 * 18), dtype=torch.uint8, device=dev),
                               torch.zeros((b, 288), dtype=torch.float32, device=dev), 288, b, 288)
     assert e.value.status_name == "Q4_ERR_UNSUPPORTED"
+
+
+def test_matvec_batched_spikes(dev):
+    """One large element per 256-k step in a row of small ones: the step's
+    power-of-two scale must come from the maximum over the whole step (every
+    lane group and wavefront), or the spike overflows binary16."""
+    _say("q4/q8 batched spikes")
+    n, k, b = 130, 1024, 8
+    x = synth.normal_f32(111, "t.batched.spike.x", (b, k)) * np.float32(1e-3)
+    for r in range(b):
+        for step in range(k // 256):
+            x[r, step * 256 + (37 * r + 61 * step) % 256] = np.float32(3e4 * (1 + r))
+    for fmt, gen, orc, fn in (("q4", synth.q4_0_matrix, oracle.q4_0_matvec, q.q4_0_matvec_batched),
+                              ("q8", synth.q8_0_matrix, oracle.q8_0_matvec, q.q8_0_matvec_batched)):
+        W = gen(111, f"t.batched.spike.{fmt}", n, k)
+        ref, terms = orc(W, n, k, x)
+        y = fn(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev), k, b, k)
+        torch.cuda.synchronize()
+        _check(y, ref, terms, f"{fmt} spikes")
