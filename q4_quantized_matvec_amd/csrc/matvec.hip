@@ -113,6 +113,9 @@ __host__ __device__ inline int ks_part_blocks(int nb, int ks) { return ((nb + ks
 #ifndef Q4_MV_WG_PER_CU
 #define Q4_MV_WG_PER_CU 0 // 0: chosen from the register footprint
 #endif
+#ifndef Q4_MV_KS_MIN
+#define Q4_MV_KS_MIN 1    // smallest K split (wavefronts per row) considered
+#endif
 #ifndef Q4_MV_MIN_WAVES
 #define Q4_MV_MIN_WAVES 1 // occupancy hint (waves per SIMD) for the register allocator
 #endif
@@ -182,6 +185,19 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     const uint32_t sel_e = odd ? 0x0C060C04u : 0x0C040C02u;
     const uint32_t sel_o = odd ? 0x0C070C05u : 0x0C050C03u;
 
+    // Rows past this group's range are clamped to a real row (loaded, unused).
+    // Without a residual the residual slot reads x[0] and is ignored.  The
+    // first PF rows are requested before the activations are staged, so the
+    // two memory latencies overlap.
+    const bool has_res = res != nullptr;
+    auto fetch = [&](int it, RowRegs<FMT, JX> &r) {
+        const int row = min(row0 + it, N - 1);
+        load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
+    };
+    RowRegs<FMT, JX> buf[NBUF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
+
     // Activations of the lane's block columns stay in registers.  With the
     // whole K in one wavefront the workgroup stages x through LDS once; the
     // input transform is applied on the way (sum of squares reduced in LDS).
@@ -191,17 +207,41 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         const float4 *ug = reinterpret_cast<const float4 *>(op.u);
         float4 *xl = reinterpret_cast<float4 *>(xs);
         float ss = 0.f;
-        for (int i = threadIdx.x; i < (K >> 2); i += kWG) {
-            float4 v = xg[i];
-            if (op.kind == 2) {
-                const float4 u = ug[i];
-                v.x = silu_mul(v.x, u.x);
-                v.y = silu_mul(v.y, u.y);
-                v.z = silu_mul(v.z, u.z);
-                v.w = silu_mul(v.w, u.w);
+        // every load of the row first (one memory round trip), then the
+        // transform and the LDS stores; indices past the row re-read its last
+        // element and are not stored
+        // (RMSNorm: the gain is applied here and 1/rms once the sum of
+        // squares is known; SwiGLU: u is loaded alongside)
+        constexpr int kXV = kXLdsFloats / 4 / kWG;
+        const int nv = K >> 2;
+        const float4 *sg = op.kind == 2 ? ug : reinterpret_cast<const float4 *>(op.w);
+        float4 v[kXV], u[kXV];
+#pragma unroll
+        for (int r = 0; r < kXV; ++r) v[r] = xg[min(static_cast<int>(threadIdx.x) + r * kWG, nv - 1)];
+        if (sg) {
+#pragma unroll
+            for (int r = 0; r < kXV; ++r) u[r] = sg[min(static_cast<int>(threadIdx.x) + r * kWG, nv - 1)];
+        }
+#pragma unroll
+        for (int r = 0; r < kXV; ++r) {
+            const int i = threadIdx.x + r * kWG;
+            if (i < nv) {
+                float4 t = v[r];
+                if (op.kind == 2) {
+                    t.x = silu_mul(t.x, u[r].x);
+                    t.y = silu_mul(t.y, u[r].y);
+                    t.z = silu_mul(t.z, u[r].z);
+                    t.w = silu_mul(t.w, u[r].w);
+                }
+                ss = __builtin_fmaf(t.x, t.x, __builtin_fmaf(t.y, t.y, __builtin_fmaf(t.z, t.z, __builtin_fmaf(t.w, t.w, ss))));
+                if (op.kind == 1 && sg) {
+                    t.x *= u[r].x;
+                    t.y *= u[r].y;
+                    t.z *= u[r].z;
+                    t.w *= u[r].w;
+                }
+                xl[i] = t;
             }
-            ss = __builtin_fmaf(v.x, v.x, __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.z, v.z, __builtin_fmaf(v.w, v.w, ss))));
-            xl[i] = v;
         }
         if (op.kind == 1) {
             ss = wave_sum(ss);
@@ -213,12 +253,19 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
             __syncthreads();  // red[] is reused by the row reductions of split-K shapes
         }
     } else if (op.kind == 1) {
-        // every wavefront reduces the whole row itself
+        // every wavefront reduces the whole row itself, 8 loads in flight per lane
         float ss = 0.f;
         const float4 *xg = reinterpret_cast<const float4 *>(x);
-        for (int i = lane; i < (K >> 2); i += 64) {
-            const float4 v = xg[i];
-            ss = __builtin_fmaf(v.x, v.x, __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.z, v.z, __builtin_fmaf(v.w, v.w, ss))));
+        const int nv = K >> 2;
+        for (int i0 = 0; i0 < nv; i0 += 8 * 64) {
+            float4 v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) v[r] = xg[min(i0 + lane + 64 * r, nv - 1)];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (i0 + lane + 64 * r < nv)
+                    ss = __builtin_fmaf(v[r].x, v[r].x, __builtin_fmaf(v[r].y, v[r].y,
+                         __builtin_fmaf(v[r].z, v[r].z, __builtin_fmaf(v[r].w, v[r].w, ss))));
         }
         inv = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(K) + op.eps);
     }
@@ -247,9 +294,20 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                 xr[j][4 * i + 3] = v.w;
             }
             if (op.kind == 1) {
-                const float *wg = op.w ? op.w + static_cast<size_t>(c) * 32 : nullptr;
+                if (kXLds || !op.w) {  // staged values already carry the gain
 #pragma unroll
-                for (int i = 0; i < 32; ++i) xr[j][i] = xr[j][i] * inv * (wg ? wg[i] : 1.0f);
+                    for (int i = 0; i < 32; ++i) xr[j][i] *= inv;
+                } else {
+                    const float4 *wg = reinterpret_cast<const float4 *>(op.w + static_cast<size_t>(c) * 32);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float4 g4 = wg[i];
+                        xr[j][4 * i + 0] = xr[j][4 * i + 0] * inv * g4.x;
+                        xr[j][4 * i + 1] = xr[j][4 * i + 1] * inv * g4.y;
+                        xr[j][4 * i + 2] = xr[j][4 * i + 2] * inv * g4.z;
+                        xr[j][4 * i + 3] = xr[j][4 * i + 3] * inv * g4.w;
+                    }
+                }
             }
 #pragma unroll
             for (int i = 0; i < 32; ++i) s += xr[j][i];
@@ -264,16 +322,6 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         xc[j] = -8.f * s;
     }
 
-    // Rows past this group's range are clamped to a real row (loaded, unused).
-    // Without a residual the residual slot reads x[0] and is ignored.
-    const bool has_res = res != nullptr;
-    auto fetch = [&](int it, RowRegs<FMT, JX> &r) {
-        const int row = min(row0 + it, N - 1);
-        load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
-    };
-    RowRegs<FMT, JX> buf[NBUF];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
 
     auto process = [&](int it, const RowRegs<FMT, JX> &cur) {
         const bool act = it < cnt;
@@ -480,7 +528,12 @@ void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int
     constexpr int PF = FMT == 0 ? Q4_MV_PREFETCH : Q4_MV_PREFETCH_Q8;
     constexpr int RG = 4 / KS;
     const int want = (N + RG - 1) / RG;
-    const int per_cu = Q4_MV_WG_PER_CU ? Q4_MV_WG_PER_CU : (JX <= 2 ? 3 : 2);
+    // Workgroups per CU: every workgroup stages the whole activation row once,
+    // so a workgroup should own enough rows to amortise that (measured on
+    // the 31B projections: about 7 rows per wavefront with the whole K in
+    // one wavefront; one workgroup per CU when K is split over wavefronts).
+    int per_cu = KS > 1 ? 1 : std::max(1, std::min(3, N / (q4::device_cus() * RG * 7)));
+    if (Q4_MV_WG_PER_CU) per_cu = Q4_MV_WG_PER_CU;
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
     hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF>), dim3(nwg, B), dim3(kWG), 0, s, W, x, y, res, N, K, op);
 }
@@ -539,9 +592,10 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     InOp op{op_kind, op_kind == Q4_IN_SWIGLU ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
             eps, ldx};
     int ks = 0;
-    if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) && ldx % 4 == 0) {
+    if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
+        (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0) {
         for (int cand : {1, 2, 4})
-            if (ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
+            if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
     }
     if (ks) {
         const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
