@@ -35,39 +35,36 @@ def matvec_bytes(n, k, b):
     return n * (k // 32) * 18 + 4 * b * k + 4 * b * n
 
 
-def time_matvec(q, torch, Ws, x, y, steps, warmup):
-    """Mean time per dispatch (ms) over `steps` back-to-back launches, HIP events
-    on the stream the kernels are launched on."""
-    stream = torch.cuda.current_stream()
+def time_dispatches(torch, launch, steps, warmup):
+    """Mean time per dispatch (ms) over `steps` back-to-back launches after
+    `warmup` untimed ones, HIP events on the stream the kernels are launched
+    on.  (Host submission takes about half a dispatch, so the GPU stays busy;
+    replaying the launches as a graph adds per-node gaps on this runtime.)"""
     for i in range(warmup):
-        q.q4_0_matvec(Ws[i % len(Ws)], x, y=y)
+        launch(i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
-        q.q4_0_matvec(Ws[i % len(Ws)], x, y=y)
+        launch(i)
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def time_matvec(q, torch, Ws, x, y, steps, warmup):
+    return time_dispatches(torch, lambda i: q.q4_0_matvec(Ws[i % len(Ws)], x, y=y), steps, warmup)
 
 
 def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):
-    """As time_matvec for the matrix-core path (prep + main kernel per call)."""
-    stream = torch.cuda.current_stream()
+    """As time_matvec for the matrix-core path."""
     N = y.shape[1]
     ws = torch.zeros(q.matvec_batched_workspace(N, K, B), dtype=torch.uint8, device=x.device)
-    for i in range(warmup):
-        q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return time_dispatches(
+        torch, lambda i: q.q4_0_matvec_batched(Ws[i % len(Ws)], x, K, B, K, y=y, ws=ws), steps,
+        warmup)
 
 
 def bench_attention_stack(q, torch, batch, reps=20, warmup=3):
@@ -281,7 +278,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-matvec", action="store_true")

@@ -87,20 +87,33 @@ q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64
  *   Q4_IN_SWIGLU   x / (1 + exp(-x)) * x2               ([GELO] 04: SwiGLU FFN) */
 typedef enum { Q4_IN_PLAIN = 0, Q4_IN_RMSNORM = 1, Q4_IN_SWIGLU = 2 } q4_input_op;
 
-/* q4_0_matvec_fused / q8_0_matvec_fused: y[b] = W op(x[b]) (+ residual[b]),
+/* Output transforms:
+ *   Q4_OUT_PLAIN   y[b][n] = z[b][n] (+ residual[b][n]),  z = W op(x), y [B][N]
+ *   Q4_OUT_SWIGLU  y[b][p] = z[b][p] / (1 + exp(-z[b][p])) * z[b][p + N/2]
+ *                  for p < N/2, y [B][N/2]: a merged gate|up projection that
+ *                  hands the FFN activation straight to the down projection
+ *                  ([GELO] 04: SwiGLU FFN; 06: merged gate|up); N even, no
+ *                  residual. */
+typedef enum { Q4_OUT_PLAIN = 0, Q4_OUT_SWIGLU = 1 } q4_output_op;
+
+/* q4_0_matvec_fused / q8_0_matvec_fused: y[b] = out_op(W op(x[b])) (+ residual[b]),
  * where row b of x (and of x2 for SwiGLU) starts at element b * ld_x
  * (ld_x >= K; a merged gate|up output passes x = gu, x2 = gu + F, ld_x = 2F).
  * The transform is computed in fp32 exactly as rmsnorm() / swiglu() define
  * it (the RMSNorm sum of squares may be added in a different order).
  * Other arguments, layouts and errors as q4_0_matvec / q8_0_matvec, plus
- * Q4_ERR_INVALID_ARG for an unknown op, a missing x2 or eps < 0 and
- * Q4_ERR_SHAPE for ld_x < K. */
+ * Q4_ERR_INVALID_ARG for an unknown op or out_op, a missing x2, eps < 0, or
+ * a SwiGLU output with odd N or a residual; Q4_ERR_SHAPE for ld_x < K; and
+ * Q4_ERR_UNSUPPORTED for a SwiGLU output unless K % 256 == 0, K <= 8192 and
+ * x, x2, norm_w are 16-byte aligned with ld_x % 4 == 0. */
 q4_status q4_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x, const float *x2,
-                            int64_t ld_x, int64_t B, q4_input_op op, const float *norm_w, float eps,
-                            float *y, const float *residual, void *stream);
+                            int64_t ld_x, int64_t B, q4_input_op op, q4_output_op out_op,
+                            const float *norm_w, float eps, float *y, const float *residual,
+                            void *stream);
 q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x, const float *x2,
-                            int64_t ld_x, int64_t B, q4_input_op op, const float *norm_w, float eps,
-                            float *y, const float *residual, void *stream);
+                            int64_t ld_x, int64_t B, q4_input_op op, q4_output_op out_op,
+                            const float *norm_w, float eps, float *y, const float *residual,
+                            void *stream);
 
 /* q4_0_matvec_batched / q8_0_matvec_batched: the same products as the fused
  * calls, computed on the matrix cores for 1 <= B <= 8 activation rows; meant
@@ -111,7 +124,8 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
  * the finished sums.  One kernel launch; bitwise reproducible.
  *   W         16-byte aligned; K % 256 == 0 (else Q4_ERR_UNSUPPORTED)
  *   x, x2     16-byte aligned, ld_x % 4 == 0; norm_w 16-byte aligned
- *   y         must not overlap x or x2 (Q4_ERR_INVALID_ARG); may alias residual
+ *   y         must not overlap x or x2 (Q4_ERR_INVALID_ARG); may alias residual;
+ *             a SwiGLU output (out_op) is supported for every K % 256 == 0
  *   ws        device workspace of at least matvec_batched_workspace(N, K, B)
  *             bytes, 256-byte aligned, owned by the caller.  Its first 16 KiB
  *             (split tickets) must be zero before the first call that uses
@@ -121,12 +135,12 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
 size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B);
 q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
                               const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
-                              const float *norm_w, float eps, float *y, const float *residual,
-                              void *ws, size_t ws_bytes, void *stream);
+                              q4_output_op out_op, const float *norm_w, float eps, float *y,
+                              const float *residual, void *ws, size_t ws_bytes, void *stream);
 q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
                               const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
-                              const float *norm_w, float eps, float *y, const float *residual,
-                              void *ws, size_t ws_bytes, void *stream);
+                              q4_output_op out_op, const float *norm_w, float eps, float *y,
+                              const float *residual, void *ws, size_t ws_bytes, void *stream);
 
 /* q8_0_gather: x[b][:] = dequantised row tokens[b] of the Q8_0 table E
  * (embedding lookup of the tied table; [GELO] 05 generation loop embeds the

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     IN_PLAIN,
     IN_RMSNORM,
     IN_SWIGLU,
+    OUT_PLAIN,
+    OUT_SWIGLU,
     q4_0_matvec,
     q4_0_matvec_fused,
     q4_0_matvec_batched,

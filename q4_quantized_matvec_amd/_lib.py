@@ -49,13 +49,15 @@ _SIGS = {
     "q4_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_gather": ([_P, _I64, _I64, _P, _I64, _P, _P], C.c_int),
-    "q4_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
-    "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P], C.c_int),
+    "q4_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P, _P],
+                          C.c_int),
+    "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P, _P],
+                          C.c_int),
     "matvec_batched_workspace": ([_I64, _I64, _I64], _SZ),
-    "q4_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P, _SZ,
-                             _P], C.c_int),
-    "q8_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, _P, _F, _P, _P, _P, _SZ,
-                             _P], C.c_int),
+    "q4_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P,
+                             _P, _SZ, _P], C.c_int),
+    "q8_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P,
+                             _P, _SZ, _P], C.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
     "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
     "qk_norm_rope": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D, _F,
@@ -164,30 +166,35 @@ def q8_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
 
 
 IN_PLAIN, IN_RMSNORM, IN_SWIGLU = 0, 1, 2
+OUT_PLAIN, OUT_SWIGLU = 0, 1
 
 
-def _matvec_fused(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, stream, n):
+def _out_cols(N, out_op):
+    return N // 2 if out_op == OUT_SWIGLU else N
+
+
+def _matvec_fused(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, stream, n, out_op):
     import torch
     N = n if n is not None else _qmatrix_dims(W, K, bpb)
     if y is None:
-        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+        y = torch.empty((B, _out_cols(N, out_op)), dtype=torch.float32, device=x.device)
     _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op),
-                                      _ptr(norm_w), float(eps), _ptr(y), _ptr(residual),
-                                      _stream(stream)))
+                                      int(out_op), _ptr(norm_w), float(eps), _ptr(y),
+                                      _ptr(residual), _stream(stream)))
     return y
 
 
 def q4_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None, residual=None,
-                      stream=None, n=None):
-    """y[B,N] = dequant(W) @ op(x rows) (+ residual); rows of x (and x2) at stride ld."""
+                      stream=None, n=None, out_op=OUT_PLAIN):
+    """y = out_op(dequant(W) @ op(x rows)) (+ residual); rows of x (and x2) at stride ld."""
     return _matvec_fused("q4_0_matvec_fused", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,
-                         residual, stream, n)
+                         residual, stream, n, out_op)
 
 
 def q8_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None, residual=None,
-                      stream=None, n=None):
+                      stream=None, n=None, out_op=OUT_PLAIN):
     return _matvec_fused("q8_0_matvec_fused", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
-                         residual, stream, n)
+                         residual, stream, n, out_op)
 
 
 def matvec_batched_workspace(N, K, B):
@@ -195,33 +202,34 @@ def matvec_batched_workspace(N, K, B):
     return int(lib().matvec_batched_workspace(N, K, B))
 
 
-def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, ws, stream, n):
+def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, ws, stream, n,
+                    out_op):
     import torch
     N = n if n is not None else _qmatrix_dims(W, K, bpb)
     if y is None:
-        y = torch.empty((B, N), dtype=torch.float32, device=x.device)
+        y = torch.empty((B, _out_cols(N, out_op)), dtype=torch.float32, device=x.device)
     if ws is None:  # split tickets must start at zero
         ws = torch.zeros(max(256, matvec_batched_workspace(N, K, B)), dtype=torch.uint8,
                          device=x.device)
     _check(name, getattr(lib(), name)(_ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op),
-                                      _ptr(norm_w), float(eps), _ptr(y), _ptr(residual),
-                                      _ptr(ws), ws.numel(), _stream(stream)))
+                                      int(out_op), _ptr(norm_w), float(eps), _ptr(y),
+                                      _ptr(residual), _ptr(ws), ws.numel(), _stream(stream)))
     return y
 
 
 def q4_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
-                        residual=None, ws=None, stream=None, n=None):
+                        residual=None, ws=None, stream=None, n=None, out_op=OUT_PLAIN):
     """As q4_0_matvec_fused, on the matrix cores (1 <= B <= 8, K % 256 == 0).  ``ws``: a
     zero-initialised uint8 device tensor of matvec_batched_workspace(N, K, B) bytes, reusable
     across calls on one stream (allocated if None)."""
     return _matvec_batched("q4_0_matvec_batched", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,
-                           residual, ws, stream, n)
+                           residual, ws, stream, n, out_op)
 
 
 def q8_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
-                        residual=None, ws=None, stream=None, n=None):
+                        residual=None, ws=None, stream=None, n=None, out_op=OUT_PLAIN):
     return _matvec_batched("q8_0_matvec_batched", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
-                           residual, ws, stream, n)
+                           residual, ws, stream, n, out_op)
 
 
 def q8_0_gather(E, tokens, K, x=None, stream=None):

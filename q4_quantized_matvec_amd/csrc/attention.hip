@@ -37,16 +37,35 @@ AttnGeom attn_geom(const q4_kv_layout &kv, int64_t n_q_heads, int64_t window) {
     return g;
 }
 
+// A copy the compiler cannot see through.  When both results of one
+// permlane swap are reinterpreted as floats, this compiler has been seen to
+// merge the two reinterpretations (computing a[0] + a[0] for a[0] + a[1]), so
+// every second result used as a float goes through this copy first.
+__device__ __forceinline__ uint32_t opaque_copy(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
 // Sum over aligned groups of L lanes (L = 8, 16, 32 or 64); every lane of a
-// group receives its group's total.
+// group receives the same bits.  Within a 16-lane row: DPP; across rows:
+// permlane swaps (no LDS traffic).
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
     v += dpp<0xB1>(v);   // xor 1
     v += dpp<0x4E>(v);   // xor 2
     v += dpp<0x141>(v);  // half-row mirror: groups of 8
     if constexpr (L >= 16) v += dpp<0x140>(v);  // row mirror: groups of 16
-    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (L >= 32) {  // rows (0,1) and (2,3)
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, opaque_copy(s[1]));
+    }
+    if constexpr (L >= 64) {  // the two halves of the wavefront
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, opaque_copy(s[1]));
+    }
     return v;
 }
 
@@ -88,8 +107,16 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     }
     const float *kb = kc + b * sb + g0 * sh;
     const float *vb = vc + b * sb + g0 * sh;
-    // slot of chunk position j (positions past the chunk end re-read its first row)
-    auto slot = [&](int j) { return ((p0 + (j < cnt ? j : 0)) % cap) * st; };
+    // slot of chunk position j (positions past the chunk end re-read its first
+    // row): one 64-bit remainder per workgroup, then 32-bit wrap-around
+    const int cap32 = static_cast<int>(cap);
+    const int sbase = static_cast<int>(p0 % cap);
+    auto slot = [&](int j) {
+        int sl = sbase + (j < cnt ? j : 0);
+        if (sl >= cap32) sl -= cap32;
+        if (sl >= cap32) sl %= cap32;  // only for caches shorter than a chunk
+        return static_cast<int64_t>(sl) * st;
+    };
 
     // ---- scores
     const int sub = lane % LPK, kgl = lane / LPK;
@@ -97,17 +124,20 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 #pragma unroll
     for (int it = 0; it < SIT; ++it) {
         const int jj = it * 4 * KPW + wave * KPW + kgl;
-        const float4 *kp = reinterpret_cast<const float4 *>(kb + slot(jj) + sub * 8);
-        const float4 a = kp[0], bq = kp[1];
+        // lane sub holds elements [4 sub, 4 sub + 4) and HD/2 + [4 sub, 4 sub + 4):
+        // each load instruction covers contiguous bytes of the key row
+        const float *kp = kb + slot(jj) + sub * 4;
+        const float4 a = *reinterpret_cast<const float4 *>(kp);
+        const float4 bq = *reinterpret_cast<const float4 *>(kp + HD / 2);
         kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
         kr[it][4] = bq.x; kr[it][5] = bq.y; kr[it][6] = bq.z; kr[it][7] = bq.w;
     }
     float qv[GM][8];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        const float4 *qh = reinterpret_cast<const float4 *>(
-            q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 8);
-        const float4 a = qh[0], bq = qh[1];
+        const float *qh = q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 4;
+        const float4 a = *reinterpret_cast<const float4 *>(qh);
+        const float4 bq = *reinterpret_cast<const float4 *>(qh + HD / 2);
         qv[g][0] = a.x * scale; qv[g][1] = a.y * scale; qv[g][2] = a.z * scale; qv[g][3] = a.w * scale;
         qv[g][4] = bq.x * scale; qv[g][5] = bq.y * scale; qv[g][6] = bq.z * scale; qv[g][7] = bq.w * scale;
     }
@@ -205,13 +235,24 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     }
     M = wave_max(M);
     float num = 0.f, den = 0.f;
-    for (int c = cg; c < nch; c += 4) {
-        const size_t u = u0 + static_cast<size_t>(c) * GM;
-        const float l = pml[2 * u + 1];
-        if (l > 0.f) {
-            const float w = __expf(pml[2 * u] - M);
-            if (d < hd) num = __builtin_fmaf(w, part[u * hd + d], num);
-            den = __builtin_fmaf(w, l, den);
+    constexpr int kU = 8;  // chunks in flight per thread, still added in ascending order
+    for (int c0 = cg; c0 < nch; c0 += 4 * kU) {
+        float lv[kU], mv[kU], pv[kU];
+#pragma unroll
+        for (int r = 0; r < kU; ++r) {
+            const int c = min(c0 + 4 * r, nch - 1);
+            const size_t u = u0 + static_cast<size_t>(c) * GM;
+            lv[r] = pml[2 * u + 1];
+            mv[r] = pml[2 * u];
+            pv[r] = d < hd ? part[u * hd + d] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < kU; ++r) {
+            if (c0 + 4 * r < nch && lv[r] > 0.f) {
+                const float w = __expf(mv[r] - M);
+                num = __builtin_fmaf(w, pv[r], num);
+                den = __builtin_fmaf(w, lv[r], den);
+            }
         }
     }
     if (cg > 0) {

@@ -174,14 +174,21 @@ bool fits(const q4_decode_model *m, int64_t pos) {
 // One projection of the step: matrix cores for two or more sequences,
 // otherwise the vector-unit kernels.
 q4_status project(q4_decode_model *m, int fmt, const void *W, int64_t N, int64_t K, const float *x,
-                  const float *x2, int64_t ldx, q4_input_op op, const float *nw, float *y,
-                  const float *res, void *s) {
+                  const float *x2, int64_t ldx, q4_input_op op, q4_output_op out, const float *nw,
+                  float *y, const float *res, void *s) {
     const q4_model_desc &d = m->desc;
     if (m->mv_ws && batched_ok(d, W, K))
         return (fmt == 0 ? q4_0_matvec_batched : q8_0_matvec_batched)(
-            W, N, K, x, x2, ldx, d.batch, op, nw, d.eps, y, res, m->mv_ws, m->mv_ws_bytes, s);
-    return (fmt == 0 ? q4_0_matvec_fused : q8_0_matvec_fused)(W, N, K, x, x2, ldx, d.batch, op, nw,
-                                                              d.eps, y, res, s);
+            W, N, K, x, x2, ldx, d.batch, op, out, nw, d.eps, y, res, m->mv_ws, m->mv_ws_bytes, s);
+    return (fmt == 0 ? q4_0_matvec_fused : q8_0_matvec_fused)(W, N, K, x, x2, ldx, d.batch, op, out,
+                                                              nw, d.eps, y, res, s);
+}
+
+// The gate|up projection can hand SiLU(gate) * up straight to the down
+// projection when its kernel supports a SwiGLU output for this shape.
+bool glu_output(const q4_model_desc &d, const void *wgu) {
+    if (batched_ok(d, wgu, d.d_model)) return true;
+    return d.d_model % 256 == 0 && d.d_model <= 8192;
 }
 
 // Enqueues one whole step on s.
@@ -196,24 +203,33 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         const int64_t hd = l.head_dim, nq = d.n_q_heads * hd, nk = l.n_kv_heads * hd;
         const int64_t nqkv = layer_qkv_rows(d, l);
         // attention RMSNorm fused into the QKV projection's input
-        Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, l.attn_norm, m->qkv,
-                       nullptr, sv));
+        Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
+                       l.attn_norm, m->qkv, nullptr, sv));
         Q4_TRY(qk_norm_rope(m->qkv, nqkv, m->qkv + nq, l.v_from_k ? nullptr : m->qkv + nq + nk, nqkv,
                             l.q_norm, l.k_norm, d.n_q_heads, &m->kv[i], m->pos_dev, l.rope_theta,
                             d.eps, l.v_from_k, l.k_cache, l.v_cache, sv));
         Q4_TRY(gqa_decode_attn(m->qkv, nqkv, d.n_q_heads, l.k_cache, l.v_cache, &m->kv[i],
                                m->pos_dev + 1, l.window, l.attn_scale, m->att, nq, m->attn_ws,
                                m->attn_ws_bytes, sv));
-        Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, nullptr, m->x, m->x, sv));
-        // FFN RMSNorm fused into gate|up; SwiGLU fused into the down projection
-        Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, l.ffn_norm, m->gu,
-                       nullptr, sv));
-        Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, Q4_IN_SWIGLU, nullptr, m->x, m->x,
-                       sv));
+        Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
+                       m->x, m->x, sv));
+        // FFN RMSNorm fused into gate|up; SwiGLU fused into gate|up's output
+        // (else into the down projection's input)
+        if (glu_output(d, l.wgu)) {
+            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_SWIGLU,
+                           l.ffn_norm, m->gu, nullptr, sv));
+            Q4_TRY(project(m, 0, l.wd, D, F, m->gu, nullptr, F, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
+                           m->x, m->x, sv));
+        } else {
+            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
+                           l.ffn_norm, m->gu, nullptr, sv));
+            Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, Q4_IN_SWIGLU, Q4_OUT_PLAIN,
+                           nullptr, m->x, m->x, sv));
+        }
     }
     float *lg = logits ? logits : m->logits;
-    Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, d.final_norm, lg,
-                   nullptr, sv));
+    Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
+                   d.final_norm, lg, nullptr, sv));
     Q4_TRY(argmax_rows(lg, B, d.vocab, next, sv));
     hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, s, m->pos_dev);
     return q4::launch_status("decode_step (advance)");

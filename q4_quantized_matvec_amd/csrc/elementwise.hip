@@ -135,11 +135,41 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ 
     const float *row = logits + static_cast<int64_t>(blockIdx.x) * V;
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int64_t i = threadIdx.x; i < V; i += 1024) {
-        const float v = row[i];
-        if (v > best || (v == best && i < bi)) {
+    auto consider = [&](float v, int i) {
+        if (v > best || (v == best && i < bi)) {  // a NaN never wins
             best = v;
-            bi = static_cast<int>(i);
+            bi = i;
+        }
+    };
+    constexpr int kU = 8;  // loads in flight per thread
+    if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+        const int nv = static_cast<int>(V >> 2);
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        for (int base = threadIdx.x; base < nv; base += 1024 * kU) {
+            float4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) v[u] = r4[min(base + u * 1024, nv - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int i = base + u * 1024;
+                if (i < nv) {
+                    consider(v[u].x, 4 * i);
+                    consider(v[u].y, 4 * i + 1);
+                    consider(v[u].z, 4 * i + 2);
+                    consider(v[u].w, 4 * i + 3);
+                }
+            }
+        }
+        for (int64_t i = 4 * static_cast<int64_t>(nv) + threadIdx.x; i < V; i += 1024)
+            consider(row[i], static_cast<int>(i));
+    } else {
+        for (int base = threadIdx.x; base < V; base += 1024 * kU) {
+            float v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) v[u] = row[min(static_cast<int64_t>(base + u * 1024), V - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (base + u * 1024 < V) consider(v[u], base + u * 1024);
         }
     }
     sv[threadIdx.x] = best;
@@ -202,8 +232,8 @@ q4_status check_kv_layout(const char *name, const q4_kv_layout *kv) {
              (long long)kv->head_dim);
     Q4_CHECK(kv->head_dim <= 512, Q4_ERR_UNSUPPORTED, "%s: head_dim %lld > 512", name,
              (long long)kv->head_dim);
-    Q4_CHECK(kv->batch <= 65535 && kv->n_kv_heads <= 4096, Q4_ERR_UNSUPPORTED,
-             "%s: batch or kv heads too large", name);
+    Q4_CHECK(kv->batch <= 65535 && kv->n_kv_heads <= 4096 && kv->cap <= (int64_t(1) << 30),
+             Q4_ERR_UNSUPPORTED, "%s: batch, kv heads or capacity too large", name);
     return Q4_OK;
 }
 }  // namespace q4
@@ -240,7 +270,7 @@ extern "C" q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int3
     q4::clear_error();
     Q4_CHECK(logits && out, Q4_ERR_INVALID_ARG, "argmax_rows: logits and out must not be NULL");
     Q4_CHECK(B >= 1 && V >= 1, Q4_ERR_INVALID_ARG, "argmax_rows: B and V must be >= 1");
-    Q4_CHECK(V <= 0x7ffffffe && B <= (1 << 30), Q4_ERR_UNSUPPORTED, "argmax_rows: sizes too large");
+    Q4_CHECK(V <= (1 << 30) && B <= (1 << 30), Q4_ERR_UNSUPPORTED, "argmax_rows: sizes too large");
     Q4_CHECK(q4::aligned(logits, 4) && q4::aligned(out, 4), Q4_ERR_ALIGNMENT,
              "argmax_rows: logits and out must be 4-byte aligned");
     hipLaunchKernelGGL(argmax_kernel, dim3(static_cast<unsigned>(B)), dim3(1024), 0,

@@ -57,6 +57,7 @@ struct InOp {
     const float *w;  // kind 1: gain
     float eps;
     int64_t ld;      // row stride of x (and u) in elements
+    int glu;         // 1: y[p] = silu(z[p]) * z[p + N/2] for the N/2 pairs (whole K per wavefront)
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
@@ -124,7 +125,7 @@ constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
 
 // B = 1 fast path.  KS wavefronts of a workgroup split K; 4 / KS row groups;
 // PF rows of loads in flight per wavefront.
-template <int FMT, int JX, int KS, int PF>
+template <int FMT, int JX, int KS, int PF, bool GLU>
 __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
                                                     const float *x, float *y, const float *res,
                                                     int N, int K, InOp op) {
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         const int64_t b = blockIdx.y;
         x += b * op.ld;
         if (op.u) op.u += b * op.ld;
-        y += b * static_cast<int64_t>(N);
+        y += b * static_cast<int64_t>(GLU ? N / 2 : N);
         if (res) res += b * static_cast<int64_t>(N);
     }
     constexpr bool kXLds = Q4_MV_X_LDS && KS == 1;
@@ -157,12 +158,16 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     const size_t row_bytes = static_cast<size_t>(nb) * Fmt<FMT>::kBytes;
 
     // Contiguous row range of this row group (sizes differ by at most one).
+    // Output units: rows, or (gate row p, up row p + N/2) pairs with a SwiGLU
+    // output, processed as two consecutive iterations.
     const int G = gridDim.x * RG;
     const int g = blockIdx.x * RG + rg;
-    const int q = N / G, r = N % G;
-    const int cnt = q + (g < r ? 1 : 0);
+    const int units = GLU ? N / 2 : N;
+    const int per = GLU ? 2 : 1;
+    const int q = units / G, r = units % G;
+    const int cnt = per * (q + (g < r ? 1 : 0));
     const int row0 = g * q + min(g, r);
-    const int iters = q + (r > 0 ? 1 : 0);  // same for every wavefront of the grid
+    const int iters = per * (q + (r > 0 ? 1 : 0));  // same for every wavefront of the grid
 
     bool valid[JX];
     int col[JX];
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     // two memory latencies overlap.
     const bool has_res = res != nullptr;
     auto fetch = [&](int it, RowRegs<FMT, JX> &r) {
-        const int row = min(row0 + it, N - 1);
+        const int row = min(GLU ? row0 + (it >> 1) + ((it & 1) ? units : 0) : row0 + it, N - 1);
         load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
     };
     RowRegs<FMT, JX> buf[NBUF];
@@ -323,6 +328,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     }
 
 
+    float gate = 0.f;  // SwiGLU output: the gate row's sum, kept for its pair
     auto process = [&](int it, const RowRegs<FMT, JX> &cur) {
         const bool act = it < cnt;
         float acc = 0.f;
@@ -384,7 +390,12 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         acc = wave_sum(acc);
         const int row = row0 + it;
         if constexpr (KS == 1) {
-            if (act && lane == 0) y[row] = has_res ? acc + cur.res : acc;
+            if constexpr (GLU) {
+                if ((it & 1) == 0) gate = acc;
+                else if (act && lane == 0) y[row0 + (it >> 1)] = silu_mul(gate, acc);
+            } else if (act && lane == 0) {
+                y[row] = has_res ? acc + cur.res : acc;
+            }
         } else {
             // split K: park the partial (and the residual) in LDS; rows are
             // reduced in batches of kFlush with two barriers per batch
@@ -535,7 +546,15 @@ void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int
     int per_cu = KS > 1 ? 1 : std::max(1, std::min(3, N / (q4::device_cus() * RG * 7)));
     if (Q4_MV_WG_PER_CU) per_cu = Q4_MV_WG_PER_CU;
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
-    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF>), dim3(nwg, B), dim3(kWG), 0, s, W, x, y, res, N, K, op);
+    if constexpr (KS == 1) {
+        if (op.glu) {
+            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true>), dim3(nwg, B), dim3(kWG), 0, s, W, x,
+                               y, res, N, K, op);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false>), dim3(nwg, B), dim3(kWG), 0, s, W, x, y,
+                       res, N, K, op);
 }
 
 template <int FMT, int KS>
@@ -566,9 +585,13 @@ void launch_generic(int B, const uint8_t *W, const float *x, float *y, const flo
 
 template <int FMT>
 q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
-                       const float *x2, int64_t ldx, int64_t B, int op_kind, const float *norm_w,
-                       float eps, float *y, const float *res, void *stream) {
+                       const float *x2, int64_t ldx, int64_t B, int op_kind, int out_op,
+                       const float *norm_w, float eps, float *y, const float *res, void *stream) {
     q4::clear_error();
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU, Q4_ERR_INVALID_ARG,
+             "%s: unknown output transform %d", name, out_op);
+    Q4_CHECK(out_op != Q4_OUT_SWIGLU || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
+             "%s: a SwiGLU output needs an even N and no residual", name);
     Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
     Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
              name, (long long)N, (long long)K, (long long)B);
@@ -590,13 +613,15 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     const int n = static_cast<int>(N), k = static_cast<int>(K);
     const int nb = k / 32;
     InOp op{op_kind, op_kind == Q4_IN_SWIGLU ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
-            eps, ldx};
+            eps, ldx, out_op == Q4_OUT_SWIGLU ? 1 : 0};
     int ks = 0;
     if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
         (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0) {
         for (int cand : {1, 2, 4})
             if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
     }
+    Q4_CHECK(out_op != Q4_OUT_SWIGLU || ks == 1, Q4_ERR_UNSUPPORTED,
+             "%s: a SwiGLU output needs K %% 256 == 0, K <= 8192, 16-byte aligned x", name);
     if (ks) {
         const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
         const int b = static_cast<int>(B);
@@ -613,30 +638,30 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
 
 extern "C" q4_status q4_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
                                  float *y, const float *residual, void *stream) {
-    return matvec_entry<0>("q4_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, nullptr, 0.f, y,
-                           residual, stream);
+    return matvec_entry<0>("q4_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, Q4_OUT_PLAIN,
+                           nullptr, 0.f, y, residual, stream);
 }
 
 extern "C" q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64_t B,
                                  float *y, const float *residual, void *stream) {
-    return matvec_entry<1>("q8_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, nullptr, 0.f, y,
-                           residual, stream);
+    return matvec_entry<1>("q8_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, Q4_OUT_PLAIN,
+                           nullptr, 0.f, y, residual, stream);
 }
 
 extern "C" q4_status q4_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                                        const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
-                                       const float *norm_w, float eps, float *y,
-                                       const float *residual, void *stream) {
-    return matvec_entry<0>("q4_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
-                           residual, stream);
+                                       q4_output_op out_op, const float *norm_w, float eps,
+                                       float *y, const float *residual, void *stream) {
+    return matvec_entry<0>("q4_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, out_op, norm_w, eps,
+                           y, residual, stream);
 }
 
 extern "C" q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                                        const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
-                                       const float *norm_w, float eps, float *y,
-                                       const float *residual, void *stream) {
-    return matvec_entry<1>("q8_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
-                           residual, stream);
+                                       q4_output_op out_op, const float *norm_w, float eps,
+                                       float *y, const float *residual, void *stream) {
+    return matvec_entry<1>("q8_0_matvec_fused", W, N, K, x, x2, ld_x, B, op, out_op, norm_w, eps,
+                           y, residual, stream);
 }
 
 extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens,

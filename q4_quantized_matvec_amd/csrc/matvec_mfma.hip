@@ -219,19 +219,25 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int cps) {
+    float *__restrict__ part, int S, int cps, int glu) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
     __shared__ f32x4_t stepmax[2][kMaxB];    // per batch row: the 4 wavefronts' maxima
     __shared__ float ssq_w[4][kMaxB];
+    __shared__ float upx[32][kMaxB];          // SwiGLU output: up-row sums of the 32 pairs
     __shared__ int ticket;
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
-    const int n = blockIdx.x * kRowsWG + wv * 16 + col;
-    const int nl = min(n, N - 1);
+    // Rows of this lane: 64 consecutive rows per workgroup, or with a SwiGLU
+    // output 32 gate rows (wavefronts 0, 1) and their 32 up rows (2, 3).
+    const int P = N >> 1;
+    const int pu = blockIdx.x * 32 + 16 * (wv & 1) + col;  // pair (SwiGLU output)
+    const int n = glu ? (wv < 2 ? pu : P + pu) : blockIdx.x * kRowsWG + wv * 16 + col;
+    const bool rvalid = glu ? pu < P : n < N;
+    const int nl = rvalid ? n : N - 1;
     const int nb = K / 32, kc = nb / kSeg;
     const int c0 = blockIdx.y * cps;
     const int c1 = min(kc, c0 + cps);
@@ -369,6 +375,20 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
             ia = 1.0f / sqrtf(range_ssq(ba) / static_cast<float>(K) + eps);
             ib = 1.0f / sqrtf(range_ssq(bb) / static_cast<float>(K) + eps);
         }
+        if (glu) {
+            const int pl = 16 * (wv & 1) + col;
+            if (wv >= 2) {
+                upx[pl][ba] = ya * ia;
+                upx[pl][bb] = yb * ib;
+            }
+            __syncthreads();
+            if (wv < 2 && rvalid) {
+                const int64_t lp = P;
+                if (ba < B) y[ba * lp + pu] = silu_mul(ya * ia, upx[pl][ba]);
+                if (bb < B) y[bb * lp + pu] = silu_mul(yb * ib, upx[pl][bb]);
+            }
+            return;
+        }
         if (n < N) {
             if (ba < B) y[ba * ln + n] = res ? ya * ia + res[ba * ln + n] : ya * ia;
             if (bb < B) y[bb * ln + n] = res ? yb * ib + res[bb * ln + n] : yb * ib;
@@ -380,7 +400,7 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     // and the last one adds the S partials in split order with device-scope
     // loads.  Device-scope fences are avoided on purpose: on this part they
     // write back and invalidate the whole L2 of the die.
-    if (n < N) {
+    if (rvalid) {
         float *pp = part + static_cast<int64_t>(blockIdx.y) * B * ln;
         if (ba < B) __hip_atomic_store(pp + ba * ln + n, ya, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (bb < B) __hip_atomic_store(pp + bb * ln + n, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -399,12 +419,9 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
         ticket = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
-    for (int o = threadIdx.x; o < kRowsWG * B; o += kWG) {
-        const int b = o / kRowsWG;
-        const int nn = blockIdx.x * kRowsWG + (o % kRowsWG);
-        if (nn >= N) continue;
-        const float *pb = part + static_cast<int64_t>(b) * ln + nn;
-        const int64_t step = static_cast<int64_t>(B) * ln;
+    const int64_t step = static_cast<int64_t>(B) * ln;
+    auto split_sum = [&](int b, int row) {
+        const float *pb = part + static_cast<int64_t>(b) * ln + row;
         float v = 0.f;
         int sp = 0;
         for (; sp + 8 <= S; sp += 8) {  // eight loads in flight, added in split order
@@ -416,14 +433,27 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
             for (int q = 0; q < 8; ++q) v += t[q];
         }
         for (; sp < S; ++sp) v += __hip_atomic_load(pb + sp * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return v;
+    };
+    const int outs = glu ? 32 : kRowsWG;
+    for (int o = threadIdx.x; o < outs * B; o += kWG) {
+        const int b = o / outs;
+        const int nn = blockIdx.x * outs + (o % outs);
+        if (nn >= (glu ? P : N)) continue;
+        float inv = 1.f;
         if constexpr (KIND == 1) {
             const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + b;
             float tot = 0.f;
             for (int sp2 = 0; sp2 < S; ++sp2)
                 tot += __hip_atomic_load(sq + sp2 * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v *= 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+            inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
         }
-        y[b * ln + nn] = res ? v + res[b * ln + nn] : v;
+        if (glu) {
+            y[b * static_cast<int64_t>(P) + nn] = silu_mul(split_sum(b, nn) * inv, split_sum(b, P + nn) * inv);
+        } else {
+            const float v = split_sum(b, nn) * inv;
+            y[b * ln + nn] = res ? v + res[b * ln + nn] : v;
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -453,12 +483,13 @@ Plan make_plan(int64_t N, int64_t K, int64_t B) {
 
 template <int FMT, int KIND>
 void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
-            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, hipStream_t s) {
+            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu,
+            hipStream_t s) {
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     hipLaunchKernelGGL((mv_mfma_kernel<FMT, KIND>), dim3(p.rg, p.S), dim3(kWG), 0, s, W, N, K, B, x,
                        u, nw, ld, eps, y, res, reinterpret_cast<int *>(w8),
                        reinterpret_cast<float *>(w8 + p.off_ssq),
-                       reinterpret_cast<float *>(w8 + p.off_part), p.S, p.cps);
+                       reinterpret_cast<float *>(w8 + p.off_part), p.S, p.cps, glu);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -468,10 +499,14 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 
 template <int FMT>
 q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
-                        const float *x2, int64_t ldx, int64_t B, int op_kind, const float *norm_w,
-                        float eps, float *y, const float *res, void *ws, size_t ws_bytes,
-                        void *stream) {
+                        const float *x2, int64_t ldx, int64_t B, int op_kind, int out_op,
+                        const float *norm_w, float eps, float *y, const float *res, void *ws,
+                        size_t ws_bytes, void *stream) {
     q4::clear_error();
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU, Q4_ERR_INVALID_ARG,
+             "%s: unknown output transform %d", name, out_op);
+    Q4_CHECK(out_op != Q4_OUT_SWIGLU || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
+             "%s: a SwiGLU output needs an even N and no residual", name);
     Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
     Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
              name, (long long)N, (long long)K, (long long)B);
@@ -493,7 +528,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     Q4_CHECK(q4::aligned(y, 4) && (!res || q4::aligned(res, 4)), Q4_ERR_ALIGNMENT,
              "%s: y and residual must be 4-byte aligned", name);
     const size_t xbytes = static_cast<size_t>((B - 1) * ldx + K) * sizeof(float);
-    const size_t ybytes = static_cast<size_t>(B * N) * sizeof(float);
+    const size_t ybytes = static_cast<size_t>(B * (out_op == Q4_OUT_SWIGLU ? N / 2 : N)) * sizeof(float);
     Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
              Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
     const Plan p = make_plan(N, K, B);
@@ -504,9 +539,10 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     hipStream_t s = q4::as_stream(stream);
     const uint8_t *W = static_cast<const uint8_t *>(Wv);
     const int n = static_cast<int>(N), k = static_cast<int>(K), b = static_cast<int>(B);
-    if (op_kind == Q4_IN_RMSNORM) launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, s);
-    else if (op_kind == Q4_IN_SWIGLU) launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, s);
-    else launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, s);
+    const int glu = out_op == Q4_OUT_SWIGLU ? 1 : 0;
+    if (op_kind == Q4_IN_RMSNORM) launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, glu, s);
+    else if (op_kind == Q4_IN_SWIGLU) launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, glu, s);
+    else launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, glu, s);
     return q4::launch_status(name);
 }
 
@@ -519,18 +555,18 @@ extern "C" size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B) {
 
 extern "C" q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
                                          const float *x2, int64_t ld_x, int64_t B,
-                                         q4_input_op op, const float *norm_w, float eps, float *y,
-                                         const float *residual, void *ws, size_t ws_bytes,
-                                         void *stream) {
-    return batched_entry<0>("q4_0_matvec_batched", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
-                            residual, ws, ws_bytes, stream);
+                                         q4_input_op op, q4_output_op out_op, const float *norm_w,
+                                         float eps, float *y, const float *residual, void *ws,
+                                         size_t ws_bytes, void *stream) {
+    return batched_entry<0>("q4_0_matvec_batched", W, N, K, x, x2, ld_x, B, op, out_op, norm_w,
+                            eps, y, residual, ws, ws_bytes, stream);
 }
 
 extern "C" q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,
                                          const float *x2, int64_t ld_x, int64_t B,
-                                         q4_input_op op, const float *norm_w, float eps, float *y,
-                                         const float *residual, void *ws, size_t ws_bytes,
-                                         void *stream) {
-    return batched_entry<1>("q8_0_matvec_batched", W, N, K, x, x2, ld_x, B, op, norm_w, eps, y,
-                            residual, ws, ws_bytes, stream);
+                                         q4_input_op op, q4_output_op out_op, const float *norm_w,
+                                         float eps, float *y, const float *residual, void *ws,
+                                         size_t ws_bytes, void *stream) {
+    return batched_entry<1>("q8_0_matvec_batched", W, N, K, x, x2, ld_x, B, op, out_op, norm_w,
+                            eps, y, residual, ws, ws_bytes, stream);
 }

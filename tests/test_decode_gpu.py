@@ -126,15 +126,19 @@ def test_decode_lockstep_per_op(dev, shape):
         proj(4, L["wo"], att, nq, nq, q.IN_PLAIN, y=x, residual=x)
         r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att), res=xo)
         _check(x, r, 2e-4 * t + 1e-6, f"L{l} o-proj + residual")
-        gu = proj(4, L["wgu"], x, D, D, q.IN_RMSNORM, norm_w=L["ffn_norm"])
+        # the step hands SiLU(gate) * up from the gate|up kernel to the down projection
+        h = proj(4, L["wgu"], x, D, D, q.IN_RMSNORM, norm_w=L["ffn_norm"], out_op=q.OUT_SWIGLU)
         r, t = oracle.q4_0_matvec(W["wgu"], 2 * F, D, oracle.rmsnorm(np_(x), W["ffn_norm"], eps))
-        _check(gu, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + gate|up")
-        g64 = np_(gu)
-        h = np.stack([oracle.swiglu(g64[b, :F], g64[b, F:]) for b in range(B)])
+        g, u = r[:, :F], r[:, F:]
+        tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+        h_ref = np.stack([oracle.swiglu(g[b], u[b]) for b in range(B)])
+        silu_g = g / (1.0 + np.exp(-g))
+        _check(h, h_ref, 1.1 * tg * np.abs(u) + np.abs(silu_g) * tu + 2e-4 * np.abs(h_ref) + 1e-6,
+               f"L{l} rmsnorm + gate|up + swiglu")
         xo = np_(x)
-        proj(4, L["wd"], gu, F, 2 * F, q.IN_SWIGLU, x2=gu[:, F:], y=x, residual=x)
-        r, t = oracle.q4_0_matvec(W["wd"], D, F, h, res=xo)
-        _check(x, r, 2e-4 * t + 1e-6, f"L{l} swiglu + down + residual")
+        proj(4, L["wd"], h, F, F, q.IN_PLAIN, y=x, residual=x)
+        r, t = oracle.q4_0_matvec(W["wd"], D, F, np_(h), res=xo)
+        _check(x, r, 2e-4 * t + 1e-6, f"L{l} down + residual")
     logits = proj(8, dmod["embed"], x, D, D, q.IN_RMSNORM, norm_w=dmod["final_norm"])
     r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D,
                               oracle.rmsnorm(np_(x), weights["final_norm"], eps))

@@ -65,7 +65,7 @@ def test_batched_matvec_rejects_bad_arguments_on_host():
     assert q.matvec_batched_workspace(100, 288, 4) == 0    # K % 256 != 0
     assert q.matvec_batched_workspace(100, 512, 9) == 0    # B > 8
     ybuf = 0x40000000  # does not overlap x
-    args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, None, 0.0, ybuf, None,
+    args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, 0, None, 0.0, ybuf, None,
                                         ws, nbytes, None)
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake, need - 1))[0] == "Q4_ERR_WORKSPACE"
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake + 16, need))[0] == "Q4_ERR_WORKSPACE"
@@ -73,3 +73,14 @@ def test_batched_matvec_rejects_bad_arguments_on_host():
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 9, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
     assert _status(L.q8_0_matvec_batched, *args(fake + 2, 512, 4, fake, need))[0] == "Q4_ERR_ALIGNMENT"
     assert _status(L.q4_0_matvec_batched, *args(None, 512, 4, fake, need))[0] == "Q4_ERR_INVALID_ARG"
+
+
+def test_swiglu_output_rejected_where_unsupported():
+    L = q.lib()
+    fake, ybuf = 0x10000, 0x40000000
+    fused = lambda N, K, res: (fake, N, K, fake, None, K, 1, 0, 1, None, 0.0, ybuf, res, None)
+    assert _status(L.q4_0_matvec_fused, *fused(101, 512, None))[0] == "Q4_ERR_INVALID_ARG"   # odd N
+    assert _status(L.q4_0_matvec_fused, *fused(100, 512, ybuf))[0] == "Q4_ERR_INVALID_ARG"  # residual
+    assert _status(L.q4_0_matvec_fused, *fused(100, 16384, None))[0] == "Q4_ERR_UNSUPPORTED"
+    assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 0, 2, None, 0.0, ybuf,
+                   None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # bad out_op

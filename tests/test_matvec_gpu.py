@@ -292,3 +292,37 @@ def test_matvec_batched_spikes(dev):
         y = fn(torch.from_numpy(W).to(dev), torch.from_numpy(x).to(dev), k, b, k)
         torch.cuda.synchronize()
         _check(y, ref, terms, f"{fmt} spikes")
+
+
+GLU_CASES = [
+    # (path, N, K, B, op): merged gate|up with the SwiGLU output; N = 2F
+    ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 300, 5376, 1, "rms"),
+    ("vector", 2 * 77, 2048, 3, "plain"), ("vector", 2 * 33, 256, 8, "rms_unit"),
+    ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 300, 2560, 8, "rms"),
+    ("batched", 2 * 77, 9728, 5, "plain"), ("batched", 2 * 1000, 5376, 2, "rms"),
+    ("batched", 2 * 33, 256, 1, "swiglu"),
+]
+
+
+@pytest.mark.parametrize("path,n,k,b,op", GLU_CASES)
+def test_matvec_swiglu_output(dev, path, n, k, b, op):
+    """y[p] = SiLU(z[p]) * z[p + N/2] with z the matvec: bound from the two
+    matvec bounds through SiLU(g) u (|SiLU'| <= 1.1) plus 2e-4 relative."""
+    _say(f"{path} swiglu output {op} N={n} K={k} B={b}")
+    W, xa, w, r, xin, ld = _fused_inputs("q4", n, k, b, op, 112)
+    z, t = oracle.q4_0_matvec(W, n, k, xin)
+    F = n // 2
+    g, u = z[:, :F], z[:, F:]
+    tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+    ref = g / (1.0 + np.exp(-g)) * u
+    tol = 1.1 * tg * np.abs(u) + np.abs(g / (1.0 + np.exp(-g))) * tu + 2e-4 * np.abs(ref) + 1e-6
+    xd = torch.from_numpy(xa).to(dev)
+    fn = q.q4_0_matvec_batched if path == "batched" else q.q4_0_matvec_fused
+    kw = dict(x2=xd[:, k:] if op == "swiglu" else None,
+              norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
+    h = fn(torch.from_numpy(W).to(dev), xd, k, b, ld, _KIND[op], out_op=q.OUT_SWIGLU, **kw)
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.float64)
+    assert got.shape == (b, F)
+    ratio = float((np.abs(got - ref) / tol).max())
+    assert np.all(np.isfinite(got)) and ratio <= 1.0, f"max err/tol {ratio:.3e}"
