@@ -55,7 +55,17 @@ def time_dispatches(torch, launch, steps, warmup):
 
 
 def time_matvec(q, torch, Ws, x, y, steps, warmup):
-    return time_dispatches(torch, lambda i: q.q4_0_matvec(Ws[i % len(Ws)], x, y=y), steps, warmup)
+    """B = 1 and vector-path B > 1: the C entry point called with prepared
+    arguments, so host submission stays far below a dispatch (also under a
+    tracing profiler, whose per-launch hooks would otherwise leave gaps)."""
+    fn = q.lib().q4_0_matvec
+    B, K = x.shape
+    N = y.shape[1]
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [(W.data_ptr(), N, K, x.data_ptr(), B, y.data_ptr(), None, stream) for W in Ws]
+    for a in args[:1]:
+        assert fn(*a) == 0, q.lib().q4dec_last_error()
+    return time_dispatches(torch, lambda i: fn(*args[i % len(args)]), steps, warmup)
 
 
 def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):

@@ -190,13 +190,16 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     const uint32_t sel_e = odd ? 0x0C060C04u : 0x0C040C02u;
     const uint32_t sel_o = odd ? 0x0C070C05u : 0x0C050C03u;
 
-    // Rows past this group's range are clamped to a real row (loaded, unused).
     // Without a residual the residual slot reads x[0] and is ignored.  The
     // first PF rows are requested before the activations are staged, so the
     // two memory latencies overlap.
     const bool has_res = res != nullptr;
+    // Iterations past the group's range re-read its last row (already in this
+    // CU's caches) instead of the next group's first rows.
+    const int ulast = min(row0 + max(cnt / per, 1) - 1, units - 1);
     auto fetch = [&](int it, RowRegs<FMT, JX> &r) {
-        const int row = min(GLU ? row0 + (it >> 1) + ((it & 1) ? units : 0) : row0 + it, N - 1);
+        const int un = min(row0 + (GLU ? (it >> 1) : it), ulast);
+        const int row = (GLU && (it & 1)) ? un + units : un;
         load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
     };
     RowRegs<FMT, JX> buf[NBUF];
