@@ -118,20 +118,9 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         return static_cast<int64_t>(sl) * st;
     };
 
-    // ---- scores
+    // ---- scores, SG keys per wavefront at a time (bounds the registers held)
+    constexpr int SG = SIT < 8 ? SIT : 8;
     const int sub = lane % LPK, kgl = lane / LPK;
-    float kr[SIT][8];
-#pragma unroll
-    for (int it = 0; it < SIT; ++it) {
-        const int jj = it * 4 * KPW + wave * KPW + kgl;
-        // lane sub holds elements [4 sub, 4 sub + 4) and HD/2 + [4 sub, 4 sub + 4):
-        // each load instruction covers contiguous bytes of the key row
-        const float *kp = kb + slot(jj) + sub * 4;
-        const float4 a = *reinterpret_cast<const float4 *>(kp);
-        const float4 bq = *reinterpret_cast<const float4 *>(kp + HD / 2);
-        kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
-        kr[it][4] = bq.x; kr[it][5] = bq.y; kr[it][6] = bq.z; kr[it][7] = bq.w;
-    }
     float qv[GM][8];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
@@ -141,16 +130,31 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         qv[g][0] = a.x * scale; qv[g][1] = a.y * scale; qv[g][2] = a.z * scale; qv[g][3] = a.w * scale;
         qv[g][4] = bq.x * scale; qv[g][5] = bq.y * scale; qv[g][6] = bq.z * scale; qv[g][7] = bq.w * scale;
     }
+#pragma unroll 1
+    for (int i0 = 0; i0 < SIT; i0 += SG) {
+        float kr[SG][8];
 #pragma unroll
-    for (int it = 0; it < SIT; ++it) {
-        const int jj = it * 4 * KPW + wave * KPW + kgl;
+        for (int it = 0; it < SG; ++it) {
+            const int jj = (i0 + it) * 4 * KPW + wave * KPW + kgl;
+            // lane sub holds elements [4 sub, 4 sub + 4) and HD/2 + [4 sub, 4 sub + 4):
+            // each load instruction covers contiguous bytes of the key row
+            const float *kp = kb + slot(jj) + sub * 4;
+            const float4 a = *reinterpret_cast<const float4 *>(kp);
+            const float4 bq = *reinterpret_cast<const float4 *>(kp + HD / 2);
+            kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
+            kr[it][4] = bq.x; kr[it][5] = bq.y; kr[it][6] = bq.z; kr[it][7] = bq.w;
+        }
 #pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            float s = 0.f;
+        for (int it = 0; it < SG; ++it) {
+            const int jj = (i0 + it) * 4 * KPW + wave * KPW + kgl;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[g][e], kr[it][e], s);
-            s = group_sum<LPK>(s);
-            if (sub == 0 && g < G) sc[jj * GM + g] = jj < cnt ? s : -INFINITY;
+            for (int g = 0; g < GM; ++g) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qv[g][e], kr[it][e], s);
+                s = group_sum<LPK>(s);
+                if (sub == 0 && g < G) sc[jj * GM + g] = jj < cnt ? s : -INFINITY;
+            }
         }
     }
     __syncthreads();
@@ -171,23 +175,27 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 
     // ---- weighted values: TPK threads per key (4 dims each), KG key groups
     const int kg = threadIdx.x / TPK, d4 = threadIdx.x % TPK;
-    float4 vv[VIT];
-#pragma unroll
-    for (int it = 0; it < VIT; ++it)
-        vv[it] = reinterpret_cast<const float4 *>(vb + slot(kg + it * KG))[d4];
+    constexpr int VG = VIT < 16 ? VIT : 16;  // keys per thread at a time
     float4 acc[GM];
 #pragma unroll
     for (int g = 0; g < GM; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+    for (int i0 = 0; i0 < VIT; i0 += VG) {
+        float4 vv[VG];
 #pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-        const int j = kg + it * KG;  // weights of positions past cnt are 0
+        for (int it = 0; it < VG; ++it)
+            vv[it] = reinterpret_cast<const float4 *>(vb + slot(kg + (i0 + it) * KG))[d4];
 #pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            const float w = sc[j * GM + g];
-            acc[g].x = __builtin_fmaf(w, vv[it].x, acc[g].x);
-            acc[g].y = __builtin_fmaf(w, vv[it].y, acc[g].y);
-            acc[g].z = __builtin_fmaf(w, vv[it].z, acc[g].z);
-            acc[g].w = __builtin_fmaf(w, vv[it].w, acc[g].w);
+        for (int it = 0; it < VG; ++it) {
+            const int j = kg + (i0 + it) * KG;  // weights of positions past cnt are 0
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                const float w = sc[j * GM + g];
+                acc[g].x = __builtin_fmaf(w, vv[it].x, acc[g].x);
+                acc[g].y = __builtin_fmaf(w, vv[it].y, acc[g].y);
+                acc[g].z = __builtin_fmaf(w, vv[it].z, acc[g].z);
+                acc[g].w = __builtin_fmaf(w, vv[it].w, acc[g].w);
+            }
         }
     }
     if constexpr (KG > 1) {

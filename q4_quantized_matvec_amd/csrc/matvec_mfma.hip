@@ -444,8 +444,16 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
         if constexpr (KIND == 1) {
             const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + b;
             float tot = 0.f;
-            for (int sp2 = 0; sp2 < S; ++sp2)
-                tot += __hip_atomic_load(sq + sp2 * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int sp = 0;
+            for (; sp + 8 <= S; sp += 8) {  // eight loads in flight, added in split order
+                float t[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    t[q] = __hip_atomic_load(sq + (sp + q) * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) tot += t[q];
+            }
+            for (; sp < S; ++sp) tot += __hip_atomic_load(sq + sp * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
         }
         if (glu) {
