@@ -127,7 +127,7 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
  *   y         must not overlap x or x2 (Q4_ERR_INVALID_ARG); may alias residual;
  *             a SwiGLU output (out_op) is supported for every K % 256 == 0
  *   ws        device workspace of at least matvec_batched_workspace(N, K, B)
- *             bytes, 256-byte aligned, owned by the caller.  Its first 16 KiB
+ *             bytes, 256-byte aligned, owned by the caller.  Its first 512 KiB
  *             (split tickets) must be zero before the first call that uses
  *             it; every call leaves them zero.  Calls sharing a workspace
  *             must be ordered (one stream).

@@ -54,8 +54,10 @@ constexpr int kRowsWG = 64;         // 16 rows per wavefront
 constexpr int kSeg = 8;             // blocks per step (one MFMA each per wavefront)
 constexpr int kTargetWGs = 1024;    // about 4 workgroups per compute unit
 constexpr int kMaxB = 8;
+constexpr int kMaxS = 32;           // K splits at most (the final writer holds them in registers)
 constexpr int kCounters = 4096;     // split tickets: row ranges of a K-split launch
-constexpr size_t kCounterBytes = kCounters * sizeof(int);
+constexpr int kCounterStride = 32;  // one ticket per 128-byte line: atomics on one line serialise
+constexpr size_t kCounterBytes = static_cast<size_t>(kCounters) * kCounterStride * sizeof(int);
 
 template <int FMT>
 struct BF;
@@ -416,54 +418,72 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = __hip_atomic_fetch_add(&counters[blockIdx.x * kCounterStride], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
+    // Final writer: every partial it needs is requested before any is added
+    // (device-scope loads miss the die's L2, so each round trip is long), and
+    // the S partials of a row are added in split order.
     const int64_t step = static_cast<int64_t>(B) * ln;
-    auto split_sum = [&](int b, int row) {
-        const float *pb = part + static_cast<int64_t>(b) * ln + row;
-        float v = 0.f;
-        int sp = 0;
-        for (; sp + 8 <= S; sp += 8) {  // eight loads in flight, added in split order
-            float t[8];
+    __shared__ float inv_s[kMaxB];
+    if constexpr (KIND == 1) {
+        if (threadIdx.x < B) {
+            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + threadIdx.x;
+            float t[kMaxS];
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                t[q] = __hip_atomic_load(pb + (sp + q) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v += t[q];
-        }
-        for (; sp < S; ++sp) v += __hip_atomic_load(pb + sp * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return v;
-    };
-    const int outs = glu ? 32 : kRowsWG;
-    for (int o = threadIdx.x; o < outs * B; o += kWG) {
-        const int b = o / outs;
-        const int nn = blockIdx.x * outs + (o % outs);
-        if (nn >= (glu ? P : N)) continue;
-        float inv = 1.f;
-        if constexpr (KIND == 1) {
-            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + b;
+            for (int q = 0; q < kMaxS; ++q)
+                t[q] = __hip_atomic_load(sq + (q < S ? q : 0) * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             float tot = 0.f;
-            int sp = 0;
-            for (; sp + 8 <= S; sp += 8) {  // eight loads in flight, added in split order
-                float t[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    t[q] = __hip_atomic_load(sq + (sp + q) * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) tot += t[q];
-            }
-            for (; sp < S; ++sp) tot += __hip_atomic_load(sq + sp * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
-        }
-        if (glu) {
-            y[b * static_cast<int64_t>(P) + nn] = silu_mul(split_sum(b, nn) * inv, split_sum(b, P + nn) * inv);
-        } else {
-            const float v = split_sum(b, nn) * inv;
-            y[b * ln + nn] = res ? v + res[b * ln + nn] : v;
+            for (int q = 0; q < kMaxS; ++q)
+                if (q < S) tot += t[q];
+            inv_s[threadIdx.x] = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
         }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // up to two rows per thread: outputs tid and tid + 256, or the gate and up
+    // rows of SwiGLU output tid
+    const int outs = glu ? 32 : kRowsWG;
+    int row[2], ob[2];
+    bool act[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int o = glu ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) + r * kWG;
+        ob[r] = o / outs;
+        const int nn = blockIdx.x * outs + (o % outs);
+        act[r] = o < outs * B && nn < (glu ? P : N);
+        row[r] = glu ? (r == 0 ? nn : P + nn) : nn;
+    }
+    float pv[2][kMaxS];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const float *pb = part + static_cast<int64_t>(act[r] ? ob[r] : 0) * ln + (act[r] ? row[r] : 0);
+#pragma unroll
+        for (int q = 0; q < kMaxS; ++q)
+            pv[r][q] = __hip_atomic_load(pb + (q < S ? q : 0) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float sum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < kMaxS; ++q)
+            if (q < S) sum[r] += pv[r][q];
+    if constexpr (KIND == 1) __syncthreads();
+    if (glu) {
+        if (act[0]) {
+            const float inv = KIND == 1 ? inv_s[ob[0]] : 1.f;
+            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = silu_mul(sum[0] * inv, sum[1] * inv);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (!act[r]) continue;
+            const float v = sum[r] * (KIND == 1 ? inv_s[ob[r]] : 1.f);
+            y[ob[r] * ln + row[r]] = res ? v + res[ob[r] * ln + row[r]] : v;
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&counters[blockIdx.x * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- host side
@@ -478,7 +498,7 @@ Plan make_plan(int64_t N, int64_t K, int64_t B) {
     Plan p;
     p.rg = static_cast<int>((N + kRowsWG - 1) / kRowsWG);
     p.kc = static_cast<int>(K / (32 * kSeg));
-    int want = std::max(1, std::min(p.kc, (kTargetWGs + p.rg - 1) / p.rg));
+    int want = std::max(1, std::min(std::min(p.kc, kMaxS), (kTargetWGs + p.rg - 1) / p.rg));
     if (p.rg > kCounters) want = 1;
     p.cps = (p.kc + want - 1) / want;
     p.S = (p.kc + p.cps - 1) / p.cps;
