@@ -230,6 +230,24 @@ q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads, const 
  * arguments). */
 size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_heads, int64_t window);
 
+/* gqa_decode_attn_rope: qk_norm_rope followed by gqa_decode_attn in one call,
+ * reading q, k (and v) raw from the merged projection row: per head
+ * RMSNorm with q_norm / k_norm, NeoX RoPE at the position *pos_dev, the new
+ * key and value rows appended at slot pos % cap (v = unit-gain RMSNorm of the
+ * raw key when v_from_k), then attention over the n = pos + 1 positions as
+ * gqa_decode_attn.  The normalised q is not written back.
+ * ([GELO] 05 Components: cached GQA attention with per-head QK-norm before
+ * RoPE; [GEM] Verified model facts: V from K on full-attention layers.)
+ *   qkv      device fp32 [B][ld]: q (n_q_heads * hd) | k (Hkv * hd) | v (Hkv * hd,
+ *            absent when v_from_k); 16-byte aligned, ld % 4 == 0
+ *   pos_dev  device int64: the position of the new token
+ * Other arguments, the workspace and errors as qk_norm_rope / gqa_decode_attn. */
+q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t n_q_heads,
+                               const float *q_norm, const float *k_norm, const q4_kv_layout *kv,
+                               const int64_t *pos_dev, double theta, float eps, int v_from_k,
+                               float *k_cache, float *v_cache, int64_t window, float scale,
+                               float *out, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------ sampling
  * argmax_rows: out[b] = index of the largest logits[b][v], lowest index on
  *   ties ([GELO] 05: greedy sampler; [GEM] Native Metal diagnostic: equal

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     DecodeModel,
     argmax_rows,
     gqa_decode_attn,
+    gqa_decode_attn_rope,
     gqa_decode_attn_workspace,
     lib,
     matvec_batched_workspace,

@@ -65,6 +65,8 @@ _SIGS = {
     "gqa_decode_attn": ([_P, _I64, _I64, _P, _P, C.POINTER(KVLayout), _P, _I64, _F, _P, _I64,
                          _P, _SZ, _P], C.c_int),
     "gqa_decode_attn_workspace": ([C.POINTER(KVLayout), _I64, _I64], _SZ),
+    "gqa_decode_attn_rope": ([_P, _I64, _I64, _P, _P, C.POINTER(KVLayout), _P, _D, _F, C.c_int, _P,
+                              _P, _I64, _F, _P, _I64, _P, _SZ, _P], C.c_int),
     "argmax_rows": ([_P, _I64, _I64, _P, _P], C.c_int),
     "decode_model_workspace": ([C.POINTER(ModelDesc), C.POINTER(_SZ)], C.c_int),
     "decode_model_create": ([C.POINTER(ModelDesc), _P, _SZ, C.POINTER(_P)], C.c_int),
@@ -288,6 +290,15 @@ def gqa_decode_attn(q, ldq, n_q_heads, k_cache, v_cache, kv, n_dev, window, scal
         _ptr(q), ldq, n_q_heads, _ptr(k_cache), _ptr(v_cache), C.byref(kv), _ptr(n_dev),
         int(window), float(scale), _ptr(out), ldo, _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def gqa_decode_attn_rope(qkv, ld, n_q_heads, q_norm, k_norm, kv, pos_dev, theta, eps, v_from_k,
+                         k_cache, v_cache, window, scale, out, ldo, ws, stream=None):
+    """QK-norm + RoPE + KV append + attention in one call (q, k, v read raw from qkv rows)."""
+    _check("gqa_decode_attn_rope", lib().gqa_decode_attn_rope(
+        _ptr(qkv), ld, n_q_heads, _ptr(q_norm), _ptr(k_norm), C.byref(kv), _ptr(pos_dev),
+        float(theta), float(eps), int(bool(v_from_k)), _ptr(k_cache), _ptr(v_cache), int(window),
+        float(scale), _ptr(out), ldo, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def argmax_rows(logits, out=None, stream=None):

@@ -71,12 +71,40 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // One workgroup per (chunk, kv head, sequence).  Loads are issued in batches
 // ahead of their use so the wavefronts keep many rows in flight.
-template <int HD, int GM>
+// Fused query/key preparation (gqa_decode_attn_rope): q and the new key are
+// read raw from the merged projection row, RMS-normalised per head with their
+// gains and rotated (NeoX pairs i, i + hd/2); the new key and value rows are
+// appended to the caches by the workgroup whose chunk holds the position.
+struct RopeArgs {
+    const float *kraw, *vraw;  // raw key / value rows of kv head 0 (vraw NULL: V from K)
+    int64_t ldkv;              // row stride of kraw / vraw
+    const float *qn, *kn;      // per-head gains [hd]
+    double theta;
+    float eps;
+    float *kcw, *vcw;          // the caches, written at slot pos % cap
+};
+
+// cos / sin of pos * theta^(-2i/hd): frequency by binary powers of
+// theta^(-2/hd) in fp64, angle reduced by 2 pi in fp64, then single-precision
+// sincos of the reduced angle (i < 256).
+__device__ __forceinline__ void rope_cs(int64_t pos, double r, int i, float &cs, float &sn) {
+    double f = 1.0, rp = r;  // r = theta^(-2/hd)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        f = ((i >> k) & 1) ? f * rp : f;
+        rp = rp * rp;
+    }
+    const double ang = static_cast<double>(pos) * f;
+    const double two_pi = 6.283185307179586;
+    const double red = __builtin_fma(-two_pi, rint(ang * (1.0 / two_pi)), ang);
+    sincosf(static_cast<float>(red), &sn, &cs);
+}
+
+template <int HD, int GM, bool ROPE>
 __global__ __launch_bounds__(kWG) void attn_split_kernel(
-    const float *__restrict__ q, int64_t ldq, int G, const float *__restrict__ kc,
-    const float *__restrict__ vc, int64_t cap, int64_t sb, int64_t sh, int64_t st,
-    const int64_t *__restrict__ n_dev, int64_t window, float scale, int nch,
-    float *__restrict__ part) {
+    const float *__restrict__ q, int64_t ldq, int G, const float *kc, const float *vc, int64_t cap,
+    int64_t sb, int64_t sh, int64_t st, const int64_t *__restrict__ n_dev, int64_t window,
+    float scale, int nch, float *__restrict__ part, RopeArgs ra) {
     constexpr int LPK = HD / 8;              // score pass: lanes per key, 8 elements per lane
     constexpr int KPW = 64 / LPK;            // keys per wavefront per step
     constexpr int SIT = kChunk / (4 * KPW);  // score steps per wavefront
@@ -88,7 +116,8 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 
     const int c = blockIdx.x, g0 = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n = *n_dev;
+    // fused preparation: n_dev holds the new token's position, n = pos + 1
+    const int64_t n = ROPE ? *n_dev + 1 : *n_dev;
     int64_t lo = window > 0 ? n - window : 0;
     lo = max(lo, n - cap);
     lo = max(lo, int64_t(0));
@@ -121,14 +150,72 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     // ---- scores, SG keys per wavefront at a time (bounds the registers held)
     constexpr int SG = SIT < 8 ? SIT : 8;
     const int sub = lane % LPK, kgl = lane / LPK;
+    // lane sub holds elements [4 sub, 4 sub + 4) and HD/2 + [4 sub, 4 sub + 4),
+    // i.e. four whole RoPE pairs
+    auto load8 = [&](const float *p, float (&v)[8]) {
+        const float4 a = *reinterpret_cast<const float4 *>(p + sub * 4);
+        const float4 bq = *reinterpret_cast<const float4 *>(p + HD / 2 + sub * 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = bq.x; v[5] = bq.y; v[6] = bq.z; v[7] = bq.w;
+    };
+    float rc[4], rs[4];   // RoPE cos / sin of this lane's pairs
+    float gq[8], gk[8];   // gains of this lane's elements
+    auto norm_rope = [&](float (&v)[8], const float (&gain)[8]) {  // in place
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+        ss = group_sum<LPK>(ss);
+        const float inv = 1.0f / sqrtf(ss / static_cast<float>(HD) + ra.eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = v[e] * inv * gain[e], x1 = v[e + 4] * inv * gain[e + 4];
+            v[e] = x0 * rc[e] - x1 * rs[e];
+            v[e + 4] = x1 * rc[e] + x0 * rs[e];
+        }
+        return inv;
+    };
+    if constexpr (ROPE) {
+        const int64_t pos = n - 1;
+        const double r = pow(ra.theta, -2.0 / static_cast<double>(HD));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_cs(pos, r, 4 * sub + e, rc[e], rs[e]);
+        load8(ra.qn, gq);
+        load8(ra.kn, gk);
+        if (pos >= p0 && pos < p0 + cnt) {
+            // this chunk holds the new position: append its key and value rows
+            float kv8[8], vv8[8];
+            const float *kr = ra.kraw + b * ra.ldkv + static_cast<int64_t>(g0) * HD;
+            load8(kr, kv8);
+            float raw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) raw[e] = kv8[e];
+            const float kinv = norm_rope(kv8, gk);
+            if (ra.vraw) load8(ra.vraw + b * ra.ldkv + static_cast<int64_t>(g0) * HD, vv8);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vv8[e] = raw[e] * kinv;  // unit-gain RMSNorm of the raw key
+            }
+            if (wave == 0 && kgl == 0) {
+                const int64_t off = b * sb + static_cast<int64_t>(g0) * sh + (pos % cap) * st;
+                float *kd = ra.kcw + off, *vd = ra.vcw + off;
+                *reinterpret_cast<float4 *>(kd + sub * 4) = make_float4(kv8[0], kv8[1], kv8[2], kv8[3]);
+                *reinterpret_cast<float4 *>(kd + HD / 2 + sub * 4) = make_float4(kv8[4], kv8[5], kv8[6], kv8[7]);
+                *reinterpret_cast<float4 *>(vd + sub * 4) = make_float4(vv8[0], vv8[1], vv8[2], vv8[3]);
+                *reinterpret_cast<float4 *>(vd + HD / 2 + sub * 4) = make_float4(vv8[4], vv8[5], vv8[6], vv8[7]);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);  // the rows are written before any wavefront reads them
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __syncthreads();
+        }
+    }
     float qv[GM][8];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        const float *qh = q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD + sub * 4;
-        const float4 a = *reinterpret_cast<const float4 *>(qh);
-        const float4 bq = *reinterpret_cast<const float4 *>(qh + HD / 2);
-        qv[g][0] = a.x * scale; qv[g][1] = a.y * scale; qv[g][2] = a.z * scale; qv[g][3] = a.w * scale;
-        qv[g][4] = bq.x * scale; qv[g][5] = bq.y * scale; qv[g][6] = bq.z * scale; qv[g][7] = bq.w * scale;
+        load8(q + b * ldq + static_cast<int64_t>(g0 * G + min(g, G - 1)) * HD, qv[g]);
+        if constexpr (ROPE) (void)norm_rope(qv[g], gq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][e] *= scale;
     }
 #pragma unroll 1
     for (int i0 = 0; i0 < SIT; i0 += SG) {
@@ -136,13 +223,8 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 #pragma unroll
         for (int it = 0; it < SG; ++it) {
             const int jj = (i0 + it) * 4 * KPW + wave * KPW + kgl;
-            // lane sub holds elements [4 sub, 4 sub + 4) and HD/2 + [4 sub, 4 sub + 4):
             // each load instruction covers contiguous bytes of the key row
-            const float *kp = kb + slot(jj) + sub * 4;
-            const float4 a = *reinterpret_cast<const float4 *>(kp);
-            const float4 bq = *reinterpret_cast<const float4 *>(kp + HD / 2);
-            kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
-            kr[it][4] = bq.x; kr[it][5] = bq.y; kr[it][6] = bq.z; kr[it][7] = bq.w;
+            load8(kb + slot(jj), kr[it]);
         }
 #pragma unroll
         for (int it = 0; it < SG; ++it) {
@@ -277,15 +359,16 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     }
 }
 
-template <int HD>
+template <int HD, bool ROPE>
 void launch_split_hd(int GM, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
                      const float *kc, const float *vc, const q4_kv_layout &kv,
-                     const int64_t *n_dev, int64_t window, float scale, int nch, float *part) {
-#define Q4_ATTN_CASE(GG)                                                                         \
-    case GG:                                                                                     \
-        hipLaunchKernelGGL((attn_split_kernel<HD, GG>), grid, dim3(kWG), 0, s, q, ldq, G, kc, vc, \
-                           kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale,  \
-                           nch, part);                                                    \
+                     const int64_t *n_dev, int64_t window, float scale, int nch, float *part,
+                     const RopeArgs &ra) {
+#define Q4_ATTN_CASE(GG)                                                                          \
+    case GG:                                                                                      \
+        hipLaunchKernelGGL((attn_split_kernel<HD, GG, ROPE>), grid, dim3(kWG), 0, s, q, ldq, G, kc, \
+                           vc, kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale, \
+                           nch, part, ra);                                                        \
         break;
     switch (GM) { Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(8) Q4_ATTN_CASE(16) }
 #undef Q4_ATTN_CASE
@@ -312,53 +395,96 @@ extern "C" size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_
     return units * (static_cast<size_t>(k2.head_dim) + 2) * sizeof(float);
 }
 
-extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads,
-                                     const float *k_cache, const float *v_cache,
-                                     const q4_kv_layout *kv, const int64_t *n_dev, int64_t window,
-                                     float scale, float *out, int64_t ldo, void *ws,
-                                     size_t ws_bytes, void *stream) {
-    q4::clear_error();
-    q4_status st = q4::check_kv_layout("gqa_decode_attn", kv);
+namespace {
+// Validation and launch shared by gqa_decode_attn and gqa_decode_attn_rope.
+q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_heads,
+                     const float *k_cache, const float *v_cache, const q4_kv_layout *kv,
+                     const int64_t *n_dev, int64_t window, float scale, float *out, int64_t ldo,
+                     void *ws, size_t ws_bytes, void *stream, const RopeArgs *ra) {
+    q4_status st = q4::check_kv_layout(name, kv);
     if (st != Q4_OK) return st;
     Q4_CHECK(q && k_cache && v_cache && n_dev && out, Q4_ERR_INVALID_ARG,
-             "gqa_decode_attn: q, caches, n_dev and out must not be NULL");
-    Q4_CHECK(window >= 0, Q4_ERR_INVALID_ARG, "gqa_decode_attn: window must be >= 0");
+             "%s: q, caches, the position / count and out must not be NULL", name);
+    Q4_CHECK(window >= 0, Q4_ERR_INVALID_ARG, "%s: window must be >= 0", name);
     Q4_CHECK(n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0, Q4_ERR_SHAPE,
-             "gqa_decode_attn: n_q_heads %lld is not a multiple of n_kv_heads %lld",
-             (long long)n_q_heads, (long long)kv->n_kv_heads);
+             "%s: n_q_heads %lld is not a multiple of n_kv_heads %lld", name, (long long)n_q_heads,
+             (long long)kv->n_kv_heads);
     const int64_t hd = kv->head_dim;
     Q4_CHECK(hd == 64 || hd == 128 || hd == 256 || hd == 512, Q4_ERR_UNSUPPORTED,
-             "gqa_decode_attn: head_dim %lld not in {64, 128, 256, 512}", (long long)hd);
+             "%s: head_dim %lld not in {64, 128, 256, 512}", name, (long long)hd);
     const int G = static_cast<int>(n_q_heads / kv->n_kv_heads);
-    Q4_CHECK(G <= 16, Q4_ERR_UNSUPPORTED, "gqa_decode_attn: %d query heads per kv head > 16", G);
+    Q4_CHECK(G <= 16, Q4_ERR_UNSUPPORTED, "%s: %d query heads per kv head > 16", name, G);
     Q4_CHECK(ldq >= n_q_heads * hd && ldo >= n_q_heads * hd, Q4_ERR_SHAPE,
-             "gqa_decode_attn: row strides smaller than the rows");
+             "%s: row strides smaller than the rows", name);
     Q4_CHECK(kv->stride_t % 4 == 0 && kv->stride_h % 4 == 0 && kv->stride_b % 4 == 0 && ldq % 4 == 0,
-             Q4_ERR_ALIGNMENT, "gqa_decode_attn: cache strides and ldq must be multiples of 4");
+             Q4_ERR_ALIGNMENT, "%s: cache strides and row strides must be multiples of 4", name);
     Q4_CHECK(q4::aligned(q, 16) && q4::aligned(k_cache, 16) && q4::aligned(v_cache, 16) &&
                  q4::aligned(out, 4) && q4::aligned(n_dev, 8),
-             Q4_ERR_ALIGNMENT, "gqa_decode_attn: q and caches must be 16-byte aligned");
+             Q4_ERR_ALIGNMENT, "%s: q and caches must be 16-byte aligned", name);
     const size_t need = gqa_decode_attn_workspace(kv, n_q_heads, window);
     Q4_CHECK(ws && ws_bytes >= need && q4::aligned(ws, 256), Q4_ERR_WORKSPACE,
-             "gqa_decode_attn: workspace of %zu bytes (256-byte aligned) needed, got %zu", need,
-             ws_bytes);
+             "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", name, need, ws_bytes);
     AttnGeom g = attn_geom(*kv, n_q_heads, window);
     const int gm = round_group(G);
     hipStream_t s = q4::as_stream(stream);
     float *part = static_cast<float *>(ws);
     dim3 grid(g.nch, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
-    switch (hd) {
-        case 64: launch_split_hd<64>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
-        case 128: launch_split_hd<128>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
-        case 256: launch_split_hd<256>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
-        default: launch_split_hd<512>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g.nch, part); break;
-    }
-    q4_status ls = q4::launch_status("gqa_decode_attn (split)");
+    const RopeArgs none{};
+#define Q4_ATTN_HD(H)                                                                             \
+    case H:                                                                                       \
+        if (ra) launch_split_hd<H, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,    \
+                                         window, scale, g.nch, part, *ra);                        \
+        else launch_split_hd<H, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,      \
+                                       window, scale, g.nch, part, none);                         \
+        break;
+    switch (hd) { Q4_ATTN_HD(64) Q4_ATTN_HD(128) Q4_ATTN_HD(256) Q4_ATTN_HD(512) }
+#undef Q4_ATTN_HD
+    q4_status ls = q4::launch_status(name);
     if (ls != Q4_OK) return ls;
     hipLaunchKernelGGL(attn_merge_kernel,
                        dim3(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(kv->batch),
                             static_cast<unsigned>((hd + 63) / 64)),
                        dim3(kWG), 0, s, part, G, static_cast<int>(kv->n_kv_heads), g.nch, gm,
                        static_cast<int>(hd), out, ldo, static_cast<int>(kv->batch));
-    return q4::launch_status("gqa_decode_attn (merge)");
+    return q4::launch_status(name);
+}
+}  // namespace
+
+extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads,
+                                     const float *k_cache, const float *v_cache,
+                                     const q4_kv_layout *kv, const int64_t *n_dev, int64_t window,
+                                     float scale, float *out, int64_t ldo, void *ws,
+                                     size_t ws_bytes, void *stream) {
+    q4::clear_error();
+    return attn_entry("gqa_decode_attn", q, ldq, n_q_heads, k_cache, v_cache, kv, n_dev, window,
+                      scale, out, ldo, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t n_q_heads,
+                                          const float *q_norm, const float *k_norm,
+                                          const q4_kv_layout *kv, const int64_t *pos_dev,
+                                          double theta, float eps, int v_from_k, float *k_cache,
+                                          float *v_cache, int64_t window, float scale, float *out,
+                                          int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
+    q4::clear_error();
+    const char *name = "gqa_decode_attn_rope";
+    Q4_CHECK(kv && qkv && q_norm && k_norm, Q4_ERR_INVALID_ARG,
+             "%s: qkv, q_norm, k_norm and kv must not be NULL", name);
+    Q4_CHECK(theta > 0.0 && eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: theta > 0, eps >= 0", name);
+    const int64_t nq = n_q_heads * kv->head_dim, nk = kv->n_kv_heads * kv->head_dim;
+    Q4_CHECK(ld >= nq + nk + (v_from_k ? 0 : nk), Q4_ERR_SHAPE, "%s: ld smaller than q | k | v", name);
+    Q4_CHECK(q4::aligned(q_norm, 16) && q4::aligned(k_norm, 16) && ld % 4 == 0, Q4_ERR_ALIGNMENT,
+             "%s: gains must be 16-byte aligned and ld a multiple of 4", name);
+    RopeArgs ra;
+    ra.kraw = qkv + nq;
+    ra.vraw = v_from_k ? nullptr : qkv + nq + nk;
+    ra.ldkv = ld;
+    ra.qn = q_norm;
+    ra.kn = k_norm;
+    ra.theta = theta;
+    ra.eps = eps;
+    ra.kcw = k_cache;
+    ra.vcw = v_cache;
+    return attn_entry(name, qkv, ld, n_q_heads, k_cache, v_cache, kv, pos_dev, window, scale, out,
+                      ldo, ws, ws_bytes, stream, &ra);
 }

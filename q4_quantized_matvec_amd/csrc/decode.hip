@@ -205,12 +205,11 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         // attention RMSNorm fused into the QKV projection's input
         Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                        l.attn_norm, m->qkv, nullptr, sv));
-        Q4_TRY(qk_norm_rope(m->qkv, nqkv, m->qkv + nq, l.v_from_k ? nullptr : m->qkv + nq + nk, nqkv,
-                            l.q_norm, l.k_norm, d.n_q_heads, &m->kv[i], m->pos_dev, l.rope_theta,
-                            d.eps, l.v_from_k, l.k_cache, l.v_cache, sv));
-        Q4_TRY(gqa_decode_attn(m->qkv, nqkv, d.n_q_heads, l.k_cache, l.v_cache, &m->kv[i],
-                               m->pos_dev + 1, l.window, l.attn_scale, m->att, nq, m->attn_ws,
-                               m->attn_ws_bytes, sv));
+        // per-head QK-norm, RoPE and the KV append fused into the attention
+        Q4_TRY(gqa_decode_attn_rope(m->qkv, nqkv, d.n_q_heads, l.q_norm, l.k_norm, &m->kv[i],
+                                    m->pos_dev, l.rope_theta, d.eps, l.v_from_k, l.k_cache,
+                                    l.v_cache, l.window, l.attn_scale, m->att, nq, m->attn_ws,
+                                    m->attn_ws_bytes, sv));
         Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
                        m->x, m->x, sv));
         // FFN RMSNorm fused into gate|up; SwiGLU fused into gate|up's output

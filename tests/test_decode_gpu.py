@@ -57,7 +57,9 @@ def test_graph_equals_eager(dev, shape):
 
 
 def _check(got, ref, tol, what):
-    got = got.detach().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    if hasattr(got, "detach"):
+        got = got.detach().cpu().numpy()
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
     ratio = float((np.abs(got - ref) / tol).max())
     assert ratio <= 1.0, f"{what}: max err/tol {ratio:.3e}"
     return ratio
@@ -97,21 +99,24 @@ def test_decode_lockstep_per_op(dev, shape):
         r, t = oracle.q4_0_matvec(W["wqkv"], nqkv, D, oracle.rmsnorm(np_(x), W["attn_norm"], eps))
         _check(qkv, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + qkv matvec")
         raw = np_(qkv).copy()
-        q.qk_norm_rope(qkv, nqkv, qkv[:, nq:], None if ly.v_from_k else qkv[:, nq + nk:], nqkv,
-                       L["q_norm"], L["k_norm"], Hq, kv_layout_of(L["k_cache"]), pos_d[0:1],
-                       ly.rope_theta, eps, ly.v_from_k, L["k_cache"], L["v_cache"])
-        for b in range(B):
-            qh = oracle.rope_neox(oracle.rmsnorm(raw[b, :nq].reshape(Hq, hd), W["q_norm"], eps),
-                                  pos, ly.rope_theta)
-            _check(qkv[b, :nq], qh, 2e-4 * np.abs(qh) + 2e-5, f"L{l} q rope")
         kv = kv_layout_of(L["k_cache"])
         ws = torch.empty(q.gqa_decode_attn_workspace(kv, Hq, ly.window), dtype=torch.uint8, device=dev)
         att = torch.empty((B, nq), dtype=torch.float32, device=dev)
-        q.gqa_decode_attn(qkv, nqkv, Hq, L["k_cache"], L["v_cache"], kv, pos_d[1:2], ly.window,
-                          ly.attn_scale, att, nq, ws)
+        # the step fuses QK-norm, RoPE and the KV append into the attention call
+        q.gqa_decode_attn_rope(qkv, nqkv, Hq, L["q_norm"], L["k_norm"], kv, pos_d[0:1], ly.rope_theta,
+                               eps, ly.v_from_k, L["k_cache"], L["v_cache"], ly.window,
+                               ly.attn_scale, att, nq, ws)
         kc, vc = np_(L["k_cache"]), np_(L["v_cache"])
-        qn = np_(qkv)
+        slot = pos % ly.cap
         for b in range(B):
+            kr = raw[b, nq:nq + nk].reshape(hkv, hd)
+            kref = oracle.rope_neox(oracle.rmsnorm(kr, W["k_norm"], eps), pos, ly.rope_theta)
+            _check(kc[b, :, slot], kref, 2e-4 * np.abs(kref) + 2e-5, f"L{l} appended key")
+            vref = (oracle.rmsnorm(kr, None, eps) if ly.v_from_k
+                    else raw[b, nq + nk:].reshape(hkv, hd))
+            _check(vc[b, :, slot], vref, 2e-4 * np.abs(vref) + 1e-6, f"L{l} appended value")
+            qh = oracle.rope_neox(oracle.rmsnorm(raw[b, :nq].reshape(Hq, hd), W["q_norm"], eps),
+                                  pos, ly.rope_theta)
             n = pos + 1
             lo = max(0, n - ly.window) if ly.window else 0
             keys = np.zeros((n, hkv, hd))
@@ -119,8 +124,7 @@ def test_decode_lockstep_per_op(dev, shape):
             for p in range(lo, n):
                 keys[p] = kc[b, :, p % ly.cap]
                 vals[p] = vc[b, :, p % ly.cap]
-            o, bound = oracle.gqa_attention(qn[b, :nq].reshape(Hq, hd), keys, vals, ly.window,
-                                            ly.attn_scale)
+            o, bound = oracle.gqa_attention(qh, keys, vals, ly.window, ly.attn_scale)
             _check(att[b], o, 2e-4 * bound + 1e-6, f"L{l} attention")
         xo = np_(x)
         proj(4, L["wo"], att, nq, nq, q.IN_PLAIN, y=x, residual=x)

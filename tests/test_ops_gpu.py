@@ -199,3 +199,60 @@ def test_argmax_rows_ties_and_parity(dev):
     got = q.argmax_rows(torch.from_numpy(lg).to(dev)).cpu().numpy()
     exp = [oracle.argmax(lg[0])[0], 7, 0, 9]
     assert got.tolist() == exp
+
+
+ROPE_ATTN_CASES = [
+    # (B, Hq, Hkv, hd, cap, pos, window, v_from_k, theta); n = pos + 1
+    (1, 16, 8, 128, 4097, 4096, 0, False, 1e6),   # the 1.7B-shaped layer
+    (3, 16, 8, 128, 300, 256, 0, False, 1e6),     # ragged chunk tail
+    (2, 32, 8, 128, 64, 0, 0, False, 1e6),        # the new key is the only key
+    (1, 32, 16, 256, 1024, 3000, 1024, False, 1e4),  # sliding window, wrapped ring
+    (1, 32, 4, 512, 8208, 8192, 0, True, 1e6),    # 31B full layer: V from K
+    (2, 16, 1, 64, 100, 76, 16, True, 1e4),       # 16:1 groups, small window
+    (8, 32, 8, 128, 2064, 2048, 0, False, 1e6),   # 4B-shaped, B = 8
+]
+
+
+@pytest.mark.parametrize("B,hq,hkv,hd,cap,pos,window,v_from_k,theta", ROPE_ATTN_CASES)
+def test_gqa_decode_attn_rope_parity(dev, B, hq, hkv, hd, cap, pos, window, v_from_k, theta):
+    """Fused QK-norm + RoPE + KV append + attention against the oracle ops."""
+    _say(f"gqa_decode_attn_rope B={B} Hq={hq} Hkv={hkv} hd={hd} cap={cap} pos={pos} "
+         f"window={window} v_from_k={v_from_k}")
+    seed = 206
+    nq, nk = hq * hd, hkv * hd
+    ld = nq + nk + (0 if v_from_k else nk)
+    rows = synth.normal_f32(seed, f"ra.rows.{hd}.{pos}", (B, ld)) * 2.0
+    qn = synth.uniform_f32(seed, f"ra.qn.{hd}", (hd,), 0.8, 1.2)
+    kn = synth.uniform_f32(seed, f"ra.kn.{hd}", (hd,), 0.8, 1.2)
+    kc0 = synth.normal_f32(seed, f"ra.kc.{hd}.{cap}", (B, hkv, cap, hd))
+    vc0 = synth.normal_f32(seed, f"ra.vc.{hd}.{cap}", (B, hkv, cap, hd))
+    scale = 1.0 / math.sqrt(hd) if not v_from_k else 1.0
+    kc_d, vc_d = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    kv = kv_layout_of(kc_d)
+    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, nq), dtype=torch.float32, device=dev)
+    pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
+    q.gqa_decode_attn_rope(torch.from_numpy(rows).to(dev), ld, hq, torch.from_numpy(qn).to(dev),
+                           torch.from_numpy(kn).to(dev), kv, pos_d, theta, 1e-6, v_from_k, kc_d, vc_d,
+                           window, scale, out, nq, ws)
+    torch.cuda.synchronize()
+    kc, vc, got = _np(kc_d), _np(vc_d), _np(out)
+    slot = pos % cap
+    others = [s for s in range(cap) if s != slot]
+    assert np.array_equal(kc[:, :, others], kc0[:, :, others])
+    assert np.array_equal(vc[:, :, others], vc0[:, :, others])
+    worst = 0.0
+    for b in range(B):
+        kr = rows[b, nq:nq + nk].reshape(hkv, hd)
+        knorm = oracle.rmsnorm(kr, kn, 1e-6)
+        kref = oracle.rope_neox(knorm, pos, theta)
+        assert np.all(np.abs(kc[b, :, slot] - kref) <= _rope_tol(knorm, pos, theta))
+        vref = (oracle.rmsnorm(kr, None, 1e-6) if v_from_k
+                else rows[b, nq + nk:].reshape(hkv, hd).astype(np.float64))
+        assert np.all(np.abs(vc[b, :, slot] - vref) <= 2e-4 * np.abs(vref) + 1e-6)
+        qref = oracle.rope_neox(oracle.rmsnorm(rows[b, :nq].reshape(hq, hd), qn, 1e-6), pos, theta)
+        o, bound = _attn_oracle(qref, kc[b].astype(np.float64), vc[b].astype(np.float64), pos + 1,
+                                window, scale, cap)
+        err = np.abs(got[b].reshape(hq, hd) - o)
+        worst = max(worst, float((err / (2e-4 * bound + 1e-6)).max()))
+    assert worst <= 1.0, f"max err/tol {worst:.3e}"
