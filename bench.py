@@ -39,7 +39,10 @@ def time_dispatches(torch, launch, steps, warmup):
     """Mean time per dispatch (ms) over `steps` back-to-back launches after
     `warmup` untimed ones, HIP events on the stream the kernels are launched
     on.  (Host submission takes about half a dispatch, so the GPU stays busy;
-    replaying the launches as a graph adds per-node gaps on this runtime.)"""
+    replaying the launches as a graph adds per-node gaps on this runtime.)
+    The part's clocks take about 15 ms of sustained memory traffic to settle
+    (a 65 MB matvec runs ~15 % slower before that), hence the long default
+    warm-up."""
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -77,11 +80,21 @@ def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):
         warmup)
 
 
-def bench_attention_stack(q, torch, batch, reps=20, warmup=3):
+def settle(torch, fn, ms=40.0):
+    """Runs fn until `ms` of wall time has passed (untimed): the clocks take
+    about 15 ms of sustained memory traffic to reach their steady state."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        fn()
+        torch.cuda.synchronize()
+
+
+def bench_attention_stack(q, torch, batch, reps=20):
     """The 28-layer Qwen3-1.7B-shaped attention stack at n_cache = 4096: per
-    layer QK-norm + RoPE + KV append at position 4096, then split-K attention
-    over the 4097 keys.  Every layer has its own cache, so a pass streams
-    28 * B * 2 * 8 * 4097 * 128 * 4 bytes of K/V."""
+    layer one fused call (QK-norm + RoPE + KV append at position 4096, then
+    split-K attention over the 4097 keys) reading raw q | k | v rows.  Every
+    layer has its own cache, so a pass streams 28 * B * 2 * 8 * 4097 * 128 * 4
+    bytes of K/V."""
     import numpy as np
 
     from q4_quantized_matvec_amd._lib import kv_layout_of
@@ -94,9 +107,9 @@ def bench_attention_stack(q, torch, batch, reps=20, warmup=3):
     for l in range(w.n_layers):
         qh, kh, vh, qn, kn, kc, vc = wl.attn_layer_inputs(w, batch, l)
         kcd = torch.from_numpy(kc).to(dev)
-        layers.append(dict(q=torch.from_numpy(qh.reshape(batch, -1).copy()).to(dev),
-                           k=torch.from_numpy(kh.reshape(batch, -1).copy()).to(dev),
-                           v=torch.from_numpy(vh.reshape(batch, -1).copy()).to(dev),
+        qkv = np.concatenate([qh.reshape(batch, -1), kh.reshape(batch, -1), vh.reshape(batch, -1)],
+                             axis=1)
+        layers.append(dict(qkv=torch.from_numpy(np.ascontiguousarray(qkv)).to(dev),
                            qn=torch.from_numpy(qn).to(dev), kn=torch.from_numpy(kn).to(dev),
                            kc=kcd, vc=torch.from_numpy(vc).to(dev), kv=kv_layout_of(kcd)))
         del kc, vc
@@ -105,16 +118,15 @@ def bench_attention_stack(q, torch, batch, reps=20, warmup=3):
     out = torch.empty((batch, hq * hd), dtype=torch.float32, device=dev)
     scale = 1.0 / np.sqrt(hd)
 
+    ld = hq * hd + 2 * hkv * hd
+
     def one_pass():
         for L in layers:
-            q.qk_norm_rope(L["q"], hq * hd, L["k"], L["v"], hkv * hd, L["qn"], L["kn"], hq,
-                           L["kv"], pos_d[0:1], w.rope_theta, w.eps, False, L["kc"], L["vc"])
-            q.gqa_decode_attn(L["q"], hq * hd, hq, L["kc"], L["vc"], L["kv"], pos_d[1:2], 0,
-                              scale, out, hq * hd, ws)
+            q.gqa_decode_attn_rope(L["qkv"], ld, hq, L["qn"], L["kn"], L["kv"], pos_d[0:1],
+                                   w.rope_theta, w.eps, False, L["kc"], L["vc"], 0, scale, out,
+                                   hq * hd, ws)
 
-    for _ in range(warmup):
-        one_pass()
-    torch.cuda.synchronize()
+    settle(torch, one_pass)
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -288,7 +300,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-matvec", action="store_true")

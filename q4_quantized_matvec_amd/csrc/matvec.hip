@@ -190,9 +190,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     const uint32_t sel_e = odd ? 0x0C060C04u : 0x0C040C02u;
     const uint32_t sel_o = odd ? 0x0C070C05u : 0x0C050C03u;
 
-    // Without a residual the residual slot reads x[0] and is ignored.  The
-    // first PF rows are requested before the activations are staged, so the
-    // two memory latencies overlap.
+    // Without a residual the residual slot reads x[0] and is ignored.
     const bool has_res = res != nullptr;
     // Iterations past the group's range re-read its last row (already in this
     // CU's caches) instead of the next group's first rows.
@@ -203,8 +201,13 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         load_row<FMT, JX>(W + static_cast<size_t>(row) * row_bytes, col, has_res ? res + row : x, r);
     };
     RowRegs<FMT, JX> buf[NBUF];
+    // The activation loads go out before the first rows: loads return in
+    // order, so activations requested after the rows would wait for them.
+    // Without LDS staging the rows go first.
+    if constexpr (!kXLds) {
 #pragma unroll
-    for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
+        for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
+    }
 
     // Activations of the lane's block columns stay in registers.  With the
     // whole K in one wavefront the workgroup stages x through LDS once; the
@@ -230,6 +233,8 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
 #pragma unroll
             for (int r = 0; r < kXV; ++r) u[r] = sg[min(static_cast<int>(threadIdx.x) + r * kWG, nv - 1)];
         }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
 #pragma unroll
         for (int r = 0; r < kXV; ++r) {
             const int i = threadIdx.x + r * kWG;
