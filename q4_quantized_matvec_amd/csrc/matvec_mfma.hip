@@ -50,10 +50,10 @@ typedef uint32_t u32x4_al4_t __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4_al16_t __attribute__((ext_vector_type(4), aligned(16)));
 
 constexpr int kWG = 256;            // 4 wavefronts
-constexpr int kRowsWG = 64;         // 16 rows per wavefront
 constexpr int kSeg = 8;             // blocks per step (one MFMA each per wavefront)
-constexpr int kTargetWGs = 1024;    // about 4 workgroups per compute unit
 constexpr int kMaxB = 8;
+constexpr int kMinWGs = 512;        // below this, the shared-step kernel
+constexpr int kTargetWGs = 1024;    // shared-step kernel: split K toward this many workgroups
 constexpr int kMaxS = 32;           // K splits at most (the final writer holds them in registers)
 constexpr int kCounters = 4096;     // split tickets: row ranges of a K-split launch
 constexpr int kCounterStride = 32;  // one ticket per 128-byte line: atomics on one line serialise
@@ -142,16 +142,19 @@ __device__ __forceinline__ half8_t make_half8(uint32_t a, uint32_t b, uint32_t c
 }
 
 // Eight Q4_0 codes of one lane (payload bytes b0..b3) as exact halves:
-// low nibbles q - 8, high nibbles 16 (q - 8).
+// low nibbles q - 8, high nibbles 16 (q - 8).  One byte permute places two
+// code bytes under the exponent byte 0x64 (the halves 1024 + byte); a mask
+// keeps one nibble of each (1024 + q or 1024 + 16 q), and a packed subtract
+// removes the offset.
 __device__ __forceinline__ half8_t q4_codes(uint32_t w) {
-    const uint32_t p01 = __builtin_amdgcn_perm(w, w, 0x0C010C00u);
-    const uint32_t p23 = __builtin_amdgcn_perm(w, w, 0x0C030C02u);
+    const uint32_t p01 = __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u);
     const half2_t lo_off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
     const half2_t hi_off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
-    const half2_t h0 = __builtin_bit_cast(half2_t, (p01 & 0x000F000Fu) | 0x64006400u) + lo_off;
-    const half2_t h1 = __builtin_bit_cast(half2_t, (p23 & 0x000F000Fu) | 0x64006400u) + lo_off;
-    const half2_t h2 = __builtin_bit_cast(half2_t, (p01 & 0x00F000F0u) | 0x64006400u) + hi_off;
-    const half2_t h3 = __builtin_bit_cast(half2_t, (p23 & 0x00F000F0u) | 0x64006400u) + hi_off;
+    const half2_t h0 = __builtin_bit_cast(half2_t, p01 & 0xFF0FFF0Fu) + lo_off;
+    const half2_t h1 = __builtin_bit_cast(half2_t, p23 & 0xFF0FFF0Fu) + lo_off;
+    const half2_t h2 = __builtin_bit_cast(half2_t, p01 & 0xFFF0FFF0u) + hi_off;
+    const half2_t h3 = __builtin_bit_cast(half2_t, p23 & 0xFFF0FFF0u) + hi_off;
     return make_half8(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
                       __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3));
 }
@@ -216,8 +219,157 @@ __device__ __forceinline__ void weight_operands(const uint32_t (&dw)[BF<FMT>::kL
     }
 }
 
+// Output of a workgroup whose wavefront w < T holds, per lane (col, g), the
+// sums ya (batch row 2g) and yb (2g + 1) of output row n of its tile, and
+// whose ssq_w holds the four wavefronts' sums of squares per batch row (RMSNorm).
+// Without a K split the workgroup writes y (residual, 1/rms or SiLU(g)*u
+// applied); with one, it stores its partials, takes a ticket, and the last
+// split of the row range adds the S partials in split order.
+struct FinishArgs {
+    int N, K, B, S, glu;
+    float eps;
+    float *y;
+    const float *res;
+    int *counters;
+    float *ssq_part;
+    float *part;
+};
+
+template <int KIND, int T>
+__device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb, int n, bool rvalid, int pl,
+                                       int pu, float (&ssq_w)[4][kMaxB]) {
+    constexpr int kRows = 16 * T, kPairs = 8 * T;
+    constexpr int kHalf = T > 1 ? T / 2 : 1;
+    __shared__ float upx[kPairs][kMaxB];  // SwiGLU output: up-row sums of the pairs
+    __shared__ int ticket;
+    const int N = fa_.N, K = fa_.K, B = fa_.B, S = fa_.S, glu = fa_.glu;
+    const float eps = fa_.eps;
+    float *y = fa_.y;
+    const float *res = fa_.res;
+    int *counters = fa_.counters;
+    float *ssq_part = fa_.ssq_part, *part = fa_.part;
+    const int P = N >> 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    auto range_ssq = [&](int b) { return ((ssq_w[0][b] + ssq_w[1][b]) + ssq_w[2][b]) + ssq_w[3][b]; };
+    const int ba = 2 * g, bb = 2 * g + 1;
+    const int64_t ln = N;
+    if (S == 1) {
+        float ia = 1.f, ib = 1.f;
+        if constexpr (KIND == 1) {
+            ia = 1.0f / sqrtf(range_ssq(ba) / static_cast<float>(K) + eps);
+            ib = 1.0f / sqrtf(range_ssq(bb) / static_cast<float>(K) + eps);
+        }
+        if (glu) {
+            if (wv >= kHalf && wv < T) {
+                upx[pl][ba] = ya * ia;
+                upx[pl][bb] = yb * ib;
+            }
+            __syncthreads();
+            if (wv < kHalf && rvalid) {
+                const int64_t lp = P;
+                if (ba < B) y[ba * lp + pu] = silu_mul(ya * ia, upx[pl][ba]);
+                if (bb < B) y[bb * lp + pu] = silu_mul(yb * ib, upx[pl][bb]);
+            }
+            return;
+        }
+        if (rvalid) {
+            if (ba < B) y[ba * ln + n] = res ? ya * ia + res[ba * ln + n] : ya * ia;
+            if (bb < B) y[bb * ln + n] = res ? yb * ib + res[bb * ln + n] : yb * ib;
+        }
+        return;
+    }
+    // Split K: partial sums go to the workspace with device-scope stores
+    // (written through the compute die's L2), the workgroup takes a ticket,
+    // and the last one adds the S partials in split order with device-scope
+    // loads.  Device-scope fences are avoided on purpose: on this part they
+    // write back and invalidate the whole L2 of the die.
+    if (rvalid) {
+        float *pp = part + static_cast<int64_t>(blockIdx.y) * B * ln;
+        if (ba < B) __hip_atomic_store(pp + ba * ln + n, ya, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bb < B) __hip_atomic_store(pp + bb * ln + n, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (KIND == 1) {
+        if (threadIdx.x < B)
+            __hip_atomic_store(ssq_part + (static_cast<int64_t>(blockIdx.x) * S + blockIdx.y) * kMaxB +
+                                   threadIdx.x,
+                               range_ssq(threadIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // every store of this wavefront has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(&counters[blockIdx.x * kCounterStride], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != S - 1) return;
+    // Final writer: every partial it needs is requested before any is added
+    // (device-scope loads miss the die's L2, so each round trip is long), and
+    // the S partials of a row are added in split order.
+    const int64_t step = static_cast<int64_t>(B) * ln;
+    __shared__ float inv_s[kMaxB];
+    if constexpr (KIND == 1) {
+        if (threadIdx.x < B) {
+            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + threadIdx.x;
+            float t[kMaxS];
+#pragma unroll
+            for (int q = 0; q < kMaxS; ++q)
+                t[q] = __hip_atomic_load(sq + (q < S ? q : 0) * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float tot = 0.f;
+#pragma unroll
+            for (int q = 0; q < kMaxS; ++q)
+                if (q < S) tot += t[q];
+            inv_s[threadIdx.x] = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+        }
+    }
+    // up to two rows per thread: outputs tid and tid + 256, or the gate and up
+    // rows of SwiGLU output tid
+    const int outs = glu ? kPairs : kRows;
+    int row[2], ob[2];
+    bool act[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int o = glu ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) + r * kWG;
+        ob[r] = o / outs;
+        const int nn = blockIdx.x * outs + (o % outs);
+        act[r] = o < outs * B && nn < (glu ? P : N);
+        row[r] = glu ? (r == 0 ? nn : P + nn) : nn;
+    }
+    float pv[2][kMaxS];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const float *pb = part + static_cast<int64_t>(act[r] ? ob[r] : 0) * ln + (act[r] ? row[r] : 0);
+#pragma unroll
+        for (int q = 0; q < kMaxS; ++q)
+            pv[r][q] = __hip_atomic_load(pb + (q < S ? q : 0) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float sum[2] = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < kMaxS; ++q)
+            if (q < S) sum[r] += pv[r][q];
+    if constexpr (KIND == 1) __syncthreads();
+    if (glu) {
+        if (act[0]) {
+            const float inv = KIND == 1 ? inv_s[ob[0]] : 1.f;
+            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = silu_mul(sum[0] * inv, sum[1] * inv);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (!act[r]) continue;
+            const float v = sum[r] * (KIND == 1 ? inv_s[ob[r]] : 1.f);
+            y[ob[r] * ln + row[r]] = res ? v + res[ob[r] * ln + row[r]] : v;
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&counters[blockIdx.x * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int FMT, int KIND>
-__global__ __launch_bounds__(kWG) void mv_mfma_kernel(
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void mv_mfma_step_kernel(
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
@@ -227,8 +379,6 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
     __shared__ f32x4_t stepmax[2][kMaxB];    // per batch row: the 4 wavefronts' maxima
     __shared__ float ssq_w[4][kMaxB];
-    __shared__ float upx[32][kMaxB];          // SwiGLU output: up-row sums of the 32 pairs
-    __shared__ int ticket;
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -237,7 +387,7 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
     // output 32 gate rows (wavefronts 0, 1) and their 32 up rows (2, 3).
     const int P = N >> 1;
     const int pu = blockIdx.x * 32 + 16 * (wv & 1) + col;  // pair (SwiGLU output)
-    const int n = glu ? (wv < 2 ? pu : P + pu) : blockIdx.x * kRowsWG + wv * 16 + col;
+    const int n = glu ? (wv < 2 ? pu : P + pu) : blockIdx.x * 64 + wv * 16 + col;
     const bool rvalid = glu ? pu < P : n < N;
     const int nl = rvalid ? n : N - 1;
     const int nb = K / 32, kc = nb / kSeg;
@@ -366,142 +516,270 @@ __global__ __launch_bounds__(kWG) void mv_mfma_kernel(
         if (g == 0 && xp == 0) ssq_w[wv][xb] = t;
         __syncthreads();
     }
-    auto range_ssq = [&](int b) { return ((ssq_w[0][b] + ssq_w[1][b]) + ssq_w[2][b]) + ssq_w[3][b]; };
-    const int ba = 2 * g, bb = 2 * g + 1;
+    const int pl = 16 * (wv & 1) + col;
     const float ya = acc[0] + acc[1];
     const float yb = acc[2] + acc[3];
-    const int64_t ln = N;
-    if (S == 1) {
-        float ia = 1.f, ib = 1.f;
-        if constexpr (KIND == 1) {
-            ia = 1.0f / sqrtf(range_ssq(ba) / static_cast<float>(K) + eps);
-            ib = 1.0f / sqrtf(range_ssq(bb) / static_cast<float>(K) + eps);
-        }
+    const FinishArgs fa_{N, K, B, S, glu, eps, y, res, counters, ssq_part, part};
+    finish<KIND, 4>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
+}
+
+template <int FMT, int KIND, int T>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void mv_mfma_tile_kernel(
+    const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
+    const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
+    const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
+    float *__restrict__ part, int S, int spw, int glu) {
+    constexpr int kBytes = BF<FMT>::kBytes;
+    constexpr int kDw = BF<FMT>::kLaneDw;
+    __shared__ u32x4_t opnd[4][kSeg][64];               // per wavefront: its step's activation operands
+    __shared__ f32x4_t red[4][T][64];                   // per-wavefront partial tiles
+    __shared__ float ssq_w[4][kMaxB];
+    constexpr int kRows = 16 * T, kPairs = 8 * T;       // output rows (pairs) of a workgroup
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int P = N >> 1;
+    // Row tile t of the workgroup: 16 consecutive rows, or with a SwiGLU
+    // output the gate rows of 16 pairs (t < T/2) and their up rows.
+    constexpr int kHalf = T > 1 ? T / 2 : 1;                       // gate tiles (SwiGLU output)
+    auto tile_pair = [&](int t) { return 16 * (t % kHalf) + col; };  // pair within the workgroup
+    auto tile_row = [&](int t, bool &valid) {
         if (glu) {
-            const int pl = 16 * (wv & 1) + col;
-            if (wv >= 2) {
-                upx[pl][ba] = ya * ia;
-                upx[pl][bb] = yb * ib;
+            const int pr = blockIdx.x * kPairs + tile_pair(t);
+            valid = pr < P;
+            return t < kHalf ? pr : P + pr;
+        }
+        const int r = blockIdx.x * kRows + 16 * t + col;
+        valid = r < N;
+        return r;
+    };
+    const int nb = K / 32, kc = nb / kSeg;
+    const int64_t seg = kSeg * kBytes;
+    const uint8_t *wrow[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        bool v;
+        const int r = tile_row(t, v);
+        wrow[t] = W + static_cast<int64_t>(v ? r : N - 1) * nb * kBytes + g * 2 * kBytes;
+    }
+    // Staging role of this lane: 4 consecutive activations (k = 4 lane ..) of
+    // its wavefront's step, for every batch row.  They land in block
+    // jl = lane / 8 at operand lane group gl, halves el .. el + 3.
+    const int jl = lane >> 3, q8 = lane & 7;
+    const int gl = FMT == 0 ? (q8 & 3) : (q8 >> 1);
+    const int el = FMT == 0 ? (q8 >= 4 ? 4 : 0) : 4 * (q8 & 1);
+    const float hscale = (FMT == 0 && q8 >= 4) ? 0.0625f : 1.0f;  // high nibbles: codes x16, x / 16
+
+    f32x4_t acc[T];
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = zero;
+    float ssq[kMaxB];
+#pragma unroll
+    for (int b = 0; b < kMaxB; ++b) ssq[b] = 0.f;
+
+    const int c_base = blockIdx.y * 4 * spw;
+    for (int r = 0; r < spw; ++r) {
+        const int c = c_base + 4 * r + wv;  // this wavefront's step
+        if (c >= kc) break;                 // wave-uniform; steps only grow with r
+        // ---- activations first (loads return in order), then the weights
+        const int64_t kx = static_cast<int64_t>(c) * (32 * kSeg) + 4 * lane;
+        // (every load is unconditional, rows past B re-read the last one and
+        // are zeroed afterwards, so the compiler can wait for these loads
+        // alone and not for the weights behind them)
+        f32x4_t xv[kMaxB], tv[kMaxB];
+        f32x4_t gv = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (KIND == 1) {
+            const f32x4_t gl4 = *reinterpret_cast<const f32x4_al16_t *>((nw ? nw : x) + kx);
+            if (nw) gv = gl4;
+        }
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            const int64_t bo = static_cast<int64_t>(min(b, B - 1)) * ld + kx;
+            xv[b] = *reinterpret_cast<const f32x4_al16_t *>(x + bo);
+            if constexpr (KIND == 2) tv[b] = *reinterpret_cast<const f32x4_al16_t *>(u + bo);
+        }
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b)
+            if (b >= B) {
+                xv[b] = zero;
+                if constexpr (KIND == 2) tv[b] = zero;
             }
-            __syncthreads();
-            if (wv < 2 && rvalid) {
-                const int64_t lp = P;
-                if (ba < B) y[ba * lp + pu] = silu_mul(ya * ia, upx[pl][ba]);
-                if (bb < B) y[bb * lp + pu] = silu_mul(yb * ib, upx[pl][bb]);
+        uint32_t dw[T][kDw];
+#pragma unroll
+        for (int t = 0; t < T; ++t) load_seg<kDw>(wrow[t] + c * seg, dw[t]);
+
+        // ---- transform, per-batch-row step maximum, exact halves into LDS
+        float mx[kMaxB];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            f32x4_t t = xv[b];
+            if constexpr (KIND == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ssq[b] = fmaf(xv[b][e], xv[b][e], ssq[b]);
+                    t[e] = xv[b][e] * gv[e];
+                }
+            } else if constexpr (KIND == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = silu_mul(xv[b][e], tv[b][e]);
             }
-            return;
+            xv[b] = t;
+            mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
         }
-        if (n < N) {
-            if (ba < B) y[ba * ln + n] = res ? ya * ia + res[ba * ln + n] : ya * ia;
-            if (bb < B) y[bb * ln + n] = res ? yb * ib + res[bb * ln + n] : yb * ib;
+        int sh[kMaxB];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) sh[b] = step_shift(wave_max(mx[b]));
+                uint8_t *obase = reinterpret_cast<uint8_t *>(&opnd[wv][jl][16 * gl]) + 2 * el;
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            const float sc = ldexpf(hscale, sh[b]);
+            half2_t h01, h23, l01, l23;
+            float v0 = xv[b][0] * sc, v1 = xv[b][1] * sc, v2 = xv[b][2] * sc, v3 = xv[b][3] * sc;
+            h01.x = static_cast<_Float16>(v0);
+            h01.y = static_cast<_Float16>(v1);
+            h23.x = static_cast<_Float16>(v2);
+            h23.y = static_cast<_Float16>(v3);
+            l01.x = static_cast<_Float16>(v0 - static_cast<float>(h01.x));
+            l01.y = static_cast<_Float16>(v1 - static_cast<float>(h01.y));
+            l23.x = static_cast<_Float16>(v2 - static_cast<float>(h23.x));
+            l23.y = static_cast<_Float16>(v3 - static_cast<float>(h23.y));
+            uint2 hv, lv;
+            hv.x = __builtin_bit_cast(uint32_t, h01);
+            hv.y = __builtin_bit_cast(uint32_t, h23);
+            lv.x = __builtin_bit_cast(uint32_t, l01);
+            lv.y = __builtin_bit_cast(uint32_t, l23);
+            *reinterpret_cast<uint2 *>(obase + 16 * (2 * b)) = hv;      // MFMA row 2b: hi
+            *reinterpret_cast<uint2 *>(obase + 16 * (2 * b + 1)) = lv;  // MFMA row 2b + 1: lo
         }
-        return;
+        // the wavefront reads back what its own lanes wrote (LDS operations
+        // of one wavefront complete in order)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        half8_t af[kSeg];
+#pragma unroll
+        for (int jj = 0; jj < kSeg; ++jj) af[jj] = __builtin_bit_cast(half8_t, opnd[wv][jj][lane]);
+        // 1/s of the two batch rows whose sums this lane accumulates
+        int sa = sh[0], sb = sh[1];
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (g == q) {
+                sa = sh[2 * q];
+                sb = sh[2 * q + 1];
+            }
+        const float fa = ldexpf(1.0f, -sa);
+        const float fb = ldexpf(1.0f, -sb);
+
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            // block scales of this lane's two blocks, then every lane group's
+            const uint32_t dp = __builtin_amdgcn_perm(dw[t][(kDw - 1) / 2], dw[t][0], 0x07060100u);
+            uint32_t dps[4];
+            {
+                auto rr = __builtin_amdgcn_permlane32_swap(dp, dp, false, false);
+                auto s01 = __builtin_amdgcn_permlane16_swap(rr[0], rr[0], false, false);
+                auto s23 = __builtin_amdgcn_permlane16_swap(rr[1], rr[1], false, false);
+                dps[0] = s01[0];
+                dps[1] = opaque_copy(s01[1]);
+                dps[2] = s23[0];
+                dps[3] = opaque_copy(s23[1]);
+            }
+            half8_t wf[kSeg];
+            weight_operands<FMT>(dw[t], wf);
+            f32x4_t st = zero;
+#pragma unroll
+            for (int jj = 0; jj < kSeg; ++jj) {
+                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[jj], wf[jj], zero, 0, 0, 0);
+                const uint32_t scw = dps[jj >> 1];
+                if (jj & 1) {
+                    st[0] = fma_hi(scw, d[0], st[0]);
+                    st[1] = fma_hi(scw, d[1], st[1]);
+                    st[2] = fma_hi(scw, d[2], st[2]);
+                    st[3] = fma_hi(scw, d[3], st[3]);
+                } else {
+                    st[0] = fma_lo(scw, d[0], st[0]);
+                    st[1] = fma_lo(scw, d[1], st[1]);
+                    st[2] = fma_lo(scw, d[2], st[2]);
+                    st[3] = fma_lo(scw, d[3], st[3]);
+                }
+            }
+            // result rows 4g..4g+3 are (batch 2g: hi, lo), (batch 2g+1: hi, lo)
+            acc[t][0] = fmaf(fa, st[0], acc[t][0]);
+            acc[t][1] = fmaf(fa, st[1], acc[t][1]);
+            acc[t][2] = fmaf(fb, st[2], acc[t][2]);
+            acc[t][3] = fmaf(fb, st[3], acc[t][3]);
+        }
+        __builtin_amdgcn_wave_barrier();  // operand reads done before the next round's writes
     }
-    // Split K: partial sums go to the workspace with device-scope stores
-    // (written through the compute die's L2), the workgroup takes a ticket,
-    // and the last one adds the S partials in split order with device-scope
-    // loads.  Device-scope fences are avoided on purpose: on this part they
-    // write back and invalidate the whole L2 of the die.
-    if (rvalid) {
-        float *pp = part + static_cast<int64_t>(blockIdx.y) * B * ln;
-        if (ba < B) __hip_atomic_store(pp + ba * ln + n, ya, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (bb < B) __hip_atomic_store(pp + bb * ln + n, yb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+
+    // ---- the four wavefronts' partial tiles meet in LDS; wavefront w < T
+    // adds tile w's partials in wavefront order
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[wv][t][lane] = acc[t];
     if constexpr (KIND == 1) {
-        if (threadIdx.x < B)
-            __hip_atomic_store(ssq_part + (static_cast<int64_t>(blockIdx.x) * S + blockIdx.y) * kMaxB +
-                                   threadIdx.x,
-                               range_ssq(threadIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // sums of squares of this workgroup's K range per batch row
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            const float t = wave_sum(ssq[b]);
+            if (lane == 0) ssq_w[wv][b] = t;
+        }
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // every store of this wavefront has completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    if (threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(&counters[blockIdx.x * kCounterStride], 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (ticket != S - 1) return;
-    // Final writer: every partial it needs is requested before any is added
-    // (device-scope loads miss the die's L2, so each round trip is long), and
-    // the S partials of a row are added in split order.
-    const int64_t step = static_cast<int64_t>(B) * ln;
-    __shared__ float inv_s[kMaxB];
-    if constexpr (KIND == 1) {
-        if (threadIdx.x < B) {
-            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + threadIdx.x;
-            float t[kMaxS];
+    const int tw = wv < T ? wv : T - 1;  // this wavefront's tile (wavefronts >= T have none)
+    f32x4_t tot = red[0][tw][lane];
 #pragma unroll
-            for (int q = 0; q < kMaxS; ++q)
-                t[q] = __hip_atomic_load(sq + (q < S ? q : 0) * kMaxB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float tot = 0.f;
-#pragma unroll
-            for (int q = 0; q < kMaxS; ++q)
-                if (q < S) tot += t[q];
-            inv_s[threadIdx.x] = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
-        }
+    for (int w = 1; w < 4; ++w) {
+        const f32x4_t p4 = red[w][tw][lane];
+        tot[0] += p4[0];
+        tot[1] += p4[1];
+        tot[2] += p4[2];
+        tot[3] += p4[3];
     }
-    // up to two rows per thread: outputs tid and tid + 256, or the gate and up
-    // rows of SwiGLU output tid
-    const int outs = glu ? 32 : kRowsWG;
-    int row[2], ob[2];
-    bool act[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int o = glu ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) + r * kWG;
-        ob[r] = o / outs;
-        const int nn = blockIdx.x * outs + (o % outs);
-        act[r] = o < outs * B && nn < (glu ? P : N);
-        row[r] = glu ? (r == 0 ? nn : P + nn) : nn;
-    }
-    float pv[2][kMaxS];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const float *pb = part + static_cast<int64_t>(act[r] ? ob[r] : 0) * ln + (act[r] ? row[r] : 0);
-#pragma unroll
-        for (int q = 0; q < kMaxS; ++q)
-            pv[r][q] = __hip_atomic_load(pb + (q < S ? q : 0) * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    float sum[2] = {0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int q = 0; q < kMaxS; ++q)
-            if (q < S) sum[r] += pv[r][q];
-    if constexpr (KIND == 1) __syncthreads();
-    if (glu) {
-        if (act[0]) {
-            const float inv = KIND == 1 ? inv_s[ob[0]] : 1.f;
-            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = silu_mul(sum[0] * inv, sum[1] * inv);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (!act[r]) continue;
-            const float v = sum[r] * (KIND == 1 ? inv_s[ob[r]] : 1.f);
-            y[ob[r] * ln + row[r]] = res ? v + res[ob[r] * ln + row[r]] : v;
-        }
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&counters[blockIdx.x * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool rvalid;
+    const int n = tile_row(tw, rvalid);
+    rvalid = rvalid && wv < T;
+    const int pl = tile_pair(tw);                     // pair within the workgroup (SwiGLU output)
+    const int pu = blockIdx.x * kPairs + pl;
+    const float ya = tot[0] + tot[1];
+    const float yb = tot[2] + tot[3];
+    const FinishArgs fa_{N, K, B, S, glu, eps, y, res, counters, ssq_part, part};
+    finish<KIND, T>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
 // ---------------------------------------------------------------- host side
 struct Plan {
-    int rg, kc, S, cps;
+    bool tiles;  // the tile kernel, else the shared-step kernel
+    int T, rg, kc, S, spw;
     size_t off_ssq, off_part, bytes;
 };
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-Plan make_plan(int64_t N, int64_t K, int64_t B) {
+// The tile kernel (each wavefront converts its own step's activations and
+// feeds four row tiles, two for Q8_0) when it yields kMinWGs workgroups;
+// otherwise the shared-step kernel (64 rows per workgroup, the four
+// wavefronts share one step's operands), whose finer K split fills the chip
+// on small matrices.  K is split over at most kMaxS workgroups, and not at
+// all when the row ranges outnumber the tickets.
+Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt) {
     Plan p;
-    p.rg = static_cast<int>((N + kRowsWG - 1) / kRowsWG);
     p.kc = static_cast<int>(K / (32 * kSeg));
-    int want = std::max(1, std::min(std::min(p.kc, kMaxS), (kTargetWGs + p.rg - 1) / p.rg));
-    if (p.rg > kCounters) want = 1;
-    p.cps = (p.kc + want - 1) / want;
-    p.S = (p.kc + p.cps - 1) / p.cps;
+    p.tiles = true;
+    p.T = fmt == 1 ? 2 : 4;
+    p.rg = static_cast<int>((N + 16 * p.T - 1) / (16 * p.T));
+    const int rounds = (p.kc + 3) / 4;
+    p.spw = p.rg > kCounters ? rounds : (rounds + kMaxS - 1) / kMaxS;
+    p.S = (rounds + p.spw - 1) / p.spw;
+    if (static_cast<int64_t>(p.rg) * p.S < kMinWGs) {
+        p.tiles = false;
+        p.T = 4;
+        p.rg = static_cast<int>((N + 63) / 64);
+        int want = std::max(1, std::min(std::min(p.kc, kMaxS), (kTargetWGs + p.rg - 1) / p.rg));
+        if (p.rg > kCounters) want = 1;
+        p.spw = (p.kc + want - 1) / want;
+        p.S = (p.kc + p.spw - 1) / p.spw;
+    }
     p.off_ssq = kCounterBytes;
     const size_t ssq = p.S > 1 ? align256(static_cast<size_t>(p.rg) * p.S * kMaxB * sizeof(float)) : 0;
     p.off_part = p.off_ssq + ssq;
@@ -514,10 +792,18 @@ void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *
             int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu,
             hipStream_t s) {
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    hipLaunchKernelGGL((mv_mfma_kernel<FMT, KIND>), dim3(p.rg, p.S), dim3(kWG), 0, s, W, N, K, B, x,
-                       u, nw, ld, eps, y, res, reinterpret_cast<int *>(w8),
-                       reinterpret_cast<float *>(w8 + p.off_ssq),
-                       reinterpret_cast<float *>(w8 + p.off_part), p.S, p.cps, glu);
+    int *ctr = reinterpret_cast<int *>(w8);
+    float *ssq = reinterpret_cast<float *>(w8 + p.off_ssq);
+    float *part = reinterpret_cast<float *>(w8 + p.off_part);
+    const dim3 grid(p.rg, p.S);
+    if (!p.tiles) {
+        hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
+                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu);
+        return;
+    }
+    constexpr int T = FMT == 1 ? 2 : 4;
+    hipLaunchKernelGGL((mv_mfma_tile_kernel<FMT, KIND, T>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
+                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -559,7 +845,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     const size_t ybytes = static_cast<size_t>(B * (out_op == Q4_OUT_SWIGLU ? N / 2 : N)) * sizeof(float);
     Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
              Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
-    const Plan p = make_plan(N, K, B);
+    const Plan p = make_plan(N, K, B, FMT);
     Q4_CHECK(ws && q4::aligned(ws, 256), Q4_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
              name);
     Q4_CHECK(ws_bytes >= p.bytes, Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", name,
@@ -578,7 +864,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
 
 extern "C" size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B) {
     if (N < 1 || K < 256 || K % 256 != 0 || B < 1 || B > kMaxB) return 0;
-    return make_plan(N, K, B).bytes;
+    return std::max(make_plan(N, K, B, 0).bytes, make_plan(N, K, B, 1).bytes);
 }
 
 extern "C" q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,

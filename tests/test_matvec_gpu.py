@@ -169,6 +169,11 @@ BATCHED_CASES = [
     ("q4", 300, 9728, 8, "swiglu"), ("q4", 2560, 4096, 8, "plain"), ("q4", 777, 5376, 3, "plain"),
     ("q4", 33, 512, 5, "rms_unit"), ("q4", 6144, 2560, 8, "rms"), ("q4", 130, 21504, 7, "swiglu"),
     ("q8", 500, 2560, 8, "rms"), ("q8", 100, 256, 4, "plain"), ("q8", 3001, 2560, 6, "plain"),
+    # shapes large enough for the tile kernel (each wavefront converts its own
+    # step for several row tiles): every transform, Q8_0, ragged rows, B < 8,
+    # with and without a K split, and two rounds per wavefront (K > 32768)
+    ("q4", 8200, 4096, 8, "rms"), ("q4", 8192, 4096, 3, "swiglu"), ("q4", 33000, 1024, 5, "plain"),
+    ("q4", 2000, 33024, 2, "rms"), ("q8", 8200, 2048, 8, "rms"), ("q8", 16400, 1024, 2, "plain"),
 ]
 
 
@@ -301,6 +306,7 @@ GLU_CASES = [
     ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 300, 2560, 8, "rms"),
     ("batched", 2 * 77, 9728, 5, "plain"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 33, 256, 1, "swiglu"),
+    ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 16500, 1024, 4, "plain"),
 ]
 
 
