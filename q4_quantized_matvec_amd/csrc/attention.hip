@@ -22,9 +22,23 @@ using namespace q4dev;
 constexpr int kWG = 256;
 constexpr int kChunk = 64;  // positions per chunk (one per lane in the softmax pass)
 
+// Up to kSplitFrom chunks over all (sequence, kv head) pairs, every chunk is
+// a workgroup of its own: that keeps the most loads in flight.  Beyond it,
+// consecutive chunks are grouped into splits (one workgroup and one partial
+// each) so that about kSplitTarget workgroups remain: fewer partials for the
+// merge and fewer per-workgroup query loads, with enough waves left to keep
+// HBM busy.
+#ifndef Q4_ATTN_SPLIT_TARGET
+#define Q4_ATTN_SPLIT_TARGET 1024
+#endif
+constexpr int kSplitTarget = Q4_ATTN_SPLIT_TARGET;
+constexpr int kSplitFrom = 4 * kSplitTarget;
+
 struct AttnGeom {
     int G;    // query heads per kv head
     int nch;  // chunks per (sequence, kv head)
+    int cps;  // chunks per split
+    int ns;   // splits per (sequence, kv head)
 };
 
 // Chunking depends only on the layout and window (never on n), so the
@@ -34,6 +48,9 @@ AttnGeom attn_geom(const q4_kv_layout &kv, int64_t n_q_heads, int64_t window) {
     g.G = static_cast<int>(n_q_heads / kv.n_kv_heads);
     const int64_t maxvis = window > 0 ? std::min<int64_t>(window, kv.cap) : kv.cap;
     g.nch = static_cast<int>((maxvis + kChunk - 1) / kChunk);
+    const int64_t total = static_cast<int64_t>(g.nch) * kv.n_kv_heads * kv.batch;
+    g.cps = total < kSplitFrom ? 1 : static_cast<int>(total / kSplitTarget);
+    g.ns = (g.nch + g.cps - 1) / g.cps;
     return g;
 }
 
@@ -69,8 +86,12 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// One workgroup per (chunk, kv head, sequence).  Loads are issued in batches
-// ahead of their use so the wavefronts keep many rows in flight.
+// One workgroup per (split, kv head, sequence).  A split is cps consecutive
+// 64-position chunks, taken in order with a running softmax: per chunk the
+// new maximum rescales the running denominator and weighted value sums by
+// exp(m_old - m_new) (exact softmax over the split, one partial per split).
+// Loads are issued in batches ahead of their use so the wavefronts keep many
+// rows in flight.
 // Fused query/key preparation (gqa_decode_attn_rope): q and the new key are
 // read raw from the merged projection row, RMS-normalised per head with their
 // gains and rotated (NeoX pairs i, i + hd/2); the new key and value rows are
@@ -100,11 +121,11 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double r, int i, float &cs,
     sincosf(static_cast<float>(red), &sn, &cs);
 }
 
-template <int HD, int GM, bool ROPE>
+template <int HD, int GM, bool ROPE, bool MULTI>
 __global__ __launch_bounds__(kWG) void attn_split_kernel(
     const float *__restrict__ q, int64_t ldq, int G, const float *kc, const float *vc, int64_t cap,
     int64_t sb, int64_t sh, int64_t st, const int64_t *__restrict__ n_dev, int64_t window,
-    float scale, int nch, float *__restrict__ part, RopeArgs ra) {
+    float scale, int ns, int cps, float *__restrict__ part, RopeArgs ra) {
     constexpr int LPK = HD / 8;              // score pass: lanes per key, 8 elements per lane
     constexpr int KPW = 64 / LPK;            // keys per wavefront per step
     constexpr int SIT = kChunk / (4 * KPW);  // score steps per wavefront
@@ -113,21 +134,22 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     constexpr int VIT = kChunk / KG;         // value pass: keys per thread
     __shared__ __align__(16) float sc[kChunk * GM];  // scores, then weights: [pos][g]
     __shared__ __align__(16) float4 red[KG > 1 ? (KG - 1) * GM * TPK : 1];
+    __shared__ float alpha_s[GM];  // rescale of the running sums at this chunk
 
-    const int c = blockIdx.x, g0 = blockIdx.y, b = blockIdx.z;
+    const int sp = blockIdx.x, g0 = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // fused preparation: n_dev holds the new token's position, n = pos + 1
     const int64_t n = ROPE ? *n_dev + 1 : *n_dev;
     int64_t lo = window > 0 ? n - window : 0;
     lo = max(lo, n - cap);
     lo = max(lo, int64_t(0));
-    const int64_t p0 = lo + static_cast<int64_t>(c) * kChunk;
-    const int cnt = static_cast<int>(max(int64_t(0), min(int64_t(kChunk), n - p0)));
+    const int64_t s0 = lo + static_cast<int64_t>(sp) * cps * kChunk;  // first position of the split
+    const int64_t span = min(static_cast<int64_t>(cps) * kChunk, n - s0);
 
-    const size_t unit = ((static_cast<size_t>(b) * gridDim.y + g0) * nch + c) * GM;
+    const size_t unit = ((static_cast<size_t>(b) * gridDim.y + g0) * ns + sp) * GM;
     float *po = part + unit * HD;  // [GM][HD]
-    float *pml = part + static_cast<size_t>(gridDim.z) * gridDim.y * nch * GM * HD + unit * 2;
-    if (cnt == 0) {
+    float *pml = part + static_cast<size_t>(gridDim.z) * gridDim.y * ns * GM * HD + unit * 2;
+    if (span <= 0) {
         if (threadIdx.x < G) {
             pml[2 * threadIdx.x] = -INFINITY;
             pml[2 * threadIdx.x + 1] = 0.f;
@@ -136,10 +158,11 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     }
     const float *kb = kc + b * sb + g0 * sh;
     const float *vb = vc + b * sb + g0 * sh;
-    // slot of chunk position j (positions past the chunk end re-read its first
-    // row): one 64-bit remainder per workgroup, then 32-bit wrap-around
+    // slot of position j of the current chunk (positions past the chunk end
+    // re-read its first row): one 64-bit remainder per chunk, then 32-bit
+    // wrap-around
     const int cap32 = static_cast<int>(cap);
-    const int sbase = static_cast<int>(p0 % cap);
+    int sbase = 0, cnt = 0;
     auto slot = [&](int j) {
         int sl = sbase + (j < cnt ? j : 0);
         if (sl >= cap32) sl -= cap32;
@@ -181,8 +204,8 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         for (int e = 0; e < 4; ++e) rope_cs(pos, r, 4 * sub + e, rc[e], rs[e]);
         load8(ra.qn, gq);
         load8(ra.kn, gk);
-        if (pos >= p0 && pos < p0 + cnt) {
-            // this chunk holds the new position: append its key and value rows
+        if (pos >= s0 && pos < s0 + span) {
+            // this split holds the new position: append its key and value rows
             float kv8[8], vv8[8];
             const float *kr = ra.kraw + b * ra.ldkv + static_cast<int64_t>(g0) * HD;
             load8(kr, kv8);
@@ -217,6 +240,27 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[g][e] *= scale;
     }
+    // ---- value-pass roles and running state
+    const int kg = threadIdx.x / TPK, d4 = threadIdx.x % TPK;
+    constexpr int VG = VIT < 16 ? VIT : 16;  // keys per thread at a time
+    constexpr int HPW = (GM + 3) / 4;        // softmax: heads per wavefront
+    float4 acc[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float m_run[HPW], l_run[HPW];
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        m_run[i] = -INFINITY;
+        l_run[i] = 0.f;
+    }
+    // one chunk per split unless MULTI (then the value sums stay live across
+    // the score pass, which costs registers)
+    const int nck = MULTI ? static_cast<int>((span + kChunk - 1) / kChunk) : 1;
+#pragma unroll 1
+    for (int ci = 0; ci < nck; ++ci) {
+    const int64_t p0 = s0 + static_cast<int64_t>(ci) * kChunk;
+    cnt = static_cast<int>(min(int64_t(kChunk), n - p0));
+    sbase = static_cast<int>(p0 % cap);
 #pragma unroll 1
     for (int i0 = 0; i0 < SIT; i0 += SG) {
         float kr[SG][8];
@@ -241,26 +285,32 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     }
     __syncthreads();
 
-    // ---- exact softmax over the chunk: one wavefront per query head, one lane per position
-    for (int g = wave; g < G; g += 4) {
-        const float s = sc[lane * GM + g];
-        const float m = wave_max(s);
-        const float e = lane < cnt ? __expf(s - m) : 0.f;
-        const float l = wave_sum(e);
-        sc[lane * GM + g] = e;
-        if (lane == 0) {
-            pml[2 * g] = m;
-            pml[2 * g + 1] = l;
+    // ---- softmax over the chunk against the running maximum: one wavefront
+    // per query head, one lane per position
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int g = wave + 4 * i;
+        if (g < G) {
+            const float s = sc[lane * GM + g];
+            const float m_new = fmaxf(m_run[i], wave_max(s));
+            const float e = lane < cnt ? __expf(s - m_new) : 0.f;
+            const float a = __expf(m_run[i] - m_new);  // 0 at the first chunk
+            l_run[i] = __builtin_fmaf(l_run[i], a, wave_sum(e));
+            m_run[i] = m_new;
+            sc[lane * GM + g] = e;
+            if (lane == 0) alpha_s[g] = a;
         }
     }
     __syncthreads();
 
     // ---- weighted values: TPK threads per key (4 dims each), KG key groups
-    const int kg = threadIdx.x / TPK, d4 = threadIdx.x % TPK;
-    constexpr int VG = VIT < 16 ? VIT : 16;  // keys per thread at a time
-    float4 acc[GM];
+    if (MULTI && ci > 0) {  // nothing to rescale at the first chunk
 #pragma unroll
-    for (int g = 0; g < GM; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int g = 0; g < GM; ++g) {
+            const float a = g < G ? alpha_s[g] : 0.f;
+            acc[g].x *= a; acc[g].y *= a; acc[g].z *= a; acc[g].w *= a;
+        }
+    }
 #pragma unroll 1
     for (int i0 = 0; i0 < VIT; i0 += VG) {
         float4 vv[VG];
@@ -278,6 +328,16 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
                 acc[g].z = __builtin_fmaf(w, vv[it].z, acc[g].z);
                 acc[g].w = __builtin_fmaf(w, vv[it].w, acc[g].w);
             }
+        }
+    }
+    if (MULTI) __syncthreads();  // sc and alpha_s are rewritten by the next chunk
+    }  // chunks
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int g = wave + 4 * i;
+        if (g < G && lane == 0) {
+            pml[2 * g] = m_run[i];
+            pml[2 * g + 1] = l_run[i];
         }
     }
     if constexpr (KG > 1) {
@@ -305,9 +365,10 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 }
 
 // Merge: one workgroup per (query head, sequence, 64-dimension slice); four
-// chunk groups accumulate interleaved chunks and are added in a fixed order.
+// groups accumulate interleaved split partials (np of them, in ascending
+// order within a group) and the groups are added in a fixed order.
 __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict__ part, int G,
-                                                         int Hkv, int nch, int GM, int hd,
+                                                         int Hkv, int np, int GM, int hd,
                                                          float *__restrict__ out, int64_t ldo,
                                                          int B) {
     __shared__ float rn[3][64], rd[3][64];
@@ -315,22 +376,22 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     const int g0 = h / G, g = h % G;
     const int cg = threadIdx.x >> 6, dl = threadIdx.x & 63;
     const int d = blockIdx.z * 64 + dl;
-    const size_t units_total = static_cast<size_t>(B) * Hkv * nch * GM;
+    const size_t units_total = static_cast<size_t>(B) * Hkv * np * GM;
     const float *pml = part + units_total * hd;
-    const size_t u0 = (static_cast<size_t>(b) * Hkv + g0) * nch * GM + g;
+    const size_t u0 = (static_cast<size_t>(b) * Hkv + g0) * np * GM + g;
     float M = -INFINITY;
-    for (int c = dl; c < nch; c += 64) {
+    for (int c = dl; c < np; c += 64) {
         const size_t u = u0 + static_cast<size_t>(c) * GM;
         if (pml[2 * u + 1] > 0.f) M = fmaxf(M, pml[2 * u]);
     }
     M = wave_max(M);
     float num = 0.f, den = 0.f;
     constexpr int kU = 8;  // chunks in flight per thread, still added in ascending order
-    for (int c0 = cg; c0 < nch; c0 += 4 * kU) {
+    for (int c0 = cg; c0 < np; c0 += 4 * kU) {
         float lv[kU], mv[kU], pv[kU];
 #pragma unroll
         for (int r = 0; r < kU; ++r) {
-            const int c = min(c0 + 4 * r, nch - 1);
+            const int c = min(c0 + 4 * r, np - 1);
             const size_t u = u0 + static_cast<size_t>(c) * GM;
             lv[r] = pml[2 * u + 1];
             mv[r] = pml[2 * u];
@@ -338,7 +399,7 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
         }
 #pragma unroll
         for (int r = 0; r < kU; ++r) {
-            if (c0 + 4 * r < nch && lv[r] > 0.f) {
+            if (c0 + 4 * r < np && lv[r] > 0.f) {
                 const float w = __expf(mv[r] - M);
                 num = __builtin_fmaf(w, pv[r], num);
                 den = __builtin_fmaf(w, lv[r], den);
@@ -359,16 +420,16 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     }
 }
 
-template <int HD, bool ROPE>
+template <int HD, bool ROPE, bool MULTI>
 void launch_split_hd(int GM, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
                      const float *kc, const float *vc, const q4_kv_layout &kv,
-                     const int64_t *n_dev, int64_t window, float scale, int nch, float *part,
+                     const int64_t *n_dev, int64_t window, float scale, int ns, int cps, float *part,
                      const RopeArgs &ra) {
 #define Q4_ATTN_CASE(GG)                                                                          \
     case GG:                                                                                      \
-        hipLaunchKernelGGL((attn_split_kernel<HD, GG, ROPE>), grid, dim3(kWG), 0, s, q, ldq, G, kc, \
+        hipLaunchKernelGGL((attn_split_kernel<HD, GG, ROPE, MULTI>), grid, dim3(kWG), 0, s, q, ldq, G, kc, \
                            vc, kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale, \
-                           nch, part, ra);                                                        \
+                           ns, cps, part, ra);                                                    \
         break;
     switch (GM) { Q4_ATTN_CASE(1) Q4_ATTN_CASE(2) Q4_ATTN_CASE(4) Q4_ATTN_CASE(8) Q4_ATTN_CASE(16) }
 #undef Q4_ATTN_CASE
@@ -391,7 +452,7 @@ extern "C" size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_
     q4_kv_layout k2 = *kv;
     // partial rows are stored padded to the kernel's group size
     const int gm = round_group(g.G);
-    const size_t units = static_cast<size_t>(k2.batch) * k2.n_kv_heads * g.nch * gm;
+    const size_t units = static_cast<size_t>(k2.batch) * k2.n_kv_heads * g.ns * gm;
     return units * (static_cast<size_t>(k2.head_dim) + 2) * sizeof(float);
 }
 
@@ -428,14 +489,22 @@ q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_
     const int gm = round_group(G);
     hipStream_t s = q4::as_stream(stream);
     float *part = static_cast<float *>(ws);
-    dim3 grid(g.nch, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
+    dim3 grid(g.ns, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
     const RopeArgs none{};
 #define Q4_ATTN_HD(H)                                                                             \
     case H:                                                                                       \
-        if (ra) launch_split_hd<H, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,    \
-                                         window, scale, g.nch, part, *ra);                        \
-        else launch_split_hd<H, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,      \
-                                       window, scale, g.nch, part, none);                         \
+        if (ra && g.cps > 1)                                                                      \
+            launch_split_hd<H, true, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,  \
+                                           window, scale, g.ns, g.cps, part, *ra);                \
+        else if (ra)                                                                              \
+            launch_split_hd<H, true, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, \
+                                            window, scale, g.ns, g.cps, part, *ra);               \
+        else if (g.cps > 1)                                                                       \
+            launch_split_hd<H, false, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, \
+                                            window, scale, g.ns, g.cps, part, none);              \
+        else                                                                                      \
+            launch_split_hd<H, false, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv,       \
+                                             n_dev, window, scale, g.ns, g.cps, part, none);      \
         break;
     switch (hd) { Q4_ATTN_HD(64) Q4_ATTN_HD(128) Q4_ATTN_HD(256) Q4_ATTN_HD(512) }
 #undef Q4_ATTN_HD
@@ -444,7 +513,7 @@ q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_
     hipLaunchKernelGGL(attn_merge_kernel,
                        dim3(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(kv->batch),
                             static_cast<unsigned>((hd + 63) / 64)),
-                       dim3(kWG), 0, s, part, G, static_cast<int>(kv->n_kv_heads), g.nch, gm,
+                       dim3(kWG), 0, s, part, G, static_cast<int>(kv->n_kv_heads), g.ns, gm,
                        static_cast<int>(hd), out, ldo, static_cast<int>(kv->batch));
     return q4::launch_status(name);
 }

@@ -122,9 +122,9 @@ def _attn_oracle(qh, kc, vc, n, window, scale, cap):
     vals = np.zeros((n, hkv, hd))
     lo = max(0, n - window) if window else 0
     lo = max(lo, n - cap)
-    for p in range(lo, n):
-        keys[p] = kc[:, p % cap]
-        vals[p] = vc[:, p % cap]
+    slots = np.arange(lo, n) % cap
+    keys[lo:n] = kc[:, slots].transpose(1, 0, 2)
+    vals[lo:n] = vc[:, slots].transpose(1, 0, 2)
     # positions below lo are never seen: the oracle window expresses the same set
     w = n - lo if (window or lo > 0) else 0
     return oracle.gqa_attention(qh, keys, vals, w, scale)
@@ -141,6 +141,15 @@ ATTN_CASES = [
     (2, 16, 1, 64, 100, 77, 16),         # 16:1 groups, window smaller than n
     (1, 6, 6, 128, 50, 33, 0),           # multi-head (G = 1)
     (8, 32, 8, 128, 2064, 2049, 0),      # Qwen3-4B-shaped, B = 8
+    # long contexts: 4096+ chunks in all, so one workgroup takes a split of
+    # several 64-key chunks with a running softmax
+    (1, 16, 8, 128, 32768, 32768, 0),    # 32K keys, every split full
+    (1, 16, 8, 128, 40000, 33001, 0),    # ragged last split, empty splits past n
+    (1, 16, 8, 128, 32768, 40000, 0),    # ring wrapped past capacity
+    (4, 16, 8, 128, 8192, 8000, 0),      # B = 4
+    (1, 16, 1, 64, 262144, 262000, 0),   # 16:1 groups, 256K keys
+    (8, 16, 16, 64, 4096, 9000, 4096),   # sliding window over a wrapped ring
+    (1, 32, 4, 512, 65552, 65536, 0),    # 31B full-layer shape at 64K keys
 ]
 
 
@@ -171,14 +180,15 @@ def test_gqa_decode_attn_parity(dev, B, hq, hkv, hd, cap, n, window):
     assert worst <= 1.0, f"max err/tol {worst:.3e}"
 
 
-def test_gqa_decode_attn_deterministic(dev):
-    B, hq, hkv, hd, cap = 2, 16, 8, 128, 3000
+@pytest.mark.parametrize("B,cap", [(2, 3000), (1, 40000)], ids=["one_chunk_splits", "long"])
+def test_gqa_decode_attn_deterministic(dev, B, cap):
+    hq, hkv, hd = 16, 8, 128
     qv = torch.randn(B, hq * hd, device=dev)
     kc = torch.randn(B, hkv, cap, hd, device=dev)
     vc = torch.randn(B, hkv, cap, hd, device=dev)
     kv = kv_layout_of(kc)
     ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
-    n_d = torch.tensor([2999], dtype=torch.int64, device=dev)
+    n_d = torch.tensor([cap - 1], dtype=torch.int64, device=dev)
     outs = []
     for _ in range(3):
         out = torch.empty((B, hq * hd), device=dev)
@@ -210,6 +220,9 @@ ROPE_ATTN_CASES = [
     (1, 32, 4, 512, 8208, 8192, 0, True, 1e6),    # 31B full layer: V from K
     (2, 16, 1, 64, 100, 76, 16, True, 1e4),       # 16:1 groups, small window
     (8, 32, 8, 128, 2064, 2048, 0, False, 1e6),   # 4B-shaped, B = 8
+    # long contexts (splits of several chunks; the append lands in the last)
+    (1, 32, 4, 512, 65552, 65536, 0, True, 1e6),  # 31B full layer at 64K keys
+    (1, 16, 8, 128, 32768, 40000, 0, False, 1e6),  # wrapped ring
 ]
 
 
@@ -238,7 +251,7 @@ def test_gqa_decode_attn_rope_parity(dev, B, hq, hkv, hd, cap, pos, window, v_fr
     torch.cuda.synchronize()
     kc, vc, got = _np(kc_d), _np(vc_d), _np(out)
     slot = pos % cap
-    others = [s for s in range(cap) if s != slot]
+    others = np.arange(cap) != slot
     assert np.array_equal(kc[:, :, others], kc0[:, :, others])
     assert np.array_equal(vc[:, :, others], vc0[:, :, others])
     worst = 0.0
