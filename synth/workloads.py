@@ -109,9 +109,18 @@ QWEN3_4B = _qwen3("decode_qwen3_4b", 36, 2560, 32, 8, 128, 9728, 151936, 8, 2048
 GEMMA4_31B = _gemma4("decode_gemma4_31b", 60, 5376, 32, 16, 256, 1024, 4, 512, 21504, 262144,
                      1, 8192, 16, SEED_BASE + 4)
 
+# The 31B-shaped model decoding at a 128K-token context (full-attention
+# caches of 131,088 slots); same weights as GEMMA4_31B.
+GEMMA4_31B_128K = _gemma4("decode_gemma4_31b_128k", 60, 5376, 32, 16, 256, 1024, 4, 512, 21504,
+                          262144, 1, 131072, 16, SEED_BASE + 4)
+
 # Small models with the same structure, for parity tests the oracle finishes fast.
 TINY_QWEN3 = _qwen3("tiny_qwen3", 2, 256, 4, 2, 64, 512, 1000, 3, 37, 4, 7001)
 TINY_GEMMA4 = _gemma4("tiny_gemma4", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 40, 4, 7002)
+# The tiny structure at a 128K-token context: its full-attention layer holds
+# 2,049 chunks of 64 keys per sequence, so attention runs as multi-chunk splits.
+TINY_GEMMA4_LONG = _gemma4("tiny_gemma4_long", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 131072,
+                           3, 7003)
 
 
 def layer_rows(m: ModelShape, ly: LayerShape):

@@ -6,7 +6,8 @@ from synth import workloads as wl
 
 
 def upload_model(m, weights, dev, caches=None):
-    """Device tensors of every weight and a prefilled cache per layer."""
+    """Device tensors of every weight and a prefilled cache per layer
+    (``caches``: per layer a (k, v) pair of host arrays or device tensors)."""
     import torch
     layers = []
     for l, ly in enumerate(m.layers):
@@ -16,13 +17,14 @@ def upload_model(m, weights, dev, caches=None):
             vc = wl.prefilled_cache(m, l, "v")
         else:
             kc, vc = caches[l]
+        as_dev = lambda a: a if isinstance(a, torch.Tensor) else torch.from_numpy(a).to(dev)
         layers.append(dict(
             wqkv=torch.from_numpy(w["wqkv"]).to(dev), wo=torch.from_numpy(w["wo"]).to(dev),
             wgu=torch.from_numpy(w["wgu"]).to(dev), wd=torch.from_numpy(w["wd"]).to(dev),
             attn_norm=torch.from_numpy(w["attn_norm"]).to(dev),
             ffn_norm=torch.from_numpy(w["ffn_norm"]).to(dev),
             q_norm=torch.from_numpy(w["q_norm"]).to(dev), k_norm=torch.from_numpy(w["k_norm"]).to(dev),
-            k_cache=torch.from_numpy(kc).to(dev), v_cache=torch.from_numpy(vc).to(dev),
+            k_cache=as_dev(kc), v_cache=as_dev(vc),
             n_kv_heads=ly.n_kv_heads, head_dim=ly.head_dim, window=ly.window,
             rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k))
     return dict(embed=torch.from_numpy(weights["embed"]).to(dev),
