@@ -116,8 +116,10 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                             void *stream);
 
 /* q4_0_matvec_batched / q8_0_matvec_batched: the same products as the fused
- * calls, computed on the matrix cores for 1 <= B <= 8 activation rows; meant
- * for B >= 2, where eight products per weight outrun the vector units.
+ * calls, computed on the matrix cores for 1 <= B <= 32 activation rows; meant
+ * for B >= 2, where eight products per weight outrun the vector units.  Rows
+ * are taken in groups of 8; the groups of one row range run back to back on
+ * one XCD, so the weights are read from HBM once per call.
  * Operands are exact binary16 (codes as integers; activations, after a
  * power-of-two scaling per row and per 256 k, split into two halves), so
  * every product is exact and sums are fp32.  RMSNorm's 1/rms is applied to
@@ -283,7 +285,10 @@ typedef struct {
 } q4_layer_desc;
 
 typedef struct {
-    int64_t n_layers, d_model, n_q_heads, ffn, vocab, batch; /* batch 1..8 */
+    /* batch 1..8; up to 32 when every projection runs on the matrix cores
+     * (d_model, ffn and n_q_heads * head_dim multiples of 256, weights
+     * 16-byte aligned), else Q4_ERR_UNSUPPORTED */
+    int64_t n_layers, d_model, n_q_heads, ffn, vocab, batch;
     float eps;
     const void *embed;        /* Q8_0 [vocab][d_model], tied input/output table */
     const float *final_norm;  /* [d_model] */

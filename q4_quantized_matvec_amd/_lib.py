@@ -221,7 +221,7 @@ def _matvec_batched(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual,
 
 def q4_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
                         residual=None, ws=None, stream=None, n=None, out_op=OUT_PLAIN):
-    """As q4_0_matvec_fused, on the matrix cores (1 <= B <= 8, K % 256 == 0).  ``ws``: a
+    """As q4_0_matvec_fused, on the matrix cores (1 <= B <= 32, K % 256 == 0).  ``ws``: a
     zero-initialised uint8 device tensor of matvec_batched_workspace(N, K, B) bytes, reusable
     across calls on one stream (allocated if None)."""
     return _matvec_batched("q4_0_matvec_batched", 18, W, x, K, B, ld, op, x2, norm_w, eps, y,

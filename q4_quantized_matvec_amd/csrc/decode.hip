@@ -129,7 +129,13 @@ q4_status validate(const q4_model_desc *d) {
     Q4_CHECK(d->d_model >= 32 && d->n_q_heads >= 1 && d->ffn >= 32 && d->vocab >= 1, Q4_ERR_INVALID_ARG,
              "decode model: sizes must be positive");
     Q4_CHECK(d->batch >= 1, Q4_ERR_INVALID_ARG, "decode model: batch must be >= 1");
-    Q4_CHECK(d->batch <= 8, Q4_ERR_UNSUPPORTED, "decode model: batch %lld > 8", (long long)d->batch);
+    Q4_CHECK(d->batch <= 32, Q4_ERR_UNSUPPORTED, "decode model: batch %lld > 32", (long long)d->batch);
+    // Beyond 8 sequences only the matrix-core projections apply.
+    const bool wide = d->batch > 8;
+    Q4_CHECK(!wide || (d->d_model % 256 == 0 && d->ffn % 256 == 0 && q4::aligned(d->embed, 16)),
+             Q4_ERR_UNSUPPORTED,
+             "decode model: batch %lld > 8 needs d_model and ffn multiples of 256 and a 16-byte aligned table",
+             (long long)d->batch);
     Q4_CHECK(d->d_model % 32 == 0 && d->ffn % 32 == 0, Q4_ERR_SHAPE,
              "decode model: d_model and ffn must be multiples of 32");
     Q4_CHECK(d->eps >= 0.f, Q4_ERR_INVALID_ARG, "decode model: eps must be >= 0");
@@ -155,6 +161,11 @@ q4_status validate(const q4_model_desc *d) {
                  (long long)i);
         Q4_CHECK((d->n_q_heads * l.head_dim) % 32 == 0, Q4_ERR_SHAPE,
                  "decode model: layer %lld: n_q_heads * head_dim must be a multiple of 32", (long long)i);
+        Q4_CHECK(!wide || ((d->n_q_heads * l.head_dim) % 256 == 0 && q4::aligned(l.wqkv, 16) &&
+                           q4::aligned(l.wo, 16) && q4::aligned(l.wgu, 16) && q4::aligned(l.wd, 16)),
+                 Q4_ERR_UNSUPPORTED,
+                 "decode model: layer %lld: batch > 8 needs n_q_heads * head_dim a multiple of 256 "
+                 "and 16-byte aligned weights", (long long)i);
     }
     return Q4_OK;
 }

@@ -1,4 +1,4 @@
-// Batched Q4_0 / Q8_0 dequant-matvec (1 <= B <= 8 activation rows) on the
+// Batched Q4_0 / Q8_0 dequant-matvec (1 <= B <= 32 activation rows) on the
 // gfx950 matrix cores.
 //
 // Definition ("Research record" page, "Native Metal diagnostic: buffer
@@ -38,6 +38,12 @@
 // build.  K is split over S workgroups when the row count alone cannot fill
 // the chip; the partial sums are added in split order by whichever workgroup
 // of the row range finishes last, so results are bitwise reproducible.
+//
+// More than 8 activation rows are taken in groups of 8 (at most 4 groups):
+// each workgroup computes one group, and the workgroups of one row range and
+// its groups are dispatched one after another to the same XCD, so the
+// weights come from HBM once and the later groups read them from that XCD's
+// L2.
 #include "common.hpp"
 
 namespace {
@@ -51,7 +57,9 @@ typedef float f32x4_al16_t __attribute__((ext_vector_type(4), aligned(16)));
 
 constexpr int kWG = 256;            // 4 wavefronts
 constexpr int kSeg = 8;             // blocks per step (one MFMA each per wavefront)
-constexpr int kMaxB = 8;
+constexpr int kMaxB = 8;             // activation rows per group (one MFMA operand)
+constexpr int kMaxGroups = 4;
+constexpr int kMaxBatch = kMaxB * kMaxGroups;
 constexpr int kMinWGs = 512;        // below this, the shared-step kernel
 constexpr int kTargetWGs = 1024;    // shared-step kernel: split K toward this many workgroups
 constexpr int kMaxS = 32;           // K splits at most (the final writer holds them in registers)
@@ -91,6 +99,22 @@ __device__ __forceinline__ int step_shift(float m) {
 }
 
 __device__ __forceinline__ float max4(f32x4_t v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+// Row range rx and batch group gi of this workgroup.  With one group the
+// grid is (row ranges, K splits).  With NG > 1 groups, workgroups go to the
+// 8 XCDs in turn (id mod 8), so id = 8 (NG r + gi) + x for row range
+// 8 r + x puts the NG groups of a row range on one XCD, consecutively; the
+// grid is padded to whole octets and ids past the last row range idle.
+struct GroupView {
+    int rx, gi, Bg;  // row range, group, activation rows of the group
+    bool live;
+};
+__device__ __forceinline__ GroupView group_view(int rg, int NG, int B) {
+    if (NG == 1) return {static_cast<int>(blockIdx.x), 0, B, true};
+    const int L = blockIdx.x, j = L >> 3;
+    const int gi = j % NG, rx = (j / NG) * 8 + (L & 7);
+    return {rx, gi, min(kMaxB, B - kMaxB * gi), rx < rg};
+}
 
 // A copy the compiler cannot see through.  When both results of one
 // permlane swap are reinterpreted as floating point, this compiler has been
@@ -226,7 +250,7 @@ __device__ __forceinline__ void weight_operands(const uint32_t (&dw)[BF<FMT>::kL
 // applied); with one, it stores its partials, takes a ticket, and the last
 // split of the row range adds the S partials in split order.
 struct FinishArgs {
-    int N, K, B, S, glu;
+    int N, K, B, S, glu, rx;  // B: rows of the group; rx: the row range
     float eps;
     float *y;
     const float *res;
@@ -242,7 +266,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     constexpr int kHalf = T > 1 ? T / 2 : 1;
     __shared__ float upx[kPairs][kMaxB];  // SwiGLU output: up-row sums of the pairs
     __shared__ int ticket;
-    const int N = fa_.N, K = fa_.K, B = fa_.B, S = fa_.S, glu = fa_.glu;
+    const int N = fa_.N, K = fa_.K, B = fa_.B, S = fa_.S, glu = fa_.glu, rx = fa_.rx;
     const float eps = fa_.eps;
     float *y = fa_.y;
     const float *res = fa_.res;
@@ -291,7 +315,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     }
     if constexpr (KIND == 1) {
         if (threadIdx.x < B)
-            __hip_atomic_store(ssq_part + (static_cast<int64_t>(blockIdx.x) * S + blockIdx.y) * kMaxB +
+            __hip_atomic_store(ssq_part + (static_cast<int64_t>(rx) * S + blockIdx.y) * kMaxB +
                                    threadIdx.x,
                                range_ssq(threadIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -300,7 +324,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(&counters[blockIdx.x * kCounterStride], 1, __ATOMIC_RELAXED,
+        ticket = __hip_atomic_fetch_add(&counters[rx * kCounterStride], 1, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
@@ -311,7 +335,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     __shared__ float inv_s[kMaxB];
     if constexpr (KIND == 1) {
         if (threadIdx.x < B) {
-            const float *sq = ssq_part + static_cast<int64_t>(blockIdx.x) * S * kMaxB + threadIdx.x;
+            const float *sq = ssq_part + static_cast<int64_t>(rx) * S * kMaxB + threadIdx.x;
             float t[kMaxS];
 #pragma unroll
             for (int q = 0; q < kMaxS; ++q)
@@ -332,7 +356,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     for (int r = 0; r < 2; ++r) {
         const int o = glu ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x) + r * kWG;
         ob[r] = o / outs;
-        const int nn = blockIdx.x * outs + (o % outs);
+        const int nn = rx * outs + (o % outs);
         act[r] = o < outs * B && nn < (glu ? P : N);
         row[r] = glu ? (r == 0 ? nn : P + nn) : nn;
     }
@@ -365,7 +389,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
         }
     }
     if (threadIdx.x == 0)
-        __hip_atomic_store(&counters[blockIdx.x * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&counters[rx * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int KIND>
@@ -373,12 +397,28 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int cps, int glu) {
+    float *__restrict__ part, int S, int cps, int glu, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
     __shared__ f32x4_t stepmax[2][kMaxB];    // per batch row: the 4 wavefronts' maxima
     __shared__ float ssq_w[4][kMaxB];
+    const GroupView gv_ = group_view(rg, NG, B);
+    if (!gv_.live) return;  // padding of the last octet (workgroup-uniform)
+    const int rx = gv_.rx;
+    {
+        // this group's activation rows, outputs and workspace regions
+        const int64_t g8 = static_cast<int64_t>(kMaxB) * gv_.gi;
+        const int64_t outw = glu ? (N >> 1) : N;
+        x += g8 * ld;
+        if (u) u += g8 * ld;
+        y += g8 * outw;
+        if (res) res += g8 * N;
+        part += static_cast<int64_t>(gv_.gi) * S * kMaxB * N;
+        ssq_part += static_cast<int64_t>(gv_.gi) * rg * S * kMaxB;
+        counters += gv_.gi * rg * kCounterStride;
+        B = gv_.Bg;
+    }
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -386,8 +426,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     // Rows of this lane: 64 consecutive rows per workgroup, or with a SwiGLU
     // output 32 gate rows (wavefronts 0, 1) and their 32 up rows (2, 3).
     const int P = N >> 1;
-    const int pu = blockIdx.x * 32 + 16 * (wv & 1) + col;  // pair (SwiGLU output)
-    const int n = glu ? (wv < 2 ? pu : P + pu) : blockIdx.x * 64 + wv * 16 + col;
+    const int pu = rx * 32 + 16 * (wv & 1) + col;  // pair (SwiGLU output)
+    const int n = glu ? (wv < 2 ? pu : P + pu) : rx * 64 + wv * 16 + col;
     const bool rvalid = glu ? pu < P : n < N;
     const int nl = rvalid ? n : N - 1;
     const int nb = K / 32, kc = nb / kSeg;
@@ -519,7 +559,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const int pl = 16 * (wv & 1) + col;
     const float ya = acc[0] + acc[1];
     const float yb = acc[2] + acc[3];
-    const FinishArgs fa_{N, K, B, S, glu, eps, y, res, counters, ssq_part, part};
+    const FinishArgs fa_{N, K, B, S, glu, rx, eps, y, res, counters, ssq_part, part};
     finish<KIND, 4>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
@@ -528,13 +568,29 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int spw, int glu) {
+    float *__restrict__ part, int S, int spw, int glu, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t opnd[4][kSeg][64];               // per wavefront: its step's activation operands
     __shared__ f32x4_t red[4][T][64];                   // per-wavefront partial tiles
     __shared__ float ssq_w[4][kMaxB];
     constexpr int kRows = 16 * T, kPairs = 8 * T;       // output rows (pairs) of a workgroup
+    const GroupView gv_ = group_view(rg, NG, B);
+    if (!gv_.live) return;  // padding of the last octet (workgroup-uniform)
+    const int rx = gv_.rx;
+    {
+        // this group's activation rows, outputs and workspace regions
+        const int64_t g8 = static_cast<int64_t>(kMaxB) * gv_.gi;
+        const int64_t outw = glu ? (N >> 1) : N;
+        x += g8 * ld;
+        if (u) u += g8 * ld;
+        y += g8 * outw;
+        if (res) res += g8 * N;
+        part += static_cast<int64_t>(gv_.gi) * S * kMaxB * N;
+        ssq_part += static_cast<int64_t>(gv_.gi) * rg * S * kMaxB;
+        counters += gv_.gi * rg * kCounterStride;
+        B = gv_.Bg;
+    }
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -546,11 +602,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     auto tile_pair = [&](int t) { return 16 * (t % kHalf) + col; };  // pair within the workgroup
     auto tile_row = [&](int t, bool &valid) {
         if (glu) {
-            const int pr = blockIdx.x * kPairs + tile_pair(t);
+            const int pr = rx * kPairs + tile_pair(t);
             valid = pr < P;
             return t < kHalf ? pr : P + pr;
         }
-        const int r = blockIdx.x * kRows + 16 * t + col;
+        const int r = rx * kRows + 16 * t + col;
         valid = r < N;
         return r;
     };
@@ -740,10 +796,10 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const int n = tile_row(tw, rvalid);
     rvalid = rvalid && wv < T;
     const int pl = tile_pair(tw);                     // pair within the workgroup (SwiGLU output)
-    const int pu = blockIdx.x * kPairs + pl;
+    const int pu = rx * kPairs + pl;
     const float ya = tot[0] + tot[1];
     const float yb = tot[2] + tot[3];
-    const FinishArgs fa_{N, K, B, S, glu, eps, y, res, counters, ssq_part, part};
+    const FinishArgs fa_{N, K, B, S, glu, rx, eps, y, res, counters, ssq_part, part};
     finish<KIND, T>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
@@ -751,6 +807,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
 struct Plan {
     bool tiles;  // the tile kernel, else the shared-step kernel
     int T, rg, kc, S, spw;
+    int NG, gx;  // batch groups; grid width (row ranges, padded to octets when NG > 1)
     size_t off_ssq, off_part, bytes;
 };
 
@@ -764,26 +821,34 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // all when the row ranges outnumber the tickets.
 Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt) {
     Plan p;
+    p.NG = static_cast<int>((B + kMaxB - 1) / kMaxB);
     p.kc = static_cast<int>(K / (32 * kSeg));
     p.tiles = true;
     p.T = fmt == 1 ? 2 : 4;
     p.rg = static_cast<int>((N + 16 * p.T - 1) / (16 * p.T));
     const int rounds = (p.kc + 3) / 4;
-    p.spw = p.rg > kCounters ? rounds : (rounds + kMaxS - 1) / kMaxS;
+    p.spw = static_cast<int64_t>(p.rg) * p.NG > kCounters ? rounds : (rounds + kMaxS - 1) / kMaxS;
     p.S = (rounds + p.spw - 1) / p.spw;
-    if (static_cast<int64_t>(p.rg) * p.S < kMinWGs) {
+    if (static_cast<int64_t>(p.rg) * p.S * p.NG < kMinWGs) {
         p.tiles = false;
         p.T = 4;
         p.rg = static_cast<int>((N + 63) / 64);
-        int want = std::max(1, std::min(std::min(p.kc, kMaxS), (kTargetWGs + p.rg - 1) / p.rg));
-        if (p.rg > kCounters) want = 1;
+        const int wgs = (kTargetWGs + p.NG - 1) / p.NG;
+        int want = std::max(1, std::min(std::min(p.kc, kMaxS), (wgs + p.rg - 1) / p.rg));
+        if (static_cast<int64_t>(p.rg) * p.NG > kCounters) want = 1;
         p.spw = (p.kc + want - 1) / want;
         p.S = (p.kc + p.spw - 1) / p.spw;
     }
+    p.gx = p.NG == 1 ? p.rg : (p.rg + 7) / 8 * 8 * p.NG;
+    // per group: S partial rows of its (up to 8) activation rows, and the
+    // sums of squares of each row range and split
+    const int64_t gB = p.NG == 1 ? B : kMaxB;
     p.off_ssq = kCounterBytes;
-    const size_t ssq = p.S > 1 ? align256(static_cast<size_t>(p.rg) * p.S * kMaxB * sizeof(float)) : 0;
+    const size_t ssq =
+        p.S > 1 ? align256(static_cast<size_t>(p.NG) * p.rg * p.S * kMaxB * sizeof(float)) : 0;
     p.off_part = p.off_ssq + ssq;
-    p.bytes = p.off_part + (p.S > 1 ? align256(static_cast<size_t>(p.S) * B * N * sizeof(float)) : 0);
+    p.bytes = p.off_part +
+              (p.S > 1 ? align256(static_cast<size_t>(p.NG) * p.S * gB * N * sizeof(float)) : 0);
     return p;
 }
 
@@ -795,15 +860,15 @@ void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *
     int *ctr = reinterpret_cast<int *>(w8);
     float *ssq = reinterpret_cast<float *>(w8 + p.off_ssq);
     float *part = reinterpret_cast<float *>(w8 + p.off_part);
-    const dim3 grid(p.rg, p.S);
+    const dim3 grid(p.gx, p.S);
     if (!p.tiles) {
         hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu);
+                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
         return;
     }
     constexpr int T = FMT == 1 ? 2 : 4;
     hipLaunchKernelGGL((mv_mfma_tile_kernel<FMT, KIND, T>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu);
+                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -831,7 +896,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     Q4_CHECK(ldx >= K, Q4_ERR_SHAPE, "%s: ld_x=%lld < K=%lld", name, (long long)ldx, (long long)K);
     Q4_CHECK(K % 256 == 0, Q4_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 256", name,
              (long long)K);
-    Q4_CHECK(B <= kMaxB, Q4_ERR_UNSUPPORTED, "%s: B=%lld > 8", name, (long long)B);
+    Q4_CHECK(B <= kMaxBatch, Q4_ERR_UNSUPPORTED, "%s: B=%lld > 32", name, (long long)B);
     Q4_CHECK(N <= (1 << 30) && K <= (1 << 24) && ldx <= (1 << 26), Q4_ERR_UNSUPPORTED,
              "%s: N or K too large", name);
     Q4_CHECK(q4::aligned(Wv, 16), Q4_ERR_ALIGNMENT, "%s: W must be 16-byte aligned", name);
@@ -863,7 +928,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
 }  // namespace
 
 extern "C" size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B) {
-    if (N < 1 || K < 256 || K % 256 != 0 || B < 1 || B > kMaxB) return 0;
+    if (N < 1 || K < 256 || K % 256 != 0 || B < 1 || B > kMaxBatch) return 0;
     return std::max(make_plan(N, K, B, 0).bytes, make_plan(N, K, B, 1).bytes);
 }
 

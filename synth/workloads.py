@@ -117,6 +117,9 @@ GEMMA4_31B_128K = _gemma4("decode_gemma4_31b_128k", 60, 5376, 32, 16, 256, 1024,
 # Small models with the same structure, for parity tests the oracle finishes fast.
 TINY_QWEN3 = _qwen3("tiny_qwen3", 2, 256, 4, 2, 64, 512, 1000, 3, 37, 4, 7001)
 TINY_GEMMA4 = _gemma4("tiny_gemma4", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 40, 4, 7002)
+# The tiny Qwen3 structure with 20 sequences (three groups of 8 in the
+# batched projections, the last one ragged).
+TINY_QWEN3_B20 = _qwen3("tiny_qwen3_b20", 2, 256, 4, 2, 64, 512, 1000, 20, 37, 4, 7004)
 # The tiny structure at a 128K-token context: its full-attention layer holds
 # 2,049 chunks of 64 keys per sequence, so attention runs as multi-chunk splits.
 TINY_GEMMA4_LONG = _gemma4("tiny_gemma4_long", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 131072,

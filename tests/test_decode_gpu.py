@@ -30,8 +30,8 @@ def _nmse(a, b):
     return float(((a - b) ** 2).sum() / (b ** 2).sum())
 
 
-@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG],
-                         ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG,
+                                   wl.TINY_QWEN3_B20], ids=lambda s: s.name)
 def test_decode_tokens_match_oracle(dev, shape):
     _say(f"decode {shape.name}: {shape.steps} steps")
     weights = wl.model_weights(shape)
@@ -44,8 +44,8 @@ def test_decode_tokens_match_oracle(dev, shape):
     assert nmse < 1e-8
 
 
-@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG],
-                         ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG,
+                                   wl.TINY_QWEN3_B20], ids=lambda s: s.name)
 def test_graph_equals_eager(dev, shape):
     _say(f"graph vs eager {shape.name}")
     weights = wl.model_weights(shape)

@@ -63,14 +63,15 @@ def test_batched_matvec_rejects_bad_arguments_on_host():
     need = q.matvec_batched_workspace(100, 512, 4)
     assert need > 0
     assert q.matvec_batched_workspace(100, 288, 4) == 0    # K % 256 != 0
-    assert q.matvec_batched_workspace(100, 512, 9) == 0    # B > 8
+    assert q.matvec_batched_workspace(100, 512, 33) == 0   # B > 32
+    assert q.matvec_batched_workspace(100, 512, 32) > 0
     ybuf = 0x40000000  # does not overlap x
     args = lambda W, K, B, ws, nbytes: (W, 100, K, fake, None, K, B, 0, 0, None, 0.0, ybuf, None,
                                         ws, nbytes, None)
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake, need - 1))[0] == "Q4_ERR_WORKSPACE"
     assert _status(L.q4_0_matvec_batched, *args(fake, 512, 4, fake + 16, need))[0] == "Q4_ERR_WORKSPACE"
     assert _status(L.q4_0_matvec_batched, *args(fake, 288, 4, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
-    assert _status(L.q4_0_matvec_batched, *args(fake, 512, 9, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
+    assert _status(L.q4_0_matvec_batched, *args(fake, 512, 33, fake, need))[0] == "Q4_ERR_UNSUPPORTED"
     assert _status(L.q8_0_matvec_batched, *args(fake + 2, 512, 4, fake, need))[0] == "Q4_ERR_ALIGNMENT"
     assert _status(L.q4_0_matvec_batched, *args(None, 512, 4, fake, need))[0] == "Q4_ERR_INVALID_ARG"
 
@@ -84,3 +85,33 @@ def test_swiglu_output_rejected_where_unsupported():
     assert _status(L.q4_0_matvec_fused, *fused(100, 16384, None))[0] == "Q4_ERR_UNSUPPORTED"
     assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 0, 2, None, 0.0, ybuf,
                    None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # bad out_op
+
+
+def test_decode_model_batch_limits_on_host():
+    """Up to 8 sequences any shape; up to 32 only where every projection runs
+    on the matrix cores (K multiples of 256, 16-byte aligned weights)."""
+    import ctypes as C
+    L = q.lib()
+    fake = 0x100000  # never dereferenced: sizes only
+
+    def status(batch, d_model=256, ffn=512, hd=64, wq_off=0):
+        ly = (_lib.LayerDesc * 1)()
+        l0 = ly[0]
+        for f in ("wqkv", "wo", "wgu", "wd", "attn_norm", "ffn_norm", "q_norm", "k_norm",
+                  "k_cache", "v_cache"):
+            setattr(l0, f, fake)
+        l0.wqkv = fake + wq_off
+        l0.n_kv_heads, l0.head_dim, l0.cap, l0.window = 2, hd, 64, 0
+        l0.rope_theta, l0.attn_scale, l0.v_from_k = 1e4, 0.125, 0
+        d = _lib.ModelDesc(1, d_model, 4, ffn, 1000, batch, 1e-6, fake, fake,
+                           C.cast(ly, C.POINTER(_lib.LayerDesc)))
+        nbytes = C.c_size_t()
+        return _status(L.decode_model_workspace, C.byref(d), C.byref(nbytes))[0]
+
+    assert status(8) == "Q4_OK" and status(16) == "Q4_OK" and status(32) == "Q4_OK"
+    assert status(33) == "Q4_ERR_UNSUPPORTED"
+    assert status(8, d_model=288) == "Q4_OK"
+    assert status(9, d_model=288) == "Q4_ERR_UNSUPPORTED"      # d_model % 256
+    assert status(16, ffn=544) == "Q4_ERR_UNSUPPORTED"         # ffn % 256
+    assert status(16, hd=64, d_model=256, wq_off=2) == "Q4_ERR_UNSUPPORTED"  # 2-byte aligned wqkv
+    assert status(8, wq_off=2) == "Q4_OK"

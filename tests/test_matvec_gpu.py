@@ -174,6 +174,11 @@ BATCHED_CASES = [
     # with and without a K split, and two rounds per wavefront (K > 32768)
     ("q4", 8200, 4096, 8, "rms"), ("q4", 8192, 4096, 3, "swiglu"), ("q4", 33000, 1024, 5, "plain"),
     ("q4", 2000, 33024, 2, "rms"), ("q8", 8200, 2048, 8, "rms"), ("q8", 16400, 1024, 2, "plain"),
+    # more than 8 rows: groups of 8 (the last one ragged), small and large
+    # shapes, every transform, and more row ranges x groups than split tickets
+    ("q4", 2000, 2560, 9, "rms"), ("q4", 2560, 4096, 16, "plain"), ("q4", 300, 9728, 13, "swiglu"),
+    ("q4", 8192, 4096, 32, "swiglu"), ("q4", 8200, 4096, 24, "rms"), ("q4", 33000, 1024, 17, "plain"),
+    ("q8", 8200, 2048, 20, "rms"), ("q8", 3001, 2560, 32, "plain"), ("q8", 140000, 256, 12, "rms"),
 ]
 
 
@@ -307,6 +312,7 @@ GLU_CASES = [
     ("batched", 2 * 77, 9728, 5, "plain"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 33, 256, 1, "swiglu"),
     ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 16500, 1024, 4, "plain"),
+    ("batched", 2 * 9728, 2560, 32, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
 ]
 
 
