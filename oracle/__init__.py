@@ -38,10 +38,10 @@ def build(force: bool = True) -> str:
 class _Layer(C.Structure):
     _fields_ = [("wqkv", _u8_p), ("wo", _u8_p), ("wgu", _u8_p), ("wd", _u8_p),
                 ("attn_norm", _dbl_p), ("ffn_norm", _dbl_p), ("q_norm", _dbl_p),
-                ("k_norm", _dbl_p), ("k_cache", _f32_p), ("v_cache", _f32_p),
+                ("k_norm", _dbl_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
                 ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64), ("cap", C.c_int64),
                 ("window", C.c_int64), ("rope_theta", C.c_double), ("attn_scale", C.c_double),
-                ("v_from_k", C.c_int32)]
+                ("v_from_k", C.c_int32), ("kv_f16", C.c_int32)]
 
 
 class _Model(C.Structure):
@@ -62,6 +62,8 @@ def lib():
         L = C.CDLL(_LIB)
         L.orc_half_to_double.argtypes = [C.c_uint16]
         L.orc_half_to_double.restype = C.c_double
+        L.orc_double_to_half.argtypes = [C.c_double]
+        L.orc_double_to_half.restype = C.c_uint16
         for name in ("orc_q4_0_dequant", "orc_q8_0_dequant"):
             getattr(L, name).argtypes = [_u8_p, C.c_int64, C.c_int64, _dbl_p]
         for name in ("orc_q4_0_matvec", "orc_q8_0_matvec"):
@@ -103,6 +105,11 @@ def num_threads() -> int:
 
 def half_to_double(bits: int) -> float:
     return lib().orc_half_to_double(bits)
+
+
+def double_to_half(v: float) -> int:
+    """Bits of the binary16 nearest to v (ties to even)."""
+    return lib().orc_double_to_half(float(v))
 
 
 def q4_0_dequant(w, n_rows, k):
@@ -214,7 +221,7 @@ class Model:
 
     ``spec``: dict with d_model, n_q_heads, ffn, vocab, batch, eps, embed (uint8),
     final_norm, layers (list of dicts with wqkv, wo, wgu, wd, attn_norm, ffn_norm,
-    q_norm, k_norm, k_cache, v_cache (float32 [B, Hkv, cap, hd], modified in
+    q_norm, k_norm, k_cache, v_cache (float32 or float16 [B, Hkv, cap, hd], modified in
     place), n_kv_heads, head_dim, window, rope_theta, attn_scale, v_from_k).
     """
 
@@ -228,16 +235,17 @@ class Model:
             for key in ("attn_norm", "ffn_norm", "q_norm", "k_norm"):
                 arrs[key] = _f64(L[key])
             kc, vc = L["k_cache"], L["v_cache"]
-            assert kc.dtype == np.float32 and kc.flags.c_contiguous
-            assert vc.dtype == np.float32 and vc.flags.c_contiguous
+            assert kc.dtype in (np.float32, np.float16) and kc.flags.c_contiguous
+            assert vc.dtype == kc.dtype and vc.flags.c_contiguous
             self._keep.append(arrs)
             ly = layers[i]
             for key in ("wqkv", "wo", "wgu", "wd"):
                 setattr(ly, key, _p(arrs[key], _u8_p))
             for key in ("attn_norm", "ffn_norm", "q_norm", "k_norm"):
                 setattr(ly, key, _p(arrs[key], _dbl_p))
-            ly.k_cache = _p(kc, _f32_p)
-            ly.v_cache = _p(vc, _f32_p)
+            ly.k_cache = kc.ctypes.data
+            ly.v_cache = vc.ctypes.data
+            ly.kv_f16 = 1 if kc.dtype == np.float16 else 0
             ly.n_kv_heads = L["n_kv_heads"]
             ly.head_dim = L["head_dim"]
             ly.cap = kc.shape[2]

@@ -42,6 +42,32 @@ double orc_half_to_double(uint16_t h) {
     return sign ? -v : v;
 }
 
+/* The binary16 nearest to v, ties to the even fraction (IEEE 754
+ * roundTiesToEven): scale |v| to units of its binade's quantum (2^-24 for
+ * subnormals, 2^(E-10) for 2^E <= |v| < 2^(E+1)), round to an integer with
+ * rint (the default rounding mode is to nearest even), and carry a rounding
+ * up to 2048 units into the next binade.  Magnitudes from 65520 up round to
+ * infinity (65504 is the largest finite value; 65520 is the midpoint). */
+uint16_t orc_double_to_half(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00);
+    if (a < ldexp(1.0, -14)) {                 /* subnormal binade (or zero) */
+        double u = rint(ldexp(a, 24));           /* 0 .. 1024; 1024 is the smallest normal */
+        return (uint16_t)(sign | (uint16_t)u);
+    }
+    int e;
+    (void)frexp(a, &e);                          /* a = m 2^e, m in [0.5, 1): E = e - 1 */
+    int E = e - 1;
+    double u = rint(ldexp(a, 10 - E));           /* 1024 .. 2048 */
+    if (u == 2048.0) {
+        u = 1024.0;
+        E += 1;
+    }
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(u - 1024.0));
+}
+
 static double read_scale(const uint8_t *p) {
     /* little-endian byte order (the GGUF blocks are stored little-endian) */
     return orc_half_to_double((uint16_t)(p[0] | (p[1] << 8)));
@@ -260,6 +286,18 @@ void orc_gqa_attention(const double *q, int64_t n_q_heads, int64_t n_kv_heads, i
     }
 }
 
+/* Cache element i of a layer's cache: fp32, or binary16 (kv_f16). */
+static double cache_load(const orc_layer *L, const void *c, int64_t i) {
+    if (L->kv_f16) return orc_half_to_double(((const uint16_t *)c)[i]);
+    return (double)((const float *)c)[i];
+}
+static void cache_store(const orc_layer *L, void *c, int64_t i, double v) {
+    if (L->kv_f16)
+        ((uint16_t *)c)[i] = orc_double_to_half(v);
+    else
+        ((float *)c)[i] = (float)v;
+}
+
 /* One decode step.  Block topology ([GELO] 06 Compute flow: pre-LN block,
  * QKV projection, per-head QK-norm before RoPE, GQA attention over the cache
  * plus the new row, O projection with residual, pre-FFN norm, gate/up,
@@ -306,13 +344,13 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
                     memcpy(vrow, vr + g * hd, sizeof(double) * (size_t)hd);
                 orc_rmsnorm(kr + g * hd, L->k_norm, 1, hd, m->eps, tmp);
                 orc_rope_neox(tmp, hd, pos, L->rope_theta);
-                /* the cache is F32: the appended row is stored rounded */
+                /* the appended row is stored rounded to the cache's
+                 * element type (fp32, or the nearest binary16) */
                 int64_t slot = pos % L->cap;
-                float *kc = L->k_cache + ((bi * Hkv + g) * L->cap + slot) * hd;
-                float *vc = L->v_cache + ((bi * Hkv + g) * L->cap + slot) * hd;
+                int64_t at = ((bi * Hkv + g) * L->cap + slot) * hd;
                 for (int64_t i = 0; i < hd; ++i) {
-                    kc[i] = (float)tmp[i];
-                    vc[i] = (float)vrow[i];
+                    cache_store(L, L->k_cache, at + i, tmp[i]);
+                    cache_store(L, L->v_cache, at + i, vrow[i]);
                 }
             }
             for (int64_t p = lo; p < n_pos; ++p) {
@@ -320,9 +358,9 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
                 for (int64_t g = 0; g < Hkv; ++g)
                     for (int64_t i = 0; i < hd; ++i) {
                         keys[(p * Hkv + g) * hd + i] =
-                            L->k_cache[((bi * Hkv + g) * L->cap + slot) * hd + i];
+                            cache_load(L, L->k_cache, ((bi * Hkv + g) * L->cap + slot) * hd + i);
                         vals[(p * Hkv + g) * hd + i] =
-                            L->v_cache[((bi * Hkv + g) * L->cap + slot) * hd + i];
+                            cache_load(L, L->v_cache, ((bi * Hkv + g) * L->cap + slot) * hd + i);
                     }
             }
             orc_gqa_attention(q, Hq, Hkv, hd, keys, vals, n_pos, L->window, L->attn_scale,

@@ -32,6 +32,7 @@ extern "C" {
 /* IEEE binary16 -> fp64, exact ([GEM] Native Metal diagnostic: the Q4_0
  * scales are binary16).  Pinned: all 65,536 patterns vs a library conversion. */
 double orc_half_to_double(uint16_t h);
+uint16_t orc_double_to_half(double v);  /* nearest binary16, ties to even */
 
 /* Dequantise an n_rows x k Q4_0 / Q8_0 matrix (row-major block rows) to fp64.
  * Pinned: hand-worked block, unit vectors, Q4_0 vs Q8_0 cross-encoding. */
@@ -93,11 +94,12 @@ typedef struct {
     const double *ffn_norm;   /* [d_model] */
     const double *q_norm;     /* [hd] */
     const double *k_norm;     /* [hd] */
-    float *k_cache;           /* [batch][Hkv][cap][hd], slot = position mod cap */
-    float *v_cache;
+    void *k_cache;            /* [batch][Hkv][cap][hd], slot = position mod cap */
+    void *v_cache;            /* fp32, or binary16 when kv_f16 */
     int64_t n_kv_heads, head_dim, cap, window;
     double rope_theta, attn_scale;
     int32_t v_from_k;         /* 1: no v rows; v = unit-gain rmsnorm of raw k */
+    int32_t kv_f16;           /* 1: binary16 caches (rows appended rounded to nearest) */
 } orc_layer;
 
 typedef struct {

@@ -346,3 +346,61 @@ def test_attention_chunk_merge_composition():
             num += mass * oc[0]
             den += mass
         assert np.allclose(num / den, full[h], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- binary16 caches
+def test_double_to_half_matches_numpy_rounding():
+    """The oracle's nearest-binary16 rounding against numpy's float64 ->
+    float16 conversion (an independent implementation of the same IEEE
+    rounding): random magnitudes across every binade, subnormals, exact ties,
+    the overflow threshold, signed zero and NaN."""
+    rng = np.random.default_rng(11)
+    vals = list(rng.standard_normal(20000) * np.exp2(rng.integers(-30, 17, 20000)))
+    # midpoints between neighbouring halves (ties go to the even fraction)
+    for h in rng.integers(0, 0x7BFF, 2000):
+        a = np.array([h, h + 1], dtype=np.uint16).view(np.float16).astype(np.float64)
+        vals.append((a[0] + a[1]) / 2)
+        vals.append(-(a[0] + a[1]) / 2)
+    vals += [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24, 2.0 ** -25,
+             2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25]
+    got = np.array([oracle.double_to_half(v) for v in vals], dtype=np.uint16)
+    exp = np.array(vals, dtype=np.float64).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, exp)
+    nan = oracle.double_to_half(float("nan"))
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+
+
+def test_double_to_half_inverts_half_to_double():
+    for h in range(0x10000):
+        if (h & 0x7C00) == 0x7C00 and (h & 0x3FF):
+            continue  # NaN payloads are not preserved
+        assert oracle.double_to_half(oracle.half_to_double(h)) == h
+
+
+def test_decode_f16_cache_appends_rounded_rows():
+    """One step with binary16 caches: layer 0's appended rows (the same
+    inputs in both models) are the fp32-cache model's appended rows rounded
+    to binary16, up to double rounding (one unit in the last place); every
+    other slot of every layer is untouched; and the logits stay close to the
+    fp32-cache model's."""
+    from synth import workloads as wl
+    m = wl.TINY_GEMMA4
+    w = wl.model_weights(m)
+    c32 = [(wl.prefilled_cache(m, l, "k").astype(np.float16).astype(np.float32),
+            wl.prefilled_cache(m, l, "v").astype(np.float16).astype(np.float32))
+           for l in range(m.n_layers)]
+    c16 = [(k.astype(np.float16), v.astype(np.float16)) for k, v in c32]
+    before = [(k.copy(), v.copy()) for k, v in c16]
+    tok = wl.start_tokens(m)
+    _, lg32, _ = oracle.Model(wl.oracle_spec(m, w, c32)).step(m.start_pos, tok, want_logits=True)
+    _, lg16, _ = oracle.Model(wl.oracle_spec(m, w, c16)).step(m.start_pos, tok, want_logits=True)
+    for l, ly in enumerate(m.layers):
+        slot = m.start_pos % ly.cap
+        for c in (0, 1):
+            if l == 0:
+                got = c16[l][c][:, :, slot].view(np.uint16).astype(np.int64)
+                ref = c32[l][c][:, :, slot].astype(np.float16).view(np.uint16).astype(np.int64)
+                assert np.all(np.abs(got - ref) <= 1) and np.mean(got == ref) > 0.99
+            others = np.arange(ly.cap) != slot
+            assert np.array_equal(c16[l][c][:, :, others], before[l][c][:, :, others])
+    assert np.abs(lg16 - lg32).max() <= 1e-2 * np.abs(lg32).max()
