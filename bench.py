@@ -89,12 +89,12 @@ def settle(torch, fn, ms=40.0):
         torch.cuda.synchronize()
 
 
-def bench_attention_stack(q, torch, batch, reps=20):
+def bench_attention_stack(q, torch, batch, reps=20, kv16=False):
     """The 28-layer Qwen3-1.7B-shaped attention stack at n_cache = 4096: per
     layer one fused call (QK-norm + RoPE + KV append at position 4096, then
     split-K attention over the 4097 keys) reading raw q | k | v rows.  Every
-    layer has its own cache, so a pass streams 28 * B * 2 * 8 * 4097 * 128 * 4
-    bytes of K/V."""
+    layer has its own cache, so a pass streams 28 * B * 2 * 8 * 4097 * 128 * e
+    bytes of K/V (e = 4, or 2 with binary16 caches)."""
     import numpy as np
 
     from q4_quantized_matvec_amd._lib import kv_layout_of
@@ -106,6 +106,8 @@ def bench_attention_stack(q, torch, batch, reps=20):
     layers = []
     for l in range(w.n_layers):
         qh, kh, vh, qn, kn, kc, vc = wl.attn_layer_inputs(w, batch, l)
+        if kv16:
+            kc, vc = kc.astype(np.float16), vc.astype(np.float16)
         kcd = torch.from_numpy(kc).to(dev)
         qkv = np.concatenate([qh.reshape(batch, -1), kh.reshape(batch, -1), vh.reshape(batch, -1)],
                              axis=1)
@@ -137,16 +139,19 @@ def bench_attention_stack(q, torch, batch, reps=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     n = pos + 1
-    nbytes = w.n_layers * batch * (2 * hkv * hd * n * 4 + 2 * hq * hd * 4 + 4 * hkv * hd * 4)
+    e = 2 if kv16 else 4
+    nbytes = w.n_layers * batch * (2 * hkv * hd * n * e + 2 * hq * hd * 4 + 2 * hkv * hd * 4 +
+                                   2 * hkv * hd * e)
     del layers
     torch.cuda.empty_cache()
     return {"ms_per_pass": round(ms, 4), "batch": batch, "layers": w.n_layers, "n_keys": n,
+            "kv": "f16" if kv16 else "f32",
             "algorithmic_GB_per_pass": round(nbytes / 1e9, 4),
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def decode_algorithmic_bytes(m, step):
+def decode_algorithmic_bytes(m, step, kv_bytes=4):
     """Bytes one decode step must move: every weight byte (Q4_0 matrices, the
     Q8_0 logit table, the gathered embedding rows, norm gains), every visible
     KV-cache byte, the appended KV rows and the logits."""
@@ -160,11 +165,11 @@ def decode_algorithmic_bytes(m, step):
         total += q4(nq + nk + nv, d) + q4(d, nq) + q4(2 * F, d) + q4(d, F)
         total += 4 * (2 * d + 2 * ly.head_dim)
         vis = min(n, ly.window) if ly.window else n
-        total += B * ly.n_kv_heads * ly.head_dim * 4 * (2 * vis + 2)
+        total += B * ly.n_kv_heads * ly.head_dim * kv_bytes * (2 * vis + 2)
     return total
 
 
-def device_prefilled_caches(torch, m, dev):
+def device_prefilled_caches(torch, m, dev, kv16=False):
     """Per layer a (k, v) pair of device caches laid out as the host recipe's
     (positions below start_pos in slot p % cap, N(0,1); other slots 0), drawn
     by torch's seeded device generator: long contexts hold tens of GB of cache,
@@ -175,8 +180,8 @@ def device_prefilled_caches(torch, m, dev):
         pair = []
         for which in (0, 1):
             gen.manual_seed(m.seed * 1000 + 2 * l + which)
-            c = torch.zeros((m.batch, ly.n_kv_heads, ly.cap, ly.head_dim), dtype=torch.float32,
-                            device=dev)
+            c = torch.zeros((m.batch, ly.n_kv_heads, ly.cap, ly.head_dim),
+                            dtype=torch.float16 if kv16 else torch.float32, device=dev)
             filled = min(m.start_pos, ly.cap)
             c[:, :, :filled].normal_(generator=gen)
             pair.append(c)
@@ -184,16 +189,19 @@ def device_prefilled_caches(torch, m, dev):
     return caches
 
 
-def bench_decode(q, torch, m, reps=3, warmup=2, device_caches=False):
+def bench_decode(q, torch, m, reps=3, warmup=2, device_caches=False, kv16=False):
     """Times 16-step greedy decode runs from the prefilled position (HIP graph
     replay, two graphs ping-ponging the token buffers)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from decode_util import gpu_model, upload_model
+    from decode_util import gpu_model, prefilled_caches, upload_model
     from synth import workloads as wl
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     weights = wl.model_weights(m)
-    caches = device_prefilled_caches(torch, m, dev) if device_caches else None
+    if device_caches:
+        caches = device_prefilled_caches(torch, m, dev, kv16=kv16)
+    else:
+        caches = prefilled_caches(m, kv16=kv16)
     dmod = upload_model(m, weights, dev, caches=caches)
     del caches
     del weights
@@ -222,13 +230,14 @@ def bench_decode(q, torch, m, reps=3, warmup=2, device_caches=False):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / m.steps)
     ms = sorted(times)[len(times) // 2]
-    nbytes = sum(decode_algorithmic_bytes(m, s_) for s_ in range(m.steps)) / m.steps
+    nbytes = sum(decode_algorithmic_bytes(m, s_, 2 if kv16 else 4) for s_ in range(m.steps)) / m.steps
     dm.close()
     del dmod
     torch.cuda.empty_cache()
     return {"tok/s": round(m.batch * 1e3 / ms, 2), "ms_per_step": round(ms, 4), "batch": m.batch,
             "steps": m.steps, "start_pos": m.start_pos,
             "kv_fill": "device generator" if device_caches else "host recipe",
+            "kv": "f16" if kv16 else "f32",
             "algorithmic_GB_per_step": round(nbytes / 1e9, 4),
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -327,7 +336,8 @@ def main():
     ap.add_argument("--copies", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-matvec", action="store_true")
-    ap.add_argument("--decode", default="qwen3_4b,gemma4_31b,gemma4_31b_128k",
+    ap.add_argument("--decode",
+                    default="qwen3_4b,gemma4_31b,gemma4_31b_128k,qwen3_4b_f16kv,gemma4_31b_128k_f16kv",
                     help="decode workloads to time (comma list, empty for none)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the B=1 HBM-streaming matvec (for profiler runs)")
@@ -363,14 +373,20 @@ def main():
     from synth import workloads as wl
 
     dev = torch.device("cuda:0")
-    shapes = {"qwen3_4b": wl.QWEN3_4B, "gemma4_31b": wl.GEMMA4_31B,
-              "gemma4_31b_128k": wl.GEMMA4_31B_128K}
-    dev_caches = {"gemma4_31b_128k"}
+    # decode legs: key -> (workload, caches drawn on the device, binary16 caches)
+    legs = {"qwen3_4b": (wl.QWEN3_4B, False, False), "gemma4_31b": (wl.GEMMA4_31B, False, False),
+            "gemma4_31b_128k": (wl.GEMMA4_31B_128K, True, False),
+            "qwen3_4b_f16kv": (wl.QWEN3_4B, False, True),
+            "gemma4_31b_128k_f16kv": (wl.GEMMA4_31B_128K, True, True)}
     decode_keys = [k for k in args.decode.split(",") if k] if not args.only_matvec else []
+
+    def run_leg(key):
+        m, on_dev, kv16 = legs[key]
+        name = m.name + ("_f16kv" if kv16 else "")
+        return name, bench_decode(q, torch, m, device_caches=on_dev, kv16=kv16)
+
     if args.only_decode:
-        res = {shapes[k].name: bench_decode(q, torch, shapes[k], device_caches=k in dev_caches)
-               for k in decode_keys}
-        print(json.dumps({"decode": res}), flush=True)
+        print(json.dumps({"decode": dict(run_leg(k) for k in decode_keys)}), flush=True)
         return
 
     w = wl.MATVEC_5376x21504
@@ -422,21 +438,33 @@ def main():
         gbs8 = matvec_bytes(w.n, w.k, 8) / (ms8 * 1e-3) / 1e9
         out["matvec_B8"] = {"GB/s": round(gbs8, 2), "ms": round(ms8, 6),
                             "frac_hbm": round(gbs8 / HBM_PEAK_GBS, 4), "path": "mfma"}
+        for bb in (16, 32):
+            _, xb = wl.matvec_inputs(w, bb)
+            xb = torch.from_numpy(xb).to(dev)
+            yb = torch.empty((bb, w.n), dtype=torch.float32, device=dev)
+            log(f"timing B={bb} (matrix cores, batch groups of 8)")
+            msb = time_matvec_batched(q, torch, Ws, xb, yb, w.k, bb, args.steps, args.warmup)
+            gbsb = matvec_bytes(w.n, w.k, bb) / (msb * 1e-3) / 1e9
+            out[f"matvec_B{bb}"] = {"GB/s": round(gbsb, 2), "ms": round(msb, 6),
+                                    "frac_hbm": round(gbsb / HBM_PEAK_GBS, 4), "path": "mfma"}
+            del xb, yb
         out["matvec_B1_cache_resident"] = {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
                                            "ms": round(ms1r, 6)}
         del Ws
         torch.cuda.empty_cache()
         if not args.no_attention:
-            out["attn_qwen3_1p7b"] = {}
-            for bb in (1, 8):
-                log(f"timing the 28-layer attention stack, B={bb}")
-                out["attn_qwen3_1p7b"][f"B{bb}"] = bench_attention_stack(q, torch, bb)
+            for kv16 in (False, True):
+                key = "attn_qwen3_1p7b" + ("_f16kv" if kv16 else "")
+                out[key] = {}
+                for bb in (1, 8):
+                    log(f"timing the 28-layer attention stack, B={bb}, {'f16' if kv16 else 'f32'} KV")
+                    out[key][f"B{bb}"] = bench_attention_stack(q, torch, bb, kv16=kv16)
         if decode_keys:
             out["decode"] = {}
             for key in decode_keys:
                 log(f"timing decode {key}")
-                out["decode"][shapes[key].name] = bench_decode(q, torch, shapes[key],
-                                                               device_caches=key in dev_caches)
+                name, res = run_leg(key)
+                out["decode"][name] = res
     if not args.no_cpu_baseline and not args.headline_only:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline_matvec(w)

@@ -173,10 +173,15 @@ q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_
 /* KV-cache layout: element strides of a [batch][n_kv_heads][cap][head_dim]
  * style cache; the head_dim axis is contiguous.  Position p of a sequence
  * lives in slot p % cap (a cache with cap >= the positions it must hold is
- * linear; a sliding-window layer may use a ring with cap == window). */
+ * linear; a sliding-window layer may use a ring with cap == window).
+ * dtype: the cache elements, fp32 or binary16.  A binary16 cache halves the
+ * attention bytes; appended rows are computed in fp32 and rounded to the
+ * nearest binary16 (ties to even), and cached elements are read exactly. */
+typedef enum { Q4_KV_F32 = 0, Q4_KV_F16 = 1 } q4_kv_dtype;
 typedef struct {
     int64_t batch, n_kv_heads, head_dim, cap;
     int64_t stride_b, stride_h, stride_t;
+    int64_t dtype; /* q4_kv_dtype */
 } q4_kv_layout;
 
 /* qk_norm_rope: for the new token of each sequence b at device position
@@ -195,6 +200,7 @@ typedef struct {
  *   k, v     device fp32, row b at k + b*ldkv (same for v)
  *   q_norm, k_norm  device fp32 [head_dim]
  *   kv       cache layout (host struct); head_dim even, <= 512
+ *   k_cache, v_cache  device, elements of kv->dtype
  *   pos_dev  device int64 [1]; the kernel writes nothing outside the cache
  *            (a position whose slot would be out of range is not written).
  * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE (n_q_heads % n_kv_heads, odd hd),
@@ -202,7 +208,7 @@ typedef struct {
 q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
                        const float *q_norm, const float *k_norm, int64_t n_q_heads,
                        const q4_kv_layout *kv, const int64_t *pos_dev, double theta,
-                       float eps, int v_from_k, float *k_cache, float *v_cache,
+                       float eps, int v_from_k, void *k_cache, void *v_cache,
                        void *stream);
 
 /* ------------------------------------------------------------------ attention
@@ -216,15 +222,16 @@ q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v, in
  * producing (max, sum, weighted V); a second pass merges the chunks in
  * ascending order, so results are bitwise reproducible.
  *   q        device fp32, row b at q + b*ldq ([n_q_heads][head_dim])
- *   k_cache, v_cache  device fp32 with layout kv (slot = position % cap)
+ *   k_cache, v_cache  device, elements of kv->dtype, with layout kv
+ *            (slot = position % cap); 16-byte aligned, strides multiples of 4
  *   n_dev    device int64 [1]; positions outside the last cap are never read
  *   out      device fp32, row b at out + b*ldo ([n_q_heads][head_dim])
  *   ws       device workspace of at least gqa_decode_attn_workspace() bytes,
  *            256-byte aligned; contents need no initialisation
  * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_SHAPE, Q4_ERR_UNSUPPORTED (hd > 512 or
  *         hd % 4, group > 16), Q4_ERR_WORKSPACE, Q4_ERR_HIP. */
-q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads, const float *k_cache,
-                          const float *v_cache, const q4_kv_layout *kv, const int64_t *n_dev,
+q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads, const void *k_cache,
+                          const void *v_cache, const q4_kv_layout *kv, const int64_t *n_dev,
                           int64_t window, float scale, float *out, int64_t ldo, void *ws,
                           size_t ws_bytes, void *stream);
 
@@ -247,7 +254,7 @@ size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_heads, int6
 q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t n_q_heads,
                                const float *q_norm, const float *k_norm, const q4_kv_layout *kv,
                                const int64_t *pos_dev, double theta, float eps, int v_from_k,
-                               float *k_cache, float *v_cache, int64_t window, float scale,
+                               void *k_cache, void *v_cache, int64_t window, float scale,
                                float *out, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ sampling
@@ -276,12 +283,13 @@ typedef struct {
     const float *ffn_norm;   /* [d_model] */
     const float *q_norm;     /* [hd] */
     const float *k_norm;     /* [hd] */
-    float *k_cache;          /* [batch][Hkv][cap][hd], contiguous */
-    float *v_cache;          /* same layout */
+    void *k_cache;           /* [batch][Hkv][cap][hd], contiguous, elements of kv_dtype */
+    void *v_cache;           /* same layout */
     int64_t n_kv_heads, head_dim, cap, window; /* window 0 = full attention */
     double rope_theta;
     float attn_scale;
     int32_t v_from_k;        /* 1: no V rows in wqkv; V = unit-gain rmsnorm(raw K) */
+    int32_t kv_dtype;        /* q4_kv_dtype of both caches */
 } q4_layer_desc;
 
 typedef struct {

@@ -20,10 +20,13 @@ class Q4Error(RuntimeError):
         super().__init__(f"{name}: {self.status_name}: {msg}")
 
 
+KV_F32, KV_F16 = 0, 1
+
+
 class KVLayout(C.Structure):
     _fields_ = [("batch", C.c_int64), ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64),
                 ("cap", C.c_int64), ("stride_b", C.c_int64), ("stride_h", C.c_int64),
-                ("stride_t", C.c_int64)]
+                ("stride_t", C.c_int64), ("dtype", C.c_int64)]
 
 
 class LayerDesc(C.Structure):
@@ -32,7 +35,7 @@ class LayerDesc(C.Structure):
                 ("k_norm", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
                 ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64), ("cap", C.c_int64),
                 ("window", C.c_int64), ("rope_theta", C.c_double), ("attn_scale", C.c_float),
-                ("v_from_k", C.c_int32)]
+                ("v_from_k", C.c_int32), ("kv_dtype", C.c_int32)]
 
 
 class ModelDesc(C.Structure):
@@ -265,11 +268,20 @@ def swiglu(g, u, rows, n, ld, h=None, stream=None):
     return h
 
 
+def kv_dtype_of(cache):
+    import torch
+    if cache.dtype == torch.float32:
+        return KV_F32
+    if cache.dtype == torch.float16:
+        return KV_F16
+    raise TypeError(f"KV cache dtype {cache.dtype} is neither float32 nor float16")
+
+
 def kv_layout_of(cache):
-    """Layout of a contiguous fp32 cache tensor [B, Hkv, cap, hd]."""
+    """Layout of a cache tensor [B, Hkv, cap, hd] (float32 or float16, hd contiguous)."""
     B, H, cap, hd = cache.shape
     s = cache.stride()
-    return KVLayout(B, H, hd, cap, s[0], s[1], s[2])
+    return KVLayout(B, H, hd, cap, s[0], s[1], s[2], kv_dtype_of(cache))
 
 
 def qk_norm_rope(q, ldq, k, v, ldkv, q_norm, k_norm, n_q_heads, kv, pos_dev, theta, eps,
@@ -336,6 +348,9 @@ class DecodeModel:
             d.rope_theta = L["rope_theta"]
             d.attn_scale = L["attn_scale"]
             d.v_from_k = 1 if L["v_from_k"] else 0
+            d.kv_dtype = kv_dtype_of(L["k_cache"])
+            if kv_dtype_of(L["v_cache"]) != d.kv_dtype:
+                raise TypeError(f"layer {i}: k_cache and v_cache dtypes differ")
         self._layers = arr
         desc = ModelDesc(len(layers), d_model, n_q_heads, ffn, vocab, batch, eps, _ptr(embed),
                          _ptr(final_norm), C.cast(arr, C.POINTER(LayerDesc)))

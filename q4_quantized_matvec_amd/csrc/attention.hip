@@ -102,8 +102,35 @@ struct RopeArgs {
     const float *qn, *kn;      // per-head gains [hd]
     double theta;
     float eps;
-    float *kcw, *vcw;          // the caches, written at slot pos % cap
+    void *kcw, *vcw;           // the caches (element type of the layout), written at slot pos % cap
 };
+
+// Cache elements: fp32, or binary16 read into fp32 exactly and written with
+// round-to-nearest-even.  Four consecutive elements per access.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+template <typename KT>
+__device__ __forceinline__ float4 load4(const KT *p) {
+    if constexpr (sizeof(KT) == 4) {
+        return *reinterpret_cast<const float4 *>(p);
+    } else {
+        const half4_t h = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(p));
+        return make_float4(static_cast<float>(h.x), static_cast<float>(h.y), static_cast<float>(h.z),
+                           static_cast<float>(h.w));
+    }
+}
+template <typename KT>
+__device__ __forceinline__ void store4(KT *p, float a, float b, float c, float d) {
+    if constexpr (sizeof(KT) == 4) {
+        *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+    } else {
+        half4_t h;
+        h.x = static_cast<_Float16>(a);
+        h.y = static_cast<_Float16>(b);
+        h.z = static_cast<_Float16>(c);
+        h.w = static_cast<_Float16>(d);
+        *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, h);
+    }
+}
 
 // cos / sin of pos * theta^(-2i/hd): frequency by binary powers of
 // theta^(-2/hd) in fp64, angle reduced by 2 pi in fp64, then single-precision
@@ -121,9 +148,9 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double r, int i, float &cs,
     sincosf(static_cast<float>(red), &sn, &cs);
 }
 
-template <int HD, int GM, bool ROPE, bool MULTI>
+template <int HD, int GM, bool ROPE, bool MULTI, typename KT>
 __global__ __launch_bounds__(kWG) void attn_split_kernel(
-    const float *__restrict__ q, int64_t ldq, int G, const float *kc, const float *vc, int64_t cap,
+    const float *__restrict__ q, int64_t ldq, int G, const KT *kc, const KT *vc, int64_t cap,
     int64_t sb, int64_t sh, int64_t st, const int64_t *__restrict__ n_dev, int64_t window,
     float scale, int ns, int cps, float *__restrict__ part, RopeArgs ra) {
     constexpr int LPK = HD / 8;              // score pass: lanes per key, 8 elements per lane
@@ -156,8 +183,8 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         }
         return;
     }
-    const float *kb = kc + b * sb + g0 * sh;
-    const float *vb = vc + b * sb + g0 * sh;
+    const KT *kb = kc + b * sb + g0 * sh;
+    const KT *vb = vc + b * sb + g0 * sh;
     // slot of position j of the current chunk (positions past the chunk end
     // re-read its first row): one 64-bit remainder per chunk, then 32-bit
     // wrap-around
@@ -220,11 +247,11 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
             }
             if (wave == 0 && kgl == 0) {
                 const int64_t off = b * sb + static_cast<int64_t>(g0) * sh + (pos % cap) * st;
-                float *kd = ra.kcw + off, *vd = ra.vcw + off;
-                *reinterpret_cast<float4 *>(kd + sub * 4) = make_float4(kv8[0], kv8[1], kv8[2], kv8[3]);
-                *reinterpret_cast<float4 *>(kd + HD / 2 + sub * 4) = make_float4(kv8[4], kv8[5], kv8[6], kv8[7]);
-                *reinterpret_cast<float4 *>(vd + sub * 4) = make_float4(vv8[0], vv8[1], vv8[2], vv8[3]);
-                *reinterpret_cast<float4 *>(vd + HD / 2 + sub * 4) = make_float4(vv8[4], vv8[5], vv8[6], vv8[7]);
+                KT *kd = static_cast<KT *>(ra.kcw) + off, *vd = static_cast<KT *>(ra.vcw) + off;
+                store4(kd + sub * 4, kv8[0], kv8[1], kv8[2], kv8[3]);
+                store4(kd + HD / 2 + sub * 4, kv8[4], kv8[5], kv8[6], kv8[7]);
+                store4(vd + sub * 4, vv8[0], vv8[1], vv8[2], vv8[3]);
+                store4(vd + HD / 2 + sub * 4, vv8[4], vv8[5], vv8[6], vv8[7]);
             }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(0);  // the rows are written before any wavefront reads them
@@ -268,7 +295,10 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         for (int it = 0; it < SG; ++it) {
             const int jj = (i0 + it) * 4 * KPW + wave * KPW + kgl;
             // each load instruction covers contiguous bytes of the key row
-            load8(kb + slot(jj), kr[it]);
+            const KT *kp = kb + slot(jj);
+            const float4 a = load4(kp + sub * 4), c = load4(kp + HD / 2 + sub * 4);
+            kr[it][0] = a.x; kr[it][1] = a.y; kr[it][2] = a.z; kr[it][3] = a.w;
+            kr[it][4] = c.x; kr[it][5] = c.y; kr[it][6] = c.z; kr[it][7] = c.w;
         }
 #pragma unroll
         for (int it = 0; it < SG; ++it) {
@@ -316,7 +346,7 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         float4 vv[VG];
 #pragma unroll
         for (int it = 0; it < VG; ++it)
-            vv[it] = reinterpret_cast<const float4 *>(vb + slot(kg + (i0 + it) * KG))[d4];
+            vv[it] = load4(vb + slot(kg + (i0 + it) * KG) + 4 * d4);
 #pragma unroll
         for (int it = 0; it < VG; ++it) {
             const int j = kg + (i0 + it) * KG;  // weights of positions past cnt are 0
@@ -420,14 +450,14 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     }
 }
 
-template <int HD, bool ROPE, bool MULTI>
+template <int HD, bool ROPE, bool MULTI, typename KT>
 void launch_split_hd(int GM, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
-                     const float *kc, const float *vc, const q4_kv_layout &kv,
+                     const KT *kc, const KT *vc, const q4_kv_layout &kv,
                      const int64_t *n_dev, int64_t window, float scale, int ns, int cps, float *part,
                      const RopeArgs &ra) {
 #define Q4_ATTN_CASE(GG)                                                                          \
     case GG:                                                                                      \
-        hipLaunchKernelGGL((attn_split_kernel<HD, GG, ROPE, MULTI>), grid, dim3(kWG), 0, s, q, ldq, G, kc, \
+        hipLaunchKernelGGL((attn_split_kernel<HD, GG, ROPE, MULTI, KT>), grid, dim3(kWG), 0, s, q, ldq, G, kc, \
                            vc, kv.cap, kv.stride_b, kv.stride_h, kv.stride_t, n_dev, window, scale, \
                            ns, cps, part, ra);                                                    \
         break;
@@ -457,9 +487,37 @@ extern "C" size_t gqa_decode_attn_workspace(const q4_kv_layout *kv, int64_t n_q_
 }
 
 namespace {
+// The split kernel for head_dim hd, cache element type KT, with or without the
+// fused preparation, one or several chunks per split.
+template <typename KT>
+void launch_split(int64_t hd, int gm, dim3 grid, hipStream_t s, const float *q, int64_t ldq, int G,
+                  const void *k_cache, const void *v_cache, const q4_kv_layout &kv,
+                  const int64_t *n_dev, int64_t window, float scale, const AttnGeom &g, float *part,
+                  const RopeArgs *ra) {
+    const KT *kc = static_cast<const KT *>(k_cache), *vc = static_cast<const KT *>(v_cache);
+    const RopeArgs none{};
+#define Q4_ATTN_HD(H)                                                                             \
+    case H:                                                                                       \
+        if (ra && g.cps > 1)                                                                      \
+            launch_split_hd<H, true, true, KT>(gm, grid, s, q, ldq, G, kc, vc, kv, n_dev, window,  \
+                                               scale, g.ns, g.cps, part, *ra);                    \
+        else if (ra)                                                                              \
+            launch_split_hd<H, true, false, KT>(gm, grid, s, q, ldq, G, kc, vc, kv, n_dev, window, \
+                                                scale, g.ns, g.cps, part, *ra);                   \
+        else if (g.cps > 1)                                                                       \
+            launch_split_hd<H, false, true, KT>(gm, grid, s, q, ldq, G, kc, vc, kv, n_dev, window, \
+                                                scale, g.ns, g.cps, part, none);                  \
+        else                                                                                      \
+            launch_split_hd<H, false, false, KT>(gm, grid, s, q, ldq, G, kc, vc, kv, n_dev,       \
+                                                 window, scale, g.ns, g.cps, part, none);         \
+        break;
+    switch (hd) { Q4_ATTN_HD(64) Q4_ATTN_HD(128) Q4_ATTN_HD(256) Q4_ATTN_HD(512) }
+#undef Q4_ATTN_HD
+}
+
 // Validation and launch shared by gqa_decode_attn and gqa_decode_attn_rope.
 q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_heads,
-                     const float *k_cache, const float *v_cache, const q4_kv_layout *kv,
+                     const void *k_cache, const void *v_cache, const q4_kv_layout *kv,
                      const int64_t *n_dev, int64_t window, float scale, float *out, int64_t ldo,
                      void *ws, size_t ws_bytes, void *stream, const RopeArgs *ra) {
     q4_status st = q4::check_kv_layout(name, kv);
@@ -490,24 +548,12 @@ q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_
     hipStream_t s = q4::as_stream(stream);
     float *part = static_cast<float *>(ws);
     dim3 grid(g.ns, static_cast<unsigned>(kv->n_kv_heads), static_cast<unsigned>(kv->batch));
-    const RopeArgs none{};
-#define Q4_ATTN_HD(H)                                                                             \
-    case H:                                                                                       \
-        if (ra && g.cps > 1)                                                                      \
-            launch_split_hd<H, true, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev,  \
-                                           window, scale, g.ns, g.cps, part, *ra);                \
-        else if (ra)                                                                              \
-            launch_split_hd<H, true, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, \
-                                            window, scale, g.ns, g.cps, part, *ra);               \
-        else if (g.cps > 1)                                                                       \
-            launch_split_hd<H, false, true>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, \
-                                            window, scale, g.ns, g.cps, part, none);              \
-        else                                                                                      \
-            launch_split_hd<H, false, false>(gm, grid, s, q, ldq, G, k_cache, v_cache, *kv,       \
-                                             n_dev, window, scale, g.ns, g.cps, part, none);      \
-        break;
-    switch (hd) { Q4_ATTN_HD(64) Q4_ATTN_HD(128) Q4_ATTN_HD(256) Q4_ATTN_HD(512) }
-#undef Q4_ATTN_HD
+    if (kv->dtype == Q4_KV_F16)
+        launch_split<_Float16>(hd, gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale,
+                               g, part, ra);
+    else
+        launch_split<float>(hd, gm, grid, s, q, ldq, G, k_cache, v_cache, *kv, n_dev, window, scale, g,
+                            part, ra);
     q4_status ls = q4::launch_status(name);
     if (ls != Q4_OK) return ls;
     hipLaunchKernelGGL(attn_merge_kernel,
@@ -520,7 +566,7 @@ q4_status attn_entry(const char *name, const float *q, int64_t ldq, int64_t n_q_
 }  // namespace
 
 extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_heads,
-                                     const float *k_cache, const float *v_cache,
+                                     const void *k_cache, const void *v_cache,
                                      const q4_kv_layout *kv, const int64_t *n_dev, int64_t window,
                                      float scale, float *out, int64_t ldo, void *ws,
                                      size_t ws_bytes, void *stream) {
@@ -532,8 +578,8 @@ extern "C" q4_status gqa_decode_attn(const float *q, int64_t ldq, int64_t n_q_he
 extern "C" q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t n_q_heads,
                                           const float *q_norm, const float *k_norm,
                                           const q4_kv_layout *kv, const int64_t *pos_dev,
-                                          double theta, float eps, int v_from_k, float *k_cache,
-                                          float *v_cache, int64_t window, float scale, float *out,
+                                          double theta, float eps, int v_from_k, void *k_cache,
+                                          void *v_cache, int64_t window, float scale, float *out,
                                           int64_t ldo, void *ws, size_t ws_bytes, void *stream) {
     q4::clear_error();
     const char *name = "gqa_decode_attn_rope";

@@ -74,6 +74,7 @@ q4_kv_layout layer_kv(const q4_model_desc &d, const q4_layer_desc &l) {
     kv.stride_t = l.head_dim;
     kv.stride_h = l.cap * l.head_dim;
     kv.stride_b = l.n_kv_heads * l.cap * l.head_dim;
+    kv.dtype = l.kv_dtype;
     return kv;
 }
 
@@ -153,6 +154,8 @@ q4_status validate(const q4_model_desc *d) {
                  "decode model: layer %lld: more than 16 query heads per kv head", (long long)i);
         Q4_CHECK(l.cap >= 1 && l.window >= 0 && l.rope_theta > 0.0, Q4_ERR_INVALID_ARG,
                  "decode model: layer %lld: cap >= 1, window >= 0, rope_theta > 0", (long long)i);
+        Q4_CHECK(l.kv_dtype == Q4_KV_F32 || l.kv_dtype == Q4_KV_F16, Q4_ERR_INVALID_ARG,
+                 "decode model: layer %lld: kv_dtype %d unknown", (long long)i, (int)l.kv_dtype);
         Q4_CHECK(q4::aligned(l.k_cache, 16) && q4::aligned(l.v_cache, 16) && q4::aligned(l.wqkv, 2) &&
                      q4::aligned(l.wo, 2) && q4::aligned(l.wgu, 2) && q4::aligned(l.wd, 2) &&
                      q4::aligned(l.attn_norm, 4) && q4::aligned(l.ffn_norm, 4) &&

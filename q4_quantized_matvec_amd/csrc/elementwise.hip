@@ -53,11 +53,14 @@ __global__ __launch_bounds__(kWG) void swiglu_kernel(const float *g, const float
 // value row) are appended to the caches at slot pos % cap.
 constexpr int kMaxPairsPerLane = 4;  // head_dim <= 512
 
+// KT: the caches' element type (fp32, or binary16 written with round to
+// nearest even).
+template <typename KT>
 __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
     const float *__restrict__ qn, const float *__restrict__ kn, int Hq, int hd,
     const int64_t *__restrict__ pos_dev, double theta, float eps, int v_from_k,
-    float *kc, float *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st) {
+    KT *kc, KT *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st) {
     const int b = blockIdx.y;
     const int head = blockIdx.x;
     const int lane = threadIdx.x;
@@ -94,13 +97,13 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
 #pragma unroll
     for (int k = 1; k < 9; ++k) rp[k] = rp[k - 1] * rp[k - 1];
 
-    float *dst = nullptr;
-    float *vdst = nullptr;
+    float *dst = nullptr;  // the query row, in place
+    KT *kdst = nullptr, *vdst = nullptr;
     if (is_q) {
         dst = q + b * ldq + static_cast<int64_t>(head) * hd;
     } else if (pos >= 0) {
         const int64_t base = b * sb + g * sh + (pos % cap) * st;
-        dst = kc + base;
+        kdst = kc + base;
         vdst = vc + base;
     }
 #pragma unroll
@@ -121,14 +124,18 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
                 dst[i] = x0 * cs - x1 * sn;
                 dst[i + half] = x1 * cs + x0 * sn;
             }
+            if (kdst) {
+                kdst[i] = static_cast<KT>(x0 * cs - x1 * sn);
+                kdst[i + half] = static_cast<KT>(x1 * cs + x0 * sn);
+            }
             if (vdst) {
                 if (v_from_k) {
-                    vdst[i] = a[p] * inv;
-                    vdst[i + half] = c[p] * inv;
+                    vdst[i] = static_cast<KT>(a[p] * inv);
+                    vdst[i + half] = static_cast<KT>(c[p] * inv);
                 } else {
                     const float *vs = v + b * ldkv + static_cast<int64_t>(g) * hd;
-                    vdst[i] = vs[i];
-                    vdst[i + half] = vs[i + half];
+                    vdst[i] = static_cast<KT>(vs[i]);
+                    vdst[i + half] = static_cast<KT>(vs[i + half]);
                 }
             }
         }
@@ -243,6 +250,8 @@ q4_status check_kv_layout(const char *name, const q4_kv_layout *kv) {
              (long long)kv->head_dim);
     Q4_CHECK(kv->batch <= 65535 && kv->n_kv_heads <= 4096 && kv->cap <= (int64_t(1) << 30),
              Q4_ERR_UNSUPPORTED, "%s: batch, kv heads or capacity too large", name);
+    Q4_CHECK(kv->dtype == Q4_KV_F32 || kv->dtype == Q4_KV_F16, Q4_ERR_INVALID_ARG,
+             "%s: kv dtype %lld is neither Q4_KV_F32 nor Q4_KV_F16", name, (long long)kv->dtype);
     return Q4_OK;
 }
 }  // namespace q4
@@ -251,7 +260,7 @@ extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const f
                                   int64_t ldkv, const float *q_norm, const float *k_norm,
                                   int64_t n_q_heads, const q4_kv_layout *kv,
                                   const int64_t *pos_dev, double theta, float eps, int v_from_k,
-                                  float *k_cache, float *v_cache, void *stream) {
+                                  void *k_cache, void *v_cache, void *stream) {
     q4::clear_error();
     q4_status st = q4::check_kv_layout("qk_norm_rope", kv);
     if (st != Q4_OK) return st;
@@ -267,10 +276,18 @@ extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const f
     Q4_CHECK(theta > 0.0 && eps >= 0.f, Q4_ERR_INVALID_ARG, "qk_norm_rope: theta > 0, eps >= 0");
     Q4_CHECK(n_q_heads + kv->n_kv_heads <= 65535, Q4_ERR_UNSUPPORTED, "qk_norm_rope: too many heads");
     dim3 grid(static_cast<unsigned>(n_q_heads + kv->n_kv_heads), static_cast<unsigned>(kv->batch));
-    hipLaunchKernelGGL(qk_norm_rope_kernel, grid, dim3(64), 0, q4::as_stream(stream), q, ldq, k, v,
-                       ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
-                       static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
-                       k_cache, v_cache, kv->cap, kv->stride_b, kv->stride_h, kv->stride_t);
+    if (kv->dtype == Q4_KV_F16)
+        hipLaunchKernelGGL(qk_norm_rope_kernel<_Float16>, grid, dim3(64), 0, q4::as_stream(stream), q,
+                           ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
+                           static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
+                           static_cast<_Float16 *>(k_cache), static_cast<_Float16 *>(v_cache), kv->cap,
+                           kv->stride_b, kv->stride_h, kv->stride_t);
+    else
+        hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(64), 0, q4::as_stream(stream), q,
+                           ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
+                           static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
+                           static_cast<float *>(k_cache), static_cast<float *>(v_cache), kv->cap,
+                           kv->stride_b, kv->stride_h, kv->stride_t);
     return q4::launch_status("qk_norm_rope");
 }
 

@@ -58,8 +58,22 @@ def run_gpu(q, m, dev_model, steps, eager=False, want_logits=True):
     return np.stack(toks), (np.stack(lgs) if want_logits else None)
 
 
-def run_oracle(oracle, m, weights, steps, want_logits=True):
-    caches = [(wl.prefilled_cache(m, l, "k"), wl.prefilled_cache(m, l, "v")) for l in range(m.n_layers)]
+def prefilled_caches(m, kv16=False):
+    """Host caches of every layer from the workload recipe; kv16 rounds them
+    to the nearest binary16 (numpy's conversion)."""
+    out = []
+    for l in range(m.n_layers):
+        k, v = wl.prefilled_cache(m, l, "k"), wl.prefilled_cache(m, l, "v")
+        if kv16:
+            k, v = k.astype(np.float16), v.astype(np.float16)
+        out.append((k, v))
+    return out
+
+
+def run_oracle(oracle, m, weights, steps, want_logits=True, caches=None):
+    """Greedy loop of the oracle; ``caches`` (modified in place) default to the recipe's."""
+    if caches is None:
+        caches = prefilled_caches(m)
     om = oracle.Model(wl.oracle_spec(m, weights, caches))
     tok = wl.start_tokens(m)
     toks, lgs, margins = [], [], []

@@ -17,7 +17,7 @@ import q4_quantized_matvec_amd as q
 from q4_quantized_matvec_amd._lib import kv_layout_of
 from synth import workloads as wl
 
-from decode_util import gpu_model, run_gpu, run_oracle, upload_model
+from decode_util import gpu_model, prefilled_caches, run_gpu, run_oracle, upload_model
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,44 @@ def test_decode_tokens_match_oracle(dev, shape):
          f"min margin {margins.min():.4f}")
     assert np.array_equal(toks_g, toks_o)
     assert nmse < 1e-8
+
+
+@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG],
+                         ids=lambda s: s.name)
+def test_decode_f16_kv_matches_oracle(dev, shape):
+    """Binary16 KV caches on both sides (the same prefilled values; each side
+    appends its rows rounded to the nearest binary16).  Where the GPU's fp32
+    row and the oracle's fp64 row fall on the two sides of a rounding
+    midpoint the appended elements differ by one unit in the last place
+    (2^-10 relative), and that difference carries through later steps; so
+    besides identical tokens the logits must be much closer to the oracle's
+    binary16 decode than binary16 caching itself moves them (the oracle's
+    binary16 decode against its fp32 one)."""
+    _say(f"decode {shape.name} with binary16 caches: {shape.steps} steps")
+    weights = wl.model_weights(shape)
+    orc_caches = prefilled_caches(shape, kv16=True)
+    toks_o, lg_o, margins = run_oracle(oracle, shape, weights, shape.steps, caches=orc_caches)
+    _, lg_o32, _ = run_oracle(oracle, shape, weights, shape.steps)
+    dmod = upload_model(shape, weights, dev, caches=prefilled_caches(shape, kv16=True))
+    assert all(L["k_cache"].dtype == torch.float16 for L in dmod["layers"])
+    toks_g, lg_g = run_gpu(q, shape, dmod, shape.steps)
+    nmse = _nmse(lg_g.astype(np.float64), lg_o)
+    effect = _nmse(lg_o, lg_o32)
+    # layer 0 of the first step sees the same inputs on both sides: its
+    # appended elements agree to one unit in the last place
+    ly0 = shape.layers[0]
+    slot = shape.start_pos % ly0.cap
+    ulps = []
+    for c, key in enumerate(("k_cache", "v_cache")):
+        g16 = dmod["layers"][0][key][:, :, slot].cpu().numpy().view(np.uint16).astype(np.int64)
+        o16 = orc_caches[0][c][:, :, slot].view(np.uint16).astype(np.int64)
+        ulps.append(int(np.abs(g16 - o16).max()))
+    _say(f"  tokens gpu {toks_g.tolist()} oracle {toks_o.tolist()} nmse {nmse:.3e} "
+         f"(binary16 caching itself: {effect:.3e}) min margin {margins.min():.4f}; "
+         f"layer 0 first appended rows differ by <= {max(ulps)} ulp")
+    assert max(ulps) <= 1
+    assert np.array_equal(toks_g, toks_o)
+    assert nmse < 0.1 * effect
 
 
 @pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG,

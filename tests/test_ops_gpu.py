@@ -56,7 +56,7 @@ def test_swiglu_parity_merged_rows(dev, rows, n):
     assert np.all(np.abs(_np(h) - ref) <= 2e-4 * np.abs(ref) + 1e-6)
 
 
-def _qk_case(dev, B, hq, hkv, hd, cap, pos, theta, v_from_k, seed):
+def _qk_case(dev, B, hq, hkv, hd, cap, pos, theta, v_from_k, seed, kv16=False):
     nq, nk = hq * hd, hkv * hd
     ld = nq + nk + (0 if v_from_k else nk)
     rows = synth.normal_f32(seed, f"qk.rows.{hd}.{pos}", (B, ld)) * 2.0
@@ -64,6 +64,8 @@ def _qk_case(dev, B, hq, hkv, hd, cap, pos, theta, v_from_k, seed):
     kn = synth.uniform_f32(seed, f"qk.kn.{hd}", (hd,), 0.8, 1.2)
     kc = synth.normal_f32(seed, f"qk.kc.{hd}", (B, hkv, cap, hd))
     vc = synth.normal_f32(seed, f"qk.vc.{hd}", (B, hkv, cap, hd))
+    if kv16:
+        kc, vc = kc.astype(np.float16), vc.astype(np.float16)
     rows_d = torch.from_numpy(rows).to(dev)
     kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
     pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
@@ -268,4 +270,125 @@ def test_gqa_decode_attn_rope_parity(dev, B, hq, hkv, hd, cap, pos, window, v_fr
                                 window, scale, cap)
         err = np.abs(got[b].reshape(hq, hd) - o)
         worst = max(worst, float((err / (2e-4 * bound + 1e-6)).max()))
+    assert worst <= 1.0, f"max err/tol {worst:.3e}"
+
+
+# ---------------------------------------------------------------- binary16 KV caches
+# Cached elements are read exactly (the oracle gets the same binary16 values
+# as fp64); appended rows are computed in fp32 and rounded to the nearest
+# binary16, so their bound adds half a unit in the last place, 2^-11 |x|.
+F16_ULP = 2.0 ** -11
+
+
+@pytest.mark.parametrize("hd", [128, 512])
+@pytest.mark.parametrize("pos,theta", [(7, 1e4), (8200, 1e6)])
+@pytest.mark.parametrize("v_from_k", [False, True])
+def test_qk_norm_rope_f16_cache(dev, hd, pos, theta, v_from_k):
+    _say(f"qk_norm_rope f16 cache hd={hd} pos={pos} v_from_k={v_from_k}")
+    B, hq, hkv, cap = 2, 4, 2, 16
+    rows, qn, kn, kc0, vc0, got, kc, vc = _qk_case(dev, B, hq, hkv, hd, cap, pos, theta,
+                                                    v_from_k, 214, kv16=True)
+    nq, nk = hq * hd, hkv * hd
+    slot = pos % cap
+    for b in range(B):
+        qnorm = oracle.rmsnorm(rows[b, :nq].reshape(hq, hd), qn, 1e-6)
+        qref = oracle.rope_neox(qnorm, pos, theta)
+        assert np.all(np.abs(got[b, :nq].reshape(hq, hd) - qref) <= _rope_tol(qnorm, pos, theta))
+        kr = rows[b, nq:nq + nk].reshape(hkv, hd)
+        knorm = oracle.rmsnorm(kr, kn, 1e-6)
+        kref = oracle.rope_neox(knorm, pos, theta)
+        assert np.all(np.abs(kc[b, :, slot] - kref) <= _rope_tol(knorm, pos, theta) +
+                      F16_ULP * np.abs(kref))
+        vref = (oracle.rmsnorm(kr, None, 1e-6) if v_from_k
+                else rows[b, nq + nk:].reshape(hkv, hd).astype(np.float64))
+        assert np.all(np.abs(vc[b, :, slot] - vref) <= (2e-4 + F16_ULP) * np.abs(vref) + 1e-6)
+    others = np.arange(cap) != slot
+    assert np.array_equal(kc[:, :, others], kc0[:, :, others].astype(np.float64))
+    assert np.array_equal(vc[:, :, others], vc0[:, :, others].astype(np.float64))
+
+
+F16_ATTN_CASES = [
+    # (B, Hq, Hkv, hd, cap, n, window)
+    (1, 16, 8, 128, 4097, 4097, 0),      # the 1.7B-shaped layer
+    (3, 16, 8, 128, 300, 257, 0),        # ragged chunk tail
+    (1, 32, 16, 256, 1024, 3000, 1024),  # sliding window, wrapped ring
+    (1, 32, 4, 512, 8208, 8193, 0),      # 31B full layer
+    (8, 32, 8, 128, 2064, 2049, 0),      # Qwen3-4B-shaped, B = 8
+    (1, 16, 8, 128, 40000, 33001, 0),    # multi-chunk splits, ragged
+    (1, 32, 4, 512, 65552, 65536, 0),    # 31B full layer at 64K keys
+]
+
+
+@pytest.mark.parametrize("B,hq,hkv,hd,cap,n,window", F16_ATTN_CASES)
+def test_gqa_decode_attn_f16_cache_parity(dev, B, hq, hkv, hd, cap, n, window):
+    _say(f"gqa_decode_attn f16 cache B={B} Hq={hq} Hkv={hkv} hd={hd} cap={cap} n={n}")
+    seed = 215
+    qv = synth.normal_f32(seed, f"att16.q.{hd}.{hq}", (B, hq * hd))
+    kc = synth.normal_f32(seed, f"att16.k.{hd}.{cap}", (B, hkv, cap, hd)).astype(np.float16)
+    vc = synth.normal_f32(seed, f"att16.v.{hd}.{cap}", (B, hkv, cap, hd)).astype(np.float16)
+    scale = 1.0 / math.sqrt(hd) if window == 0 else 1.0
+    kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    kv = kv_layout_of(kc_d)
+    assert kv.dtype == 1
+    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, hq * hd), dtype=torch.float32, device=dev)
+    n_d = torch.tensor([n], dtype=torch.int64, device=dev)
+    q.gqa_decode_attn(torch.from_numpy(qv).to(dev), hq * hd, hq, kc_d, vc_d, kv, n_d, window, scale,
+                      out, hq * hd, ws)
+    torch.cuda.synchronize()
+    got = _np(out)
+    worst = 0.0
+    for b in range(B):
+        o, bound = _attn_oracle(qv[b].reshape(hq, hd).astype(np.float64), kc[b].astype(np.float64),
+                                vc[b].astype(np.float64), n, window, scale, cap)
+        worst = max(worst, float((np.abs(got[b].reshape(hq, hd) - o) / (2e-4 * bound + 1e-6)).max()))
+    assert worst <= 1.0, f"max err/tol {worst:.3e}"
+
+
+@pytest.mark.parametrize("B,hq,hkv,hd,cap,pos,window,v_from_k,theta", [
+    (1, 16, 8, 128, 4097, 4096, 0, False, 1e6),
+    (1, 32, 16, 256, 1024, 3000, 1024, False, 1e4),
+    (1, 32, 4, 512, 8208, 8192, 0, True, 1e6),
+    (8, 32, 8, 128, 2064, 2048, 0, False, 1e6),
+    (1, 32, 4, 512, 65552, 65536, 0, True, 1e6),
+])
+def test_gqa_decode_attn_rope_f16_cache(dev, B, hq, hkv, hd, cap, pos, window, v_from_k, theta):
+    """Fused preparation, binary16 append and attention over binary16 caches."""
+    _say(f"gqa_decode_attn_rope f16 cache B={B} Hq={hq} Hkv={hkv} hd={hd} cap={cap} pos={pos}")
+    seed = 216
+    nq, nk = hq * hd, hkv * hd
+    ld = nq + nk + (0 if v_from_k else nk)
+    rows = synth.normal_f32(seed, f"ra16.rows.{hd}.{pos}", (B, ld)) * 2.0
+    qn = synth.uniform_f32(seed, f"ra16.qn.{hd}", (hd,), 0.8, 1.2)
+    kn = synth.uniform_f32(seed, f"ra16.kn.{hd}", (hd,), 0.8, 1.2)
+    kc0 = synth.normal_f32(seed, f"ra16.kc.{hd}.{cap}", (B, hkv, cap, hd)).astype(np.float16)
+    vc0 = synth.normal_f32(seed, f"ra16.vc.{hd}.{cap}", (B, hkv, cap, hd)).astype(np.float16)
+    scale = 1.0 / math.sqrt(hd) if not v_from_k else 1.0
+    kc_d, vc_d = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    kv = kv_layout_of(kc_d)
+    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, nq), dtype=torch.float32, device=dev)
+    pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
+    q.gqa_decode_attn_rope(torch.from_numpy(rows).to(dev), ld, hq, torch.from_numpy(qn).to(dev),
+                           torch.from_numpy(kn).to(dev), kv, pos_d, theta, 1e-6, v_from_k, kc_d, vc_d,
+                           window, scale, out, nq, ws)
+    torch.cuda.synchronize()
+    kc, vc, got = _np(kc_d), _np(vc_d), _np(out)
+    slot = pos % cap
+    others = np.arange(cap) != slot
+    assert np.array_equal(kc[:, :, others], kc0[:, :, others].astype(np.float64))
+    assert np.array_equal(vc[:, :, others], vc0[:, :, others].astype(np.float64))
+    worst = 0.0
+    for b in range(B):
+        kr = rows[b, nq:nq + nk].reshape(hkv, hd)
+        knorm = oracle.rmsnorm(kr, kn, 1e-6)
+        kref = oracle.rope_neox(knorm, pos, theta)
+        assert np.all(np.abs(kc[b, :, slot] - kref) <= _rope_tol(knorm, pos, theta) +
+                      F16_ULP * np.abs(kref))
+        vref = (oracle.rmsnorm(kr, None, 1e-6) if v_from_k
+                else rows[b, nq + nk:].reshape(hkv, hd).astype(np.float64))
+        assert np.all(np.abs(vc[b, :, slot] - vref) <= (2e-4 + F16_ULP) * np.abs(vref) + 1e-6)
+        qref = oracle.rope_neox(oracle.rmsnorm(rows[b, :nq].reshape(hq, hd), qn, 1e-6), pos, theta)
+        o, bound = _attn_oracle(qref, kc[b], vc[b], pos + 1, window, scale, cap)
+        worst = max(worst, float((np.abs(got[b].reshape(hq, hd) - o) / (2e-4 * bound + 1e-6)).max()))
     assert worst <= 1.0, f"max err/tol {worst:.3e}"
