@@ -41,14 +41,16 @@ class _Layer(C.Structure):
                 ("k_norm", _dbl_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
                 ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64), ("cap", C.c_int64),
                 ("window", C.c_int64), ("rope_theta", C.c_double), ("attn_scale", C.c_double),
-                ("v_from_k", C.c_int32), ("kv_f16", C.c_int32)]
+                ("v_from_k", C.c_int32), ("kv_f16", C.c_int32), ("rope_dims", C.c_int64),
+                ("post_attn_norm", _dbl_p), ("post_ffn_norm", _dbl_p)]
 
 
 class _Model(C.Structure):
     _fields_ = [("n_layers", C.c_int64), ("d_model", C.c_int64), ("n_q_heads", C.c_int64),
                 ("ffn", C.c_int64), ("vocab", C.c_int64), ("batch", C.c_int64),
                 ("eps", C.c_double), ("embed", _u8_p), ("final_norm", _dbl_p),
-                ("layers", C.POINTER(_Layer))]
+                ("layers", C.POINTER(_Layer)), ("ffn_act", C.c_int32),
+                ("embed_scale", C.c_double), ("logit_softcap", C.c_double)]
 
 
 _lib = None
@@ -73,6 +75,8 @@ def lib():
         L.orc_rmsnorm.argtypes = [_dbl_p, _dbl_p, C.c_int64, C.c_int64, C.c_double, _dbl_p]
         L.orc_rope_neox.argtypes = [_dbl_p, C.c_int64, C.c_int64, C.c_double]
         L.orc_swiglu.argtypes = [_dbl_p, _dbl_p, C.c_int64, _dbl_p]
+        L.orc_geglu.argtypes = [_dbl_p, _dbl_p, C.c_int64, _dbl_p]
+        L.orc_softcap.argtypes = [_dbl_p, C.c_int64, C.c_double]
         L.orc_argmax.argtypes = [_dbl_p, C.c_int64, _dbl_p]
         L.orc_argmax.restype = C.c_int64
         L.orc_gqa_attention.argtypes = [_dbl_p, C.c_int64, C.c_int64, C.c_int64, _dbl_p,
@@ -171,14 +175,16 @@ def rmsnorm(x, w, eps):
     return y
 
 
-def rope_neox(x, pos, theta):
-    """Rotate every head vector (last axis) of x at position pos."""
+def rope_neox(x, pos, theta, rot_dims=0):
+    """Rotate every head vector (last axis) of x at position pos; with
+    rot_dims (p-RoPE) only the first rot_dims elements rotate."""
     y = _f64(x).copy()
     hd = y.shape[-1]
+    rot = rot_dims if rot_dims else hd
     flat = y.reshape(-1, hd)
     for r in range(flat.shape[0]):
         row = np.ascontiguousarray(flat[r])
-        lib().orc_rope_neox(_p(row, _dbl_p), hd, int(pos), theta)
+        lib().orc_rope_neox(_p(row, _dbl_p), rot, int(pos), theta)
         flat[r] = row
     return flat.reshape(y.shape)
 
@@ -189,6 +195,20 @@ def swiglu(g, u):
     h = np.empty_like(g)
     lib().orc_swiglu(_p(g, _dbl_p), _p(u, _dbl_p), g.size, _p(h, _dbl_p))
     return h
+
+
+def geglu(g, u):
+    g = _f64(g)
+    u = _f64(u)
+    h = np.empty_like(g)
+    lib().orc_geglu(_p(g, _dbl_p), _p(u, _dbl_p), g.size, _p(h, _dbl_p))
+    return h
+
+
+def softcap(v, c):
+    y = _f64(v).copy()
+    lib().orc_softcap(_p(y, _dbl_p), y.size, float(c))
+    return y
 
 
 def argmax(v):
@@ -253,6 +273,12 @@ class Model:
             ly.rope_theta = L["rope_theta"]
             ly.attn_scale = L["attn_scale"]
             ly.v_from_k = 1 if L["v_from_k"] else 0
+            # Gemma-4 block variants (absent keys: the plain pre-norm block)
+            ly.rope_dims = int(L.get("rope_dims", 0) or 0)
+            for key in ("post_attn_norm", "post_ffn_norm"):
+                if L.get(key) is not None:
+                    arrs[key] = _f64(L[key])
+                    setattr(ly, key, _p(arrs[key], _dbl_p))
         self._layers = layers
         self.embed = _u8(spec["embed"])
         self.final_norm = _f64(spec["final_norm"])
@@ -267,6 +293,9 @@ class Model:
         m.embed = _p(self.embed, _u8_p)
         m.final_norm = _p(self.final_norm, _dbl_p)
         m.layers = C.cast(layers, C.POINTER(_Layer))
+        m.ffn_act = {"silu": 0, "gelu_tanh": 1}[spec.get("ffn_act", "silu")]
+        m.embed_scale = float(spec.get("embed_scale", 0.0) or 0.0)
+        m.logit_softcap = float(spec.get("logit_softcap", 0.0) or 0.0)
         self._m = m
         self.batch = spec["batch"]
         self.vocab = spec["vocab"]

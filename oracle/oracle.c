@@ -207,6 +207,25 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *h) {
         h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
 }
 
+/* GeGLU with the tanh form of GELU ([GELO] generation page, Gemma 4
+ * blockers: the FFN activation is gelu_pytorch_tanh rather than SiLU; the
+ * tanh form is Hendrycks and Gimpel's approximation):
+ * h = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u. */
+void orc_geglu(const double *g, const double *u, int64_t n, double *h) {
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    for (int64_t i = 0; i < n; ++i) {
+        double z = g[i];
+        h[i] = 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z))) * u[i];
+    }
+}
+
+/* Final-logit soft capping ([GELO] generation page, Gemma 4 developed list:
+ * final_logit_softcapping wired through the logits): l <- c tanh(l / c). */
+void orc_softcap(double *v, int64_t n, double c) {
+    for (int64_t i = 0; i < n; ++i)
+        v[i] = c * tanh(v[i] / c);
+}
+
 /* Greedy choice ([GELO] 05: greedy sampler; [GEM] Native Metal diagnostic:
  * equal logits resolve deterministically by token id -> lowest id wins). */
 int64_t orc_argmax(const double *v, int64_t n, double *margin) {
@@ -298,6 +317,16 @@ static void cache_store(const orc_layer *L, void *c, int64_t i, double v) {
         ((float *)c)[i] = (float)v;
 }
 
+/* x += rmsnorm(y) * w, row by row (a post-norm joining the residual). */
+static void post_norm_add(double *x, const double *y, const double *w, int64_t B, int64_t D,
+                          double eps) {
+    double *t = (double *)malloc(sizeof(double) * (size_t)(B * D));
+    orc_rmsnorm(y, w, B, D, eps, t);
+    for (int64_t i = 0; i < B * D; ++i)
+        x[i] += t[i];
+    free(t);
+}
+
 /* One decode step.  Block topology ([GELO] 06 Compute flow: pre-LN block,
  * QKV projection, per-head QK-norm before RoPE, GQA attention over the cache
  * plus the new row, O projection with residual, pre-FFN norm, gate/up,
@@ -310,11 +339,18 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
     double *x = (double *)malloc(sizeof(double) * (size_t)(B * D));
     double *xn = (double *)malloc(sizeof(double) * (size_t)(B * D));
     orc_q8_0_gather(m->embed, m->vocab, D, tok, B, x);
+    if (m->embed_scale != 0.0)  /* Gemma: the gathered rows are scaled (by sqrt(d)) */
+        for (int64_t i = 0; i < B * D; ++i)
+            x[i] *= m->embed_scale;
 
     for (int64_t l = 0; l < m->n_layers; ++l) {
         const orc_layer *L = &m->layers[l];
         int64_t hd = L->head_dim, Hkv = L->n_kv_heads;
         int64_t nq = Hq * hd, nk = Hkv * hd, nv = L->v_from_k ? 0 : nk;
+        /* p-RoPE ([GELO] generation page, glossary: only the first p * d_head
+         * dims rotate, the rest pass through): the first rot dims rotate as a
+         * NeoX rotation of a rot-dimensional vector */
+        int64_t rot = L->rope_dims > 0 ? L->rope_dims : hd;
         int64_t nqkv = nq + nk + nv;
         double *qkv = (double *)malloc(sizeof(double) * (size_t)(B * nqkv));
         double *att = (double *)malloc(sizeof(double) * (size_t)(B * nq));
@@ -334,7 +370,7 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
             double *vr = L->v_from_k ? NULL : kr + nk;
             for (int64_t h = 0; h < Hq; ++h) {
                 orc_rmsnorm(q + h * hd, L->q_norm, 1, hd, m->eps, tmp);
-                orc_rope_neox(tmp, hd, pos, L->rope_theta);
+                orc_rope_neox(tmp, rot, pos, L->rope_theta);
                 memcpy(q + h * hd, tmp, sizeof(double) * (size_t)hd);
             }
             for (int64_t g = 0; g < Hkv; ++g) {
@@ -343,7 +379,7 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
                 else
                     memcpy(vrow, vr + g * hd, sizeof(double) * (size_t)hd);
                 orc_rmsnorm(kr + g * hd, L->k_norm, 1, hd, m->eps, tmp);
-                orc_rope_neox(tmp, hd, pos, L->rope_theta);
+                orc_rope_neox(tmp, rot, pos, L->rope_theta);
                 /* the appended row is stored rounded to the cache's
                  * element type (fp32, or the nearest binary16) */
                 int64_t slot = pos % L->cap;
@@ -371,17 +407,34 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
         free(tmp);
         free(vrow);
 
-        orc_q4_0_matvec(L->wo, D, nq, att, B, x, xn, NULL);
-        memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+        /* sandwich norms ([GEM] 31B trace: post-attention RMSNorm, residual
+         * add, FFN RMSNorm): with a post-norm gain the sublayer output is
+         * RMS-normalised before it joins the residual */
+        if (L->post_attn_norm) {
+            orc_q4_0_matvec(L->wo, D, nq, att, B, NULL, xn, NULL);
+            post_norm_add(x, xn, L->post_attn_norm, B, D, m->eps);
+        } else {
+            orc_q4_0_matvec(L->wo, D, nq, att, B, x, xn, NULL);
+            memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+        }
 
         double *gu = (double *)malloc(sizeof(double) * (size_t)(B * 2 * F));
         double *hh = (double *)malloc(sizeof(double) * (size_t)(B * F));
         orc_rmsnorm(x, L->ffn_norm, B, D, m->eps, xn);
         orc_q4_0_matvec(L->wgu, 2 * F, D, xn, B, NULL, gu, NULL);
-        for (int64_t bi = 0; bi < B; ++bi)
-            orc_swiglu(gu + bi * 2 * F, gu + bi * 2 * F + F, F, hh + bi * F);
-        orc_q4_0_matvec(L->wd, D, F, hh, B, x, xn, NULL);
-        memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+        for (int64_t bi = 0; bi < B; ++bi) {
+            if (m->ffn_act == 1)
+                orc_geglu(gu + bi * 2 * F, gu + bi * 2 * F + F, F, hh + bi * F);
+            else
+                orc_swiglu(gu + bi * 2 * F, gu + bi * 2 * F + F, F, hh + bi * F);
+        }
+        if (L->post_ffn_norm) {
+            orc_q4_0_matvec(L->wd, D, F, hh, B, NULL, xn, NULL);
+            post_norm_add(x, xn, L->post_ffn_norm, B, D, m->eps);
+        } else {
+            orc_q4_0_matvec(L->wd, D, F, hh, B, x, xn, NULL);
+            memcpy(x, xn, sizeof(double) * (size_t)(B * D));
+        }
         free(gu);
         free(hh);
         free(qkv);
@@ -391,6 +444,8 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
     orc_rmsnorm(x, m->final_norm, B, D, m->eps, xn);
     double *lg = logits ? logits : (double *)malloc(sizeof(double) * (size_t)(B * m->vocab));
     orc_q8_0_matvec(m->embed, m->vocab, D, xn, B, NULL, lg, NULL);
+    if (m->logit_softcap > 0.0)
+        orc_softcap(lg, B * m->vocab, m->logit_softcap);
     for (int64_t bi = 0; bi < B; ++bi) {
         double mg;
         next[bi] = (int32_t)orc_argmax(lg + bi * m->vocab, m->vocab, &mg);

@@ -33,6 +33,8 @@ extern "C" {
  * scales are binary16).  Pinned: all 65,536 patterns vs a library conversion. */
 double orc_half_to_double(uint16_t h);
 uint16_t orc_double_to_half(double v);  /* nearest binary16, ties to even */
+void orc_geglu(const double *g, const double *u, int64_t n, double *h);
+void orc_softcap(double *v, int64_t n, double c);
 
 /* Dequantise an n_rows x k Q4_0 / Q8_0 matrix (row-major block rows) to fp64.
  * Pinned: hand-worked block, unit vectors, Q4_0 vs Q8_0 cross-encoding. */
@@ -100,6 +102,9 @@ typedef struct {
     double rope_theta, attn_scale;
     int32_t v_from_k;         /* 1: no v rows; v = unit-gain rmsnorm of raw k */
     int32_t kv_f16;           /* 1: binary16 caches (rows appended rounded to nearest) */
+    int64_t rope_dims;        /* rotated dims (p-RoPE); 0 = all of head_dim */
+    const double *post_attn_norm; /* sandwich post-norm gains [d_model], or NULL */
+    const double *post_ffn_norm;
 } orc_layer;
 
 typedef struct {
@@ -108,6 +113,9 @@ typedef struct {
     const uint8_t *embed;     /* Q8_0 [vocab][d_model], tied input/output table */
     const double *final_norm; /* [d_model] */
     orc_layer *layers;
+    int32_t ffn_act;          /* 0: SwiGLU (SiLU gate); 1: GeGLU (tanh-form GELU gate) */
+    double embed_scale;       /* gathered rows times this (0: unscaled) */
+    double logit_softcap;     /* logits c tanh(l / c) (0: none) */
 } orc_model;
 
 /* One greedy decode step for all batch rows at position pos (rows of the new

@@ -66,6 +66,7 @@ class LayerShape:
     attn_scale: float
     v_from_k: bool
     cap: int             # cache slots per (sequence, kv head); slot = position % cap
+    rope_dims: int = 0   # rotated dims (p-RoPE); 0 = the whole head
 
 
 @dataclass(frozen=True)
@@ -81,6 +82,11 @@ class ModelShape:
     layers: tuple
     seed: int
     steps: int = 16
+    # Gemma-4 block variants (defaults: the plain pre-norm SwiGLU block)
+    ffn_act: str = "silu"       # or "gelu_tanh" (GeGLU)
+    embed_scale: float = 0.0    # gathered embedding rows times this (0: unscaled)
+    logit_softcap: float = 0.0  # logits c tanh(l / c) (0: none)
+    sandwich: bool = False      # post-attention and post-FFN RMSNorm before the residual adds
 
     @property
     def n_layers(self):
@@ -94,14 +100,22 @@ def _qwen3(name, n_layers, d, hq, hkv, hd, ffn, vocab, batch, start, steps, seed
 
 
 def _gemma4(name, n_layers, d, hq, swa_hkv, swa_hd, window, full_hkv, full_hd, ffn, vocab,
-            batch, start, steps, seed):
+            batch, start, steps, seed, exact=False):
+    """exact: the Gemma-4 block variants the pages name -- p-RoPE (p = 0.25) on
+    the full layers, GeGLU, sandwich norms, sqrt(d) embedding scale and a final
+    logit soft cap (30, a reading: the pages give no value)."""
     layers = []
     for l in range(n_layers):
         if l % 6 == 5:
-            layers.append(LayerShape(full_hkv, full_hd, 0, 1e6, 1.0, True, start + steps))
+            layers.append(LayerShape(full_hkv, full_hd, 0, 1e6, 1.0, True, start + steps,
+                                     full_hd // 4 if exact else 0))
         else:
             layers.append(LayerShape(swa_hkv, swa_hd, window, 1e4, 1.0, False, window))
-    return ModelShape(name, d, hq, ffn, vocab, batch, 1e-6, start, tuple(layers), seed, steps)
+    if not exact:
+        return ModelShape(name, d, hq, ffn, vocab, batch, 1e-6, start, tuple(layers), seed, steps)
+    return ModelShape(name, d, hq, ffn, vocab, batch, 1e-6, start, tuple(layers), seed, steps,
+                      ffn_act="gelu_tanh", embed_scale=math.sqrt(d), logit_softcap=30.0,
+                      sandwich=True)
 
 
 QWEN3_4B = _qwen3("decode_qwen3_4b", 36, 2560, 32, 8, 128, 9728, 151936, 8, 2048, 16,
@@ -120,6 +134,13 @@ TINY_GEMMA4 = _gemma4("tiny_gemma4", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2,
 # The tiny Qwen3 structure with 20 sequences (three groups of 8 in the
 # batched projections, the last one ragged).
 TINY_QWEN3_B20 = _qwen3("tiny_qwen3_b20", 2, 256, 4, 2, 64, 512, 1000, 20, 37, 4, 7004)
+# The tiny structure with the exact Gemma-4 block variants.
+TINY_GEMMA4_EXACT = _gemma4("tiny_gemma4_exact", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 40, 4,
+                            7005, exact=True)
+# The 31B shape with the exact Gemma-4 block variants (same matrices as
+# GEMMA4_31B plus the post-norm gains).
+GEMMA4_31B_EXACT = _gemma4("decode_gemma4_31b_exact", 60, 5376, 32, 16, 256, 1024, 4, 512, 21504,
+                           262144, 1, 8192, 16, SEED_BASE + 4, exact=True)
 # The tiny structure at a 128K-token context: its full-attention layer holds
 # 2,049 chunks of 64 keys per sequence, so attention runs as multi-chunk splits.
 TINY_GEMMA4_LONG = _gemma4("tiny_gemma4_long", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 131072,
@@ -148,6 +169,11 @@ def model_weights(m: ModelShape):
             q_norm=uniform_f32(s, f"L{l}.q_norm", (ly.head_dim,), 0.8, 1.2),
             k_norm=uniform_f32(s, f"L{l}.k_norm", (ly.head_dim,), 0.8, 1.2),
         ))
+        if m.sandwich:
+            layers[-1]["post_attn_norm"] = uniform_f32(s, f"L{l}.post_attn_norm", (m.d_model,),
+                                                       0.8, 1.2)
+            layers[-1]["post_ffn_norm"] = uniform_f32(s, f"L{l}.post_ffn_norm", (m.d_model,),
+                                                      0.8, 1.2)
     return dict(
         embed=q8_0_matrix(s, "embed", m.vocab, m.d_model),
         final_norm=uniform_f32(s, "final_norm", (m.d_model,), 0.8, 1.2),
@@ -184,10 +210,13 @@ def oracle_spec(m: ModelShape, weights, caches):
             attn_norm=w["attn_norm"], ffn_norm=w["ffn_norm"], q_norm=w["q_norm"],
             k_norm=w["k_norm"], k_cache=caches[l][0], v_cache=caches[l][1],
             n_kv_heads=ly.n_kv_heads, head_dim=ly.head_dim, window=ly.window,
-            rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k))
+            rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k,
+            rope_dims=ly.rope_dims, post_attn_norm=w.get("post_attn_norm"),
+            post_ffn_norm=w.get("post_ffn_norm")))
     return dict(d_model=m.d_model, n_q_heads=m.n_q_heads, ffn=m.ffn, vocab=m.vocab,
                 batch=m.batch, eps=m.eps, embed=weights["embed"],
-                final_norm=weights["final_norm"], layers=layers)
+                final_norm=weights["final_norm"], layers=layers, ffn_act=m.ffn_act,
+                embed_scale=m.embed_scale, logit_softcap=m.logit_softcap)
 
 
 @dataclass(frozen=True)

@@ -72,6 +72,8 @@ def _compose_one_step(shape, w, caches, pos, tok):
     """The block topology restated with the separately pinned oracle ops."""
     B, D, Hq, F = shape.batch, shape.d_model, shape.n_q_heads, shape.ffn
     x = oracle.q8_0_gather(w["embed"], shape.vocab, D, tok)
+    if shape.embed_scale:
+        x = x * shape.embed_scale
     for l, ly in enumerate(shape.layers):
         L = w["layers"][l]
         hd, hkv = ly.head_dim, ly.n_kv_heads
@@ -84,8 +86,10 @@ def _compose_one_step(shape, w, caches, pos, tok):
             kr = qkv[b, nq:nq + nk].reshape(hkv, hd)
             v = (oracle.rmsnorm(kr, None, shape.eps) if ly.v_from_k
                  else qkv[b, nq + nk:].reshape(hkv, hd))
-            q = oracle.rope_neox(oracle.rmsnorm(q, L["q_norm"], shape.eps), pos, ly.rope_theta)
-            k = oracle.rope_neox(oracle.rmsnorm(kr, L["k_norm"], shape.eps), pos, ly.rope_theta)
+            q = oracle.rope_neox(oracle.rmsnorm(q, L["q_norm"], shape.eps), pos, ly.rope_theta,
+                                 ly.rope_dims)
+            k = oracle.rope_neox(oracle.rmsnorm(kr, L["k_norm"], shape.eps), pos, ly.rope_theta,
+                                 ly.rope_dims)
             kc, vc = caches[l]
             kc[b, :, pos % ly.cap] = k.astype(np.float32)
             vc[b, :, pos % ly.cap] = v.astype(np.float32)
@@ -99,17 +103,29 @@ def _compose_one_step(shape, w, caches, pos, tok):
                 vals[p] = vc[b, :, slots[p]]
             o, _ = oracle.gqa_attention(q, keys, vals, ly.window, ly.attn_scale)
             att[b] = o.reshape(-1)
-        x, _ = oracle.q4_0_matvec(L["wo"], D, nq, att, res=x)
+        if shape.sandwich:
+            o_, _ = oracle.q4_0_matvec(L["wo"], D, nq, att)
+            x = x + oracle.rmsnorm(o_, L["post_attn_norm"], shape.eps)
+        else:
+            x, _ = oracle.q4_0_matvec(L["wo"], D, nq, att, res=x)
         xn = oracle.rmsnorm(x, L["ffn_norm"], shape.eps)
         gu, _ = oracle.q4_0_matvec(L["wgu"], 2 * F, D, xn)
-        h = oracle.swiglu(gu[:, :F], gu[:, F:])
-        x, _ = oracle.q4_0_matvec(L["wd"], D, F, h, res=x)
+        act = oracle.geglu if shape.ffn_act == "gelu_tanh" else oracle.swiglu
+        h = act(gu[:, :F], gu[:, F:])
+        if shape.sandwich:
+            d_, _ = oracle.q4_0_matvec(L["wd"], D, F, h)
+            x = x + oracle.rmsnorm(d_, L["post_ffn_norm"], shape.eps)
+        else:
+            x, _ = oracle.q4_0_matvec(L["wd"], D, F, h, res=x)
     xn = oracle.rmsnorm(x, w["final_norm"], shape.eps)
     logits, _ = oracle.q8_0_matvec(w["embed"], shape.vocab, D, xn)
+    if shape.logit_softcap:
+        logits = oracle.softcap(logits, shape.logit_softcap)
     return logits
 
 
-@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_EXACT],
+                         ids=lambda s: s.name)
 def test_decode_equals_composition_of_pinned_ops(shape):
     w = wl.model_weights(shape)
     tok = wl.start_tokens(shape)
@@ -126,3 +142,34 @@ def test_decode_equals_composition_of_pinned_ops(shape):
             assert np.array_equal(comp_caches[l][0], caches[l][0])
         tok = nxt
         pos += 1
+
+
+def test_gemma_exact_variants_change_the_step():
+    """Each Gemma-4 variant is live: switching any one of them off changes the
+    logits (the soft cap alone leaves the tokens unchanged: tanh is
+    increasing)."""
+    import dataclasses
+    m = wl.TINY_GEMMA4_EXACT
+    w = wl.model_weights(m)
+    tok = wl.start_tokens(m)
+
+    def run(shape):
+        caches = [(wl.prefilled_cache(shape, l, "k"), wl.prefilled_cache(shape, l, "v"))
+                  for l in range(shape.n_layers)]
+        spec = wl.oracle_spec(shape, w, caches)
+        if not shape.sandwich:
+            for L in spec["layers"]:
+                L["post_attn_norm"] = L["post_ffn_norm"] = None
+        return oracle.Model(spec).step(shape.start_pos, tok, want_logits=True)
+
+    n0, l0, _ = run(m)
+    no_cap = dataclasses.replace(m, logit_softcap=0.0)
+    n1, l1, _ = run(no_cap)
+    assert np.array_equal(n0, n1)
+    assert np.allclose(l0, oracle.softcap(l1, m.logit_softcap), rtol=1e-13, atol=1e-13)
+    full_rope = dataclasses.replace(
+        m, layers=tuple(dataclasses.replace(ly, rope_dims=0) for ly in m.layers))
+    for variant in (dataclasses.replace(m, ffn_act="silu"), dataclasses.replace(m, embed_scale=0.0),
+                    dataclasses.replace(m, sandwich=False), full_rope):
+        _, lv, _ = run(variant)
+        assert np.abs(lv - l0).max() > 1e-6

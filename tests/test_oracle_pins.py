@@ -404,3 +404,50 @@ def test_decode_f16_cache_appends_rounded_rows():
             others = np.arange(ly.cap) != slot
             assert np.array_equal(c16[l][c][:, :, others], before[l][c][:, :, others])
     assert np.abs(lg16 - lg32).max() <= 1e-2 * np.abs(lg32).max()
+
+
+# ---------------------------------------------------------------- Gemma-4 variants
+def test_geglu_tanh_form():
+    """GELU's tanh form: gelu(x) - gelu(-x) = x exactly (the form is x times an
+    odd-symmetric sigmoid-like factor), zero at zero, within 1e-3 of the
+    erf definition x Phi(x) everywhere (math.erf; a dropped cubic term misses
+    by ~2e-2), and the up operand multiplies."""
+    x = np.linspace(-6, 6, 2001)
+    one = np.ones_like(x)
+    g = oracle.geglu(x, one)
+    assert np.allclose(g - oracle.geglu(-x, one), x, rtol=0, atol=1e-12)
+    assert oracle.geglu(np.zeros(1), np.ones(1))[0] == 0.0
+    exact = np.array([0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x])
+    assert np.abs(g - exact).max() < 1e-3
+    u = np.linspace(-2, 3, 2001)
+    assert np.allclose(oracle.geglu(x, u), g * u, rtol=1e-15, atol=0)
+    # large arguments: identity on the right, zero on the left
+    assert abs(oracle.geglu(np.array([12.0]), np.ones(1))[0] - 12.0) < 1e-12
+    assert abs(oracle.geglu(np.array([-12.0]), np.ones(1))[0]) < 1e-12
+
+
+def test_softcap_properties():
+    c = 30.0
+    v = np.linspace(-500, 500, 4001)
+    s = oracle.softcap(v, c)
+    assert np.all(np.abs(s) <= c) and np.all(np.diff(s) >= 0)     # bounded, non-decreasing
+    mid = oracle.softcap(np.linspace(-150, 150, 3001), c)
+    assert np.all(np.abs(mid) < c) and np.all(np.diff(mid) > 0)  # strictly below saturation
+    assert np.allclose(s, -oracle.softcap(-v, c), rtol=0, atol=1e-12)
+    small = np.linspace(-0.3, 0.3, 101)
+    assert np.allclose(oracle.softcap(small, c), small - small ** 3 / (3 * c * c), rtol=0, atol=1e-9)
+    assert np.allclose(oracle.softcap(v, c), c * oracle.softcap(v / c, 1.0), rtol=1e-14, atol=1e-12)
+    assert abs(oracle.softcap(np.array([1e6]), c)[0] - c) < 1e-12
+
+
+def test_partial_rope_prefix_and_passthrough():
+    """p-RoPE: the first r dims rotate exactly as a full NeoX rotation of the
+    r-dim prefix (pinned above); the rest pass through; r = hd is full RoPE."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 512))
+    for pos, r in ((0, 128), (77, 128), (8191, 128), (5, 64), (300, 512)):
+        y = oracle.rope_neox(x, pos, 1e6, r)
+        assert np.array_equal(y[:, r:], x[:, r:])
+        assert np.allclose(y[:, :r], oracle.rope_neox(x[:, :r], pos, 1e6), rtol=0, atol=1e-15)
+        assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.array_equal(oracle.rope_neox(x, 9, 1e4, 512), oracle.rope_neox(x, 9, 1e4))
