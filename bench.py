@@ -163,7 +163,7 @@ def decode_algorithmic_bytes(m, step, kv_bytes=4):
     for ly in m.layers:
         nq, nk, nv = wl.layer_rows(m, ly)
         total += q4(nq + nk + nv, d) + q4(d, nq) + q4(2 * F, d) + q4(d, F)
-        total += 4 * (2 * d + 2 * ly.head_dim)
+        total += 4 * (2 * d + 2 * ly.head_dim) + (8 * d if m.sandwich else 0)
         vis = min(n, ly.window) if ly.window else n
         total += B * ly.n_kv_heads * ly.head_dim * kv_bytes * (2 * vis + 2)
     return total
@@ -337,7 +337,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-matvec", action="store_true")
     ap.add_argument("--decode",
-                    default="qwen3_4b,gemma4_31b,gemma4_31b_128k,qwen3_4b_f16kv,gemma4_31b_128k_f16kv",
+                    default="qwen3_4b,gemma4_31b,gemma4_31b_128k,qwen3_4b_f16kv,gemma4_31b_128k_f16kv,"
+                            "gemma4_31b_exact",
                     help="decode workloads to time (comma list, empty for none)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the B=1 HBM-streaming matvec (for profiler runs)")
@@ -377,7 +378,8 @@ def main():
     legs = {"qwen3_4b": (wl.QWEN3_4B, False, False), "gemma4_31b": (wl.GEMMA4_31B, False, False),
             "gemma4_31b_128k": (wl.GEMMA4_31B_128K, True, False),
             "qwen3_4b_f16kv": (wl.QWEN3_4B, False, True),
-            "gemma4_31b_128k_f16kv": (wl.GEMMA4_31B_128K, True, True)}
+            "gemma4_31b_128k_f16kv": (wl.GEMMA4_31B_128K, True, True),
+            "gemma4_31b_exact": (wl.GEMMA4_31B_EXACT, False, False)}
     decode_keys = [k for k in args.decode.split(",") if k] if not args.only_matvec else []
 
     def run_leg(key):

@@ -84,8 +84,10 @@ q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const float *x, int64
  *   Q4_IN_PLAIN    x
  *   Q4_IN_RMSNORM  norm_w * x / sqrt(mean(x^2) + eps)  (norm_w NULL: unit gain)
  *                  ([GELO] 05 Components: decoder RMSNorm)
- *   Q4_IN_SWIGLU   x / (1 + exp(-x)) * x2               ([GELO] 04: SwiGLU FFN) */
-typedef enum { Q4_IN_PLAIN = 0, Q4_IN_RMSNORM = 1, Q4_IN_SWIGLU = 2 } q4_input_op;
+ *   Q4_IN_SWIGLU   x / (1 + exp(-x)) * x2               ([GELO] 04: SwiGLU FFN)
+ *   Q4_IN_GEGLU    gelu(x) * x2, gelu in its tanh form  ([GELO] generation page, Gemma 4
+ *                  blockers: gelu_pytorch_tanh): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+typedef enum { Q4_IN_PLAIN = 0, Q4_IN_RMSNORM = 1, Q4_IN_SWIGLU = 2, Q4_IN_GEGLU = 3 } q4_input_op;
 
 /* Output transforms:
  *   Q4_OUT_PLAIN   y[b][n] = z[b][n] (+ residual[b][n]),  z = W op(x), y [B][N]
@@ -93,8 +95,9 @@ typedef enum { Q4_IN_PLAIN = 0, Q4_IN_RMSNORM = 1, Q4_IN_SWIGLU = 2 } q4_input_o
  *                  for p < N/2, y [B][N/2]: a merged gate|up projection that
  *                  hands the FFN activation straight to the down projection
  *                  ([GELO] 04: SwiGLU FFN; 06: merged gate|up); N even, no
- *                  residual. */
-typedef enum { Q4_OUT_PLAIN = 0, Q4_OUT_SWIGLU = 1 } q4_output_op;
+ *                  residual.
+ *   Q4_OUT_GEGLU   the same with gelu (tanh form) in place of x / (1 + exp(-x)). */
+typedef enum { Q4_OUT_PLAIN = 0, Q4_OUT_SWIGLU = 1, Q4_OUT_GEGLU = 2 } q4_output_op;
 
 /* q4_0_matvec_fused / q8_0_matvec_fused: y[b] = out_op(W op(x[b])) (+ residual[b]),
  * where row b of x (and of x2 for SwiGLU) starts at element b * ld_x
@@ -154,6 +157,12 @@ q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *
 q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens, int64_t B,
                       float *x, void *stream);
 
+/* q8_0_gather_scaled: the same rows times scale (Gemma-4 multiplies the
+ * embedding by sqrt(d_model); the value is the caller's).  x = (d * q) * scale
+ * per element.  Errors as q8_0_gather. */
+q4_status q8_0_gather_scaled(const void *E, int64_t V, int64_t K, const int32_t *tokens,
+                             int64_t B, float scale, float *x, void *stream);
+
 /* ------------------------------------------------------------------ norms
  * rmsnorm: y[r][i] = w[i] * x[r][i] / sqrt(mean_i(x[r][i]^2) + eps)
  *   ([GELO] 05 Components: decoder RMSNorm.)  x, y device fp32 [rows][dim]
@@ -162,6 +171,14 @@ q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens
 q4_status rmsnorm(const float *x, const float *w, int64_t rows, int64_t dim, float eps,
                   float *y, void *stream);
 
+/* rmsnorm_add: x[r][i] += w[i] * y[r][i] / sqrt(mean_i(y[r][i]^2) + eps), the
+ *   post-sublayer RMSNorm of a sandwich-norm block joining the residual
+ *   stream x ([GEM] 31B trace: post-attention RMSNorm, residual add, FFN
+ *   RMSNorm).  y, x device fp32 [rows][dim], not overlapping; w [dim] or NULL.
+ * Errors: Q4_ERR_INVALID_ARG (NULL, sizes, overlap), Q4_ERR_ALIGNMENT, Q4_ERR_HIP. */
+q4_status rmsnorm_add(const float *y, const float *w, int64_t rows, int64_t dim, float eps,
+                      float *x, void *stream);
+
 /* swiglu: h[r][i] = g[r][i] / (1 + exp(-g[r][i])) * u[r][i], 0 <= i < n.
  *   ([GELO] 04: SwiGLU FFN.)  g and u are read with row stride ld (ld >= n;
  *   a merged gate|up projection output passes g = gu, u = gu + n, ld = 2n);
@@ -169,6 +186,18 @@ q4_status rmsnorm(const float *x, const float *w, int64_t rows, int64_t dim, flo
  * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_HIP. */
 q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld, float *h,
                  void *stream);
+
+/* geglu: as swiglu with gelu (tanh form) in place of SiLU:
+ *   h = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u
+ *   ([GELO] generation page, Gemma 4 blockers: gelu_pytorch_tanh). */
+q4_status geglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld, float *h,
+                void *stream);
+
+/* softcap: v[i] = cap * tanh(v[i] / cap) in place, cap > 0 (final-logit soft
+ *   capping; [GELO] generation page, Gemma 4: final_logit_softcapping).  The
+ *   map is increasing, so the greedy choice is unchanged.  v device fp32 [n].
+ * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_ALIGNMENT, Q4_ERR_HIP. */
+q4_status softcap(float *v, int64_t n, float cap, void *stream);
 
 /* KV-cache layout: element strides of a [batch][n_kv_heads][cap][head_dim]
  * style cache; the head_dim axis is contiguous.  Position p of a sequence
@@ -210,6 +239,19 @@ q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v, in
                        const q4_kv_layout *kv, const int64_t *pos_dev, double theta,
                        float eps, int v_from_k, void *k_cache, void *v_cache,
                        void *stream);
+
+/* qk_norm_rope_partial: qk_norm_rope with p-RoPE ([GELO] generation page,
+ * glossary: only the first p * head_dim dimensions rotate, the rest pass
+ * through; Gemma 4 global layers use p = 0.25).  Reading: elements
+ * [0, rot_dims) rotate as a NeoX rotation of a rot_dims-dimensional vector
+ * (pairs i, i + rot_dims/2, angle pos * theta^(-2i/rot_dims)); elements
+ * [rot_dims, head_dim) are normalised only.  rot_dims even, 2..head_dim
+ * (head_dim: qk_norm_rope).  Errors as qk_norm_rope. */
+q4_status qk_norm_rope_partial(float *q, int64_t ldq, const float *k, const float *v,
+                               int64_t ldkv, const float *q_norm, const float *k_norm,
+                               int64_t n_q_heads, const q4_kv_layout *kv, const int64_t *pos_dev,
+                               double theta, float eps, int v_from_k, int64_t rot_dims,
+                               void *k_cache, void *v_cache, void *stream);
 
 /* ------------------------------------------------------------------ attention
  * gqa_decode_attn: one query row per sequence attends the cached positions
@@ -290,6 +332,10 @@ typedef struct {
     float attn_scale;
     int32_t v_from_k;        /* 1: no V rows in wqkv; V = unit-gain rmsnorm(raw K) */
     int32_t kv_dtype;        /* q4_kv_dtype of both caches */
+    /* Gemma-4 block variants (zero / NULL: the plain pre-norm block) */
+    int64_t rope_dims;       /* rotated dims (p-RoPE, qk_norm_rope_partial); 0 = head_dim */
+    const float *post_attn_norm; /* [d_model]: sandwich post-norm of the attention output */
+    const float *post_ffn_norm;  /* [d_model]: sandwich post-norm of the FFN output */
 } q4_layer_desc;
 
 typedef struct {
@@ -301,6 +347,10 @@ typedef struct {
     const void *embed;        /* Q8_0 [vocab][d_model], tied input/output table */
     const float *final_norm;  /* [d_model] */
     const q4_layer_desc *layers; /* host array [n_layers], copied at create */
+    /* Gemma-4 block variants (zero: off) */
+    int32_t ffn_act;          /* 0: SwiGLU; 1: GeGLU (tanh-form GELU gate) */
+    float embed_scale;        /* embedding rows times this (Gemma: sqrt(d_model)); 0 = 1 */
+    float logit_softcap;      /* logits cap * tanh(l / cap); 0 = none */
 } q4_model_desc;
 
 typedef struct q4_decode_model q4_decode_model;

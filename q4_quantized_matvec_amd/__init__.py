@@ -18,8 +18,10 @@ from ._lib import (  # noqa: F401
     IN_PLAIN,
     IN_RMSNORM,
     IN_SWIGLU,
+    IN_GEGLU,
     OUT_PLAIN,
     OUT_SWIGLU,
+    OUT_GEGLU,
     q4_0_matvec,
     q4_0_matvec_fused,
     q4_0_matvec_batched,
@@ -29,6 +31,9 @@ from ._lib import (  # noqa: F401
     q8_0_matvec,
     qk_norm_rope,
     rmsnorm,
+    rmsnorm_add,
+    softcap,
     swiglu,
+    geglu,
     version,
 )

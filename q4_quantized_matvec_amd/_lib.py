@@ -35,14 +35,16 @@ class LayerDesc(C.Structure):
                 ("k_norm", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p),
                 ("n_kv_heads", C.c_int64), ("head_dim", C.c_int64), ("cap", C.c_int64),
                 ("window", C.c_int64), ("rope_theta", C.c_double), ("attn_scale", C.c_float),
-                ("v_from_k", C.c_int32), ("kv_dtype", C.c_int32)]
+                ("v_from_k", C.c_int32), ("kv_dtype", C.c_int32), ("rope_dims", C.c_int64),
+                ("post_attn_norm", C.c_void_p), ("post_ffn_norm", C.c_void_p)]
 
 
 class ModelDesc(C.Structure):
     _fields_ = [("n_layers", C.c_int64), ("d_model", C.c_int64), ("n_q_heads", C.c_int64),
                 ("ffn", C.c_int64), ("vocab", C.c_int64), ("batch", C.c_int64),
                 ("eps", C.c_float), ("embed", C.c_void_p), ("final_norm", C.c_void_p),
-                ("layers", C.POINTER(LayerDesc))]
+                ("layers", C.POINTER(LayerDesc)), ("ffn_act", C.c_int32),
+                ("embed_scale", C.c_float), ("logit_softcap", C.c_float)]
 
 
 _P, _I64, _F, _D, _SZ = C.c_void_p, C.c_int64, C.c_float, C.c_double, C.c_size_t
@@ -52,6 +54,7 @@ _SIGS = {
     "q4_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_matvec": ([_P, _I64, _I64, _P, _I64, _P, _P, _P], C.c_int),
     "q8_0_gather": ([_P, _I64, _I64, _P, _I64, _P, _P], C.c_int),
+    "q8_0_gather_scaled": ([_P, _I64, _I64, _P, _I64, _F, _P, _P], C.c_int),
     "q4_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P, _P],
                           C.c_int),
     "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P, _P],
@@ -63,6 +66,11 @@ _SIGS = {
                              _P, _SZ, _P], C.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
     "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
+    "geglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
+    "rmsnorm_add": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
+    "softcap": ([_P, _I64, _F, _P], C.c_int),
+    "qk_norm_rope_partial": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D,
+                              _F, C.c_int, _I64, _P, _P, _P], C.c_int),
     "qk_norm_rope": ([_P, _I64, _P, _P, _I64, _P, _P, _I64, C.POINTER(KVLayout), _P, _D, _F,
                       C.c_int, _P, _P, _P], C.c_int),
     "gqa_decode_attn": ([_P, _I64, _I64, _P, _P, C.POINTER(KVLayout), _P, _I64, _F, _P, _I64,
@@ -170,12 +178,12 @@ def q8_0_matvec(W, x, y=None, residual=None, stream=None, n=None):
     return _matvec("q8_0_matvec", 34, W, x, y, residual, stream, n)
 
 
-IN_PLAIN, IN_RMSNORM, IN_SWIGLU = 0, 1, 2
-OUT_PLAIN, OUT_SWIGLU = 0, 1
+IN_PLAIN, IN_RMSNORM, IN_SWIGLU, IN_GEGLU = 0, 1, 2, 3
+OUT_PLAIN, OUT_SWIGLU, OUT_GEGLU = 0, 1, 2
 
 
 def _out_cols(N, out_op):
-    return N // 2 if out_op == OUT_SWIGLU else N
+    return N // 2 if out_op in (OUT_SWIGLU, OUT_GEGLU) else N
 
 
 def _matvec_fused(name, bpb, W, x, K, B, ld, op, x2, norm_w, eps, y, residual, stream, n, out_op):
@@ -237,14 +245,20 @@ def q8_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=N
                            residual, ws, stream, n, out_op)
 
 
-def q8_0_gather(E, tokens, K, x=None, stream=None):
+def q8_0_gather(E, tokens, K, x=None, stream=None, scale=None):
+    """Rows tokens of the Q8_0 table E dequantised (times scale if given)."""
     import torch
     V = _qmatrix_dims(E, K, 34)
     B = tokens.numel()
     if x is None:
         x = torch.empty((B, K), dtype=torch.float32, device=tokens.device)
-    _check("q8_0_gather", lib().q8_0_gather(_ptr(E), V, K, _ptr(tokens), B, _ptr(x),
-                                            _stream(stream)))
+    if scale is None:
+        _check("q8_0_gather", lib().q8_0_gather(_ptr(E), V, K, _ptr(tokens), B, _ptr(x),
+                                                _stream(stream)))
+    else:
+        _check("q8_0_gather_scaled", lib().q8_0_gather_scaled(_ptr(E), V, K, _ptr(tokens), B,
+                                                              float(scale), _ptr(x),
+                                                              _stream(stream)))
     return x
 
 
@@ -268,6 +282,31 @@ def swiglu(g, u, rows, n, ld, h=None, stream=None):
     return h
 
 
+def geglu(g, u, rows, n, ld, h=None, stream=None):
+    """h[rows, n] = gelu(g) * u (tanh form), g/u read with row stride ld."""
+    import torch
+    if h is None:
+        h = torch.empty((rows, n), dtype=torch.float32, device=g.device)
+    _check("geglu", lib().geglu(_ptr(g), _ptr(u), rows, n, ld, _ptr(h), _stream(stream)))
+    return h
+
+
+def rmsnorm_add(y, w, eps, x, stream=None):
+    """x += w * y / rms(y), row by row (the last axis)."""
+    _cuda_f32(y, "y")
+    dim = y.shape[-1]
+    rows = y.numel() // dim
+    _check("rmsnorm_add", lib().rmsnorm_add(_ptr(y), _ptr(w), rows, dim, eps, _ptr(x),
+                                            _stream(stream)))
+    return x
+
+
+def softcap(v, cap, stream=None):
+    """v = cap * tanh(v / cap) in place."""
+    _check("softcap", lib().softcap(_ptr(v), v.numel(), float(cap), _stream(stream)))
+    return v
+
+
 def kv_dtype_of(cache):
     import torch
     if cache.dtype == torch.float32:
@@ -285,11 +324,18 @@ def kv_layout_of(cache):
 
 
 def qk_norm_rope(q, ldq, k, v, ldkv, q_norm, k_norm, n_q_heads, kv, pos_dev, theta, eps,
-                 v_from_k, k_cache, v_cache, stream=None):
-    _check("qk_norm_rope", lib().qk_norm_rope(
-        _ptr(q), ldq, _ptr(k), _ptr(v), ldkv, _ptr(q_norm), _ptr(k_norm), n_q_heads,
-        C.byref(kv), _ptr(pos_dev), float(theta), float(eps), int(bool(v_from_k)),
-        _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+                 v_from_k, k_cache, v_cache, stream=None, rot_dims=None):
+    """rot_dims (p-RoPE): rotate only the first rot_dims elements of each head."""
+    if rot_dims is None:
+        _check("qk_norm_rope", lib().qk_norm_rope(
+            _ptr(q), ldq, _ptr(k), _ptr(v), ldkv, _ptr(q_norm), _ptr(k_norm), n_q_heads,
+            C.byref(kv), _ptr(pos_dev), float(theta), float(eps), int(bool(v_from_k)),
+            _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+    else:
+        _check("qk_norm_rope_partial", lib().qk_norm_rope_partial(
+            _ptr(q), ldq, _ptr(k), _ptr(v), ldkv, _ptr(q_norm), _ptr(k_norm), n_q_heads,
+            C.byref(kv), _ptr(pos_dev), float(theta), float(eps), int(bool(v_from_k)),
+            int(rot_dims), _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def gqa_decode_attn_workspace(kv, n_q_heads, window):
@@ -327,11 +373,14 @@ class DecodeModel:
 
     ``layers``: list of dicts with device tensors wqkv, wo, wgu, wd, attn_norm,
     ffn_norm, q_norm, k_norm, k_cache, v_cache and ints/floats n_kv_heads,
-    head_dim, window, rope_theta, attn_scale, v_from_k.
+    head_dim, window, rope_theta, attn_scale, v_from_k; optionally rope_dims
+    (p-RoPE) and post_attn_norm / post_ffn_norm tensors (sandwich norms).
+    ``ffn_act`` ("silu" or "gelu_tanh"), ``embed_scale`` and ``logit_softcap``
+    select the Gemma-4 block variants (defaults: off).
     """
 
     def __init__(self, *, d_model, n_q_heads, ffn, vocab, batch, eps, embed, final_norm,
-                 layers, device=None):
+                 layers, device=None, ffn_act="silu", embed_scale=0.0, logit_softcap=0.0):
         import torch
         self._keep = [embed, final_norm]
         arr = (LayerDesc * len(layers))()
@@ -351,9 +400,19 @@ class DecodeModel:
             d.kv_dtype = kv_dtype_of(L["k_cache"])
             if kv_dtype_of(L["v_cache"]) != d.kv_dtype:
                 raise TypeError(f"layer {i}: k_cache and v_cache dtypes differ")
+            d.rope_dims = int(L.get("rope_dims", 0) or 0)
+            for key in ("post_attn_norm", "post_ffn_norm"):
+                if L.get(key) is not None:
+                    _cuda_f32(L[key], key)
+                    setattr(d, key, _ptr(L[key]))
+                    self._keep.append(L[key])
         self._layers = arr
+        acts = {"silu": 0, "gelu_tanh": 1}
+        if ffn_act not in acts:
+            raise ValueError(f"ffn_act {ffn_act!r} is neither 'silu' nor 'gelu_tanh'")
         desc = ModelDesc(len(layers), d_model, n_q_heads, ffn, vocab, batch, eps, _ptr(embed),
-                         _ptr(final_norm), C.cast(arr, C.POINTER(LayerDesc)))
+                         _ptr(final_norm), C.cast(arr, C.POINTER(LayerDesc)), acts[ffn_act],
+                         float(embed_scale or 0.0), float(logit_softcap or 0.0))
         self._desc = desc
         nbytes = C.c_size_t()
         _check("decode_model_workspace", lib().decode_model_workspace(C.byref(desc),

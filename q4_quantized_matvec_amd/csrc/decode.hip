@@ -22,6 +22,7 @@ struct q4_decode_model {
     std::vector<q4_kv_layout> kv;
     int64_t *pos_dev = nullptr;  // [0] = position of the next token, [1] = n = position + 1
     float *x = nullptr, *qkv = nullptr, *att = nullptr, *gu = nullptr;
+    float *tmp = nullptr;  // a sublayer output before its sandwich post-norm [B][d_model]
     float *logits = nullptr;
     void *attn_ws = nullptr;
     size_t attn_ws_bytes = 0;
@@ -57,7 +58,7 @@ __global__ void advance_position_kernel(int64_t *pos) {
 }
 
 struct Layout {
-    size_t pos, x, qkv, att, gu, logits, mv, mv_bytes, attn, total;
+    size_t pos, x, qkv, att, gu, logits, tmp, mv, mv_bytes, attn, total;
 };
 
 int64_t layer_qkv_rows(const q4_model_desc &d, const q4_layer_desc &l) {
@@ -116,6 +117,7 @@ Layout plan(const q4_model_desc &d) {
     L.att = take(sizeof(float) * B * att);
     L.gu = take(sizeof(float) * B * 2 * d.ffn);
     L.logits = take(sizeof(float) * B * d.vocab);
+    L.tmp = take(sizeof(float) * B * d.d_model);
     L.mv = take(mv);
     L.mv_bytes = mv;
     L.attn = take(attn);
@@ -140,6 +142,11 @@ q4_status validate(const q4_model_desc *d) {
     Q4_CHECK(d->d_model % 32 == 0 && d->ffn % 32 == 0, Q4_ERR_SHAPE,
              "decode model: d_model and ffn must be multiples of 32");
     Q4_CHECK(d->eps >= 0.f, Q4_ERR_INVALID_ARG, "decode model: eps must be >= 0");
+    Q4_CHECK(d->ffn_act == 0 || d->ffn_act == 1, Q4_ERR_INVALID_ARG,
+             "decode model: ffn_act %d is neither 0 (SwiGLU) nor 1 (GeGLU)", (int)d->ffn_act);
+    Q4_CHECK(d->embed_scale >= 0.f && d->embed_scale <= 1e30f && d->logit_softcap >= 0.f &&
+                 d->logit_softcap <= 1e30f,
+             Q4_ERR_INVALID_ARG, "decode model: embed_scale and logit_softcap must be finite and >= 0");
     for (int64_t i = 0; i < d->n_layers; ++i) {
         const q4_layer_desc &l = d->layers[i];
         Q4_CHECK(l.wqkv && l.wo && l.wgu && l.wd && l.attn_norm && l.ffn_norm && l.q_norm && l.k_norm &&
@@ -156,6 +163,13 @@ q4_status validate(const q4_model_desc *d) {
                  "decode model: layer %lld: cap >= 1, window >= 0, rope_theta > 0", (long long)i);
         Q4_CHECK(l.kv_dtype == Q4_KV_F32 || l.kv_dtype == Q4_KV_F16, Q4_ERR_INVALID_ARG,
                  "decode model: layer %lld: kv_dtype %d unknown", (long long)i, (int)l.kv_dtype);
+        Q4_CHECK(l.rope_dims == 0 || (l.rope_dims >= 2 && l.rope_dims <= l.head_dim && l.rope_dims % 2 == 0),
+                 Q4_ERR_INVALID_ARG, "decode model: layer %lld: rope_dims %lld must be 0 or even in [2, head_dim]",
+                 (long long)i, (long long)l.rope_dims);
+        Q4_CHECK((!l.post_attn_norm || q4::aligned(l.post_attn_norm, 4)) &&
+                     (!l.post_ffn_norm || q4::aligned(l.post_ffn_norm, 4)),
+                 Q4_ERR_ALIGNMENT, "decode model: layer %lld: post-norm gains must be 4-byte aligned",
+                 (long long)i);
         Q4_CHECK(q4::aligned(l.k_cache, 16) && q4::aligned(l.v_cache, 16) && q4::aligned(l.wqkv, 2) &&
                      q4::aligned(l.wo, 2) && q4::aligned(l.wgu, 2) && q4::aligned(l.wd, 2) &&
                      q4::aligned(l.attn_norm, 4) && q4::aligned(l.ffn_norm, 4) &&
@@ -211,7 +225,12 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
     const q4_model_desc &d = m->desc;
     const int64_t B = d.batch, D = d.d_model, F = d.ffn;
     void *sv = s;
-    Q4_TRY(q8_0_gather(d.embed, d.vocab, D, tok, B, m->x, sv));
+    if (d.embed_scale != 0.f && d.embed_scale != 1.f)
+        Q4_TRY(q8_0_gather_scaled(d.embed, d.vocab, D, tok, B, d.embed_scale, m->x, sv));
+    else
+        Q4_TRY(q8_0_gather(d.embed, d.vocab, D, tok, B, m->x, sv));
+    const q4_input_op gated_in = d.ffn_act ? Q4_IN_GEGLU : Q4_IN_SWIGLU;
+    const q4_output_op gated_out = d.ffn_act ? Q4_OUT_GEGLU : Q4_OUT_SWIGLU;
     for (size_t i = 0; i < m->layers.size(); ++i) {
         const q4_layer_desc &l = m->layers[i];
         const int64_t hd = l.head_dim, nq = d.n_q_heads * hd, nk = l.n_kv_heads * hd;
@@ -219,30 +238,54 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         // attention RMSNorm fused into the QKV projection's input
         Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                        l.attn_norm, m->qkv, nullptr, sv));
-        // per-head QK-norm, RoPE and the KV append fused into the attention
-        Q4_TRY(gqa_decode_attn_rope(m->qkv, nqkv, d.n_q_heads, l.q_norm, l.k_norm, &m->kv[i],
-                                    m->pos_dev, l.rope_theta, d.eps, l.v_from_k, l.k_cache,
-                                    l.v_cache, l.window, l.attn_scale, m->att, nq, m->attn_ws,
-                                    m->attn_ws_bytes, sv));
-        Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
-                       m->x, m->x, sv));
+        if (l.rope_dims == 0 || l.rope_dims == hd) {
+            // per-head QK-norm, RoPE and the KV append fused into the attention
+            Q4_TRY(gqa_decode_attn_rope(m->qkv, nqkv, d.n_q_heads, l.q_norm, l.k_norm, &m->kv[i],
+                                        m->pos_dev, l.rope_theta, d.eps, l.v_from_k, l.k_cache,
+                                        l.v_cache, l.window, l.attn_scale, m->att, nq, m->attn_ws,
+                                        m->attn_ws_bytes, sv));
+        } else {
+            // p-RoPE: the standalone preparation (q in place, the append),
+            // then attention over n = pos + 1 positions
+            Q4_TRY(qk_norm_rope_partial(m->qkv, nqkv, m->qkv + nq,
+                                        l.v_from_k ? nullptr : m->qkv + nq + nk, nqkv, l.q_norm,
+                                        l.k_norm, d.n_q_heads, &m->kv[i], m->pos_dev, l.rope_theta,
+                                        d.eps, l.v_from_k, l.rope_dims, l.k_cache, l.v_cache, sv));
+            Q4_TRY(gqa_decode_attn(m->qkv, nqkv, d.n_q_heads, l.k_cache, l.v_cache, &m->kv[i],
+                                   m->pos_dev + 1, l.window, l.attn_scale, m->att, nq, m->attn_ws,
+                                   m->attn_ws_bytes, sv));
+        }
+        // O projection; with a sandwich post-norm the output is normalised
+        // before it joins the residual
+        if (l.post_attn_norm) {
+            Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
+                           m->tmp, nullptr, sv));
+            Q4_TRY(rmsnorm_add(m->tmp, l.post_attn_norm, B, D, d.eps, m->x, sv));
+        } else {
+            Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
+                           m->x, m->x, sv));
+        }
         // FFN RMSNorm fused into gate|up; SwiGLU fused into gate|up's output
         // (else into the down projection's input)
+        float *dy = l.post_ffn_norm ? m->tmp : m->x;          // down projection output
+        const float *dres = l.post_ffn_norm ? nullptr : m->x;  // and its residual
         if (glu_output(d, l.wgu)) {
-            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_SWIGLU,
+            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, gated_out,
                            l.ffn_norm, m->gu, nullptr, sv));
             Q4_TRY(project(m, 0, l.wd, D, F, m->gu, nullptr, F, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
-                           m->x, m->x, sv));
+                           dy, dres, sv));
         } else {
             Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                            l.ffn_norm, m->gu, nullptr, sv));
-            Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, Q4_IN_SWIGLU, Q4_OUT_PLAIN,
-                           nullptr, m->x, m->x, sv));
+            Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, gated_in, Q4_OUT_PLAIN,
+                           nullptr, dy, dres, sv));
         }
+        if (l.post_ffn_norm) Q4_TRY(rmsnorm_add(m->tmp, l.post_ffn_norm, B, D, d.eps, m->x, sv));
     }
     float *lg = logits ? logits : m->logits;
     Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                    d.final_norm, lg, nullptr, sv));
+    if (d.logit_softcap > 0.f) Q4_TRY(softcap(lg, B * d.vocab, d.logit_softcap, sv));
     Q4_TRY(argmax_rows(lg, B, d.vocab, next, sv));
     hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, s, m->pos_dev);
     return q4::launch_status("decode_step (advance)");
@@ -293,6 +336,7 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     m->att = reinterpret_cast<float *>(base + L.att);
     m->gu = reinterpret_cast<float *>(base + L.gu);
     m->logits = reinterpret_cast<float *>(base + L.logits);
+    m->tmp = reinterpret_cast<float *>(base + L.tmp);
     m->attn_ws = base + L.attn;
     m->attn_ws_bytes = L.total - L.attn;
     m->mv_ws = L.mv_bytes ? base + L.mv : nullptr;

@@ -6,7 +6,9 @@
 //   rmsnorm  y = w * x / sqrt(mean(x^2) + eps)
 //   QK-norm  the same RMSNorm per head_dim slice with one shared gain, before RoPE
 //   RoPE     NeoX pairing (i, i + hd/2), angle pos * theta^(-2i/hd)
-//   SwiGLU   silu(g) * u
+//   SwiGLU   silu(g) * u;  GeGLU  gelu(g) * u with gelu in its tanh form
+//   post-norm x += w * y / sqrt(mean(y^2) + eps)  (sandwich norm before the residual add)
+//   softcap  l = c * tanh(l / c)
 //   argmax   greedy choice, lowest token id on equal logits
 #include "common.hpp"
 
@@ -15,43 +17,86 @@ using namespace q4dev;
 
 constexpr int kWG = 256;
 
-// Sum over a 256-thread workgroup; every thread receives the total.
-__device__ __forceinline__ float block_sum(float v, float *lds4) {
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const float t = lds4[0] + lds4[1] + lds4[2] + lds4[3];
-    __syncthreads();
-    return t;
-}
-
-__global__ __launch_bounds__(kWG) void rmsnorm_kernel(const float *x, const float *__restrict__ w,
-                                                      float *y, int dim, float eps) {
-    __shared__ float red[4];
+// One workgroup of 1024 threads per row.  ADD: y[i] += the normalised x[i]
+// (a post-norm joining the residual stream y) instead of y[i] = it.  Rows of
+// up to 8192 elements are loaded once, all loads of a thread in flight
+// together; longer rows are read twice.
+constexpr int kNormWG = 1024, kNormU = 8;
+template <bool ADD>
+__global__ __launch_bounds__(kNormWG) void rmsnorm_kernel(const float *x, const float *__restrict__ w,
+                                                          float *y, int dim, float eps) {
+    __shared__ float red[kNormWG / 64];
     const float *xr = x + static_cast<size_t>(blockIdx.x) * dim;
     float *yr = y + static_cast<size_t>(blockIdx.x) * dim;
+    const int tid = threadIdx.x;
+    float v[kNormU];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < dim; i += kWG) ss = __builtin_fmaf(xr[i], xr[i], ss);
-    ss = block_sum(ss, red);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(dim) + eps);
-    for (int i = threadIdx.x; i < dim; i += kWG) yr[i] = xr[i] * inv * (w ? w[i] : 1.0f);
+    const bool held = dim <= kNormWG * kNormU;
+    if (held) {
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int i = tid + u * kNormWG;
+            v[u] = i < dim ? xr[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) ss = __builtin_fmaf(v[u], v[u], ss);
+    } else {
+        for (int i0 = 0; i0 < dim; i0 += kNormWG * kNormU) {
+#pragma unroll
+            for (int u = 0; u < kNormU; ++u) {
+                const int i = i0 + tid + u * kNormWG;
+                v[u] = i < dim ? xr[i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kNormU; ++u) ss = __builtin_fmaf(v[u], v[u], ss);
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < kNormWG / 64; ++k) tot += red[k];  // fixed order
+    const float inv = 1.0f / sqrtf(tot / static_cast<float>(dim) + eps);
+    for (int i0 = 0; i0 < dim; i0 += kNormWG * kNormU) {
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int i = i0 + tid + u * kNormWG;
+            if (i < dim) {
+                const float xv = held ? v[u] : xr[i];
+                const float t = xv * inv * (w ? w[i] : 1.0f);
+                if constexpr (ADD) yr[i] += t;
+                else yr[i] = t;
+            }
+        }
+    }
 }
 
-__global__ __launch_bounds__(kWG) void swiglu_kernel(const float *g, const float *u, float *h,
-                                                     int64_t rows, int64_t n, int64_t ld) {
+// act(g) * u, act = SiLU (a == 0) or the tanh form of GELU (a == 1).
+__global__ __launch_bounds__(kWG) void glu_kernel(const float *g, const float *u, float *h,
+                                                  int64_t rows, int64_t n, int64_t ld, int a) {
     const int64_t total = rows * n;
     for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWG + threadIdx.x; t < total;
          t += static_cast<int64_t>(gridDim.x) * kWG) {
         const int64_t r = t / n, i = t % n;
         const float gv = g[r * ld + i];
-        h[t] = gv / (1.0f + expf(-gv)) * u[r * ld + i];
+        const float act = a ? 0.5f * gv * (1.0f + tanhf(0.7978845608028654f * (gv + 0.044715f * gv * gv * gv)))
+                            : gv / (1.0f + expf(-gv));
+        h[t] = act * u[r * ld + i];
     }
+}
+
+__global__ __launch_bounds__(kWG) void softcap_kernel(float *v, int64_t n, float c, float inv_c) {
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWG + threadIdx.x; t < n;
+         t += static_cast<int64_t>(gridDim.x) * kWG)
+        v[t] = c * tanhf(v[t] * inv_c);
 }
 
 // One wavefront per (sequence, head).  Heads [0, Hq) are query heads (written
 // back in place); heads [Hq, Hq + Hkv) are key heads whose rotated row (and the
 // value row) are appended to the caches at slot pos % cap.
 constexpr int kMaxPairsPerLane = 4;  // head_dim <= 512
+constexpr int kMaxPassPerLane = 8;   // unrotated elements (p-RoPE), head_dim <= 512
 
 // KT: the caches' element type (fp32, or binary16 written with round to
 // nearest even).
@@ -60,11 +105,14 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
     const float *__restrict__ qn, const float *__restrict__ kn, int Hq, int hd,
     const int64_t *__restrict__ pos_dev, double theta, float eps, int v_from_k,
-    KT *kc, KT *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st) {
+    KT *kc, KT *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st, int rot) {
+    // p-RoPE: elements [0, rot) rotate as a NeoX rotation of a rot-dimensional
+    // vector (pairs i, i + rot/2, angle pos * theta^(-2i/rot)); elements
+    // [rot, hd) are only normalised.  rot == hd is the full rotation.
     const int b = blockIdx.y;
     const int head = blockIdx.x;
     const int lane = threadIdx.x;
-    const int half = hd >> 1;
+    const int half = rot >> 1;
     const bool is_q = head < Hq;
     const int g = head - Hq;
     const float *src = is_q ? q + b * ldq + static_cast<int64_t>(head) * hd
@@ -84,6 +132,13 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
             ss = __builtin_fmaf(a[p], a[p], __builtin_fmaf(c[p], c[p], ss));
         }
     }
+    float t[kMaxPassPerLane];
+#pragma unroll
+    for (int p = 0; p < kMaxPassPerLane; ++p) {
+        const int i = rot + lane + 64 * p;
+        t[p] = i < hd ? src[i] : 0.f;
+        ss = __builtin_fmaf(t[p], t[p], ss);
+    }
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(hd) + eps);
     const int64_t pos = *pos_dev;
@@ -91,7 +146,7 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     // powers in fp64 (a relative error of a few 1e-16, far below what the
     // angle needs); the angle pos * r^i is reduced by 2 pi in fp64 and the
     // reduced angle (|a| <= pi) goes to single-precision sincos.
-    const double r = pow(theta, -2.0 / static_cast<double>(hd));
+    const double r = pow(theta, -2.0 / static_cast<double>(rot));
     double rp[9];  // r^(2^k), k = 0..8 (pairs i < 256)
     rp[0] = r;
 #pragma unroll
@@ -137,6 +192,19 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
                     vdst[i] = static_cast<KT>(vs[i]);
                     vdst[i + half] = static_cast<KT>(vs[i + half]);
                 }
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxPassPerLane; ++p) {
+        const int i = rot + lane + 64 * p;
+        if (i < hd) {
+            const float x0 = t[p] * inv * gain[i];
+            if (dst) dst[i] = x0;
+            if (kdst) kdst[i] = static_cast<KT>(x0);
+            if (vdst) {
+                if (v_from_k) vdst[i] = static_cast<KT>(t[p] * inv);
+                else vdst[i] = static_cast<KT>(v[b * ldkv + static_cast<int64_t>(g) * hd + i]);
             }
         }
     }
@@ -216,25 +284,66 @@ extern "C" q4_status rmsnorm(const float *x, const float *w, int64_t rows, int64
     Q4_CHECK(rows <= (1 << 30) && dim <= (1 << 26), Q4_ERR_UNSUPPORTED, "rmsnorm: sizes too large");
     Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!w || q4::aligned(w, 4)), Q4_ERR_ALIGNMENT,
              "rmsnorm: x, w, y must be 4-byte aligned");
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(rows)), dim3(kWG), 0,
+    hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(kNormWG), 0,
                        q4::as_stream(stream), x, w, y, static_cast<int>(dim), eps);
     return q4::launch_status("rmsnorm");
 }
 
-extern "C" q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld,
-                            float *h, void *stream) {
+extern "C" q4_status rmsnorm_add(const float *y, const float *w, int64_t rows, int64_t dim,
+                                 float eps, float *x, void *stream) {
     q4::clear_error();
-    Q4_CHECK(g && u && h, Q4_ERR_INVALID_ARG, "swiglu: g, u and h must not be NULL");
+    Q4_CHECK(x && y, Q4_ERR_INVALID_ARG, "rmsnorm_add: y and x must not be NULL");
+    Q4_CHECK(rows >= 1 && dim >= 1 && eps >= 0.f, Q4_ERR_INVALID_ARG,
+             "rmsnorm_add: rows, dim must be >= 1 and eps >= 0");
+    Q4_CHECK(rows <= (1 << 30) && dim <= (1 << 26), Q4_ERR_UNSUPPORTED, "rmsnorm_add: sizes too large");
+    Q4_CHECK(q4::aligned(x, 4) && q4::aligned(y, 4) && (!w || q4::aligned(w, 4)), Q4_ERR_ALIGNMENT,
+             "rmsnorm_add: y, w, x must be 4-byte aligned");
+    const size_t bytes = static_cast<size_t>(rows * dim) * sizeof(float);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    Q4_CHECK(a + bytes <= b || b + bytes <= a, Q4_ERR_INVALID_ARG, "rmsnorm_add: y must not overlap x");
+    hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(kNormWG), 0,
+                       q4::as_stream(stream), y, w, x, static_cast<int>(dim), eps);
+    return q4::launch_status("rmsnorm_add");
+}
+
+namespace {
+q4_status glu_entry(const char *name, const float *g, const float *u, int64_t rows, int64_t n,
+                    int64_t ld, float *h, void *stream, int a) {
+    q4::clear_error();
+    Q4_CHECK(g && u && h, Q4_ERR_INVALID_ARG, "%s: g, u and h must not be NULL", name);
     Q4_CHECK(rows >= 1 && n >= 1 && ld >= n, Q4_ERR_INVALID_ARG,
-             "swiglu: rows, n must be >= 1 and ld >= n");
+             "%s: rows, n must be >= 1 and ld >= n", name);
     Q4_CHECK(q4::aligned(g, 4) && q4::aligned(u, 4) && q4::aligned(h, 4), Q4_ERR_ALIGNMENT,
-             "swiglu: g, u, h must be 4-byte aligned");
+             "%s: g, u, h must be 4-byte aligned", name);
     const int64_t total = rows * n;
     const int64_t want = (total + kWG - 1) / kWG;
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>(want, 4096));
-    hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(kWG), 0, q4::as_stream(stream), g, u, h,
-                       rows, n, ld);
-    return q4::launch_status("swiglu");
+    hipLaunchKernelGGL(glu_kernel, dim3(grid), dim3(kWG), 0, q4::as_stream(stream), g, u, h, rows, n,
+                       ld, a);
+    return q4::launch_status(name);
+}
+}  // namespace
+
+extern "C" q4_status swiglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld,
+                            float *h, void *stream) {
+    return glu_entry("swiglu", g, u, rows, n, ld, h, stream, 0);
+}
+
+extern "C" q4_status geglu(const float *g, const float *u, int64_t rows, int64_t n, int64_t ld,
+                           float *h, void *stream) {
+    return glu_entry("geglu", g, u, rows, n, ld, h, stream, 1);
+}
+
+extern "C" q4_status softcap(float *v, int64_t n, float cap, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(v && n >= 1, Q4_ERR_INVALID_ARG, "softcap: v must not be NULL and n >= 1");
+    Q4_CHECK(cap > 0.f && cap <= 3.0e38f, Q4_ERR_INVALID_ARG, "softcap: cap must be > 0 and finite");
+    Q4_CHECK(q4::aligned(v, 4), Q4_ERR_ALIGNMENT, "softcap: v must be 4-byte aligned");
+    const int64_t want = (n + kWG - 1) / kWG;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>(want, 4096));
+    hipLaunchKernelGGL(softcap_kernel, dim3(grid), dim3(kWG), 0, q4::as_stream(stream), v, n, cap,
+                       1.0f / cap);
+    return q4::launch_status("softcap");
 }
 
 namespace q4 {
@@ -256,14 +365,17 @@ q4_status check_kv_layout(const char *name, const q4_kv_layout *kv) {
 }
 }  // namespace q4
 
-extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v,
-                                  int64_t ldkv, const float *q_norm, const float *k_norm,
-                                  int64_t n_q_heads, const q4_kv_layout *kv,
-                                  const int64_t *pos_dev, double theta, float eps, int v_from_k,
-                                  void *k_cache, void *v_cache, void *stream) {
+extern "C" q4_status qk_norm_rope_partial(float *q, int64_t ldq, const float *k, const float *v,
+                                          int64_t ldkv, const float *q_norm, const float *k_norm,
+                                          int64_t n_q_heads, const q4_kv_layout *kv,
+                                          const int64_t *pos_dev, double theta, float eps,
+                                          int v_from_k, int64_t rot_dims, void *k_cache,
+                                          void *v_cache, void *stream) {
     q4::clear_error();
     q4_status st = q4::check_kv_layout("qk_norm_rope", kv);
     if (st != Q4_OK) return st;
+    Q4_CHECK(rot_dims >= 2 && rot_dims <= kv->head_dim && rot_dims % 2 == 0, Q4_ERR_INVALID_ARG,
+             "qk_norm_rope: rotated dims %lld must be even and in [2, head_dim]", (long long)rot_dims);
     Q4_CHECK(q && k && q_norm && k_norm && pos_dev && k_cache && v_cache, Q4_ERR_INVALID_ARG,
              "qk_norm_rope: q, k, q_norm, k_norm, pos_dev and the caches must not be NULL");
     Q4_CHECK(v_from_k ? v == nullptr : v != nullptr, Q4_ERR_INVALID_ARG,
@@ -281,14 +393,25 @@ extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const f
                            ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
                            static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
                            static_cast<_Float16 *>(k_cache), static_cast<_Float16 *>(v_cache), kv->cap,
-                           kv->stride_b, kv->stride_h, kv->stride_t);
+                           kv->stride_b, kv->stride_h, kv->stride_t, static_cast<int>(rot_dims));
     else
         hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(64), 0, q4::as_stream(stream), q,
                            ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
                            static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
                            static_cast<float *>(k_cache), static_cast<float *>(v_cache), kv->cap,
-                           kv->stride_b, kv->stride_h, kv->stride_t);
+                           kv->stride_b, kv->stride_h, kv->stride_t, static_cast<int>(rot_dims));
     return q4::launch_status("qk_norm_rope");
+}
+
+extern "C" q4_status qk_norm_rope(float *q, int64_t ldq, const float *k, const float *v,
+                                  int64_t ldkv, const float *q_norm, const float *k_norm,
+                                  int64_t n_q_heads, const q4_kv_layout *kv,
+                                  const int64_t *pos_dev, double theta, float eps, int v_from_k,
+                                  void *k_cache, void *v_cache, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(kv, Q4_ERR_INVALID_ARG, "qk_norm_rope: kv layout must not be NULL");
+    return qk_norm_rope_partial(q, ldq, k, v, ldkv, q_norm, k_norm, n_q_heads, kv, pos_dev, theta,
+                                eps, v_from_k, kv->head_dim, k_cache, v_cache, stream);
 }
 
 extern "C" q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int32_t *out,

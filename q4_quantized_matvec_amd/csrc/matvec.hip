@@ -50,17 +50,31 @@ struct Fmt<1> {  // Q8_0
 // producer of the matvec input into its prologue):
 //   kind 0: x
 //   kind 1: rmsnorm(x) = w * x / sqrt(mean(x^2) + eps)   (w NULL: unit gain)
-//   kind 2: swiglu(x, u) = x / (1 + exp(-x)) * u
+//   kind 2: act(x) * u, act = silu (x / (1 + exp(-x))) or gelu (tanh form)
 struct InOp {
     int kind;
     const float *u;  // kind 2: second operand, same row stride as x
     const float *w;  // kind 1: gain
     float eps;
     int64_t ld;      // row stride of x (and u) in elements
-    int glu;         // 1: y[p] = silu(z[p]) * z[p + N/2] for the N/2 pairs (whole K per wavefront)
+    int glu;         // 1 / 2: y[p] = act(z[p]) * z[p + N/2] for the N/2 pairs, act = silu / gelu
+                     // (whole K per wavefront)
+    int act;         // kind 2: 0 silu, 1 gelu
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// act(g) * u with act = SiLU or (GELU) the tanh form of GELU.  A template
+// parameter, not a runtime flag: the GELU code would otherwise sit in every
+// instantiation, and kernels that start with cold instruction caches (one
+// after another in a decode step) are measurably slower when larger.
+template <bool GELU>
+__device__ __forceinline__ float act_mul(float g, float u) {
+    if constexpr (GELU) return 0.5f * g * (1.0f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
+    else return g / (1.0f + expf(-g)) * u;
+}
+// The runtime form, for the generic (slow-path) kernel.
+__device__ __forceinline__ float glu_mul(int a, float g, float u) {
+    return a ? act_mul<true>(g, u) : act_mul<false>(g, u);
+}
 
 template <int FMT, int JX>
 struct RowRegs {
@@ -125,7 +139,7 @@ constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
 
 // B = 1 fast path.  KS wavefronts of a workgroup split K; 4 / KS row groups;
 // PF rows of loads in flight per wavefront.
-template <int FMT, int JX, int KS, int PF, bool GLU>
+template <int FMT, int JX, int KS, int PF, bool GLU, bool GELU>
 __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
                                                     const float *x, float *y, const float *res,
                                                     int N, int K, InOp op) {
@@ -241,10 +255,10 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
             if (i < nv) {
                 float4 t = v[r];
                 if (op.kind == 2) {
-                    t.x = silu_mul(t.x, u[r].x);
-                    t.y = silu_mul(t.y, u[r].y);
-                    t.z = silu_mul(t.z, u[r].z);
-                    t.w = silu_mul(t.w, u[r].w);
+                    t.x = act_mul<GELU>(t.x, u[r].x);
+                    t.y = act_mul<GELU>(t.y, u[r].y);
+                    t.z = act_mul<GELU>(t.z, u[r].z);
+                    t.w = act_mul<GELU>(t.w, u[r].w);
                 }
                 ss = __builtin_fmaf(t.x, t.x, __builtin_fmaf(t.y, t.y, __builtin_fmaf(t.z, t.z, __builtin_fmaf(t.w, t.w, ss))));
                 if (op.kind == 1 && sg) {
@@ -296,10 +310,10 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                 float4 v = xp[i];
                 if (!kXLds && op.kind == 2) {
                     const float4 u = reinterpret_cast<const float4 *>(op.u + static_cast<size_t>(c) * 32)[i];
-                    v.x = silu_mul(v.x, u.x);
-                    v.y = silu_mul(v.y, u.y);
-                    v.z = silu_mul(v.z, u.z);
-                    v.w = silu_mul(v.w, u.w);
+                    v.x = act_mul<GELU>(v.x, u.x);
+                    v.y = act_mul<GELU>(v.y, u.y);
+                    v.z = act_mul<GELU>(v.z, u.z);
+                    v.w = act_mul<GELU>(v.w, u.w);
                 }
                 xr[j][4 * i + 0] = v.x;
                 xr[j][4 * i + 1] = v.y;
@@ -400,7 +414,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         if constexpr (KS == 1) {
             if constexpr (GLU) {
                 if ((it & 1) == 0) gate = acc;
-                else if (act && lane == 0) y[row0 + (it >> 1)] = silu_mul(gate, acc);
+                else if (act && lane == 0) y[row0 + (it >> 1)] = act_mul<GELU>(gate, acc);
             } else if (act && lane == 0) {
                 y[row] = has_res ? acc + cur.res : acc;
             }
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(kWG) void mv_generic_kernel(const uint8_t *__restri
                 for (int i = 0; i < 32; ++i) {
                     float xv = xb[i];
                     if constexpr (KIND == 1) xv = xv * inv[b] * (op.w ? op.w[c * 32 + i] : 1.0f);
-                    else if constexpr (KIND == 2) xv = silu_mul(xv, op.u[off + i]);
+                    else if constexpr (KIND == 2) xv = glu_mul(op.act, xv, op.u[off + i]);
                     s = __builtin_fmaf(w[i], xv, s);
                 }
                 acc[b] = __builtin_fmaf(d, s, acc[b]);
@@ -520,7 +534,7 @@ __global__ __launch_bounds__(kWG) void mv_generic_kernel(const uint8_t *__restri
 __global__ __launch_bounds__(kWG) void q8_gather_kernel(const uint8_t *__restrict__ E,
                                                         const int32_t *__restrict__ tok,
                                                         float *__restrict__ x, int V, int K,
-                                                        int B) {
+                                                        int B, float scale) {
     const int nb = K >> 5;
     const int t = blockIdx.x * kWG + threadIdx.x;
     if (t >= B * nb) return;
@@ -533,11 +547,12 @@ __global__ __launch_bounds__(kWG) void q8_gather_kernel(const uint8_t *__restric
     }
     const uint8_t *blk = E + (static_cast<size_t>(id) * nb + c) * 34;
     const float d = half_bits_to_float(*reinterpret_cast<const uint16_t *>(blk));
+    // scaled rows: (d * q) * scale, the product of the dequantised value and the scale
     const uint16_t *h = reinterpret_cast<const uint16_t *>(blk + 2);
     for (int j = 0; j < 16; ++j) {
         const uint32_t v = h[j];
-        out[2 * j] = d * static_cast<float>(static_cast<int8_t>(v & 0xFFu));
-        out[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(v >> 8));
+        out[2 * j] = d * static_cast<float>(static_cast<int8_t>(v & 0xFFu)) * scale;
+        out[2 * j + 1] = d * static_cast<float>(static_cast<int8_t>(v >> 8)) * scale;
     }
 }
 
@@ -554,15 +569,31 @@ void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int
     int per_cu = KS > 1 ? 1 : std::max(1, std::min(3, N / (q4::device_cus() * RG * 7)));
     if (Q4_MV_WG_PER_CU) per_cu = Q4_MV_WG_PER_CU;
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
+    // GeGLU kernels exist for Q4_0 only (the gated projections)
+    const bool gelu = (op.kind == 2 && op.act) || op.glu == 2;
     if constexpr (KS == 1) {
         if (op.glu) {
-            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true>), dim3(nwg, B), dim3(kWG), 0, s, W, x,
-                               y, res, N, K, op);
+            if constexpr (FMT == 0) {
+                if (gelu) {
+                    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, true>), dim3(nwg, B), dim3(kWG),
+                                       0, s, W, x, y, res, N, K, op);
+                    return;
+                }
+            }
+            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, false>), dim3(nwg, B), dim3(kWG), 0, s,
+                               W, x, y, res, N, K, op);
             return;
         }
     }
-    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false>), dim3(nwg, B), dim3(kWG), 0, s, W, x, y,
-                       res, N, K, op);
+    if constexpr (FMT == 0) {
+        if (gelu) {
+            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, true>), dim3(nwg, B), dim3(kWG), 0, s,
+                               W, x, y, res, N, K, op);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, false>), dim3(nwg, B), dim3(kWG), 0, s, W, x,
+                       y, res, N, K, op);
 }
 
 template <int FMT, int KS>
@@ -596,16 +627,23 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
                        const float *x2, int64_t ldx, int64_t B, int op_kind, int out_op,
                        const float *norm_w, float eps, float *y, const float *res, void *stream) {
     q4::clear_error();
-    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU, Q4_ERR_INVALID_ARG,
-             "%s: unknown output transform %d", name, out_op);
-    Q4_CHECK(out_op != Q4_OUT_SWIGLU || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
-             "%s: a SwiGLU output needs an even N and no residual", name);
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU || out_op == Q4_OUT_GEGLU,
+             Q4_ERR_INVALID_ARG, "%s: unknown output transform %d", name, out_op);
+    const bool glu_out = out_op != Q4_OUT_PLAIN;
+    Q4_CHECK(!glu_out || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
+             "%s: a gated (SwiGLU / GeGLU) output needs an even N and no residual", name);
     Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
     Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
              name, (long long)N, (long long)K, (long long)B);
-    Q4_CHECK(op_kind >= Q4_IN_PLAIN && op_kind <= Q4_IN_SWIGLU, Q4_ERR_INVALID_ARG,
+    Q4_CHECK(op_kind >= Q4_IN_PLAIN && op_kind <= Q4_IN_GEGLU, Q4_ERR_INVALID_ARG,
              "%s: unknown input transform %d", name, op_kind);
-    Q4_CHECK(op_kind != Q4_IN_SWIGLU || x2, Q4_ERR_INVALID_ARG, "%s: SwiGLU needs x2", name);
+    const bool gated_in = op_kind == Q4_IN_SWIGLU || op_kind == Q4_IN_GEGLU;
+    Q4_CHECK(!gated_in || x2, Q4_ERR_INVALID_ARG, "%s: a gated input needs x2", name);
+    Q4_CHECK(!(gated_in && glu_out) || (op_kind == Q4_IN_GEGLU) == (out_op == Q4_OUT_GEGLU),
+             Q4_ERR_UNSUPPORTED, "%s: a gated input and a gated output must use the same activation",
+             name);
+    Q4_CHECK(FMT == 0 || (op_kind != Q4_IN_GEGLU && out_op != Q4_OUT_GEGLU), Q4_ERR_UNSUPPORTED,
+             "%s: GeGLU transforms are provided for Q4_0 weights", name);
     Q4_CHECK(op_kind != Q4_IN_RMSNORM || eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
     Q4_CHECK(ldx >= K, Q4_ERR_SHAPE, "%s: ld_x=%lld < K=%lld", name, (long long)ldx, (long long)K);
     Q4_CHECK(K % 32 == 0, Q4_ERR_SHAPE, "%s: K=%lld is not a multiple of 32", name, (long long)K);
@@ -620,16 +658,17 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     hipStream_t s = q4::as_stream(stream);
     const int n = static_cast<int>(N), k = static_cast<int>(K);
     const int nb = k / 32;
-    InOp op{op_kind, op_kind == Q4_IN_SWIGLU ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
-            eps, ldx, out_op == Q4_OUT_SWIGLU ? 1 : 0};
+    InOp op{gated_in ? 2 : op_kind, gated_in ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
+            eps, ldx, out_op == Q4_OUT_SWIGLU ? 1 : out_op == Q4_OUT_GEGLU ? 2 : 0,
+            op_kind == Q4_IN_GEGLU ? 1 : 0};
     int ks = 0;
     if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
         (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0) {
         for (int cand : {1, 2, 4})
             if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
     }
-    Q4_CHECK(out_op != Q4_OUT_SWIGLU || ks == 1, Q4_ERR_UNSUPPORTED,
-             "%s: a SwiGLU output needs K %% 256 == 0, K <= 8192, 16-byte aligned x", name);
+    Q4_CHECK(!glu_out || ks == 1, Q4_ERR_UNSUPPORTED,
+             "%s: a gated output needs K %% 256 == 0, K <= 8192, 16-byte aligned x", name);
     if (ks) {
         const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
         const int b = static_cast<int>(B);
@@ -672,8 +711,9 @@ extern "C" q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, cons
                            y, residual, stream);
 }
 
-extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens,
-                                 int64_t B, float *x, void *stream) {
+extern "C" q4_status q8_0_gather_scaled(const void *E, int64_t V, int64_t K,
+                                        const int32_t *tokens, int64_t B, float scale, float *x,
+                                        void *stream) {
     q4::clear_error();
     Q4_CHECK(E && tokens && x, Q4_ERR_INVALID_ARG, "q8_0_gather: E, tokens and x must not be NULL");
     Q4_CHECK(V >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "q8_0_gather: V, K, B must be >= 1");
@@ -685,6 +725,11 @@ extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int3
     const int total = static_cast<int>(B) * static_cast<int>(K / 32);
     hipLaunchKernelGGL(q8_gather_kernel, dim3((total + kWG - 1) / kWG), dim3(kWG), 0,
                        q4::as_stream(stream), static_cast<const uint8_t *>(E), tokens, x,
-                       static_cast<int>(V), static_cast<int>(K), static_cast<int>(B));
+                       static_cast<int>(V), static_cast<int>(K), static_cast<int>(B), scale);
     return q4::launch_status("q8_0_gather");
+}
+
+extern "C" q4_status q8_0_gather(const void *E, int64_t V, int64_t K, const int32_t *tokens,
+                                 int64_t B, float *x, void *stream) {
+    return q8_0_gather_scaled(E, V, K, tokens, B, 1.0f, x, stream);
 }

@@ -80,7 +80,11 @@ struct BF<1> {
     static constexpr int kLaneDw = 17;  // two blocks: 68 bytes
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// act(g) * u with act = SiLU (a == 0) or the tanh form of GELU (a == 1).
+__device__ __forceinline__ float glu_mul(int a, float g, float u) {
+    if (a) return 0.5f * g * (1.0f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
+    return g / (1.0f + expf(-g)) * u;
+}
 
 // Offset inside a block of element e (0..7) of lane group g.
 template <int FMT>
@@ -250,7 +254,8 @@ __device__ __forceinline__ void weight_operands(const uint32_t (&dw)[BF<FMT>::kL
 // applied); with one, it stores its partials, takes a ticket, and the last
 // split of the row range adds the S partials in split order.
 struct FinishArgs {
-    int N, K, B, S, glu, rx;  // B: rows of the group; rx: the row range
+    int N, K, B, S, glu, rx;  // B: rows of the group; glu: 0, or 1 + act of a gated output;
+                              // rx: the row range
     float eps;
     float *y;
     const float *res;
@@ -292,8 +297,8 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
             __syncthreads();
             if (wv < kHalf && rvalid) {
                 const int64_t lp = P;
-                if (ba < B) y[ba * lp + pu] = silu_mul(ya * ia, upx[pl][ba]);
-                if (bb < B) y[bb * lp + pu] = silu_mul(yb * ib, upx[pl][bb]);
+                if (ba < B) y[ba * lp + pu] = glu_mul(glu - 1, ya * ia, upx[pl][ba]);
+                if (bb < B) y[bb * lp + pu] = glu_mul(glu - 1, yb * ib, upx[pl][bb]);
             }
             return;
         }
@@ -378,7 +383,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     if (glu) {
         if (act[0]) {
             const float inv = KIND == 1 ? inv_s[ob[0]] : 1.f;
-            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = silu_mul(sum[0] * inv, sum[1] * inv);
+            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = glu_mul(glu - 1, sum[0] * inv, sum[1] * inv);
         }
     } else {
 #pragma unroll
@@ -397,7 +402,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int cps, int glu, int rg, int NG) {
+    float *__restrict__ part, int S, int cps, int glu, int iact, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
                     ssq = fmaf(a, a, ssq);
                     t = a * tv[h][e >> 2][e & 3];
                 } else if constexpr (KIND == 2) {
-                    t = silu_mul(a, tv[h][e >> 2][e & 3]);
+                    t = glu_mul(iact, a, tv[h][e >> 2][e & 3]);
                 }
                 v[h][e] = t;
                 lm = fmaxf(lm, fabsf(t));
@@ -568,7 +573,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int spw, int glu, int rg, int NG) {
+    float *__restrict__ part, int S, int spw, int glu, int iact, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t opnd[4][kSeg][64];               // per wavefront: its step's activation operands
@@ -679,7 +684,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
                 }
             } else if constexpr (KIND == 2) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = silu_mul(xv[b][e], tv[b][e]);
+                for (int e = 0; e < 4; ++e) t[e] = glu_mul(iact, xv[b][e], tv[b][e]);
             }
             xv[b] = t;
             mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
@@ -854,7 +859,7 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt) {
 
 template <int FMT, int KIND>
 void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
-            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu,
+            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu, int iact,
             hipStream_t s) {
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     int *ctr = reinterpret_cast<int *>(w8);
@@ -863,12 +868,12 @@ void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *
     const dim3 grid(p.gx, p.S);
     if (!p.tiles) {
         hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
+                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, iact, p.rg, p.NG);
         return;
     }
     constexpr int T = FMT == 1 ? 2 : 4;
     hipLaunchKernelGGL((mv_mfma_tile_kernel<FMT, KIND, T>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
+                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, iact, p.rg, p.NG);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -882,16 +887,17 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
                         const float *norm_w, float eps, float *y, const float *res, void *ws,
                         size_t ws_bytes, void *stream) {
     q4::clear_error();
-    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU, Q4_ERR_INVALID_ARG,
-             "%s: unknown output transform %d", name, out_op);
-    Q4_CHECK(out_op != Q4_OUT_SWIGLU || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
-             "%s: a SwiGLU output needs an even N and no residual", name);
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU || out_op == Q4_OUT_GEGLU,
+             Q4_ERR_INVALID_ARG, "%s: unknown output transform %d", name, out_op);
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || (N % 2 == 0 && !res), Q4_ERR_INVALID_ARG,
+             "%s: a gated (SwiGLU / GeGLU) output needs an even N and no residual", name);
     Q4_CHECK(Wv && x && y, Q4_ERR_INVALID_ARG, "%s: W, x and y must not be NULL", name);
     Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
              name, (long long)N, (long long)K, (long long)B);
-    Q4_CHECK(op_kind >= Q4_IN_PLAIN && op_kind <= Q4_IN_SWIGLU, Q4_ERR_INVALID_ARG,
+    Q4_CHECK(op_kind >= Q4_IN_PLAIN && op_kind <= Q4_IN_GEGLU, Q4_ERR_INVALID_ARG,
              "%s: unknown input transform %d", name, op_kind);
-    Q4_CHECK(op_kind != Q4_IN_SWIGLU || x2, Q4_ERR_INVALID_ARG, "%s: SwiGLU needs x2", name);
+    Q4_CHECK((op_kind != Q4_IN_SWIGLU && op_kind != Q4_IN_GEGLU) || x2, Q4_ERR_INVALID_ARG,
+             "%s: a gated input needs x2", name);
     Q4_CHECK(op_kind != Q4_IN_RMSNORM || eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
     Q4_CHECK(ldx >= K, Q4_ERR_SHAPE, "%s: ld_x=%lld < K=%lld", name, (long long)ldx, (long long)K);
     Q4_CHECK(K % 256 == 0, Q4_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 256", name,
@@ -907,7 +913,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     Q4_CHECK(q4::aligned(y, 4) && (!res || q4::aligned(res, 4)), Q4_ERR_ALIGNMENT,
              "%s: y and residual must be 4-byte aligned", name);
     const size_t xbytes = static_cast<size_t>((B - 1) * ldx + K) * sizeof(float);
-    const size_t ybytes = static_cast<size_t>(B * (out_op == Q4_OUT_SWIGLU ? N / 2 : N)) * sizeof(float);
+    const size_t ybytes = static_cast<size_t>(B * (out_op != Q4_OUT_PLAIN ? N / 2 : N)) * sizeof(float);
     Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
              Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
     const Plan p = make_plan(N, K, B, FMT);
@@ -918,10 +924,14 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     hipStream_t s = q4::as_stream(stream);
     const uint8_t *W = static_cast<const uint8_t *>(Wv);
     const int n = static_cast<int>(N), k = static_cast<int>(K), b = static_cast<int>(B);
-    const int glu = out_op == Q4_OUT_SWIGLU ? 1 : 0;
-    if (op_kind == Q4_IN_RMSNORM) launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, glu, s);
-    else if (op_kind == Q4_IN_SWIGLU) launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, glu, s);
-    else launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, glu, s);
+    const int glu = out_op == Q4_OUT_SWIGLU ? 1 : out_op == Q4_OUT_GEGLU ? 2 : 0;
+    const int iact = op_kind == Q4_IN_GEGLU ? 1 : 0;
+    if (op_kind == Q4_IN_RMSNORM)
+        launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, glu, iact, s);
+    else if (op_kind == Q4_IN_SWIGLU || op_kind == Q4_IN_GEGLU)
+        launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, glu, iact, s);
+    else
+        launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, glu, iact, s);
     return q4::launch_status(name);
 }
 

@@ -26,7 +26,11 @@ def upload_model(m, weights, dev, caches=None):
             q_norm=torch.from_numpy(w["q_norm"]).to(dev), k_norm=torch.from_numpy(w["k_norm"]).to(dev),
             k_cache=as_dev(kc), v_cache=as_dev(vc),
             n_kv_heads=ly.n_kv_heads, head_dim=ly.head_dim, window=ly.window,
-            rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k))
+            rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k,
+            rope_dims=ly.rope_dims))
+        for key in ("post_attn_norm", "post_ffn_norm"):
+            if key in w:
+                layers[-1][key] = torch.from_numpy(w[key]).to(dev)
     return dict(embed=torch.from_numpy(weights["embed"]).to(dev),
                 final_norm=torch.from_numpy(weights["final_norm"]).to(dev), layers=layers)
 
@@ -34,7 +38,9 @@ def upload_model(m, weights, dev, caches=None):
 def gpu_model(q, m, dev_model):
     return q.DecodeModel(d_model=m.d_model, n_q_heads=m.n_q_heads, ffn=m.ffn, vocab=m.vocab,
                          batch=m.batch, eps=m.eps, embed=dev_model["embed"],
-                         final_norm=dev_model["final_norm"], layers=dev_model["layers"])
+                         final_norm=dev_model["final_norm"], layers=dev_model["layers"],
+                         ffn_act=m.ffn_act, embed_scale=m.embed_scale,
+                         logit_softcap=m.logit_softcap)
 
 
 def run_gpu(q, m, dev_model, steps, eager=False, want_logits=True):

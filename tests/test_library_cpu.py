@@ -83,8 +83,29 @@ def test_swiglu_output_rejected_where_unsupported():
     assert _status(L.q4_0_matvec_fused, *fused(101, 512, None))[0] == "Q4_ERR_INVALID_ARG"   # odd N
     assert _status(L.q4_0_matvec_fused, *fused(100, 512, ybuf))[0] == "Q4_ERR_INVALID_ARG"  # residual
     assert _status(L.q4_0_matvec_fused, *fused(100, 16384, None))[0] == "Q4_ERR_UNSUPPORTED"
-    assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 0, 2, None, 0.0, ybuf,
+    assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 0, 3, None, 0.0, ybuf,
                    None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # bad out_op
+    assert _status(L.q4_0_matvec_fused, fake, 101, 512, fake, None, 512, 1, 0, 2, None, 0.0, ybuf,
+                   None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # GeGLU, odd N
+    assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 4, 0, None, 0.0, ybuf,
+                   None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # bad op
+    assert _status(L.q4_0_matvec_fused, fake, 100, 512, fake, None, 512, 1, 3, 0, None, 0.0, ybuf,
+                   None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # GeGLU, no x2
+
+
+def test_gemma_variant_ops_reject_bad_arguments_on_host():
+    import ctypes as C
+    L = q.lib()
+    a, b = 0x10000, 0x20000
+    assert _status(L.rmsnorm_add, a, None, 4, 100, 1e-6, a + 200, None)[0] == "Q4_ERR_INVALID_ARG"  # overlap
+    assert _status(L.rmsnorm_add, a, None, 4, 100, -1.0, b, None)[0] == "Q4_ERR_INVALID_ARG"      # eps
+    assert _status(L.softcap, a, 10, 0.0, None)[0] == "Q4_ERR_INVALID_ARG"                       # cap
+    assert _status(L.softcap, a + 2, 10, 30.0, None)[0] == "Q4_ERR_ALIGNMENT"
+    assert _status(L.geglu, a, None, 1, 8, 8, b, None)[0] == "Q4_ERR_INVALID_ARG"
+    kv = _lib.KVLayout(1, 2, 128, 16, 4096, 2048, 128, 0)
+    args = lambda rot: (a, 512, a, a, 512, a, a, 4, C.byref(kv), b, 1e4, 1e-6, 0, rot, a, a, None)
+    for rot in (0, 3, 130):  # too small, odd, beyond head_dim
+        assert _status(L.qk_norm_rope_partial, *args(rot))[0] == "Q4_ERR_INVALID_ARG"
 
 
 def test_decode_model_batch_limits_on_host():
@@ -115,3 +136,31 @@ def test_decode_model_batch_limits_on_host():
     assert status(16, ffn=544) == "Q4_ERR_UNSUPPORTED"         # ffn % 256
     assert status(16, hd=64, d_model=256, wq_off=2) == "Q4_ERR_UNSUPPORTED"  # 2-byte aligned wqkv
     assert status(8, wq_off=2) == "Q4_OK"
+
+
+def test_decode_model_variant_options_on_host():
+    import ctypes as C
+    L = q.lib()
+    fake = 0x100000
+
+    def status(ffn_act=0, embed_scale=0.0, softcap=0.0, rope_dims=0, post=0):
+        ly = (_lib.LayerDesc * 1)()
+        l0 = ly[0]
+        for f in ("wqkv", "wo", "wgu", "wd", "attn_norm", "ffn_norm", "q_norm", "k_norm",
+                  "k_cache", "v_cache"):
+            setattr(l0, f, fake)
+        l0.n_kv_heads, l0.head_dim, l0.cap, l0.window = 2, 64, 64, 0
+        l0.rope_theta, l0.attn_scale, l0.v_from_k, l0.rope_dims = 1e4, 0.125, 0, rope_dims
+        l0.post_attn_norm = fake + post if post else None
+        d = _lib.ModelDesc(1, 256, 4, 512, 1000, 2, 1e-6, fake, fake,
+                           C.cast(ly, C.POINTER(_lib.LayerDesc)), ffn_act, embed_scale, softcap)
+        nbytes = C.c_size_t()
+        return _status(L.decode_model_workspace, C.byref(d), C.byref(nbytes))[0]
+
+    assert status() == "Q4_OK"
+    assert status(ffn_act=1, embed_scale=16.0, softcap=30.0, rope_dims=16, post=0x100) == "Q4_OK"
+    assert status(ffn_act=2) == "Q4_ERR_INVALID_ARG"
+    assert status(softcap=-1.0) == "Q4_ERR_INVALID_ARG"
+    assert status(rope_dims=15) == "Q4_ERR_INVALID_ARG"
+    assert status(rope_dims=66) == "Q4_ERR_INVALID_ARG"
+    assert status(post=2) == "Q4_ERR_ALIGNMENT"

@@ -134,6 +134,8 @@ FUSED_CASES = [
     ("q4", 300, 2560, 1, "rms"), ("q4", 257, 5376, 1, "swiglu"), ("q4", 200, 21504, 1, "swiglu"),
     ("q4", 130, 21504, 1, "rms"), ("q4", 100, 2560, 8, "rms"), ("q4", 64, 9728, 8, "swiglu"),
     ("q8", 1000, 5376, 1, "rms"), ("q8", 300, 2560, 8, "rms"), ("q4", 77, 2048, 1, "rms_unit"),
+    # GeGLU input (tanh-form GELU gate): LDS-staged, split-K, B > 1
+    ("q4", 257, 5376, 1, "geglu"), ("q4", 200, 21504, 1, "geglu"), ("q4", 64, 9728, 8, "geglu"),
 ]
 
 
@@ -144,19 +146,22 @@ def test_matvec_fused_input_parity(dev, fmt, n, k, b, op):
     orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
     fn = q.q4_0_matvec_fused if fmt == "q4" else q.q8_0_matvec_fused
     W = gen(106, f"t.fused.{fmt}.{n}.{k}", n, k)
-    ld = 2 * k if op == "swiglu" else k
+    ld = 2 * k if op in ("swiglu", "geglu") else k
     xa = synth.normal_f32(106, f"t.fused.x.{k}.{b}", (b, ld)) * 2.0
     w = synth.uniform_f32(106, f"t.fused.w.{k}", (k,), 0.8, 1.2)
     r = synth.normal_f32(106, f"t.fused.r.{n}.{b}", (b, n))
     if op == "swiglu":
         xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
+    elif op == "geglu":
+        xin = np.stack([oracle.geglu(xa[i, :k], xa[i, k:]) for i in range(b)])
     else:
         xin = oracle.rmsnorm(xa[:, :k], None if op == "rms_unit" else w, 1e-6)
     ref, terms = orc(W, n, k, xin, res=r)
     xd = torch.from_numpy(xa).to(dev)
     yr = torch.from_numpy(r).to(dev)
-    kind = q.IN_SWIGLU if op == "swiglu" else q.IN_RMSNORM
-    fn(torch.from_numpy(W).to(dev), xd, k, b, ld, kind, x2=xd[:, k:] if op == "swiglu" else None,
+    kind = {"swiglu": q.IN_SWIGLU, "geglu": q.IN_GEGLU}.get(op, q.IN_RMSNORM)
+    fn(torch.from_numpy(W).to(dev), xd, k, b, ld, kind,
+       x2=xd[:, k:] if op in ("swiglu", "geglu") else None,
        norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6, y=yr, residual=yr)
     torch.cuda.synchronize()
     _check(yr, ref, terms, f"{fmt} fused {op} {n}x{k} B={b}")
@@ -179,18 +184,22 @@ BATCHED_CASES = [
     ("q4", 2000, 2560, 9, "rms"), ("q4", 2560, 4096, 16, "plain"), ("q4", 300, 9728, 13, "swiglu"),
     ("q4", 8192, 4096, 32, "swiglu"), ("q4", 8200, 4096, 24, "rms"), ("q4", 33000, 1024, 17, "plain"),
     ("q8", 8200, 2048, 20, "rms"), ("q8", 3001, 2560, 32, "plain"), ("q8", 140000, 256, 12, "rms"),
+    # GeGLU input on both kernels
+    ("q4", 300, 9728, 8, "geglu"), ("q4", 8192, 4096, 16, "geglu"), ("q4", 130, 21504, 3, "geglu"),
 ]
 
 
 def _fused_inputs(fmt, n, k, b, op, seed):
     gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
     W = gen(seed, f"t.batched.{fmt}.{n}.{k}", n, k)
-    ld = 2 * k if op == "swiglu" else k
+    ld = 2 * k if op in ("swiglu", "geglu") else k
     xa = synth.normal_f32(seed, f"t.batched.x.{k}.{b}", (b, ld)) * 2.0
     w = synth.uniform_f32(seed, f"t.batched.w.{k}", (k,), 0.8, 1.2)
     r = synth.normal_f32(seed, f"t.batched.r.{n}.{b}", (b, n))
     if op == "swiglu":
         xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
+    elif op == "geglu":
+        xin = np.stack([oracle.geglu(xa[i, :k], xa[i, k:]) for i in range(b)])
     elif op == "plain":
         xin = xa[:, :k].astype(np.float64)
     else:
@@ -198,7 +207,8 @@ def _fused_inputs(fmt, n, k, b, op, seed):
     return W, xa, w, r, xin, ld
 
 
-_KIND = {"plain": q.IN_PLAIN, "rms": q.IN_RMSNORM, "rms_unit": q.IN_RMSNORM, "swiglu": q.IN_SWIGLU}
+_KIND = {"plain": q.IN_PLAIN, "rms": q.IN_RMSNORM, "rms_unit": q.IN_RMSNORM, "swiglu": q.IN_SWIGLU,
+         "geglu": q.IN_GEGLU}
 
 
 @pytest.mark.parametrize("fmt,n,k,b,op", BATCHED_CASES)
@@ -211,7 +221,7 @@ def test_matvec_batched_parity(dev, fmt, n, k, b, op):
     xd = torch.from_numpy(xa).to(dev)
     yr = torch.from_numpy(r).to(dev)
     Wd = torch.from_numpy(W).to(dev)
-    kw = dict(x2=xd[:, k:] if op == "swiglu" else None,
+    kw = dict(x2=xd[:, k:] if op in ("swiglu", "geglu") else None,
               norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
     y0 = fn(Wd, xd, k, b, ld, _KIND[op], **kw)
     fn(Wd, xd, k, b, ld, _KIND[op], y=yr, residual=yr, **kw)
@@ -330,7 +340,7 @@ def test_matvec_swiglu_output(dev, path, n, k, b, op):
     tol = 1.1 * tg * np.abs(u) + np.abs(g / (1.0 + np.exp(-g))) * tu + 2e-4 * np.abs(ref) + 1e-6
     xd = torch.from_numpy(xa).to(dev)
     fn = q.q4_0_matvec_batched if path == "batched" else q.q4_0_matvec_fused
-    kw = dict(x2=xd[:, k:] if op == "swiglu" else None,
+    kw = dict(x2=xd[:, k:] if op in ("swiglu", "geglu") else None,
               norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
     h = fn(torch.from_numpy(W).to(dev), xd, k, b, ld, _KIND[op], out_op=q.OUT_SWIGLU, **kw)
     torch.cuda.synchronize()
@@ -338,3 +348,51 @@ def test_matvec_swiglu_output(dev, path, n, k, b, op):
     assert got.shape == (b, F)
     ratio = float((np.abs(got - ref) / tol).max())
     assert np.all(np.isfinite(got)) and ratio <= 1.0, f"max err/tol {ratio:.3e}"
+
+
+
+GEGLU_OUT_CASES = [
+    # (path, N, K, B, op): merged gate|up with the GeGLU output (tanh-form GELU gate)
+    ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 77, 2048, 3, "plain"),
+    ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 1000, 5376, 2, "rms"),
+    ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
+]
+
+
+@pytest.mark.parametrize("path,n,k,b,op", GEGLU_OUT_CASES)
+def test_matvec_geglu_output(dev, path, n, k, b, op):
+    """y[p] = gelu(z[p]) * z[p + N/2]: bound from the two matvec bounds through
+    gelu(g) u (|gelu'| <= 1.13 for the tanh form) plus 2e-4 relative."""
+    _say(f"{path} geglu output {op} N={n} K={k} B={b}")
+    W, xa, w, r, xin, ld = _fused_inputs("q4", n, k, b, op, 117)
+    z, t = oracle.q4_0_matvec(W, n, k, xin)
+    F = n // 2
+    g, u = z[:, :F], z[:, F:]
+    tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+    ref = oracle.geglu(g, u)
+    gel = np.abs(oracle.geglu(g, np.ones_like(g)))
+    tol = 1.13 * tg * np.abs(u) + gel * tu + 2e-4 * np.abs(ref) + 1e-6
+    xd = torch.from_numpy(xa).to(dev)
+    fn = q.q4_0_matvec_batched if path == "batched" else q.q4_0_matvec_fused
+    kw = dict(norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
+    h = fn(torch.from_numpy(W).to(dev), xd, k, b, ld, _KIND[op], out_op=q.OUT_GEGLU, **kw)
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.float64)
+    assert got.shape == (b, F)
+    ratio = float((np.abs(got - ref) / tol).max())
+    assert np.all(np.isfinite(got)) and ratio <= 1.0, f"max err/tol {ratio:.3e}"
+
+
+def test_q8_0_gather_scaled(dev):
+    """Rows times a scale (the Gemma-4 sqrt(d) embedding scale): (d q) s in fp32,
+    within one rounding of the exact product."""
+    _say("q8_0_gather_scaled")
+    v, k = 1000, 5376
+    E = synth.q8_0_matrix(108, "t.gather_s", v, k)
+    tok = np.array([0, 999, 17, 512], dtype=np.int32)
+    s = float(np.float32(np.sqrt(5376.0)))
+    ref = oracle.q8_0_gather(E, v, k, tok) * s
+    x = q.q8_0_gather(torch.from_numpy(E).to(dev), torch.from_numpy(tok).to(dev), k, scale=s)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -24 * np.abs(ref))

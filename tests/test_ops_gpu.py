@@ -392,3 +392,87 @@ def test_gqa_decode_attn_rope_f16_cache(dev, B, hq, hkv, hd, cap, pos, window, v
         o, bound = _attn_oracle(qref, kc[b], vc[b], pos + 1, window, scale, cap)
         worst = max(worst, float((np.abs(got[b].reshape(hq, hd) - o) / (2e-4 * bound + 1e-6)).max()))
     assert worst <= 1.0, f"max err/tol {worst:.3e}"
+
+
+# ---------------------------------------------------------------- Gemma-4 variants
+@pytest.mark.parametrize("rows,n", [(1, 21504), (8, 9728), (3, 7)])
+def test_geglu_parity(dev, rows, n):
+    _say(f"geglu {rows}x{n}")
+    gu = synth.normal_f32(217, f"geglu.{rows}.{n}", (rows, 2 * n)) * 4.0
+    ref = np.stack([oracle.geglu(gu[r, :n], gu[r, n:]) for r in range(rows)])
+    g = torch.from_numpy(gu).to(dev)
+    h = q.geglu(g, g[:, n:], rows, n, 2 * n)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(_np(h) - ref) <= 2e-4 * np.abs(ref) + 1e-6)
+
+
+@pytest.mark.parametrize("rows,dim,gain", [(1, 5376, True), (8, 2560, True), (3, 100, False)])
+def test_rmsnorm_add_parity(dev, rows, dim, gain):
+    """x += w * y / rms(y): the sandwich post-norm joining the residual."""
+    _say(f"rmsnorm_add {rows}x{dim}")
+    y = synth.normal_f32(218, f"rna.y.{rows}.{dim}", (rows, dim)) * 3.0
+    x0 = synth.normal_f32(218, f"rna.x.{rows}.{dim}", (rows, dim))
+    w = synth.uniform_f32(218, f"rna.w.{dim}", (dim,), 0.8, 1.2) if gain else None
+    normed = oracle.rmsnorm(y, w, 1e-6)
+    ref = x0.astype(np.float64) + normed
+    xd = torch.from_numpy(x0).to(dev)
+    q.rmsnorm_add(torch.from_numpy(y).to(dev), torch.from_numpy(w).to(dev) if gain else None, 1e-6, xd)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(_np(xd) - ref) <= 2e-4 * np.abs(normed) + 2.0 ** -23 * np.abs(ref) + 1e-6)
+
+
+def test_softcap_parity(dev):
+    _say("softcap")
+    v = synth.normal_f32(219, "softcap", (4, 262144)) * 40.0
+    ref = oracle.softcap(v, 30.0)
+    vd = torch.from_numpy(v).to(dev)
+    q.softcap(vd, 30.0)
+    torch.cuda.synchronize()
+    got = _np(vd)
+    assert np.all(np.abs(got - ref) <= 2e-6 * 30.0)
+    # increasing: the greedy choice is the same before and after
+    assert np.array_equal(got.argmax(axis=1), v.argmax(axis=1))
+
+
+@pytest.mark.parametrize("hd,rot", [(512, 128), (256, 64), (128, 32), (64, 16), (128, 128)])
+@pytest.mark.parametrize("v_from_k", [False, True])
+def test_qk_norm_rope_partial_parity(dev, hd, rot, v_from_k):
+    """p-RoPE: the first rot elements rotate (as a rot-dim NeoX rotation), the
+    rest are only normalised; q in place, k and v appended."""
+    _say(f"qk_norm_rope_partial hd={hd} rot={rot} v_from_k={v_from_k}")
+    B, hq, hkv, cap, pos, theta = 2, 4, 2, 16, 8200, 1e6
+    nq, nk = hq * hd, hkv * hd
+    ld = nq + nk + (0 if v_from_k else nk)
+    rows = synth.normal_f32(220, f"qkp.rows.{hd}", (B, ld)) * 2.0
+    qn = synth.uniform_f32(220, f"qkp.qn.{hd}", (hd,), 0.8, 1.2)
+    kn = synth.uniform_f32(220, f"qkp.kn.{hd}", (hd,), 0.8, 1.2)
+    kc0 = synth.normal_f32(220, f"qkp.kc.{hd}", (B, hkv, cap, hd))
+    vc0 = synth.normal_f32(220, f"qkp.vc.{hd}", (B, hkv, cap, hd))
+    rows_d = torch.from_numpy(rows).to(dev)
+    kc_d, vc_d = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
+    q.qk_norm_rope(rows_d, ld, rows_d[:, nq:], None if v_from_k else rows_d[:, nq + nk:], ld,
+                   torch.from_numpy(qn).to(dev), torch.from_numpy(kn).to(dev), hq,
+                   kv_layout_of(kc_d), pos_d, theta, 1e-6, v_from_k, kc_d, vc_d, rot_dims=rot)
+    torch.cuda.synchronize()
+    got, kc, vc = _np(rows_d), _np(kc_d), _np(vc_d)
+    slot = pos % cap
+
+    def tol(normed):
+        t = np.concatenate([_rope_tol(normed[..., :rot], pos, theta),
+                            2e-4 * np.abs(normed[..., rot:]) + 1e-6], axis=-1)
+        return t
+
+    for b in range(B):
+        qnorm = oracle.rmsnorm(rows[b, :nq].reshape(hq, hd), qn, 1e-6)
+        qref = oracle.rope_neox(qnorm, pos, theta, rot)
+        assert np.all(np.abs(got[b, :nq].reshape(hq, hd) - qref) <= tol(qnorm))
+        kr = rows[b, nq:nq + nk].reshape(hkv, hd)
+        knorm = oracle.rmsnorm(kr, kn, 1e-6)
+        kref = oracle.rope_neox(knorm, pos, theta, rot)
+        assert np.all(np.abs(kc[b, :, slot] - kref) <= tol(knorm))
+        vref = (oracle.rmsnorm(kr, None, 1e-6) if v_from_k
+                else rows[b, nq + nk:].reshape(hkv, hd).astype(np.float64))
+        assert np.all(np.abs(vc[b, :, slot] - vref) <= 2e-4 * np.abs(vref) + 1e-6)
+    others = np.arange(cap) != slot
+    assert np.array_equal(kc[:, :, others], kc0[:, :, others])
