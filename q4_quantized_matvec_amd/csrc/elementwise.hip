@@ -29,17 +29,24 @@ __global__ __launch_bounds__(kNormWG) void rmsnorm_kernel(const float *x, const 
     const float *xr = x + static_cast<size_t>(blockIdx.x) * dim;
     float *yr = y + static_cast<size_t>(blockIdx.x) * dim;
     const int tid = threadIdx.x;
-    float v[kNormU];
+    float v[kNormU], g[kNormU], d[kNormU];  // input, gain, (ADD) the accumulated row
     float ss = 0.f;
     const bool held = dim <= kNormWG * kNormU;
     if (held) {
+        // every load of the thread goes out before the reduction: one round trip
 #pragma unroll
         for (int u = 0; u < kNormU; ++u) {
             const int i = tid + u * kNormWG;
-            v[u] = i < dim ? xr[i] : 0.f;
+            const int ic = i < dim ? i : dim - 1;
+            v[u] = xr[ic];
+            g[u] = w ? w[ic] : 1.0f;
+            if constexpr (ADD) d[u] = yr[ic];
         }
 #pragma unroll
-        for (int u = 0; u < kNormU; ++u) ss = __builtin_fmaf(v[u], v[u], ss);
+        for (int u = 0; u < kNormU; ++u) {
+            if (tid + u * kNormWG >= dim) v[u] = 0.f;
+            ss = __builtin_fmaf(v[u], v[u], ss);
+        }
     } else {
         for (int i0 = 0; i0 < dim; i0 += kNormWG * kNormU) {
 #pragma unroll
@@ -58,13 +65,24 @@ __global__ __launch_bounds__(kNormWG) void rmsnorm_kernel(const float *x, const 
 #pragma unroll
     for (int k = 0; k < kNormWG / 64; ++k) tot += red[k];  // fixed order
     const float inv = 1.0f / sqrtf(tot / static_cast<float>(dim) + eps);
+    if (held) {
+#pragma unroll
+        for (int u = 0; u < kNormU; ++u) {
+            const int i = tid + u * kNormWG;
+            if (i < dim) {
+                const float t = v[u] * inv * g[u];
+                if constexpr (ADD) yr[i] = d[u] + t;
+                else yr[i] = t;
+            }
+        }
+        return;
+    }
     for (int i0 = 0; i0 < dim; i0 += kNormWG * kNormU) {
 #pragma unroll
         for (int u = 0; u < kNormU; ++u) {
             const int i = i0 + tid + u * kNormWG;
             if (i < dim) {
-                const float xv = held ? v[u] : xr[i];
-                const float t = xv * inv * (w ? w[i] : 1.0f);
+                const float t = xr[i] * inv * (w ? w[i] : 1.0f);
                 if constexpr (ADD) yr[i] += t;
                 else yr[i] = t;
             }
@@ -119,24 +137,33 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
                             : k + b * ldkv + static_cast<int64_t>(g) * hd;
     const float *gain = is_q ? qn : kn;
 
-    float a[kMaxPairsPerLane], c[kMaxPairsPerLane];
+    // Every load (values and gains) goes out before the reduction, with
+    // clamped addresses (zeroed afterwards), so all return in one round trip.
+    float a[kMaxPairsPerLane], c[kMaxPairsPerLane], ga[kMaxPairsPerLane], gc[kMaxPairsPerLane];
+#pragma unroll
+    for (int p = 0; p < kMaxPairsPerLane; ++p) {
+        const int i = min(lane + 64 * p, half - 1);
+        a[p] = src[i];
+        c[p] = src[i + half];
+        ga[p] = gain[i];
+        gc[p] = gain[i + half];
+    }
+    float t[kMaxPassPerLane], gt[kMaxPassPerLane];
+#pragma unroll
+    for (int p = 0; p < kMaxPassPerLane; ++p) {
+        const int i = min(rot + lane + 64 * p, hd - 1);
+        t[p] = src[i];
+        gt[p] = gain[i];
+    }
     float ss = 0.f;
 #pragma unroll
     for (int p = 0; p < kMaxPairsPerLane; ++p) {
-        const int i = lane + 64 * p;
-        a[p] = 0.f;
-        c[p] = 0.f;
-        if (i < half) {
-            a[p] = src[i];
-            c[p] = src[i + half];
-            ss = __builtin_fmaf(a[p], a[p], __builtin_fmaf(c[p], c[p], ss));
-        }
+        if (lane + 64 * p >= half) a[p] = c[p] = 0.f;
+        ss = __builtin_fmaf(a[p], a[p], __builtin_fmaf(c[p], c[p], ss));
     }
-    float t[kMaxPassPerLane];
 #pragma unroll
     for (int p = 0; p < kMaxPassPerLane; ++p) {
-        const int i = rot + lane + 64 * p;
-        t[p] = i < hd ? src[i] : 0.f;
+        if (rot + lane + 64 * p >= hd) t[p] = 0.f;
         ss = __builtin_fmaf(t[p], t[p], ss);
     }
     ss = wave_sum(ss);
@@ -173,8 +200,8 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
             const double red = __builtin_fma(-two_pi, rint(ang * (1.0 / two_pi)), ang);
             float sn, cs;
             sincosf(static_cast<float>(red), &sn, &cs);
-            const float x0 = a[p] * inv * gain[i];
-            const float x1 = c[p] * inv * gain[i + half];
+            const float x0 = a[p] * inv * ga[p];
+            const float x1 = c[p] * inv * gc[p];
             if (dst) {
                 dst[i] = x0 * cs - x1 * sn;
                 dst[i + half] = x1 * cs + x0 * sn;
@@ -199,7 +226,7 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     for (int p = 0; p < kMaxPassPerLane; ++p) {
         const int i = rot + lane + 64 * p;
         if (i < hd) {
-            const float x0 = t[p] * inv * gain[i];
+            const float x0 = t[p] * inv * gt[p];
             if (dst) dst[i] = x0;
             if (kdst) kdst[i] = static_cast<KT>(x0);
             if (vdst) {
