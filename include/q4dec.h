@@ -307,6 +307,15 @@ q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t n_q_heads,
  * Errors: Q4_ERR_INVALID_ARG, Q4_ERR_HIP. */
 q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int32_t *out, void *stream);
 
+/* argmax_rows_ws: the same choice in two passes with a caller-owned device
+ * workspace of argmax_rows_workspace(B) bytes (4-byte aligned, no
+ * initialisation needed): 64 workgroups per row reduce slices, then one
+ * wavefront per row reduces the slices in order.  Calls sharing a workspace
+ * must be ordered.  Errors as argmax_rows, plus Q4_ERR_WORKSPACE. */
+size_t argmax_rows_workspace(int64_t B);
+q4_status argmax_rows_ws(const float *logits, int64_t B, int64_t V, int32_t *out, void *ws,
+                         size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------ decode step
  * One autoregressive decode step of a pre-norm decoder ([GELO] 06 Compute
  * flow: per block RMSNorm -> merged QKV projection -> per-head QK-norm +

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     KVLayout,
     DecodeModel,
     argmax_rows,
+    argmax_rows_ws,
     gqa_decode_attn,
     gqa_decode_attn_rope,
     gqa_decode_attn_workspace,

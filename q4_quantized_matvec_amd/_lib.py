@@ -79,6 +79,8 @@ _SIGS = {
     "gqa_decode_attn_rope": ([_P, _I64, _I64, _P, _P, C.POINTER(KVLayout), _P, _D, _F, C.c_int, _P,
                               _P, _I64, _F, _P, _I64, _P, _SZ, _P], C.c_int),
     "argmax_rows": ([_P, _I64, _I64, _P, _P], C.c_int),
+    "argmax_rows_workspace": ([_I64], _SZ),
+    "argmax_rows_ws": ([_P, _I64, _I64, _P, _P, _SZ, _P], C.c_int),
     "decode_model_workspace": ([C.POINTER(ModelDesc), C.POINTER(_SZ)], C.c_int),
     "decode_model_create": ([C.POINTER(ModelDesc), _P, _SZ, C.POINTER(_P)], C.c_int),
     "decode_model_set_position": ([_P, _I64, _P], C.c_int),
@@ -365,6 +367,19 @@ def argmax_rows(logits, out=None, stream=None):
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=logits.device)
     _check("argmax_rows", lib().argmax_rows(_ptr(logits), B, V, _ptr(out), _stream(stream)))
+    return out
+
+
+def argmax_rows_ws(logits, out=None, ws=None, stream=None):
+    """argmax_rows in two passes (64 workgroups per row) with a workspace."""
+    import torch
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    if ws is None:
+        ws = torch.empty(lib().argmax_rows_workspace(B), dtype=torch.uint8, device=logits.device)
+    _check("argmax_rows_ws", lib().argmax_rows_ws(_ptr(logits), B, V, _ptr(out), _ptr(ws),
+                                                  ws.numel(), _stream(stream)))
     return out
 
 

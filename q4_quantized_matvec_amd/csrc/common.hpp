@@ -19,6 +19,12 @@ q4_status launch_status(const char *what);
 int device_cus();
 // Host validation of a KV-cache layout shared by the attention-side calls.
 q4_status check_kv_layout(const char *name, const q4_kv_layout *kv);
+// argmax_rows in two passes with a caller-owned scratch of
+// argmax_scratch_bytes(B) bytes (4-byte aligned): many workgroups per row
+// instead of one.  Same result as argmax_rows.
+size_t argmax_scratch_bytes(int64_t B);
+q4_status argmax_rows_scratch(const float *logits, int64_t B, int64_t V, int32_t *out,
+                              void *scratch, hipStream_t s);
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

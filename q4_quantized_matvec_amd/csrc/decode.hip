@@ -23,6 +23,7 @@ struct q4_decode_model {
     int64_t *pos_dev = nullptr;  // [0] = position of the next token, [1] = n = position + 1
     float *x = nullptr, *qkv = nullptr, *att = nullptr, *gu = nullptr;
     float *tmp = nullptr;  // a sublayer output before its sandwich post-norm [B][d_model]
+    void *arg = nullptr;  // the two-pass argmax's partial maxima
     float *logits = nullptr;
     void *attn_ws = nullptr;
     size_t attn_ws_bytes = 0;
@@ -58,7 +59,7 @@ __global__ void advance_position_kernel(int64_t *pos) {
 }
 
 struct Layout {
-    size_t pos, x, qkv, att, gu, logits, tmp, mv, mv_bytes, attn, total;
+    size_t pos, x, qkv, att, gu, logits, tmp, arg, mv, mv_bytes, attn, total;
 };
 
 int64_t layer_qkv_rows(const q4_model_desc &d, const q4_layer_desc &l) {
@@ -118,6 +119,7 @@ Layout plan(const q4_model_desc &d) {
     L.gu = take(sizeof(float) * B * 2 * d.ffn);
     L.logits = take(sizeof(float) * B * d.vocab);
     L.tmp = take(sizeof(float) * B * d.d_model);
+    L.arg = take(q4::argmax_scratch_bytes(B));
     L.mv = take(mv);
     L.mv_bytes = mv;
     L.attn = take(attn);
@@ -286,7 +288,7 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
     Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                    d.final_norm, lg, nullptr, sv));
     if (d.logit_softcap > 0.f) Q4_TRY(softcap(lg, B * d.vocab, d.logit_softcap, sv));
-    Q4_TRY(argmax_rows(lg, B, d.vocab, next, sv));
+    Q4_TRY(q4::argmax_rows_scratch(lg, B, d.vocab, next, m->arg, s));
     hipLaunchKernelGGL(advance_position_kernel, dim3(1), dim3(1), 0, s, m->pos_dev);
     return q4::launch_status("decode_step (advance)");
 }
@@ -337,6 +339,7 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     m->gu = reinterpret_cast<float *>(base + L.gu);
     m->logits = reinterpret_cast<float *>(base + L.logits);
     m->tmp = reinterpret_cast<float *>(base + L.tmp);
+    m->arg = base + L.arg;
     m->attn_ws = base + L.attn;
     m->attn_ws_bytes = L.total - L.attn;
     m->mv_ws = L.mv_bytes ? base + L.mv : nullptr;

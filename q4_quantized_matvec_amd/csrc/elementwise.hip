@@ -237,6 +237,83 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     }
 }
 
+// (value, index) order of the greedy choice: larger value, then lower index;
+// NaN never compares greater, so it never wins.
+__device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// Two-pass argmax.  Pass 1: kArgParts workgroups per row, each reducing a
+// contiguous slice (8 loads in flight per thread) to (value, index).
+constexpr int kArgParts = 64;
+__global__ __launch_bounds__(256) void argmax_part_kernel(const float *__restrict__ logits, int64_t V,
+                                                          float *__restrict__ pv, int *__restrict__ pi) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int part = blockIdx.x, b = blockIdx.y;
+    const int64_t per = (V + kArgParts - 1) / kArgParts;
+    const int64_t s = static_cast<int64_t>(part) * per;
+    const int64_t e = min(V, s + per);
+    const float *row = logits + static_cast<int64_t>(b) * V;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    constexpr int kU = 8;
+    for (int64_t i0 = s + threadIdx.x; i0 < e; i0 += 256 * kU) {
+        float v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = row[min(i0 + u * 256, e - 1)];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = i0 + u * 256;
+            if (i < e && arg_better(v[u], static_cast<int>(i), best, bi)) {
+                best = v[u];
+                bi = static_cast<int>(i);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (arg_better(ov, oi, best, bi)) {
+            best = ov;
+            bi = oi;
+        }
+    }
+    if ((threadIdx.x & 63) == 0) {
+        sv[threadIdx.x >> 6] = best;
+        si[threadIdx.x >> 6] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (arg_better(sv[w], si[w], best, bi)) {
+                best = sv[w];
+                bi = si[w];
+            }
+        pv[b * kArgParts + part] = best;
+        pi[b * kArgParts + part] = bi;
+    }
+}
+
+// Pass 2: one wavefront per row, lane l holding slice l.
+__global__ __launch_bounds__(64) void argmax_final_kernel(const float *__restrict__ pv,
+                                                          const int *__restrict__ pi, int32_t *out) {
+    const int b = blockIdx.x, l = threadIdx.x;
+    float best = pv[b * kArgParts + l];
+    int bi = pi[b * kArgParts + l];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bi, off);
+        if (arg_better(ov, oi, best, bi)) {
+            best = ov;
+            bi = oi;
+        }
+    }
+    if (l == 0) out[b] = bi == 0x7fffffff ? 0 : bi;
+}
+
 // One workgroup per row; (value, index) with the lowest index among equal
 // maxima.  NaN never compares greater, so it never wins.
 __global__ __launch_bounds__(1024) void argmax_kernel(const float *__restrict__ logits,
@@ -452,4 +529,38 @@ extern "C" q4_status argmax_rows(const float *logits, int64_t B, int64_t V, int3
     hipLaunchKernelGGL(argmax_kernel, dim3(static_cast<unsigned>(B)), dim3(1024), 0,
                        q4::as_stream(stream), logits, out, V);
     return q4::launch_status("argmax_rows");
+}
+
+namespace q4 {
+size_t argmax_scratch_bytes(int64_t B) {
+    return static_cast<size_t>(B) * kArgParts * (sizeof(float) + sizeof(int));
+}
+
+q4_status argmax_rows_scratch(const float *logits, int64_t B, int64_t V, int32_t *out, void *scratch,
+                              hipStream_t s) {
+    Q4_CHECK(logits && out && scratch, Q4_ERR_INVALID_ARG, "argmax: logits, out, scratch must not be NULL");
+    Q4_CHECK(B >= 1 && V >= 1 && B <= 65535 && V <= (1 << 30), Q4_ERR_INVALID_ARG, "argmax: bad sizes");
+    Q4_CHECK(aligned(scratch, 4), Q4_ERR_ALIGNMENT, "argmax: scratch must be 4-byte aligned");
+    float *pv = static_cast<float *>(scratch);
+    int *pi = reinterpret_cast<int *>(pv + B * kArgParts);
+    hipLaunchKernelGGL(argmax_part_kernel, dim3(kArgParts, static_cast<unsigned>(B)), dim3(256), 0, s,
+                       logits, V, pv, pi);
+    q4_status st = launch_status("argmax (parts)");
+    if (st != Q4_OK) return st;
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(static_cast<unsigned>(B)), dim3(64), 0, s, pv, pi, out);
+    return launch_status("argmax (final)");
+}
+}  // namespace q4
+
+extern "C" size_t argmax_rows_workspace(int64_t B) { return B >= 1 ? q4::argmax_scratch_bytes(B) : 0; }
+
+extern "C" q4_status argmax_rows_ws(const float *logits, int64_t B, int64_t V, int32_t *out, void *ws,
+                                    size_t ws_bytes, void *stream) {
+    q4::clear_error();
+    Q4_CHECK(B >= 1, Q4_ERR_INVALID_ARG, "argmax_rows_ws: B must be >= 1");
+    Q4_CHECK(ws && ws_bytes >= q4::argmax_scratch_bytes(B), Q4_ERR_WORKSPACE,
+             "argmax_rows_ws: workspace of %zu bytes needed, got %zu", q4::argmax_scratch_bytes(B), ws_bytes);
+    Q4_CHECK(q4::aligned(logits, 4) && q4::aligned(out, 4), Q4_ERR_ALIGNMENT,
+             "argmax_rows_ws: logits and out must be 4-byte aligned");
+    return q4::argmax_rows_scratch(logits, B, V, out, ws, q4::as_stream(stream));
 }

@@ -200,17 +200,28 @@ def test_gqa_decode_attn_deterministic(dev, B, cap):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-def test_argmax_rows_ties_and_parity(dev):
-    _say("argmax_rows")
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
+def test_argmax_rows_ties_and_parity(dev, two_pass):
+    _say(f"argmax_rows two_pass={two_pass}")
     V = 262144
-    lg = synth.normal_f32(206, "argmax", (4, V)) * 10.0
+    lg = synth.normal_f32(206, "argmax", (6, V)) * 10.0
     lg[1, 100] = lg[1, 7] = lg[1].max() + 1.0   # tie: lowest id wins
     lg[2, :] = -np.inf
     lg[3, 5] = np.nan
     lg[3, 9] = 1e30
-    got = q.argmax_rows(torch.from_numpy(lg).to(dev)).cpu().numpy()
-    exp = [oracle.argmax(lg[0])[0], 7, 0, 9]
+    # a tie across the two-pass slices (4096 columns each) and a row maximum
+    # in the last, partial position
+    lg[4, 5000] = lg[4, 200000] = lg[4].max() + 1.0
+    lg[5, V - 1] = lg[5].max() + 1.0
+    fn = q.argmax_rows_ws if two_pass else q.argmax_rows
+    got = fn(torch.from_numpy(lg).to(dev)).cpu().numpy()
+    exp = [oracle.argmax(lg[0])[0], 7, 0, 9, 5000, V - 1]
     assert got.tolist() == exp
+    if two_pass:  # odd vocabulary sizes, shorter than the slice count, B = 1..3
+        for v_, b_ in ((151936, 3), (1000, 2), (37, 1)):
+            x = synth.normal_f32(207, f"argmax.{v_}", (b_, v_))
+            g = q.argmax_rows_ws(torch.from_numpy(x).to(dev)).cpu().numpy()
+            assert g.tolist() == [oracle.argmax(x[i])[0] for i in range(b_)]
 
 
 ROPE_ATTN_CASES = [
