@@ -1,4 +1,5 @@
-// Split-K grouped-query decode attention over an fp32 KV cache, gfx950.
+// Split-K grouped-query decode attention over an fp32 or binary16 KV cache,
+// gfx950.
 //
 // Definition ("GELO LLM" page, 05 "Components": cached GQA attention where a
 // decode step's single query row attends every cached position plus the new
@@ -7,13 +8,15 @@
 //   o_h = sum_j softmax_j(scale * q_h . k_j) v_j ,  j in [lo, n),
 //   lo = max(0, n - W) (W = 0: lo = 0), kv head of query head h = h / G.
 //
-// Pass 1 (one workgroup per (chunk, kv head, sequence)): the G query heads
-// that share the kv head are held in VGPRs (pre-scaled), the chunk's keys are
-// read once for all of them, an exact softmax over the chunk gives (m, l) and
-// the un-normalised sum_j e^(s_j - m) v_j is formed with the same weights for
-// every query head.  Pass 2 merges the chunks of each query head in ascending
-// chunk order: o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the
-// non-empty chunks, M = max m_c, so the result does not depend on scheduling.
+// Pass 1 (one workgroup per (split, kv head, sequence); a split is one
+// 64-position chunk, or at long context several in a row): the G query heads
+// that share the kv head are held in VGPRs (pre-scaled), the keys are read
+// once for all of them, an exact softmax (running over the split's chunks)
+// gives (m, l) and the un-normalised sum_j e^(s_j - m) v_j is formed with the
+// same weights for every query head.  Pass 2 merges the splits of each query
+// head: o = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the non-empty
+// splits, M = max m_c, taken in a fixed order, so the result does not depend
+// on scheduling.
 #include "common.hpp"
 
 namespace {
@@ -395,13 +398,17 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 }
 
 // Merge: one workgroup per (query head, sequence, 64-dimension slice); four
-// groups accumulate interleaved split partials (np of them, in ascending
-// order within a group) and the groups are added in a fixed order.
+// groups take interleaved split partials (np of them, in ascending order
+// within a group), each with a running maximum: the maxima, sums and
+// partial vectors are requested together (one memory round trip), every
+// batch of kU partials rescales what came before by exp(m_old - m_new), and
+// the four groups are combined in a fixed order, rescaled to the largest
+// maximum.  So the result does not depend on scheduling.
 __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict__ part, int G,
                                                          int Hkv, int np, int GM, int hd,
                                                          float *__restrict__ out, int64_t ldo,
                                                          int B) {
-    __shared__ float rn[3][64], rd[3][64];
+    __shared__ float rm[3][64], rn[3][64], rd[3][64];
     const int h = blockIdx.x, b = blockIdx.y;
     const int g0 = h / G, g = h % G;
     const int cg = threadIdx.x >> 6, dl = threadIdx.x & 63;
@@ -409,14 +416,8 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
     const size_t units_total = static_cast<size_t>(B) * Hkv * np * GM;
     const float *pml = part + units_total * hd;
     const size_t u0 = (static_cast<size_t>(b) * Hkv + g0) * np * GM + g;
-    float M = -INFINITY;
-    for (int c = dl; c < np; c += 64) {
-        const size_t u = u0 + static_cast<size_t>(c) * GM;
-        if (pml[2 * u + 1] > 0.f) M = fmaxf(M, pml[2 * u]);
-    }
-    M = wave_max(M);
-    float num = 0.f, den = 0.f;
-    constexpr int kU = 8;  // chunks in flight per thread, still added in ascending order
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    constexpr int kU = 8;  // partials in flight per thread, added in ascending order
     for (int c0 = cg; c0 < np; c0 += 4 * kU) {
         float lv[kU], mv[kU], pv[kU];
 #pragma unroll
@@ -426,6 +427,16 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
             lv[r] = pml[2 * u + 1];
             mv[r] = pml[2 * u];
             pv[r] = d < hd ? part[u * hd + d] : 0.f;
+        }
+        float mb = M;
+#pragma unroll
+        for (int r = 0; r < kU; ++r)
+            if (c0 + 4 * r < np && lv[r] > 0.f) mb = fmaxf(mb, mv[r]);
+        if (mb > M) {  // rescale what the earlier batches added (nothing before the first)
+            const float a = __expf(M - mb);
+            num *= a;
+            den *= a;
+            M = mb;
         }
 #pragma unroll
         for (int r = 0; r < kU; ++r) {
@@ -437,14 +448,25 @@ __global__ __launch_bounds__(kWG) void attn_merge_kernel(const float *__restrict
         }
     }
     if (cg > 0) {
+        rm[cg - 1][dl] = M;
         rn[cg - 1][dl] = num;
         rd[cg - 1][dl] = den;
     }
     __syncthreads();
     if (cg == 0 && d < hd) {
+        float Mx = M;
+        for (int k = 0; k < 3; ++k) Mx = fmaxf(Mx, rm[k][dl]);
+        if (Mx == -INFINITY) {  // no key at all
+            out[b * ldo + static_cast<int64_t>(h) * hd + d] = 0.f;
+            return;
+        }
+        const float a0 = __expf(M - Mx);  // 0 for a group without partials
+        num *= a0;
+        den *= a0;
         for (int k = 0; k < 3; ++k) {
-            num += rn[k][dl];
-            den += rd[k][dl];
+            const float a = __expf(rm[k][dl] - Mx);
+            num = __builtin_fmaf(a, rn[k][dl], num);
+            den = __builtin_fmaf(a, rd[k][dl], den);
         }
         out[b * ldo + static_cast<int64_t>(h) * hd + d] = den > 0.f ? num / den : 0.f;
     }
