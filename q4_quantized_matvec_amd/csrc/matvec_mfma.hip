@@ -80,10 +80,13 @@ struct BF<1> {
     static constexpr int kLaneDw = 17;  // two blocks: 68 bytes
 };
 
-// act(g) * u with act = SiLU (a == 0) or the tanh form of GELU (a == 1).
-__device__ __forceinline__ float glu_mul(int a, float g, float u) {
-    if (a) return 0.5f * g * (1.0f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
-    return g / (1.0f + expf(-g)) * u;
+// act(g) * u with act = SiLU or (GELU) the tanh form of GELU; a template
+// parameter so that the GELU code is only in the kernels that use it (larger
+// kernels start measurably slower when launched back to back with others).
+template <bool GELU>
+__device__ __forceinline__ float act_mul(float g, float u) {
+    if constexpr (GELU) return 0.5f * g * (1.0f + tanhf(0.7978845608028654f * (g + 0.044715f * g * g * g))) * u;
+    else return g / (1.0f + expf(-g)) * u;
 }
 
 // Offset inside a block of element e (0..7) of lane group g.
@@ -254,8 +257,7 @@ __device__ __forceinline__ void weight_operands(const uint32_t (&dw)[BF<FMT>::kL
 // applied); with one, it stores its partials, takes a ticket, and the last
 // split of the row range adds the S partials in split order.
 struct FinishArgs {
-    int N, K, B, S, glu, rx;  // B: rows of the group; glu: 0, or 1 + act of a gated output;
-                              // rx: the row range
+    int N, K, B, S, glu, rx;  // B: rows of the group; glu: a gated output; rx: the row range
     float eps;
     float *y;
     const float *res;
@@ -264,7 +266,7 @@ struct FinishArgs {
     float *part;
 };
 
-template <int KIND, int T>
+template <int KIND, int T, bool GELU>
 __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb, int n, bool rvalid, int pl,
                                        int pu, float (&ssq_w)[4][kMaxB]) {
     constexpr int kRows = 16 * T, kPairs = 8 * T;
@@ -297,8 +299,8 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
             __syncthreads();
             if (wv < kHalf && rvalid) {
                 const int64_t lp = P;
-                if (ba < B) y[ba * lp + pu] = glu_mul(glu - 1, ya * ia, upx[pl][ba]);
-                if (bb < B) y[bb * lp + pu] = glu_mul(glu - 1, yb * ib, upx[pl][bb]);
+                if (ba < B) y[ba * lp + pu] = act_mul<GELU>(ya * ia, upx[pl][ba]);
+                if (bb < B) y[bb * lp + pu] = act_mul<GELU>(yb * ib, upx[pl][bb]);
             }
             return;
         }
@@ -383,7 +385,7 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
     if (glu) {
         if (act[0]) {
             const float inv = KIND == 1 ? inv_s[ob[0]] : 1.f;
-            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = glu_mul(glu - 1, sum[0] * inv, sum[1] * inv);
+            y[ob[0] * static_cast<int64_t>(P) + (row[0])] = act_mul<GELU>(sum[0] * inv, sum[1] * inv);
         }
     } else {
 #pragma unroll
@@ -397,12 +399,12 @@ __device__ __forceinline__ void finish(const FinishArgs &fa_, float ya, float yb
         __hip_atomic_store(&counters[rx * kCounterStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FMT, int KIND>
+template <int FMT, int KIND, bool GELU>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void mv_mfma_step_kernel(
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int cps, int glu, int iact, int rg, int NG) {
+    float *__restrict__ part, int S, int cps, int glu, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t frag[2][kSeg][64];    // activation operands of a step
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
                     ssq = fmaf(a, a, ssq);
                     t = a * tv[h][e >> 2][e & 3];
                 } else if constexpr (KIND == 2) {
-                    t = glu_mul(iact, a, tv[h][e >> 2][e & 3]);
+                    t = act_mul<GELU>(a, tv[h][e >> 2][e & 3]);
                 }
                 v[h][e] = t;
                 lm = fmaxf(lm, fabsf(t));
@@ -565,15 +567,15 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const float ya = acc[0] + acc[1];
     const float yb = acc[2] + acc[3];
     const FinishArgs fa_{N, K, B, S, glu, rx, eps, y, res, counters, ssq_part, part};
-    finish<KIND, 4>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
+    finish<KIND, 4, GELU>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
-template <int FMT, int KIND, int T>
+template <int FMT, int KIND, int T, bool GELU>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void mv_mfma_tile_kernel(
     const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
     const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
     const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
-    float *__restrict__ part, int S, int spw, int glu, int iact, int rg, int NG) {
+    float *__restrict__ part, int S, int spw, int glu, int rg, int NG) {
     constexpr int kBytes = BF<FMT>::kBytes;
     constexpr int kDw = BF<FMT>::kLaneDw;
     __shared__ u32x4_t opnd[4][kSeg][64];               // per wavefront: its step's activation operands
@@ -684,7 +686,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
                 }
             } else if constexpr (KIND == 2) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = glu_mul(iact, xv[b][e], tv[b][e]);
+                for (int e = 0; e < 4; ++e) t[e] = act_mul<GELU>(xv[b][e], tv[b][e]);
             }
             xv[b] = t;
             mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
@@ -805,7 +807,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     const float ya = tot[0] + tot[1];
     const float yb = tot[2] + tot[3];
     const FinishArgs fa_{N, K, B, S, glu, rx, eps, y, res, counters, ssq_part, part};
-    finish<KIND, T>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
+    finish<KIND, T, GELU>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
 // ---------------------------------------------------------------- host side
@@ -857,23 +859,37 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt) {
     return p;
 }
 
-template <int FMT, int KIND>
-void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
-            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu, int iact,
-            hipStream_t s) {
+template <int FMT, int KIND, bool GELU>
+void launch_act(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
+                int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu,
+                hipStream_t s) {
     uint8_t *w8 = static_cast<uint8_t *>(ws);
     int *ctr = reinterpret_cast<int *>(w8);
     float *ssq = reinterpret_cast<float *>(w8 + p.off_ssq);
     float *part = reinterpret_cast<float *>(w8 + p.off_part);
     const dim3 grid(p.gx, p.S);
     if (!p.tiles) {
-        hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                           ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, iact, p.rg, p.NG);
+        hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND, GELU>), grid, dim3(kWG), 0, s, W, N, K, B, x, u,
+                           nw, ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
         return;
     }
     constexpr int T = FMT == 1 ? 2 : 4;
-    hipLaunchKernelGGL((mv_mfma_tile_kernel<FMT, KIND, T>), grid, dim3(kWG), 0, s, W, N, K, B, x, u, nw,
-                       ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, iact, p.rg, p.NG);
+    hipLaunchKernelGGL((mv_mfma_tile_kernel<FMT, KIND, T, GELU>), grid, dim3(kWG), 0, s, W, N, K, B, x, u,
+                       nw, ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
+}
+
+// GeGLU kernels exist for Q4_0 only (the gated projections).
+template <int FMT, int KIND>
+void launch(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
+            int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu, bool gelu,
+            hipStream_t s) {
+    if constexpr (FMT == 0) {
+        if (gelu) {
+            launch_act<FMT, KIND, true>(W, N, K, B, x, u, nw, ld, eps, y, res, ws, p, glu, s);
+            return;
+        }
+    }
+    launch_act<FMT, KIND, false>(W, N, K, B, x, u, nw, ld, eps, y, res, ws, p, glu, s);
 }
 
 bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
@@ -898,6 +914,11 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
              "%s: unknown input transform %d", name, op_kind);
     Q4_CHECK((op_kind != Q4_IN_SWIGLU && op_kind != Q4_IN_GEGLU) || x2, Q4_ERR_INVALID_ARG,
              "%s: a gated input needs x2", name);
+    Q4_CHECK(!((op_kind == Q4_IN_SWIGLU || op_kind == Q4_IN_GEGLU) && out_op != Q4_OUT_PLAIN) ||
+                 (op_kind == Q4_IN_GEGLU) == (out_op == Q4_OUT_GEGLU),
+             Q4_ERR_UNSUPPORTED, "%s: a gated input and a gated output must use the same activation", name);
+    Q4_CHECK(FMT == 0 || (op_kind != Q4_IN_GEGLU && out_op != Q4_OUT_GEGLU), Q4_ERR_UNSUPPORTED,
+             "%s: GeGLU transforms are provided for Q4_0 weights", name);
     Q4_CHECK(op_kind != Q4_IN_RMSNORM || eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
     Q4_CHECK(ldx >= K, Q4_ERR_SHAPE, "%s: ld_x=%lld < K=%lld", name, (long long)ldx, (long long)K);
     Q4_CHECK(K % 256 == 0, Q4_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 256", name,
@@ -924,14 +945,14 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     hipStream_t s = q4::as_stream(stream);
     const uint8_t *W = static_cast<const uint8_t *>(Wv);
     const int n = static_cast<int>(N), k = static_cast<int>(K), b = static_cast<int>(B);
-    const int glu = out_op == Q4_OUT_SWIGLU ? 1 : out_op == Q4_OUT_GEGLU ? 2 : 0;
-    const int iact = op_kind == Q4_IN_GEGLU ? 1 : 0;
+    const int glu = out_op == Q4_OUT_PLAIN ? 0 : 1;
+    const bool gelu = op_kind == Q4_IN_GEGLU || out_op == Q4_OUT_GEGLU;
     if (op_kind == Q4_IN_RMSNORM)
-        launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, glu, iact, s);
+        launch<FMT, 1>(W, n, k, b, x, nullptr, norm_w, ldx, eps, y, res, ws, p, glu, gelu, s);
     else if (op_kind == Q4_IN_SWIGLU || op_kind == Q4_IN_GEGLU)
-        launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, glu, iact, s);
+        launch<FMT, 2>(W, n, k, b, x, x2, nullptr, ldx, eps, y, res, ws, p, glu, gelu, s);
     else
-        launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, glu, iact, s);
+        launch<FMT, 0>(W, n, k, b, x, nullptr, nullptr, ldx, eps, y, res, ws, p, glu, gelu, s);
     return q4::launch_status(name);
 }
 
