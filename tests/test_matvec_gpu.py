@@ -265,18 +265,20 @@ def test_matvec_batched_matches_fused_path(dev):
     _check(y2, ref, terms, "fused")
 
 
-def test_matvec_batched_5376x21504_B8_full(dev):
-    """The 31B FFN-shape workload at B = 8, every output."""
-    _say("q4_0_matvec_batched 5376x21504 B=8 full")
+@pytest.mark.parametrize("b", [8, 16, 32])
+def test_matvec_batched_5376x21504_full(dev, b):
+    """The 31B FFN-shape workload at B = 8 (the bench's B = 8 line) and at 16
+    and 32 rows (batch groups), every output, bitwise repeatable."""
+    _say(f"q4_0_matvec_batched 5376x21504 B={b} full")
     w = wl.MATVEC_5376x21504
-    W, x = wl.matvec_inputs(w, 8)
+    W, x = wl.matvec_inputs(w, b)
     ref, terms = oracle.q4_0_matvec(W, w.n, w.k, x)
     Wd = torch.from_numpy(W).to(dev)
     xd = torch.from_numpy(x).to(dev)
-    y1 = q.q4_0_matvec_batched(Wd, xd, w.k, 8, w.k)
-    y2 = q.q4_0_matvec_batched(Wd, xd, w.k, 8, w.k)
+    y1 = q.q4_0_matvec_batched(Wd, xd, w.k, b, w.k)
+    y2 = q.q4_0_matvec_batched(Wd, xd, w.k, b, w.k)
     torch.cuda.synchronize()
-    _check(y1, ref, terms, "5376x21504 B=8 batched")
+    _check(y1, ref, terms, f"5376x21504 B={b} batched")
     assert torch.equal(y1, y2)
 
 
