@@ -39,7 +39,8 @@ def time_dispatches(torch, launch, steps, warmup):
     """Mean time per dispatch (ms) over `steps` back-to-back launches after
     `warmup` untimed ones, HIP events on the stream the kernels are launched
     on.  (Host submission takes about half a dispatch, so the GPU stays busy;
-    replaying the launches as a graph adds per-node gaps on this runtime.)
+    the same dispatches replayed as one HIP graph take the same time per
+    dispatch, see time_matvec_graph.)
     The part's clocks take about 15 ms of sustained memory traffic to settle
     (a 65 MB matvec runs ~15 % slower before that), hence the long default
     warm-up."""
@@ -69,6 +70,45 @@ def time_matvec(q, torch, Ws, x, y, steps, warmup):
     for a in args[:1]:
         assert fn(*a) == 0, q.lib().q4dec_last_error()
     return time_dispatches(torch, lambda i: fn(*args[i % len(args)]), steps, warmup)
+
+
+def matvec_repeats(q, torch, Ws, x, y, steps, windows=5):
+    """Spread of the B = 1 timing: `windows` more timed windows of `steps`
+    dispatches each (the clocks are settled by then), median and coefficient
+    of variation of the per-dispatch time."""
+    import statistics
+    t = [time_matvec(q, torch, Ws, x, y, steps, 50) for _ in range(windows)]
+    med = statistics.median(t)
+    return {"windows": windows, "dispatches_per_window": steps, "median_ms": round(med, 6),
+            "cv": round(statistics.pstdev(t) / statistics.mean(t), 4)}
+
+
+def time_matvec_graph(q, torch, Ws, x, y, nodes, replays=5):
+    """The same B = 1 dispatches captured as one HIP graph of `nodes` kernel
+    nodes (rotating over the weight copies) and replayed: mean time per node
+    over `replays` timed replays after three untimed ones."""
+    fn = q.lib().q4_0_matvec
+    B, K = x.shape
+    N = y.shape[1]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(nodes):
+            W = Ws[i % len(Ws)]
+            assert fn(W.data_ptr(), N, K, x.data_ptr(), B, y.data_ptr(), None, stream) == 0, \
+                q.lib().q4dec_last_error()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * nodes)
 
 
 def time_matvec_batched(q, torch, Ws, x, y, K, B, steps, warmup):
@@ -365,7 +405,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -452,6 +492,11 @@ def main():
             del xb, yb
         out["matvec_B1_cache_resident"] = {"GB/s": round(bytes1 / (ms1r * 1e-3) / 1e9, 2),
                                            "ms": round(ms1r, 6)}
+        log("timing B=1: repeat windows, then as one HIP graph")
+        out["matvec_B1_repeats"] = matvec_repeats(q, torch, Ws, x1, y1, args.steps)
+        msg = time_matvec_graph(q, torch, Ws, x1, y1, args.steps)
+        out["matvec_B1_graph"] = {"nodes": args.steps, "GB/s": round(bytes1 / (msg * 1e-3) / 1e9, 2),
+                                  "ms_per_node": round(msg, 6)}
         del Ws
         torch.cuda.empty_cache()
         if not args.no_attention:
