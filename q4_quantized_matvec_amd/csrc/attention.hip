@@ -103,7 +103,7 @@ struct RopeArgs {
     const float *kraw, *vraw;  // raw key / value rows of kv head 0 (vraw NULL: V from K)
     int64_t ldkv;              // row stride of kraw / vraw
     const float *qn, *kn;      // per-head gains [hd]
-    double theta;
+    double rstep;              // theta^(-2/hd), computed on the host
     float eps;
     void *kcw, *vcw;           // the caches (element type of the layout), written at slot pos % cap
 };
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     };
     if constexpr (ROPE) {
         const int64_t pos = n - 1;
-        const double r = pow(ra.theta, -2.0 / static_cast<double>(HD));
+        const double r = ra.rstep;
 #pragma unroll
         for (int e = 0; e < 4; ++e) rope_cs(pos, r, 4 * sub + e, rc[e], rs[e]);
         load8(ra.qn, gq);
@@ -618,7 +618,7 @@ extern "C" q4_status gqa_decode_attn_rope(const float *qkv, int64_t ld, int64_t 
     ra.ldkv = ld;
     ra.qn = q_norm;
     ra.kn = k_norm;
-    ra.theta = theta;
+    ra.rstep = std::pow(theta, -2.0 / static_cast<double>(kv->head_dim));
     ra.eps = eps;
     ra.kcw = k_cache;
     ra.vcw = v_cache;

@@ -122,7 +122,7 @@ template <typename KT>
 __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     float *q, int64_t ldq, const float *k, const float *v, int64_t ldkv,
     const float *__restrict__ qn, const float *__restrict__ kn, int Hq, int hd,
-    const int64_t *__restrict__ pos_dev, double theta, float eps, int v_from_k,
+    const int64_t *__restrict__ pos_dev, double r, float eps, int v_from_k,
     KT *kc, KT *vc, int64_t cap, int64_t sb, int64_t sh, int64_t st, int rot) {
     // p-RoPE: elements [0, rot) rotate as a NeoX rotation of a rot-dimensional
     // vector (pairs i, i + rot/2, angle pos * theta^(-2i/rot)); elements
@@ -169,11 +169,11 @@ __global__ __launch_bounds__(64) void qk_norm_rope_kernel(
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(hd) + eps);
     const int64_t pos = *pos_dev;
-    // Frequencies theta^(-2i/hd) = r^i with r = theta^(-2/hd), by binary
-    // powers in fp64 (a relative error of a few 1e-16, far below what the
-    // angle needs); the angle pos * r^i is reduced by 2 pi in fp64 and the
-    // reduced angle (|a| <= pi) goes to single-precision sincos.
-    const double r = pow(theta, -2.0 / static_cast<double>(rot));
+    // Frequencies theta^(-2i/rot) = r^i with r = theta^(-2/rot) (computed once
+    // on the host), by binary powers in fp64 (a relative error of a few
+    // 1e-16, far below what the angle needs); the angle pos * r^i is reduced
+    // by 2 pi in fp64 and the reduced angle (|a| <= pi) goes to
+    // single-precision sincos.
     double rp[9];  // r^(2^k), k = 0..8 (pairs i < 256)
     rp[0] = r;
 #pragma unroll
@@ -492,16 +492,17 @@ extern "C" q4_status qk_norm_rope_partial(float *q, int64_t ldq, const float *k,
     Q4_CHECK(theta > 0.0 && eps >= 0.f, Q4_ERR_INVALID_ARG, "qk_norm_rope: theta > 0, eps >= 0");
     Q4_CHECK(n_q_heads + kv->n_kv_heads <= 65535, Q4_ERR_UNSUPPORTED, "qk_norm_rope: too many heads");
     dim3 grid(static_cast<unsigned>(n_q_heads + kv->n_kv_heads), static_cast<unsigned>(kv->batch));
+    const double r = std::pow(theta, -2.0 / static_cast<double>(rot_dims));
     if (kv->dtype == Q4_KV_F16)
         hipLaunchKernelGGL(qk_norm_rope_kernel<_Float16>, grid, dim3(64), 0, q4::as_stream(stream), q,
                            ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
-                           static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
+                           static_cast<int>(kv->head_dim), pos_dev, r, eps, v_from_k ? 1 : 0,
                            static_cast<_Float16 *>(k_cache), static_cast<_Float16 *>(v_cache), kv->cap,
                            kv->stride_b, kv->stride_h, kv->stride_t, static_cast<int>(rot_dims));
     else
         hipLaunchKernelGGL(qk_norm_rope_kernel<float>, grid, dim3(64), 0, q4::as_stream(stream), q,
                            ldq, k, v, ldkv, q_norm, k_norm, static_cast<int>(n_q_heads),
-                           static_cast<int>(kv->head_dim), pos_dev, theta, eps, v_from_k ? 1 : 0,
+                           static_cast<int>(kv->head_dim), pos_dev, r, eps, v_from_k ? 1 : 0,
                            static_cast<float *>(k_cache), static_cast<float *>(v_cache), kv->cap,
                            kv->stride_b, kv->stride_h, kv->stride_t, static_cast<int>(rot_dims));
     return q4::launch_status("qk_norm_rope");
