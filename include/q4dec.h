@@ -118,6 +118,26 @@ q4_status q8_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,
                             const float *norm_w, float eps, float *y, const float *residual,
                             void *stream);
 
+/* q4_0_matvec_post_norm: a sandwich-norm block boundary and the next
+ * projection in one call ([GEM] 31B trace: post-sublayer RMSNorm, residual
+ * add, then the next pre-norm RMSNorm and projection):
+ *   h_out[b] = h[b] + post_w * z[b] / sqrt(mean(z[b]^2) + eps)
+ *   y[b]     = out_op(W (pre_w * h_out[b] / sqrt(mean(h_out[b]^2) + eps)))
+ * (pre_w NULL: unit gain).  Rows b of h, z and h_out start at b * ld; y is
+ * [B][N] ([B][N/2] for a gated out_op).  B <= 8 (vector units); every
+ * workgroup computes h_out itself and one per row writes it, so h_out must
+ * not overlap h or z.
+ *   W       16-bit aligned Q4_0 [N][K/32] blocks; K % 256 == 0, K <= 8192
+ *   h, z, h_out, post_w, pre_w   16-byte aligned, ld % 4 == 0, ld >= K
+ *   y       must not overlap h, z or h_out
+ * Errors: Q4_ERR_INVALID_ARG (NULL, sizes, eps < 0, odd N with a gated output,
+ * overlap), Q4_ERR_SHAPE (ld < K), Q4_ERR_ALIGNMENT, Q4_ERR_UNSUPPORTED (B > 8,
+ * K), Q4_ERR_HIP. */
+q4_status q4_0_matvec_post_norm(const void *W, int64_t N, int64_t K, const float *h,
+                                const float *z, int64_t ld, int64_t B, const float *post_w,
+                                const float *pre_w, float eps, float *h_out,
+                                q4_output_op out_op, float *y, void *stream);
+
 /* q4_0_matvec_batched / q8_0_matvec_batched: the same products as the fused
  * calls, computed on the matrix cores for 1 <= B <= 32 activation rows; meant
  * for B >= 2, where eight products per weight outrun the vector units.  Rows

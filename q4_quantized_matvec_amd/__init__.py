@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     OUT_GEGLU,
     q4_0_matvec,
     q4_0_matvec_fused,
+    q4_0_matvec_post_norm,
     q4_0_matvec_batched,
     q8_0_matvec_batched,
     q8_0_matvec_fused,

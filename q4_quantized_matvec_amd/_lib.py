@@ -59,6 +59,8 @@ _SIGS = {
                           C.c_int),
     "q8_0_matvec_fused": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P, _P],
                           C.c_int),
+    "q4_0_matvec_post_norm": ([_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _F, _P, C.c_int, _P, _P],
+                              C.c_int),
     "matvec_batched_workspace": ([_I64, _I64, _I64], _SZ),
     "q4_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P,
                              _P, _SZ, _P], C.c_int),
@@ -210,6 +212,20 @@ def q8_0_matvec_fused(W, x, K, B, ld, op, x2=None, norm_w=None, eps=0.0, y=None,
                       stream=None, n=None, out_op=OUT_PLAIN):
     return _matvec_fused("q8_0_matvec_fused", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
                          residual, stream, n, out_op)
+
+
+def q4_0_matvec_post_norm(W, h, z, K, B, ld, post_w, pre_w, eps, h_out, y=None, stream=None,
+                          n=None, out_op=OUT_PLAIN):
+    """h_out = h + post_w * rmsnorm(z); y = out_op(dequant(W) @ (pre_w * rmsnorm(h_out)));
+    rows of h, z and h_out at stride ld."""
+    import torch
+    N = n if n is not None else _qmatrix_dims(W, K, 18)
+    if y is None:
+        y = torch.empty((B, _out_cols(N, out_op)), dtype=torch.float32, device=h.device)
+    _check("q4_0_matvec_post_norm", lib().q4_0_matvec_post_norm(
+        _ptr(W), N, K, _ptr(h), _ptr(z), ld, B, _ptr(post_w), _ptr(pre_w), float(eps), _ptr(h_out),
+        int(out_op), _ptr(y), _stream(stream)))
+    return y
 
 
 def matvec_batched_workspace(N, K, B):

@@ -23,6 +23,7 @@ struct q4_decode_model {
     int64_t *pos_dev = nullptr;  // [0] = position of the next token, [1] = n = position + 1
     float *x = nullptr, *qkv = nullptr, *att = nullptr, *gu = nullptr;
     float *tmp = nullptr;  // a sublayer output before its sandwich post-norm [B][d_model]
+    float *x2 = nullptr;   // the residual stream's second buffer (fused post-norms) [B][d_model]
     void *arg = nullptr;  // the two-pass argmax's partial maxima
     float *logits = nullptr;
     void *attn_ws = nullptr;
@@ -59,7 +60,7 @@ __global__ void advance_position_kernel(int64_t *pos) {
 }
 
 struct Layout {
-    size_t pos, x, qkv, att, gu, logits, tmp, arg, mv, mv_bytes, attn, total;
+    size_t pos, x, qkv, att, gu, logits, tmp, x2, arg, mv, mv_bytes, attn, total;
 };
 
 int64_t layer_qkv_rows(const q4_model_desc &d, const q4_layer_desc &l) {
@@ -119,6 +120,7 @@ Layout plan(const q4_model_desc &d) {
     L.gu = take(sizeof(float) * B * 2 * d.ffn);
     L.logits = take(sizeof(float) * B * d.vocab);
     L.tmp = take(sizeof(float) * B * d.d_model);
+    L.x2 = take(sizeof(float) * B * d.d_model);
     L.arg = take(q4::argmax_scratch_bytes(B));
     L.mv = take(mv);
     L.mv_bytes = mv;
@@ -214,6 +216,15 @@ q4_status project(q4_decode_model *m, int fmt, const void *W, int64_t N, int64_t
                                                               nw, d.eps, y, res, s);
 }
 
+// A waiting post-norm can be fused into a pre-normed Q4_0 projection on the
+// vector kernels (q4_0_matvec_post_norm: up to 8 rows, K % 256 == 0,
+// K <= 8192, 16-byte aligned gains).
+bool post_fusable(const q4_decode_model *m, const void *W, const float *post_w, const float *pre_w) {
+    const q4_model_desc &d = m->desc;
+    return !(m->mv_ws && batched_ok(d, W, d.d_model)) && d.batch <= 8 && d.d_model % 256 == 0 &&
+           d.d_model <= 8192 && q4::aligned(post_w, 16) && (!pre_w || q4::aligned(pre_w, 16));
+}
+
 // The gate|up projection can hand SiLU(gate) * up straight to the down
 // projection when its kernel supports a SwiGLU output for this shape.
 bool glu_output(const q4_model_desc &d, const void *wgu) {
@@ -233,13 +244,30 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         Q4_TRY(q8_0_gather(d.embed, d.vocab, D, tok, B, m->x, sv));
     const q4_input_op gated_in = d.ffn_act ? Q4_IN_GEGLU : Q4_IN_SWIGLU;
     const q4_output_op gated_out = d.ffn_act ? Q4_OUT_GEGLU : Q4_OUT_SWIGLU;
+    // The residual stream lives in hc.  A sandwich post-norm whose sublayer
+    // output waits in tmp (gain pend) joins the stream inside the next
+    // pre-normed projection where the vector kernels can take it, writing the
+    // stream's other buffer; otherwise rmsnorm_add applies it in place first.
+    float *hc = m->x, *ha = m->x2;
+    const float *pend = nullptr;
+    auto normed_proj = [&](const void *W, int64_t N, const float *gain, q4_output_op out,
+                           float *y) -> q4_status {
+        if (pend && post_fusable(m, W, pend, gain)) {
+            Q4_TRY(q4_0_matvec_post_norm(W, N, D, hc, m->tmp, D, B, pend, gain, d.eps, ha, out, y, sv));
+            std::swap(hc, ha);
+            pend = nullptr;
+            return Q4_OK;
+        }
+        if (pend) Q4_TRY(rmsnorm_add(m->tmp, pend, B, D, d.eps, hc, sv));
+        pend = nullptr;
+        return project(m, 0, W, N, D, hc, nullptr, D, Q4_IN_RMSNORM, out, gain, y, nullptr, sv);
+    };
     for (size_t i = 0; i < m->layers.size(); ++i) {
         const q4_layer_desc &l = m->layers[i];
         const int64_t hd = l.head_dim, nq = d.n_q_heads * hd, nk = l.n_kv_heads * hd;
         const int64_t nqkv = layer_qkv_rows(d, l);
         // attention RMSNorm fused into the QKV projection's input
-        Q4_TRY(project(m, 0, l.wqkv, nqkv, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
-                       l.attn_norm, m->qkv, nullptr, sv));
+        Q4_TRY(normed_proj(l.wqkv, nqkv, l.attn_norm, Q4_OUT_PLAIN, m->qkv));
         if (l.rope_dims == 0 || l.rope_dims == hd) {
             // per-head QK-norm, RoPE and the KV append fused into the attention
             Q4_TRY(gqa_decode_attn_rope(m->qkv, nqkv, d.n_q_heads, l.q_norm, l.k_norm, &m->kv[i],
@@ -262,30 +290,28 @@ q4_status enqueue_step(q4_decode_model *m, const int32_t *tok, int32_t *next, fl
         if (l.post_attn_norm) {
             Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
                            m->tmp, nullptr, sv));
-            Q4_TRY(rmsnorm_add(m->tmp, l.post_attn_norm, B, D, d.eps, m->x, sv));
+            pend = l.post_attn_norm;
         } else {
             Q4_TRY(project(m, 0, l.wo, D, nq, m->att, nullptr, nq, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
-                           m->x, m->x, sv));
+                           hc, hc, sv));
         }
         // FFN RMSNorm fused into gate|up; SwiGLU fused into gate|up's output
         // (else into the down projection's input)
-        float *dy = l.post_ffn_norm ? m->tmp : m->x;          // down projection output
-        const float *dres = l.post_ffn_norm ? nullptr : m->x;  // and its residual
-        if (glu_output(d, l.wgu)) {
-            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, gated_out,
-                           l.ffn_norm, m->gu, nullptr, sv));
+        const bool gout = glu_output(d, l.wgu);
+        Q4_TRY(normed_proj(l.wgu, 2 * F, l.ffn_norm, gout ? gated_out : Q4_OUT_PLAIN, m->gu));
+        float *dy = l.post_ffn_norm ? m->tmp : hc;          // down projection output
+        const float *dres = l.post_ffn_norm ? nullptr : hc;  // and its residual
+        if (gout)
             Q4_TRY(project(m, 0, l.wd, D, F, m->gu, nullptr, F, Q4_IN_PLAIN, Q4_OUT_PLAIN, nullptr,
                            dy, dres, sv));
-        } else {
-            Q4_TRY(project(m, 0, l.wgu, 2 * F, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
-                           l.ffn_norm, m->gu, nullptr, sv));
+        else
             Q4_TRY(project(m, 0, l.wd, D, F, m->gu, m->gu + F, 2 * F, gated_in, Q4_OUT_PLAIN,
                            nullptr, dy, dres, sv));
-        }
-        if (l.post_ffn_norm) Q4_TRY(rmsnorm_add(m->tmp, l.post_ffn_norm, B, D, d.eps, m->x, sv));
+        if (l.post_ffn_norm) pend = l.post_ffn_norm;
     }
+    if (pend) Q4_TRY(rmsnorm_add(m->tmp, pend, B, D, d.eps, hc, sv));
     float *lg = logits ? logits : m->logits;
-    Q4_TRY(project(m, 1, d.embed, d.vocab, D, m->x, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
+    Q4_TRY(project(m, 1, d.embed, d.vocab, D, hc, nullptr, D, Q4_IN_RMSNORM, Q4_OUT_PLAIN,
                    d.final_norm, lg, nullptr, sv));
     if (d.logit_softcap > 0.f) Q4_TRY(softcap(lg, B * d.vocab, d.logit_softcap, sv));
     Q4_TRY(q4::argmax_rows_scratch(lg, B, d.vocab, next, m->arg, s));
@@ -339,6 +365,7 @@ extern "C" q4_status decode_model_create(const q4_model_desc *desc, void *ws, si
     m->gu = reinterpret_cast<float *>(base + L.gu);
     m->logits = reinterpret_cast<float *>(base + L.logits);
     m->tmp = reinterpret_cast<float *>(base + L.tmp);
+    m->x2 = reinterpret_cast<float *>(base + L.x2);
     m->arg = base + L.arg;
     m->attn_ws = base + L.attn;
     m->attn_ws_bytes = L.total - L.attn;

@@ -51,15 +51,21 @@ struct Fmt<1> {  // Q8_0
 //   kind 0: x
 //   kind 1: rmsnorm(x) = w * x / sqrt(mean(x^2) + eps)   (w NULL: unit gain)
 //   kind 2: act(x) * u, act = silu (x / (1 + exp(-x))) or gelu (tanh form)
+//   post-norm (the kernels' POST parameter, with kind 1): x is the residual
+//   stream h and u a block output z; the input is rmsnorm(h') with
+//   h' = h + pw * z / sqrt(mean(z^2) + eps), and workgroup 0 of each row
+//   writes h' to hout
 struct InOp {
     int kind;
-    const float *u;  // kind 2: second operand, same row stride as x
+    const float *u;  // kind 2: second operand; post-norm: z; same row stride as x
     const float *w;  // kind 1: gain
     float eps;
-    int64_t ld;      // row stride of x (and u) in elements
+    int64_t ld;      // row stride of x (and u, hout) in elements
     int glu;         // 1 / 2: y[p] = act(z[p]) * z[p + N/2] for the N/2 pairs, act = silu / gelu
                      // (whole K per wavefront)
     int act;         // kind 2: 0 silu, 1 gelu
+    const float *pw; // post-norm gain
+    float *hout;     // post-norm: h'
 };
 
 // act(g) * u with act = SiLU or (GELU) the tanh form of GELU.  A template
@@ -139,7 +145,7 @@ constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
 
 // B = 1 fast path.  KS wavefronts of a workgroup split K; 4 / KS row groups;
 // PF rows of loads in flight per wavefront.
-template <int FMT, int JX, int KS, int PF, bool GLU, bool GELU>
+template <int FMT, int JX, int KS, int PF, bool GLU, bool GELU, bool POST>
 __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
                                                     const float *x, float *y, const float *res,
                                                     int N, int K, InOp op) {
@@ -151,6 +157,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         const int64_t b = blockIdx.y;
         x += b * op.ld;
         if (op.u) op.u += b * op.ld;
+        if (POST) op.hout += b * op.ld;
         y += b * static_cast<int64_t>(GLU ? N / 2 : N);
         if (res) res += b * static_cast<int64_t>(N);
     }
@@ -227,7 +234,69 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     // whole K in one wavefront the workgroup stages x through LDS once; the
     // input transform is applied on the way (sum of squares reduced in LDS).
     float inv = 1.f;
-    if constexpr (kXLds) {
+    if constexpr (POST) {
+        static_assert(kXLds, "the post-norm input is staged through LDS");
+        // Post-norm: h' = h + pw * z / rms(z), then RMSNorm of h' as for kind
+        // 1.  Every operand of the row is requested before the first weight
+        // rows (loads return in order); z's sum of squares is reduced first.
+        // K <= 2048 JX here, so 2 JX float4 per thread cover the row.
+        constexpr int kXV = 2 * JX;
+        static_assert(kXV * 4 * kWG <= kXLdsFloats, "row staging");
+        const int nv = K >> 2;
+        const float4 *hg = reinterpret_cast<const float4 *>(x);
+        const float4 *zg = reinterpret_cast<const float4 *>(op.u);
+        const float4 *pg = reinterpret_cast<const float4 *>(op.pw);
+        const float4 *gg = reinterpret_cast<const float4 *>(op.w);
+        float4 *xl = reinterpret_cast<float4 *>(xs);
+        float4 *ho = reinterpret_cast<float4 *>(op.hout);
+        float4 zv[kXV], hv[kXV], pv[kXV], gv[kXV];
+#pragma unroll
+        for (int r = 0; r < kXV; ++r) {
+            const int i = min(static_cast<int>(threadIdx.x) + r * kWG, nv - 1);
+            zv[r] = zg[i];
+            hv[r] = hg[i];
+            pv[r] = pg[i];
+            gv[r] = gg ? gg[i] : make_float4(1.f, 1.f, 1.f, 1.f);
+        }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) fetch(p, buf[p]);
+        float sz = 0.f;
+#pragma unroll
+        for (int r = 0; r < kXV; ++r)
+            if (static_cast<int>(threadIdx.x) + r * kWG < nv)
+                sz = __builtin_fmaf(zv[r].x, zv[r].x, __builtin_fmaf(zv[r].y, zv[r].y,
+                     __builtin_fmaf(zv[r].z, zv[r].z, __builtin_fmaf(zv[r].w, zv[r].w, sz))));
+        sz = wave_sum(sz);
+        if (lane == 0) red[wave] = sz;
+        __syncthreads();
+        const float rz = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / static_cast<float>(K) + op.eps);
+        __syncthreads();  // red[] is reused for h'
+        const bool writer = blockIdx.x == 0;
+        float ss = 0.f;
+#pragma unroll
+        for (int r = 0; r < kXV; ++r) {
+            const int i = threadIdx.x + r * kWG;
+            if (i < nv) {
+                float4 t;
+                t.x = __builtin_fmaf(pv[r].x, zv[r].x * rz, hv[r].x);
+                t.y = __builtin_fmaf(pv[r].y, zv[r].y * rz, hv[r].y);
+                t.z = __builtin_fmaf(pv[r].z, zv[r].z * rz, hv[r].z);
+                t.w = __builtin_fmaf(pv[r].w, zv[r].w * rz, hv[r].w);
+                if (writer) ho[i] = t;
+                ss = __builtin_fmaf(t.x, t.x, __builtin_fmaf(t.y, t.y, __builtin_fmaf(t.z, t.z, __builtin_fmaf(t.w, t.w, ss))));
+                t.x *= gv[r].x;
+                t.y *= gv[r].y;
+                t.z *= gv[r].z;
+                t.w *= gv[r].w;
+                xl[i] = t;
+            }
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / static_cast<float>(K) + op.eps);
+        __syncthreads();
+    } else if constexpr (kXLds) {
         const float4 *xg = reinterpret_cast<const float4 *>(x);
         const float4 *ug = reinterpret_cast<const float4 *>(op.u);
         float4 *xl = reinterpret_cast<float4 *>(xs);
@@ -571,28 +640,42 @@ void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
     // GeGLU kernels exist for Q4_0 only (the gated projections)
     const bool gelu = (op.kind == 2 && op.act) || op.glu == 2;
+    if constexpr (FMT == 0 && KS == 1) {
+        if (op.pw) {  // post-norm input (q4_0_matvec_post_norm)
+            if (op.glu && gelu)
+                hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, true, true>), dim3(nwg, B), dim3(kWG), 0,
+                                   s, W, x, y, res, N, K, op);
+            else if (op.glu)
+                hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, false, true>), dim3(nwg, B), dim3(kWG), 0,
+                                   s, W, x, y, res, N, K, op);
+            else
+                hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, false, true>), dim3(nwg, B), dim3(kWG),
+                                   0, s, W, x, y, res, N, K, op);
+            return;
+        }
+    }
     if constexpr (KS == 1) {
         if (op.glu) {
             if constexpr (FMT == 0) {
                 if (gelu) {
-                    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, true>), dim3(nwg, B), dim3(kWG),
+                    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, true, false>), dim3(nwg, B), dim3(kWG),
                                        0, s, W, x, y, res, N, K, op);
                     return;
                 }
             }
-            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, false>), dim3(nwg, B), dim3(kWG), 0, s,
+            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, true, false, false>), dim3(nwg, B), dim3(kWG), 0, s,
                                W, x, y, res, N, K, op);
             return;
         }
     }
     if constexpr (FMT == 0) {
         if (gelu) {
-            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, true>), dim3(nwg, B), dim3(kWG), 0, s,
+            hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, true, false>), dim3(nwg, B), dim3(kWG), 0, s,
                                W, x, y, res, N, K, op);
             return;
         }
     }
-    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, false>), dim3(nwg, B), dim3(kWG), 0, s, W, x,
+    hipLaunchKernelGGL((mv_b1_kernel<FMT, JX, KS, PF, false, false, false>), dim3(nwg, B), dim3(kWG), 0, s, W, x,
                        y, res, N, K, op);
 }
 
@@ -693,6 +776,56 @@ extern "C" q4_status q8_0_matvec(const void *W, int64_t N, int64_t K, const floa
                                  float *y, const float *residual, void *stream) {
     return matvec_entry<1>("q8_0_matvec", W, N, K, x, nullptr, K, B, Q4_IN_PLAIN, Q4_OUT_PLAIN,
                            nullptr, 0.f, y, residual, stream);
+}
+
+namespace {
+bool spans_overlap(const void *a, size_t an, const void *b, size_t bn) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(a), q = reinterpret_cast<uintptr_t>(b);
+    return p < q + bn && q < p + an;
+}
+}  // namespace
+
+extern "C" q4_status q4_0_matvec_post_norm(const void *W, int64_t N, int64_t K, const float *h,
+                                           const float *z, int64_t ld, int64_t B,
+                                           const float *post_w, const float *pre_w, float eps,
+                                           float *h_out, q4_output_op out_op, float *y,
+                                           void *stream) {
+    q4::clear_error();
+    const char *name = "q4_0_matvec_post_norm";
+    Q4_CHECK(W && h && z && post_w && h_out && y, Q4_ERR_INVALID_ARG,
+             "%s: W, h, z, post_w, h_out and y must not be NULL", name);
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU || out_op == Q4_OUT_GEGLU,
+             Q4_ERR_INVALID_ARG, "%s: unknown output transform %d", name, out_op);
+    Q4_CHECK(N >= 1 && K >= 1 && B >= 1, Q4_ERR_INVALID_ARG, "%s: N=%lld K=%lld B=%lld must be >= 1",
+             name, (long long)N, (long long)K, (long long)B);
+    Q4_CHECK(out_op == Q4_OUT_PLAIN || N % 2 == 0, Q4_ERR_INVALID_ARG,
+             "%s: a gated (SwiGLU / GeGLU) output needs an even N", name);
+    Q4_CHECK(eps >= 0.f, Q4_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
+    Q4_CHECK(B <= 8, Q4_ERR_UNSUPPORTED, "%s: B=%lld > 8", name, (long long)B);
+    Q4_CHECK(K % 256 == 0 && K <= kXLdsFloats, Q4_ERR_UNSUPPORTED,
+             "%s: K=%lld must be a multiple of 256 and at most %d", name, (long long)K, kXLdsFloats);
+    Q4_CHECK(ld >= K, Q4_ERR_SHAPE, "%s: ld=%lld < K=%lld", name, (long long)ld, (long long)K);
+    Q4_CHECK(N <= (1 << 30) && ld <= (1 << 26), Q4_ERR_UNSUPPORTED, "%s: N or ld too large", name);
+    Q4_CHECK(q4::aligned(W, 2), Q4_ERR_ALIGNMENT, "%s: W must be 2-byte aligned", name);
+    Q4_CHECK(q4::aligned(h, 16) && q4::aligned(z, 16) && q4::aligned(h_out, 16) &&
+                 q4::aligned(post_w, 16) && (!pre_w || q4::aligned(pre_w, 16)) && ld % 4 == 0,
+             Q4_ERR_ALIGNMENT,
+             "%s: h, z, h_out and the gains must be 16-byte aligned with ld a multiple of 4", name);
+    Q4_CHECK(q4::aligned(y, 4), Q4_ERR_ALIGNMENT, "%s: y must be 4-byte aligned", name);
+    const size_t rows = static_cast<size_t>((B - 1) * ld + K) * sizeof(float);
+    const size_t ybytes = static_cast<size_t>(B * (out_op != Q4_OUT_PLAIN ? N / 2 : N)) * sizeof(float);
+    Q4_CHECK(!spans_overlap(h_out, rows, h, rows) && !spans_overlap(h_out, rows, z, rows),
+             Q4_ERR_INVALID_ARG, "%s: h_out must not overlap h or z", name);
+    Q4_CHECK(!spans_overlap(y, ybytes, h, rows) && !spans_overlap(y, ybytes, z, rows) &&
+                 !spans_overlap(y, ybytes, h_out, rows),
+             Q4_ERR_INVALID_ARG, "%s: y must not overlap h, z or h_out", name);
+    const int glu = out_op == Q4_OUT_SWIGLU ? 1 : out_op == Q4_OUT_GEGLU ? 2 : 0;
+    InOp op{1, z, pre_w, eps, ld, glu, 0, post_w, h_out};
+    const int nb = static_cast<int>(K / 32);
+    launch_b1_jx<0, 1>((ks_part_blocks(nb, 1) + 63) / 64, static_cast<const uint8_t *>(W), h, y, nullptr,
+                       static_cast<int>(N), static_cast<int>(K), static_cast<int>(B), op,
+                       q4::as_stream(stream));
+    return q4::launch_status(name);
 }
 
 extern "C" q4_status q4_0_matvec_fused(const void *W, int64_t N, int64_t K, const float *x,

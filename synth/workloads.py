@@ -137,6 +137,10 @@ TINY_QWEN3_B20 = _qwen3("tiny_qwen3_b20", 2, 256, 4, 2, 64, 512, 1000, 20, 37, 4
 # The tiny structure with the exact Gemma-4 block variants.
 TINY_GEMMA4_EXACT = _gemma4("tiny_gemma4_exact", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 2, 40, 4,
                             7005, exact=True)
+# The same with one sequence: the projections run on the vector kernels, which
+# take the sandwich post-norms into the next projection's input.
+TINY_GEMMA4_EXACT_B1 = _gemma4("tiny_gemma4_exact_b1", 6, 256, 4, 2, 64, 16, 1, 128, 512, 1000, 1, 40,
+                               4, 7006, exact=True)
 # The 31B shape with the exact Gemma-4 block variants (same matrices as
 # GEMMA4_31B plus the post-norm gains).
 GEMMA4_31B_EXACT = _gemma4("decode_gemma4_31b_exact", 60, 5376, 32, 16, 256, 1024, 4, 512, 21504,

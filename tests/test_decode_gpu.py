@@ -31,7 +31,8 @@ def _nmse(a, b):
 
 
 @pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG,
-                                   wl.TINY_QWEN3_B20, wl.TINY_GEMMA4_EXACT], ids=lambda s: s.name)
+                                   wl.TINY_QWEN3_B20, wl.TINY_GEMMA4_EXACT,
+                                   wl.TINY_GEMMA4_EXACT_B1], ids=lambda s: s.name)
 def test_decode_tokens_match_oracle(dev, shape):
     _say(f"decode {shape.name}: {shape.steps} steps")
     weights = wl.model_weights(shape)
@@ -83,7 +84,8 @@ def test_decode_f16_kv_matches_oracle(dev, shape):
 
 
 @pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_LONG,
-                                   wl.TINY_QWEN3_B20, wl.TINY_GEMMA4_EXACT], ids=lambda s: s.name)
+                                   wl.TINY_QWEN3_B20, wl.TINY_GEMMA4_EXACT,
+                                   wl.TINY_GEMMA4_EXACT_B1], ids=lambda s: s.name)
 def test_graph_equals_eager(dev, shape):
     _say(f"graph vs eager {shape.name}")
     weights = wl.model_weights(shape)

@@ -93,6 +93,31 @@ def test_swiglu_output_rejected_where_unsupported():
                    None, None)[0] == "Q4_ERR_INVALID_ARG"                                     # GeGLU, no x2
 
 
+def test_post_norm_matvec_rejects_bad_arguments_on_host():
+    """q4_0_matvec_post_norm: NULLs, K limits of the staged row, B > 8, odd N with a gated
+    output, alignment, and h_out overlapping h or z (other workgroups read them)."""
+    L = q.lib()
+    W, h, z, ho, pw, y = 0x10000, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+    def st(W=W, N=64, K=512, h=h, z=z, ld=512, B=1, pw=pw, ho=ho, out=0, y=y):
+        return _status(L.q4_0_matvec_post_norm, W, N, K, h, z, ld, B, pw, None, 1e-6, ho, out, y,
+                       None)[0]
+    assert st(h=None) == "Q4_ERR_INVALID_ARG"
+    assert st(pw=None) == "Q4_ERR_INVALID_ARG"
+    assert st(ho=None) == "Q4_ERR_INVALID_ARG"
+    assert st(K=288, ld=288) == "Q4_ERR_UNSUPPORTED"      # K % 256
+    assert st(K=8448, ld=8448) == "Q4_ERR_UNSUPPORTED"    # K > 8192
+    assert st(B=9) == "Q4_ERR_UNSUPPORTED"
+    assert st(N=65, out=1) == "Q4_ERR_INVALID_ARG"        # gated output, odd N
+    assert st(out=3) == "Q4_ERR_INVALID_ARG"
+    assert st(ld=256) == "Q4_ERR_SHAPE"
+    assert st(h=h + 4) == "Q4_ERR_ALIGNMENT"
+    assert st(ld=514) == "Q4_ERR_ALIGNMENT"
+    assert st(ho=h + 1024) == "Q4_ERR_INVALID_ARG"        # h_out inside h's rows
+    assert st(ho=z) == "Q4_ERR_INVALID_ARG"
+    assert st(y=ho + 16) == "Q4_ERR_INVALID_ARG"
+
+
 def test_gemma_variant_ops_reject_bad_arguments_on_host():
     import ctypes as C
     L = q.lib()

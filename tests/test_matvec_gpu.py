@@ -385,6 +385,53 @@ def test_matvec_geglu_output(dev, path, n, k, b, op):
     assert np.all(np.isfinite(got)) and ratio <= 1.0, f"max err/tol {ratio:.3e}"
 
 
+# (N, K, B, output transform, pre-norm gain): ragged rows, every JX (K = 256 .. 8192),
+# B up to 8, gated outputs, a unit pre-norm gain
+POST_NORM_CASES = [(300, 256, 1, "plain", True), (1027, 5376, 1, "plain", True),
+                   (1026, 2048, 3, "swiglu", True), (1400, 1024, 2, "geglu", False),
+                   (96, 8192, 1, "plain", True), (64, 768, 8, "plain", True)]
+
+
+@pytest.mark.parametrize("n,k,b,out,gain", POST_NORM_CASES)
+def test_matvec_post_norm(dev, n, k, b, out, gain):
+    """h_out = h + pw * rmsnorm(z) against the oracle's post-norm add; y against the
+    oracle's matvec of pre_w * rmsnorm(h_out) fed the GPU's h_out (bounds as for the
+    fused RMSNorm matvec and the gated outputs); h_out's row padding is not written."""
+    _say(f"post-norm matvec {out} N={n} K={k} B={b}")
+    W = synth.q4_0_matrix(121, f"pn.W.{n}.{k}", n, k)
+    ld = k + 32
+    h = synth.normal_f32(121, f"pn.h.{k}.{b}", (b, ld))
+    z = synth.normal_f32(121, f"pn.z.{k}.{b}", (b, ld)) * 3.0
+    pw = synth.uniform_f32(121, f"pn.pw.{k}", (k,), 0.8, 1.2)
+    gw = synth.uniform_f32(121, f"pn.gw.{k}", (k,), 0.8, 1.2) if gain else None
+    hod = torch.zeros((b, ld), dtype=torch.float32, device=dev)
+    oo = {"plain": q.OUT_PLAIN, "swiglu": q.OUT_SWIGLU, "geglu": q.OUT_GEGLU}[out]
+    y = q.q4_0_matvec_post_norm(torch.from_numpy(W).to(dev), torch.from_numpy(h).to(dev),
+                                torch.from_numpy(z).to(dev), k, b, ld, torch.from_numpy(pw).to(dev),
+                                torch.from_numpy(gw).to(dev) if gain else None, 1e-6, hod,
+                                out_op=oo)
+    torch.cuda.synchronize()
+    ho = hod.cpu().numpy().astype(np.float64)
+    assert np.all(ho[:, k:] == 0.0)
+    normed = oracle.rmsnorm(z[:, :k], pw, 1e-6)
+    ref_h = h[:, :k].astype(np.float64) + normed
+    assert np.all(np.abs(ho[:, :k] - ref_h) <= 2e-4 * np.abs(normed) + 2.0 ** -23 * np.abs(ref_h) + 1e-6)
+    zz, t = oracle.q4_0_matvec(W, n, k, oracle.rmsnorm(ho[:, :k], gw, 1e-6))
+    got = y.cpu().numpy().astype(np.float64)
+    if out == "plain":
+        ref, tol = zz, 2e-4 * t + 1e-6
+    else:
+        F = n // 2
+        g, u = zz[:, :F], zz[:, F:]
+        tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+        act = oracle.swiglu if out == "swiglu" else oracle.geglu
+        ref = act(g, u)
+        tol = 1.13 * tg * np.abs(u) + np.abs(act(g, np.ones_like(g))) * tu + 2e-4 * np.abs(ref) + 1e-6
+    assert got.shape == ref.shape
+    ratio = float((np.abs(got - ref) / tol).max())
+    assert np.all(np.isfinite(got)) and ratio <= 1.0, f"max err/tol {ratio:.3e}"
+
+
 def test_q8_0_gather_scaled(dev):
     """Rows times a scale (the Gemma-4 sqrt(d) embedding scale): (d q) s in fp32,
     within one rounding of the exact product."""

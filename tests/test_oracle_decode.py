@@ -124,7 +124,8 @@ def _compose_one_step(shape, w, caches, pos, tok):
     return logits
 
 
-@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_EXACT],
+@pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4, wl.TINY_GEMMA4_EXACT,
+                                   wl.TINY_GEMMA4_EXACT_B1],
                          ids=lambda s: s.name)
 def test_decode_equals_composition_of_pinned_ops(shape):
     w = wl.model_weights(shape)
