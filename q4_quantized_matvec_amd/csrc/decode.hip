@@ -12,6 +12,13 @@
 // The position of the next token and n = position + 1 live in device memory
 // and are advanced by the step's last kernel, so a graph captured once is
 // valid for every later step.
+//
+// Sandwich post-norms (Gemma-4 block variant, "Research record" page, 31B
+// trace: post-sublayer RMSNorm before the residual add) are applied by the
+// next pre-normed projection where the vector kernels take them, so they cost
+// no launch of their own; the residual stream then alternates between two
+// buffers, since that projection's workgroups read the old stream while one
+// of them writes the new one.
 #include <vector>
 
 #include "common.hpp"
