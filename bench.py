@@ -232,9 +232,8 @@ def device_prefilled_caches(torch, m, dev, kv16=False):
 def bench_decode(q, torch, m, reps=3, warmup=2, device_caches=False, kv16=False):
     """Times 16-step greedy decode runs from the prefilled position (HIP graph
     replay, two graphs ping-ponging the token buffers)."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from decode_util import gpu_model, prefilled_caches, upload_model
     from synth import workloads as wl
+    from synth.device import model_kwargs, prefilled_caches, upload_model
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     weights = wl.model_weights(m)
@@ -246,7 +245,7 @@ def bench_decode(q, torch, m, reps=3, warmup=2, device_caches=False, kv16=False)
     del caches
     del weights
     log(f"{m.name}: generated and uploaded in {time.perf_counter() - t0:.1f} s")
-    dm = gpu_model(q, m, dmod)
+    dm = q.DecodeModel(**model_kwargs(m, dmod))
     a = torch.from_numpy(wl.start_tokens(m)).to(dev)
     b = torch.empty_like(a)
     stream = torch.cuda.current_stream()

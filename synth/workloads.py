@@ -157,32 +157,45 @@ def layer_rows(m: ModelShape, ly: LayerShape):
     return nq, nk, (0 if ly.v_from_k else nk)
 
 
-def model_weights(m: ModelShape):
-    """Host arrays of every weight of the model (merged QKV and gate|up rows)."""
+def layer_weights(m: ModelShape, l: int):
+    """Host arrays of layer ``l`` (its index in the full model) of the model."""
     s = m.seed
-    layers = []
-    for l, ly in enumerate(m.layers):
-        nq, nk, nv = layer_rows(m, ly)
-        layers.append(dict(
-            wqkv=q4_0_matrix(s, f"L{l}.wqkv", nq + nk + nv, m.d_model),
-            wo=q4_0_matrix(s, f"L{l}.wo", m.d_model, nq),
-            wgu=q4_0_matrix(s, f"L{l}.wgu", 2 * m.ffn, m.d_model),
-            wd=q4_0_matrix(s, f"L{l}.wd", m.d_model, m.ffn),
-            attn_norm=uniform_f32(s, f"L{l}.attn_norm", (m.d_model,), 0.8, 1.2),
-            ffn_norm=uniform_f32(s, f"L{l}.ffn_norm", (m.d_model,), 0.8, 1.2),
-            q_norm=uniform_f32(s, f"L{l}.q_norm", (ly.head_dim,), 0.8, 1.2),
-            k_norm=uniform_f32(s, f"L{l}.k_norm", (ly.head_dim,), 0.8, 1.2),
-        ))
-        if m.sandwich:
-            layers[-1]["post_attn_norm"] = uniform_f32(s, f"L{l}.post_attn_norm", (m.d_model,),
-                                                       0.8, 1.2)
-            layers[-1]["post_ffn_norm"] = uniform_f32(s, f"L{l}.post_ffn_norm", (m.d_model,),
-                                                      0.8, 1.2)
+    ly = m.layers[l]
+    nq, nk, nv = layer_rows(m, ly)
+    w = dict(
+        wqkv=q4_0_matrix(s, f"L{l}.wqkv", nq + nk + nv, m.d_model),
+        wo=q4_0_matrix(s, f"L{l}.wo", m.d_model, nq),
+        wgu=q4_0_matrix(s, f"L{l}.wgu", 2 * m.ffn, m.d_model),
+        wd=q4_0_matrix(s, f"L{l}.wd", m.d_model, m.ffn),
+        attn_norm=uniform_f32(s, f"L{l}.attn_norm", (m.d_model,), 0.8, 1.2),
+        ffn_norm=uniform_f32(s, f"L{l}.ffn_norm", (m.d_model,), 0.8, 1.2),
+        q_norm=uniform_f32(s, f"L{l}.q_norm", (ly.head_dim,), 0.8, 1.2),
+        k_norm=uniform_f32(s, f"L{l}.k_norm", (ly.head_dim,), 0.8, 1.2),
+    )
+    if m.sandwich:
+        w["post_attn_norm"] = uniform_f32(s, f"L{l}.post_attn_norm", (m.d_model,), 0.8, 1.2)
+        w["post_ffn_norm"] = uniform_f32(s, f"L{l}.post_ffn_norm", (m.d_model,), 0.8, 1.2)
+    return w
+
+
+def model_weights(m: ModelShape, layer_ids=None):
+    """Host arrays of every weight of the model (merged QKV and gate|up rows);
+    with ``layer_ids`` only those layers (full-model indices), in that order."""
+    s = m.seed
+    ids = range(m.n_layers) if layer_ids is None else layer_ids
     return dict(
         embed=q8_0_matrix(s, "embed", m.vocab, m.d_model),
         final_norm=uniform_f32(s, "final_norm", (m.d_model,), 0.8, 1.2),
-        layers=layers,
+        layers=[layer_weights(m, l) for l in ids],
     )
+
+
+def submodel(m: ModelShape, layer_ids, name=None):
+    """The model restricted to the full-model layers ``layer_ids`` (same
+    widths, vocabulary, batch and start position); pair it with
+    ``model_weights(m, layer_ids)`` and the caches of those layers."""
+    return replace(m, name=name or f"{m.name}_L" + "_".join(str(i) for i in layer_ids),
+                   layers=tuple(m.layers[i] for i in layer_ids))
 
 
 def prefilled_cache(m: ModelShape, l: int, which: str):

@@ -1,46 +1,14 @@
-"""Helpers shared by the decode-step GPU tests and the benchmark: upload a
-synthetic model to the device and run GPU / oracle decode loops."""
+"""Helpers of the decode-step GPU tests: GPU and oracle greedy loops, and a
+step recomposed op by op from the C-ABI calls with every op checked against
+the oracle fed the GPU's own inputs (lockstep)."""
 import numpy as np
 
 from synth import workloads as wl
-
-
-def upload_model(m, weights, dev, caches=None):
-    """Device tensors of every weight and a prefilled cache per layer
-    (``caches``: per layer a (k, v) pair of host arrays or device tensors)."""
-    import torch
-    layers = []
-    for l, ly in enumerate(m.layers):
-        w = weights["layers"][l]
-        if caches is None:
-            kc = wl.prefilled_cache(m, l, "k")
-            vc = wl.prefilled_cache(m, l, "v")
-        else:
-            kc, vc = caches[l]
-        as_dev = lambda a: a if isinstance(a, torch.Tensor) else torch.from_numpy(a).to(dev)
-        layers.append(dict(
-            wqkv=torch.from_numpy(w["wqkv"]).to(dev), wo=torch.from_numpy(w["wo"]).to(dev),
-            wgu=torch.from_numpy(w["wgu"]).to(dev), wd=torch.from_numpy(w["wd"]).to(dev),
-            attn_norm=torch.from_numpy(w["attn_norm"]).to(dev),
-            ffn_norm=torch.from_numpy(w["ffn_norm"]).to(dev),
-            q_norm=torch.from_numpy(w["q_norm"]).to(dev), k_norm=torch.from_numpy(w["k_norm"]).to(dev),
-            k_cache=as_dev(kc), v_cache=as_dev(vc),
-            n_kv_heads=ly.n_kv_heads, head_dim=ly.head_dim, window=ly.window,
-            rope_theta=ly.rope_theta, attn_scale=ly.attn_scale, v_from_k=ly.v_from_k,
-            rope_dims=ly.rope_dims))
-        for key in ("post_attn_norm", "post_ffn_norm"):
-            if key in w:
-                layers[-1][key] = torch.from_numpy(w[key]).to(dev)
-    return dict(embed=torch.from_numpy(weights["embed"]).to(dev),
-                final_norm=torch.from_numpy(weights["final_norm"]).to(dev), layers=layers)
+from synth.device import model_kwargs, prefilled_caches, upload_model  # noqa: F401 (re-exported)
 
 
 def gpu_model(q, m, dev_model):
-    return q.DecodeModel(d_model=m.d_model, n_q_heads=m.n_q_heads, ffn=m.ffn, vocab=m.vocab,
-                         batch=m.batch, eps=m.eps, embed=dev_model["embed"],
-                         final_norm=dev_model["final_norm"], layers=dev_model["layers"],
-                         ffn_act=m.ffn_act, embed_scale=m.embed_scale,
-                         logit_softcap=m.logit_softcap)
+    return q.DecodeModel(**model_kwargs(m, dev_model))
 
 
 def run_gpu(q, m, dev_model, steps, eager=False, want_logits=True):
@@ -64,18 +32,6 @@ def run_gpu(q, m, dev_model, steps, eager=False, want_logits=True):
     return np.stack(toks), (np.stack(lgs) if want_logits else None)
 
 
-def prefilled_caches(m, kv16=False):
-    """Host caches of every layer from the workload recipe; kv16 rounds them
-    to the nearest binary16 (numpy's conversion)."""
-    out = []
-    for l in range(m.n_layers):
-        k, v = wl.prefilled_cache(m, l, "k"), wl.prefilled_cache(m, l, "v")
-        if kv16:
-            k, v = k.astype(np.float16), v.astype(np.float16)
-        out.append((k, v))
-    return out
-
-
 def run_oracle(oracle, m, weights, steps, want_logits=True, caches=None):
     """Greedy loop of the oracle; ``caches`` (modified in place) default to the recipe's."""
     if caches is None:
@@ -91,3 +47,111 @@ def run_oracle(oracle, m, weights, steps, want_logits=True, caches=None):
             lgs.append(lg)
         tok = nxt
     return np.stack(toks), (np.stack(lgs) if want_logits else None), np.stack(margins)
+
+
+def check(got, ref, tol, what, report=None):
+    """max |got - ref| / tol <= 1 elementwise; returns the ratio."""
+    if hasattr(got, "detach"):
+        got = got.detach().cpu().numpy()
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
+    ratio = float((np.abs(got - ref) / tol).max())
+    if report is not None:
+        report[what] = ratio
+    assert ratio <= 1.0, f"{what}: max err/tol {ratio:.3e}"
+    return ratio
+
+
+def lockstep_step(q, oracle, m, weights, dmod, dev, say=print, caches_ids=None):
+    """Recomposes one decode step of model ``m`` (uploaded as ``dmod``, host
+    weights ``weights``) from the C-ABI calls the library's step makes, in its
+    order, and checks each call's output against the oracle op fed the GPU's
+    own inputs.  Returns (next tokens, logits) as device tensors and a dict of
+    the worst err/tol per op.  The plain pre-norm block only (no sandwich
+    norms, no p-RoPE)."""
+    import torch
+    from q4_quantized_matvec_amd._lib import kv_layout_of
+
+    B, D, Hq, F, eps = m.batch, m.d_model, m.n_q_heads, m.ffn, m.eps
+    pos = m.start_pos
+    tok = torch.from_numpy(wl.start_tokens(m)).to(dev)
+    rep = {}
+    np_ = lambda t: t.detach().cpu().numpy().astype(np.float64)
+
+    def proj(fmt, W, xx, K, ld, op, **kw):
+        # the step runs its projections on the matrix cores when B >= 2
+        if B >= 2 and K % 256 == 0:
+            fn = q.q4_0_matvec_batched if fmt == 4 else q.q8_0_matvec_batched
+        else:
+            fn = q.q4_0_matvec_fused if fmt == 4 else q.q8_0_matvec_fused
+        return fn(W, xx, K, B, ld, op, eps=eps, **kw)
+
+    pos_d = torch.tensor([pos, pos + 1], dtype=torch.int64, device=dev)
+    x = q.q8_0_gather(dmod["embed"], tok, D)
+    check(x, oracle.q8_0_gather(weights["embed"], m.vocab, D, tok.cpu().numpy()),
+          np.full((B, D), 1e-30), "gather (exact)", rep)
+    for l, ly in enumerate(m.layers):
+        assert ly.rope_dims == 0 and not m.sandwich and m.ffn_act == "silu"
+        L, W = dmod["layers"][l], weights["layers"][l]
+        hd, hkv = ly.head_dim, ly.n_kv_heads
+        nq, nk, nv = wl.layer_rows(m, ly)
+        nqkv = nq + nk + nv
+        say(f"  lockstep layer {l}: hd {hd}, {hkv} kv heads, window {ly.window}, cap {ly.cap}")
+        qkv = proj(4, L["wqkv"], x, D, D, q.IN_RMSNORM, norm_w=L["attn_norm"])
+        r, t = oracle.q4_0_matvec(W["wqkv"], nqkv, D, oracle.rmsnorm(np_(x), W["attn_norm"], eps))
+        check(qkv, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + qkv matvec", rep)
+        raw = np_(qkv).copy()
+        kv = kv_layout_of(L["k_cache"])
+        ws = torch.empty(q.gqa_decode_attn_workspace(kv, Hq, ly.window), dtype=torch.uint8, device=dev)
+        att = torch.empty((B, nq), dtype=torch.float32, device=dev)
+        # the step fuses QK-norm, RoPE and the KV append into the attention call
+        q.gqa_decode_attn_rope(qkv, nqkv, Hq, L["q_norm"], L["k_norm"], kv, pos_d[0:1], ly.rope_theta,
+                               eps, ly.v_from_k, L["k_cache"], L["v_cache"], ly.window,
+                               ly.attn_scale, att, nq, ws)
+        slot = pos % ly.cap
+        n = pos + 1
+        lo = max(0, n - ly.window) if ly.window else 0
+        vis = np.arange(lo, n)
+        kc_t, vc_t = L["k_cache"], L["v_cache"]
+        for b in range(B):
+            kr = raw[b, nq:nq + nk].reshape(hkv, hd)
+            kref = oracle.rope_neox(oracle.rmsnorm(kr, W["k_norm"], eps), pos, ly.rope_theta)
+            check(np_(kc_t[b, :, slot]), kref, 2e-4 * np.abs(kref) + 2e-5, f"L{l} appended key", rep)
+            vref = (oracle.rmsnorm(kr, None, eps) if ly.v_from_k
+                    else raw[b, nq + nk:].reshape(hkv, hd))
+            check(np_(vc_t[b, :, slot]), vref, 2e-4 * np.abs(vref) + 1e-6, f"L{l} appended value", rep)
+            qh = oracle.rope_neox(oracle.rmsnorm(raw[b, :nq].reshape(Hq, hd), W["q_norm"], eps),
+                                  pos, ly.rope_theta)
+            # the visible positions' rows, read back from their slots (a ring
+            # wraps: position p lives in slot p % cap)
+            sl = torch.from_numpy(vis % ly.cap).to(dev)
+            keys = np.zeros((n, hkv, hd))
+            vals = np.zeros((n, hkv, hd))
+            keys[lo:] = np_(kc_t[b][:, sl].permute(1, 0, 2))
+            vals[lo:] = np_(vc_t[b][:, sl].permute(1, 0, 2))
+            o, bound = oracle.gqa_attention(qh, keys, vals, ly.window, ly.attn_scale)
+            check(att[b], o, 2e-4 * bound + 1e-6, f"L{l} attention", rep)
+        xo = np_(x)
+        proj(4, L["wo"], att, nq, nq, q.IN_PLAIN, y=x, residual=x)
+        r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att), res=xo)
+        check(x, r, 2e-4 * t + 1e-6, f"L{l} o-proj + residual", rep)
+        # the step hands SiLU(gate) * up from the gate|up kernel to the down projection
+        h = proj(4, L["wgu"], x, D, D, q.IN_RMSNORM, norm_w=L["ffn_norm"], out_op=q.OUT_SWIGLU)
+        r, t = oracle.q4_0_matvec(W["wgu"], 2 * F, D, oracle.rmsnorm(np_(x), W["ffn_norm"], eps))
+        g, u = r[:, :F], r[:, F:]
+        tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+        h_ref = np.stack([oracle.swiglu(g[b], u[b]) for b in range(B)])
+        silu_g = g / (1.0 + np.exp(-g))
+        check(h, h_ref, 1.1 * tg * np.abs(u) + np.abs(silu_g) * tu + 2e-4 * np.abs(h_ref) + 1e-6,
+              f"L{l} rmsnorm + gate|up + swiglu", rep)
+        xo = np_(x)
+        proj(4, L["wd"], h, F, F, q.IN_PLAIN, y=x, residual=x)
+        r, t = oracle.q4_0_matvec(W["wd"], D, F, np_(h), res=xo)
+        check(x, r, 2e-4 * t + 1e-6, f"L{l} down + residual", rep)
+    logits = proj(8, dmod["embed"], x, D, D, q.IN_RMSNORM, norm_w=dmod["final_norm"])
+    r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D,
+                              oracle.rmsnorm(np_(x), weights["final_norm"], eps))
+    check(logits, r, 2e-4 * t + 1e-6, "final rmsnorm + logits", rep)
+    nxt = q.argmax_rows(logits)
+    lg = np_(logits)
+    assert nxt.cpu().numpy().tolist() == [oracle.argmax(lg[b])[0] for b in range(B)]
+    return tok, nxt, logits, rep

@@ -3,9 +3,11 @@
 Runs only the fp64 oracle (oracle/) on the seeded inputs of synth/: nothing
 here touches the HIP library.  For each model it stores, per step and
 sequence, the greedy token, the oracle's top-2 margin, and the oracle logits
-at a sample of vocabulary indices (the 8 largest plus 24 fixed seeded ones),
-so the GPU test can compare tokens exactly and logits on the sample without
-re-running a multi-minute fp64 decode on every test run.
+at a sample of vocabulary indices (the 8 largest plus 24 fixed seeded ones);
+for the first and the last step it also stores every logit of the vocabulary
+(fp32, ``<name>_logits_sNN.npy``), so the GPU test compares the whole
+vocabulary there without re-running a multi-minute fp64 decode on every test
+run.
 
 Usage:  python tests/golden/make_decode_oracle.py [decode_qwen3_4b] [decode_gemma4_31b]
 """
@@ -16,7 +18,8 @@ import time
 
 import numpy as np
 
-ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
@@ -27,18 +30,28 @@ N_TOP = 8
 N_FIXED = 24
 
 
+def full_logit_steps(m):
+    return [0, m.steps - 1]
+
+
+def logits_path(name, step):
+    return os.path.join(HERE, f"{name}_logits_s{step:02d}.npy")
+
+
 def run(m):
     t0 = time.time()
     weights = wl.model_weights(m)
     caches = [(wl.prefilled_cache(m, l, "k"), wl.prefilled_cache(m, l, "v"))
               for l in range(m.n_layers)]
-    print(f"{m.name}: inputs in {time.time() - t0:.0f} s", flush=True)
+    print(f"{m.name}: inputs in {time.time() - t0:.0f} s, {oracle.num_threads()} oracle threads",
+          flush=True)
     om = oracle.Model(wl.oracle_spec(m, weights, caches))
     fixed = synth.tokens(m.seed, "logit_sample", N_FIXED, m.vocab).astype(np.int64)
     tok = wl.start_tokens(m)
     out = dict(workload=m.name, seed=m.seed, start_pos=m.start_pos, steps=m.steps,
                batch=m.batch, vocab=m.vocab, start_tokens=tok.tolist(),
-               tokens=[], margins=[], sample_idx=[], sample_logits=[], logits_sq_sum=[])
+               tokens=[], margins=[], sample_idx=[], sample_logits=[], logits_sq_sum=[],
+               full_logit_steps=full_logit_steps(m))
     for s in range(m.steps):
         t1 = time.time()
         nxt, lg, mg = om.step(m.start_pos + s, tok, want_logits=True)
@@ -54,6 +67,8 @@ def run(m):
         out["sample_idx"].append(idx)
         out["sample_logits"].append(vals)
         out["logits_sq_sum"].append([float((lg[b] ** 2).sum()) for b in range(m.batch)])
+        if s in out["full_logit_steps"]:
+            np.save(logits_path(m.name, s), lg.astype(np.float32))
         print(f"  step {s}: {time.time() - t1:.1f} s tokens {nxt.tolist()} "
               f"min margin {mg.min():.4f}", flush=True)
         tok = nxt
@@ -65,7 +80,7 @@ def main():
     shapes = {wl.QWEN3_4B.name: wl.QWEN3_4B, wl.GEMMA4_31B.name: wl.GEMMA4_31B}
     for name in names:
         out = run(shapes[name])
-        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{name}_oracle.json")
+        path = os.path.join(HERE, f"{name}_oracle.json")
         with open(path, "w") as f:
             json.dump(out, f)
         print(f"wrote {path}", flush=True)
