@@ -167,6 +167,26 @@ q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *
                               q4_output_op out_op, const float *norm_w, float eps, float *y,
                               const float *residual, void *ws, size_t ws_bytes, void *stream);
 
+/* q4_0_matvec_batched_noalloc: q4_0_matvec_batched without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments (less ws / ws_bytes), results bit-identical to
+ * q4_0_matvec_batched's, same errors.  The split tickets, sums of squares and
+ * split-K partials live in a static device array of
+ * Q4_NOALLOC_SCRATCH_BYTES per device, held until the process ends; a shape
+ * whose plan needs more (matvec_batched_workspace(N, K, B) > that size)
+ * returns Q4_ERR_UNSUPPORTED before any HIP call.  The call allocates and
+ * frees nothing.  The first call on a device looks the array up and clears
+ * its tickets with a small kernel on `stream`; every call leaves them zero.
+ * All calls on one device share the array: calls that overlap in time (on
+ * different streams, or from several threads without ordering) race and
+ * give undefined results. */
+#define Q4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+q4_status q4_0_matvec_batched_noalloc(const void *W, int64_t N, int64_t K, const float *x,
+                                      const float *x2, int64_t ld_x, int64_t B, q4_input_op op,
+                                      q4_output_op out_op, const float *norm_w, float eps,
+                                      float *y, const float *residual, void *stream);
+
 /* q8_0_gather: x[b][:] = dequantised row tokens[b] of the Q8_0 table E
  * (embedding lookup of the tied table; [GELO] 05 generation loop embeds the
  * previous token).

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     q4_0_matvec_fused,
     q4_0_matvec_post_norm,
     q4_0_matvec_batched,
+    q4_0_matvec_batched_noalloc,
     q8_0_matvec_batched,
     q8_0_matvec_fused,
     q8_0_gather,

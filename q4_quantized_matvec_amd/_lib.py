@@ -66,6 +66,8 @@ _SIGS = {
                              _P, _SZ, _P], C.c_int),
     "q8_0_matvec_batched": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F, _P, _P,
                              _P, _SZ, _P], C.c_int),
+    "q4_0_matvec_batched_noalloc": ([_P, _I64, _I64, _P, _P, _I64, _I64, C.c_int, C.c_int, _P, _F,
+                                     _P, _P, _P], C.c_int),
     "rmsnorm": ([_P, _P, _I64, _I64, _F, _P, _P], C.c_int),
     "swiglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
     "geglu": ([_P, _P, _I64, _I64, _I64, _P, _P], C.c_int),
@@ -261,6 +263,24 @@ def q8_0_matvec_batched(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=N
                         residual=None, ws=None, stream=None, n=None, out_op=OUT_PLAIN):
     return _matvec_batched("q8_0_matvec_batched", 34, W, x, K, B, ld, op, x2, norm_w, eps, y,
                            residual, ws, stream, n, out_op)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # Q4_NOALLOC_SCRATCH_BYTES
+
+
+def q4_0_matvec_batched_noalloc(W, x, K, B, ld, op=0, x2=None, norm_w=None, eps=0.0, y=None,
+                                residual=None, stream=None, n=None, out_op=OUT_PLAIN):
+    """q4_0_matvec_batched with its scratch in the library's static per-device array
+    (no workspace argument; the library allocates nothing).  Pass ``y`` to avoid the
+    output allocation on the Python side."""
+    import torch
+    N = n if n is not None else _qmatrix_dims(W, K, 18)
+    if y is None:
+        y = torch.empty((B, _out_cols(N, out_op)), dtype=torch.float32, device=x.device)
+    _check("q4_0_matvec_batched_noalloc", lib().q4_0_matvec_batched_noalloc(
+        _ptr(W), N, K, _ptr(x), _ptr(x2), ld, B, int(op), int(out_op), _ptr(norm_w), float(eps),
+        _ptr(y), _ptr(residual), _stream(stream)))
+    return y
 
 
 def q8_0_gather(E, tokens, K, x=None, stream=None, scale=None):

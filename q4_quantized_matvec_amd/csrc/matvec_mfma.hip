@@ -44,6 +44,8 @@
 // its groups are dispatched one after another to the same XCD, so the
 // weights come from HBM once and the later groups read them from that XCD's
 // L2.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -897,11 +899,16 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
+constexpr size_t kStaticScratchBytes = Q4_NOALLOC_SCRATCH_BYTES;  // allocation-free variant's scratch
+q4_status static_scratch(hipStream_t s, void **out);
+
+// use_static: the allocation-free variant; ws / ws_bytes are ignored and the
+// per-device static scratch is used once every argument has been checked.
 template <int FMT>
 q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
                         const float *x2, int64_t ldx, int64_t B, int op_kind, int out_op,
                         const float *norm_w, float eps, float *y, const float *res, void *ws,
-                        size_t ws_bytes, void *stream) {
+                        size_t ws_bytes, void *stream, bool use_static = false) {
     q4::clear_error();
     Q4_CHECK(out_op == Q4_OUT_PLAIN || out_op == Q4_OUT_SWIGLU || out_op == Q4_OUT_GEGLU,
              Q4_ERR_INVALID_ARG, "%s: unknown output transform %d", name, out_op);
@@ -938,11 +945,19 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
              Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
     const Plan p = make_plan(N, K, B, FMT);
+    hipStream_t s = q4::as_stream(stream);
+    if (use_static) {
+        Q4_CHECK(p.bytes <= kStaticScratchBytes, Q4_ERR_UNSUPPORTED,
+                 "%s: N=%lld K=%lld B=%lld needs %zu bytes of scratch, more than the %zu held per device",
+                 name, (long long)N, (long long)K, (long long)B, p.bytes, kStaticScratchBytes);
+        q4_status st = static_scratch(s, &ws);
+        if (st != Q4_OK) return st;
+        ws_bytes = kStaticScratchBytes;
+    }
     Q4_CHECK(ws && q4::aligned(ws, 256), Q4_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
              name);
     Q4_CHECK(ws_bytes >= p.bytes, Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", name,
              ws_bytes, p.bytes);
-    hipStream_t s = q4::as_stream(stream);
     const uint8_t *W = static_cast<const uint8_t *>(Wv);
     const int n = static_cast<int>(N), k = static_cast<int>(K), b = static_cast<int>(B);
     const int glu = out_op == Q4_OUT_PLAIN ? 0 : 1;
@@ -979,4 +994,58 @@ extern "C" q4_status q8_0_matvec_batched(const void *W, int64_t N, int64_t K, co
                                          size_t ws_bytes, void *stream) {
     return batched_entry<1>("q8_0_matvec_batched", W, N, K, x, x2, ld_x, B, op, out_op, norm_w,
                             eps, y, residual, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------ allocation-free variant
+namespace {
+
+// Scratch of q4_0_matvec_batched_noalloc: the split tickets, sums of squares
+// and split-K partials live in this array, one copy per device, held until
+// the process ends.  In host code its name is only a stand-in; the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch.  On the first call on a
+// device the tickets are cleared by a fill kernel on `s`, ordered before the
+// caller's kernel (a memset node would not be safe inside a captured graph).
+q4_status static_scratch(hipStream_t s, void **out) {
+    int dev = -1;
+    Q4_HIP_CHECK(hipGetDevice(&dev));
+    Q4_CHECK(dev >= 0 && dev < kMaxDevices, Q4_ERR_UNSUPPORTED,
+             "q4_0_matvec_batched_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        Q4_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        Q4_CHECK(p && q4::aligned(p, 256), Q4_ERR_HIP,
+                 "q4_0_matvec_batched_noalloc: the scratch symbol has no usable device address");
+        const int words = static_cast<int>(kCounterBytes / sizeof(uint32_t));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s,
+                           static_cast<uint32_t *>(p), words);
+        q4_status st = q4::launch_status("q4_0_matvec_batched_noalloc (scratch clear)");
+        if (st != Q4_OK) return st;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" q4_status q4_0_matvec_batched_noalloc(const void *W, int64_t N, int64_t K,
+                                                 const float *x, const float *x2, int64_t ld_x,
+                                                 int64_t B, q4_input_op op, q4_output_op out_op,
+                                                 const float *norm_w, float eps, float *y,
+                                                 const float *residual, void *stream) {
+    return batched_entry<0>("q4_0_matvec_batched_noalloc", W, N, K, x, x2, ld_x, B, op, out_op,
+                            norm_w, eps, y, residual, nullptr, 0, stream, true);
 }
