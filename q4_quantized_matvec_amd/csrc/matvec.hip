@@ -82,6 +82,18 @@ __device__ __forceinline__ float glu_mul(int a, float g, float u) {
     return a ? act_mul<true>(g, u) : act_mul<false>(g, u);
 }
 
+// Sum of the staged float4 t over the 8 consecutive lanes that hold one
+// 32-element block (lanes 8m .. 8m+7); every lane of the group gets it.  The
+// adds run in a fixed order, so the sums are reproducible.  All lanes must be
+// active.
+__device__ __forceinline__ float block_sum8(float4 t) {
+    float p = (t.x + t.y) + (t.z + t.w);
+    p += dpp<0xB1>(p);   // quad_perm [1,0,3,2]
+    p += dpp<0x4E>(p);   // quad_perm [2,3,0,1]
+    p += dpp<0x141>(p);  // row_half_mirror: the other quad of the 8
+    return p;
+}
+
 template <int FMT, int JX>
 struct RowRegs {
     uint32_t w[JX][Fmt<FMT>::kDwords + 1];
@@ -145,8 +157,10 @@ constexpr int kXLdsFloats = 8192;  // LDS staging of x when the whole K fits
 
 // B = 1 fast path.  KS wavefronts of a workgroup split K; 4 / KS row groups;
 // PF rows of loads in flight per wavefront.
+// With three Q4_0 block columns per lane (K up to 6144) the kernel fits three
+// wavefronts per SIMD only at <= 168 VGPRs; the launch bound holds it there.
 template <int FMT, int JX, int KS, int PF, bool GLU, bool GELU, bool POST>
-__global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
+__global__ __launch_bounds__(kWG, FMT == 0 && JX == 3 && KS == 1 ? 3 : Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8_t *__restrict__ W,
                                                     const float *x, float *y, const float *res,
                                                     int N, int K, InOp op) {
     constexpr int RG = 4 / KS;
@@ -167,6 +181,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
     __shared__ float kpart[KS > 1 ? 4 * kFlush : 1];
     __shared__ float kres[KS > 1 ? 4 * kFlush : 1];
     __shared__ float xs[kXLds ? kXLdsFloats : 1];
+    __shared__ float xsum[kXLds ? kXLdsFloats / 32 : 1];  // per-block sums of the staged activations
     const int lane = threadIdx.x & 63;
     // wave-uniform: keeps row addressing in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -276,19 +291,23 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
 #pragma unroll
         for (int r = 0; r < kXV; ++r) {
             const int i = threadIdx.x + r * kWG;
+            float4 t;
+            t.x = __builtin_fmaf(pv[r].x, zv[r].x * rz, hv[r].x);
+            t.y = __builtin_fmaf(pv[r].y, zv[r].y * rz, hv[r].y);
+            t.z = __builtin_fmaf(pv[r].z, zv[r].z * rz, hv[r].z);
+            t.w = __builtin_fmaf(pv[r].w, zv[r].w * rz, hv[r].w);
             if (i < nv) {
-                float4 t;
-                t.x = __builtin_fmaf(pv[r].x, zv[r].x * rz, hv[r].x);
-                t.y = __builtin_fmaf(pv[r].y, zv[r].y * rz, hv[r].y);
-                t.z = __builtin_fmaf(pv[r].z, zv[r].z * rz, hv[r].z);
-                t.w = __builtin_fmaf(pv[r].w, zv[r].w * rz, hv[r].w);
                 if (writer) ho[i] = t;
                 ss = __builtin_fmaf(t.x, t.x, __builtin_fmaf(t.y, t.y, __builtin_fmaf(t.z, t.z, __builtin_fmaf(t.w, t.w, ss))));
-                t.x *= gv[r].x;
-                t.y *= gv[r].y;
-                t.z *= gv[r].z;
-                t.w *= gv[r].w;
+            }
+            t.x *= gv[r].x;
+            t.y *= gv[r].y;
+            t.z *= gv[r].z;
+            t.w *= gv[r].w;
+            const float bs = block_sum8(t);  // K is a multiple of 256: no group straddles nv
+            if (i < nv) {
                 xl[i] = t;
+                if ((i & 7) == 0) xsum[i >> 3] = bs;
             }
         }
         ss = wave_sum(ss);
@@ -321,22 +340,25 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
 #pragma unroll
         for (int r = 0; r < kXV; ++r) {
             const int i = threadIdx.x + r * kWG;
-            if (i < nv) {
-                float4 t = v[r];
-                if (op.kind == 2) {
-                    t.x = act_mul<GELU>(t.x, u[r].x);
-                    t.y = act_mul<GELU>(t.y, u[r].y);
-                    t.z = act_mul<GELU>(t.z, u[r].z);
-                    t.w = act_mul<GELU>(t.w, u[r].w);
-                }
+            float4 t = v[r];
+            if (op.kind == 2) {
+                t.x = act_mul<GELU>(t.x, u[r].x);
+                t.y = act_mul<GELU>(t.y, u[r].y);
+                t.z = act_mul<GELU>(t.z, u[r].z);
+                t.w = act_mul<GELU>(t.w, u[r].w);
+            }
+            if (i < nv)
                 ss = __builtin_fmaf(t.x, t.x, __builtin_fmaf(t.y, t.y, __builtin_fmaf(t.z, t.z, __builtin_fmaf(t.w, t.w, ss))));
-                if (op.kind == 1 && sg) {
-                    t.x *= u[r].x;
-                    t.y *= u[r].y;
-                    t.z *= u[r].z;
-                    t.w *= u[r].w;
-                }
+            if (op.kind == 1 && sg) {
+                t.x *= u[r].x;
+                t.y *= u[r].y;
+                t.z *= u[r].z;
+                t.w *= u[r].w;
+            }
+            const float bs = block_sum8(t);  // K is a multiple of 256: no group straddles nv
+            if (i < nv) {
                 xl[i] = t;
+                if ((i & 7) == 0) xsum[i >> 3] = bs;
             }
         }
         if (op.kind == 1) {
@@ -365,6 +387,8 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
         }
         inv = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(K) + op.eps);
     }
+    // 1/rms is the same for the whole workgroup: keep it in a scalar register
+    inv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, inv)));
     float xr[JX][32];
     float xc[JX];
 #pragma unroll
@@ -389,27 +413,22 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                 xr[j][4 * i + 2] = v.z;
                 xr[j][4 * i + 3] = v.w;
             }
-            if (op.kind == 1) {
-                if (kXLds || !op.w) {  // staged values already carry the gain
+            if (op.kind == 1 && !kXLds && op.w) {  // staged values already carry the gain
+                const float4 *wg = reinterpret_cast<const float4 *>(op.w + static_cast<size_t>(c) * 32);
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) xr[j][i] *= inv;
-                } else {
-                    const float4 *wg = reinterpret_cast<const float4 *>(op.w + static_cast<size_t>(c) * 32);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float4 g4 = wg[i];
-                        xr[j][4 * i + 0] = xr[j][4 * i + 0] * inv * g4.x;
-                        xr[j][4 * i + 1] = xr[j][4 * i + 1] * inv * g4.y;
-                        xr[j][4 * i + 2] = xr[j][4 * i + 2] * inv * g4.z;
-                        xr[j][4 * i + 3] = xr[j][4 * i + 3] * inv * g4.w;
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    const float4 g4 = wg[i];
+                    xr[j][4 * i + 0] *= g4.x;
+                    xr[j][4 * i + 1] *= g4.y;
+                    xr[j][4 * i + 2] *= g4.z;
+                    xr[j][4 * i + 3] *= g4.w;
                 }
             }
+            if constexpr (kXLds) {
+                s = xsum[c];
+            } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) s += xr[j][i];
-            if constexpr (FMT == 0) {
-#pragma unroll
-                for (int i = 16; i < 32; ++i) xr[j][i] *= 0.0625f;  // exact power-of-two scaling
+                for (int i = 0; i < 32; ++i) s += xr[j][i];
             }
         } else {
 #pragma unroll
@@ -436,8 +455,8 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                     for (int j = 0; j < JX; ++j) {
                         // e = code bytes (4i, 4i+2), o = (4i+1, 4i+3), one per 16-bit
                         // lane.  Low nibbles -> binary16 subnormals q * 2^-24; high
-                        // nibbles stay in bits 4..7 (16 q * 2^-24) and meet
-                        // activations pre-scaled by 1/16 (exact).
+                        // nibbles stay in bits 4..7 (16 q * 2^-24) and are summed
+                        // apart, the sum scaled by 1/16 once (exact).
                         const uint32_t e = __builtin_amdgcn_perm(cur.w[j][i + 1], cur.w[j][i], sel_e);
                         const uint32_t o = __builtin_amdgcn_perm(cur.w[j][i + 1], cur.w[j][i], sel_o);
                         const uint32_t le = e & 0x000F000Fu, he = e & 0x00F000F0u;
@@ -455,7 +474,8 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
 #pragma unroll
                 for (int j = 0; j < JX; ++j) {
                     const float d = half_bits_to_float(__builtin_amdgcn_perm(0u, cur.w[j][0], sel_d));
-                    const float t = __builtin_fmaf(d, __builtin_fmaf(sa[j] + sb[j], 16777216.f, xc[j]), acc);
+                    // high nibbles were taken x16: sb / 16 (exact)
+                    const float t = __builtin_fmaf(d, __builtin_fmaf(__builtin_fmaf(sb[j], 0.0625f, sa[j]), 16777216.f, xc[j]), acc);
                     acc = valid[j] ? t : acc;
                 }
             } else {
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(kWG, Q4_MV_MIN_WAVES) void mv_b1_kernel(const uint8
                 }
             }
         }
-        acc = wave_sum(acc);
+        acc = wave_sum(acc) * inv;  // RMSNorm: 1/rms of the row, once per output
         const int row = row0 + it;
         if constexpr (KS == 1) {
             if constexpr (GLU) {
