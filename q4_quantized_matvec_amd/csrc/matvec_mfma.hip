@@ -119,7 +119,7 @@ struct GroupView {
     bool live;
 };
 __device__ __forceinline__ GroupView group_view(int rg, int NG, int B) {
-    if (NG == 1) return {static_cast<int>(blockIdx.x), 0, B, true};
+    if (NG == 1) return {static_cast<int>(blockIdx.x), 0, B, static_cast<int>(blockIdx.x) < rg};
     const int L = blockIdx.x, j = L >> 3;
     const int gi = j % NG, rx = (j / NG) * 8 + (L & 7);
     return {rx, gi, min(kMaxB, B - kMaxB * gi), rx < rg};
@@ -812,9 +812,369 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     finish<KIND, T, GELU>(fa_, ya, yb, n, rvalid, pl, pu, ssq_w);
 }
 
+// ------------------------------------------ K-stationary streaming kernel
+// A workgroup of WV wavefronts owns a K range of WV steps (one per
+// wavefront) and a run of up to TMAX row tiles of 16 rows.  Each wavefront
+// converts its step's activations into exact halves once, keeps them in
+// registers for the whole kernel, and streams the row tiles' weights past
+// them (PF tiles in flight), writing each tile's partial sums to LDS.  At the
+// end the wavefronts' partials are added in wavefront order.  When the
+// workgroup covers the whole K (S = 1) it writes y itself; otherwise it
+// stores its K range's partials and mv_splitk_reduce_kernel, launched next,
+// adds the S ranges in order (no tickets or device-scope synchronisation: on
+// this part those cost three memory round trips at the end of every row
+// range).  With a SwiGLU output the first half of the workgroup's tiles are
+// gate tiles and the second half the matching up tiles.
+template <int FMT, int KIND, int TMAX, bool GELU, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) void mv_mfma_kstat_kernel(
+    const uint8_t *__restrict__ W, int N, int K, int B, const float *__restrict__ x,
+    const float *__restrict__ u, const float *__restrict__ nw, int64_t ld, float eps, float *y,
+    const float *res, int *__restrict__ counters, float *__restrict__ ssq_part,
+    float *__restrict__ part, int S, int tpw, int glu, int rg, int NG) {
+    constexpr int kBytes = BF<FMT>::kBytes;
+    constexpr int kDw = BF<FMT>::kLaneDw;
+#ifndef Q4_KS_PF
+#define Q4_KS_PF 3
+#endif
+    constexpr int PF = FMT == 1 ? 2 : Q4_KS_PF;  // row tiles in flight ahead of the one multiplied
+    // operand transposition (per wavefront, at the start) and the partials of
+    // every tile (at the end) share one LDS region; a barrier separates them
+    constexpr size_t kOpndBytes = sizeof(u32x4_t) * WV * kSeg * 64;
+    constexpr size_t kRedBytes = sizeof(float2) * WV * TMAX * 64;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kOpndBytes > kRedBytes ? kOpndBytes : kRedBytes];
+    auto opnd = reinterpret_cast<u32x4_t(*)[kSeg][64]>(smem);
+    auto red = reinterpret_cast<float2(*)[TMAX][64]>(smem);
+    __shared__ float ssq_w[WV][kMaxB];
+    __shared__ float inv_s[kMaxB];
+    const GroupView gv_ = group_view(rg, NG, B);
+    if (!gv_.live) return;  // padding of the last octet (workgroup-uniform)
+    const int rx = gv_.rx;
+    {
+        const int64_t g8 = static_cast<int64_t>(kMaxB) * gv_.gi;
+        const int64_t outw = glu ? (N >> 1) : N;
+        x += g8 * ld;
+        if (u) u += g8 * ld;
+        y += g8 * outw;
+        if (res) res += g8 * N;
+        part += static_cast<int64_t>(gv_.gi) * S * kMaxB * N;
+        ssq_part += static_cast<int64_t>(gv_.gi) * S * kMaxB;
+        B = gv_.Bg;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int nb = K / 32, kc = nb / kSeg;
+    const int c = blockIdx.y * WV + wv;  // this wavefront's step
+    const bool active = c < kc;         // wave-uniform
+    const int P = N >> 1;
+    // tiles of this workgroup: t < nt; row of tile t for this lane
+    const int half = tpw >> 1;
+    const int units = glu ? (P + 15) / 16 : (N + 15) / 16;  // gate tiles (SwiGLU output) or tiles
+    const int per = glu ? half : tpw;
+    const int u0 = rx * per;
+    const int nu = max(0, min(per, units - u0));
+    const int nt = glu ? 2 * nu : nu;
+    auto tile_row = [&](int t, bool &valid) {
+        if (glu) {
+            const int pr = 16 * (u0 + (t < half ? t : t - half)) + col;
+            valid = pr < P;
+            return t < half ? pr : P + pr;
+        }
+        const int r = 16 * (u0 + t) + col;
+        valid = r < N;
+        return r;
+    };
+    auto tile_of = [&](int t) { return glu ? (t < nu ? t : t - nu + half) : t; };  // slot of the t-th live tile
+    const int64_t seg = kSeg * kBytes;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- this wavefront's step: activations -> exact halves (MFMA operand order)
+    half8_t af[kSeg];
+    float fa = 0.f, fb = 0.f;
+    float sqa = 0.f;  // RMSNorm: lane b < 8 holds batch row b's sum of squares over the step
+    if (active) {
+        const int jl = lane >> 3, q8 = lane & 7;
+        const int gl = FMT == 0 ? (q8 & 3) : (q8 >> 1);
+        const int el = FMT == 0 ? (q8 >= 4 ? 4 : 0) : 4 * (q8 & 1);
+        const float hscale = (FMT == 0 && q8 >= 4) ? 0.0625f : 1.0f;
+        const int64_t kx = static_cast<int64_t>(c) * (32 * kSeg) + 4 * lane;
+        f32x4_t xv[kMaxB], tv[kMaxB];
+        f32x4_t gvv = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (KIND == 1) {
+            if (nw) gvv = *reinterpret_cast<const f32x4_al16_t *>(nw + kx);
+        }
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            const int64_t bo = static_cast<int64_t>(min(b, B - 1)) * ld + kx;
+            xv[b] = *reinterpret_cast<const f32x4_al16_t *>(x + bo);
+            if constexpr (KIND == 2) tv[b] = *reinterpret_cast<const f32x4_al16_t *>(u + bo);
+        }
+        float ssq[kMaxB], mx[kMaxB];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            if (b >= B) {
+                xv[b] = zero;
+                if constexpr (KIND == 2) tv[b] = zero;
+            }
+            f32x4_t t = xv[b];
+            ssq[b] = 0.f;
+            if constexpr (KIND == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ssq[b] = fmaf(xv[b][e], xv[b][e], ssq[b]);
+                    t[e] = xv[b][e] * gvv[e];
+                }
+            } else if constexpr (KIND == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = act_mul<GELU>(xv[b][e], tv[b][e]);
+            }
+            xv[b] = t;
+            mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
+        }
+        int sh[kMaxB];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) sh[b] = step_shift(wave_max(mx[b]));
+        uint8_t *obase = reinterpret_cast<uint8_t *>(&opnd[wv][jl][16 * gl]) + 2 * el;
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b) {
+            const float sc = ldexpf(hscale, sh[b]);
+            half2_t h01, h23, l01, l23;
+            const float v0 = xv[b][0] * sc, v1 = xv[b][1] * sc, v2 = xv[b][2] * sc, v3 = xv[b][3] * sc;
+            h01.x = static_cast<_Float16>(v0);
+            h01.y = static_cast<_Float16>(v1);
+            h23.x = static_cast<_Float16>(v2);
+            h23.y = static_cast<_Float16>(v3);
+            l01.x = static_cast<_Float16>(v0 - static_cast<float>(h01.x));
+            l01.y = static_cast<_Float16>(v1 - static_cast<float>(h01.y));
+            l23.x = static_cast<_Float16>(v2 - static_cast<float>(h23.x));
+            l23.y = static_cast<_Float16>(v3 - static_cast<float>(h23.y));
+            uint2 hv, lv;
+            hv.x = __builtin_bit_cast(uint32_t, h01);
+            hv.y = __builtin_bit_cast(uint32_t, h23);
+            lv.x = __builtin_bit_cast(uint32_t, l01);
+            lv.y = __builtin_bit_cast(uint32_t, l23);
+            *reinterpret_cast<uint2 *>(obase + 16 * (2 * b)) = hv;      // MFMA row 2b: hi
+            *reinterpret_cast<uint2 *>(obase + 16 * (2 * b + 1)) = lv;  // MFMA row 2b + 1: lo
+        }
+        if constexpr (KIND == 1) {
+#pragma unroll
+            for (int b = 0; b < kMaxB; ++b) {
+                const float t = wave_sum(ssq[b]);
+                if (lane == b) sqa = t;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wavefront reads back its own writes
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int jj = 0; jj < kSeg; ++jj) af[jj] = __builtin_bit_cast(half8_t, opnd[wv][jj][lane]);
+        int sa = sh[0], sb = sh[1];
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (g == q) {
+                sa = sh[2 * q];
+                sb = sh[2 * q + 1];
+            }
+        fa = ldexpf(1.0f, -sa);
+        fb = ldexpf(1.0f, -sb);
+    }
+    __syncthreads();  // every wavefront holds its operands: the LDS region is free
+
+    // ---- stream the row tiles past the step's operands; each tile's partial
+    // sums go to its LDS slot at once (live tile i -> slot tile_of(i): gate
+    // tiles first, up tiles from slot tpw / 2; only live slots are read back)
+    // Every wavefront runs the same stream: one past the last step re-reads the
+    // last step's weights (L2 hits) with zero operands and scales, so it adds
+    // exact zeros to its slots.
+    if (!active) {
+#pragma unroll
+        for (int jj = 0; jj < kSeg; ++jj) af[jj] = half8_t{};
+    }
+    if (nt > 0) {  // workgroup-uniform
+        constexpr int NBUF = PF + 1;
+        const uint8_t *wbase = W + g * 2 * kBytes + static_cast<int64_t>(min(c, kc - 1)) * seg;
+        auto fetch = [&](int i, uint32_t (&dst)[kDw]) {  // i-th live tile, clamped to the last
+            bool v;
+            const int r = tile_row(tile_of(min(i, nt - 1)), v);
+            load_seg<kDw>(wbase + static_cast<int64_t>(v ? r : N - 1) * nb * kBytes, dst);
+        };
+        auto process = [&](int i, const uint32_t (&cur)[kDw]) {
+            const uint32_t dp = __builtin_amdgcn_perm(cur[(kDw - 1) / 2], cur[0], 0x07060100u);
+            uint32_t dps[4];
+            {
+                auto rr = __builtin_amdgcn_permlane32_swap(dp, dp, false, false);
+                auto s01 = __builtin_amdgcn_permlane16_swap(rr[0], rr[0], false, false);
+                auto s23 = __builtin_amdgcn_permlane16_swap(rr[1], rr[1], false, false);
+                dps[0] = s01[0];
+                dps[1] = opaque_copy(s01[1]);
+                dps[2] = s23[0];
+                dps[3] = opaque_copy(s23[1]);
+            }
+            half8_t wf[kSeg];
+            weight_operands<FMT>(cur, wf);
+            f32x4_t st = zero;
+#pragma unroll
+            for (int jj = 0; jj < kSeg; ++jj) {
+                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[jj], wf[jj], zero, 0, 0, 0);
+                const uint32_t scw = dps[jj >> 1];
+                if (jj & 1) {
+                    st[0] = fma_hi(scw, d[0], st[0]);
+                    st[1] = fma_hi(scw, d[1], st[1]);
+                    st[2] = fma_hi(scw, d[2], st[2]);
+                    st[3] = fma_hi(scw, d[3], st[3]);
+                } else {
+                    st[0] = fma_lo(scw, d[0], st[0]);
+                    st[1] = fma_lo(scw, d[1], st[1]);
+                    st[2] = fma_lo(scw, d[2], st[2]);
+                    st[3] = fma_lo(scw, d[3], st[3]);
+                }
+            }
+            // result rows 4g..4g+3 are (batch 2g: hi, lo), (batch 2g+1: hi, lo)
+            red[wv][tile_of(i)][lane] = make_float2(fa * (st[0] + st[1]), fb * (st[2] + st[3]));
+        };
+        // ring of NBUF tiles: tile i lives in ring[i % NBUF]; every load is
+        // unconditional (clamped), so the outstanding-load count stays exact
+        uint32_t ring[NBUF][kDw];
+#pragma unroll
+        for (int p = 0; p < PF; ++p) fetch(p, ring[p]);
+        int i0 = 0;
+        for (; i0 + NBUF <= nt; i0 += NBUF) {
+#pragma unroll
+            for (int q = 0; q < NBUF; ++q) {
+                fetch(i0 + q + PF, ring[(q + PF) % NBUF]);
+                process(i0 + q, ring[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NBUF; ++q)
+            if (i0 + q < nt) process(i0 + q, ring[q]);
+    }
+
+    if constexpr (KIND == 1) {
+        if (lane < kMaxB) ssq_w[wv][lane] = sqa;
+    }
+    __syncthreads();
+    // outputs of the workgroup: (live tile i, batch row b, row col) -> thread o
+    // (tid + 256 k); with a SwiGLU output only the gate tiles are walked and
+    // each output also reads its up tile
+    constexpr int kNT = 64 * WV;
+    constexpr int kOut = (TMAX * 16 * kMaxB + kNT - 1) / kNT;  // outputs per thread at most
+    const int nout = (glu ? nu : nt) * 16 * kMaxB;
+    float vg[kOut], vu[kOut];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int o = threadIdx.x + kNT * k;
+        vg[k] = vu[k] = 0.f;
+        if (o < nout) {
+            const int i = o / (16 * kMaxB), b = (o / 16) % kMaxB, r = o % 16;
+            const int ln = r + 16 * (b >> 1);
+            const int sg = tile_of(i), su = glu ? tile_of(i + nu) : 0;
+            float a = 0.f, a2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < WV; ++w) {
+                const float2 q = red[w][sg][ln];
+                a += (b & 1) ? q.y : q.x;
+                if (glu) {
+                    const float2 q2 = red[w][su][ln];
+                    a2 += (b & 1) ? q2.y : q2.x;
+                }
+            }
+            vg[k] = a;
+            vu[k] = a2;
+        }
+    }
+    auto out_index = [&](int o, int &b, int &n, bool &ok) {
+        const int i = o / (16 * kMaxB), r = o % 16;
+        b = (o / 16) % kMaxB;
+        n = 16 * (u0 + i) + r;  // row (or pair) index of the gate / plain tile
+        ok = o < nout && b < B && n < (glu ? P : N);
+    };
+    const int64_t ln = N;
+    if (S == 1) {
+        if constexpr (KIND == 1) {
+            if (threadIdx.x < kMaxB) {
+                const int b = threadIdx.x;
+                float tot = 0.f;
+                for (int w = 0; w < WV; ++w) tot += ssq_w[w][b];
+                inv_s[b] = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            int b, n;
+            bool ok;
+            out_index(threadIdx.x + kNT * k, b, n, ok);
+            if (!ok) continue;
+            const float inv = KIND == 1 ? inv_s[b] : 1.f;
+            if (glu) y[b * static_cast<int64_t>(P) + n] = act_mul<GELU>(vg[k] * inv, vu[k] * inv);
+            else y[b * ln + n] = res ? vg[k] * inv + res[b * ln + n] : vg[k] * inv;
+        }
+        return;
+    }
+    // K split over S workgroups: plain stores of this K range's partials (and,
+    // once per K range, its sums of squares); mv_splitk_reduce_kernel, the
+    // next launch, adds the S partials in split order.
+    {
+        float *pp = part + static_cast<int64_t>(blockIdx.y) * B * ln;
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            int b, n;
+            bool ok;
+            out_index(threadIdx.x + kNT * k, b, n, ok);
+            if (!ok) continue;
+            pp[b * ln + n] = vg[k];
+            if (glu) pp[b * ln + P + n] = vu[k];
+        }
+    }
+    if constexpr (KIND == 1) {
+        if (rx == 0 && threadIdx.x < B) {
+            const int b = threadIdx.x;
+            float tot = 0.f;
+            for (int w = 0; w < WV; ++w) tot += ssq_w[w][b];
+            ssq_part[static_cast<int64_t>(blockIdx.y) * kMaxB + b] = tot;
+        }
+    }
+}
+
+// Adds the S partials of a K-split launch in split order and applies the
+// epilogue: 1/rms (sums of squares of the S K ranges), residual, or the
+// SwiGLU / GeGLU of the gate and up sums.  One thread per output.
+template <int KIND, bool GELU>
+__global__ __launch_bounds__(kWG) void mv_splitk_reduce_kernel(int N, int K, int B, int S, int glu,
+                                                              float eps, const float *__restrict__ part,
+                                                              const float *__restrict__ ssq_part,
+                                                              float *y, const float *res) {
+    const int P = N >> 1;
+    const int outw = glu ? P : N;
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * kWG + threadIdx.x;
+    if (o >= static_cast<int64_t>(B) * outw) return;
+    const int b = static_cast<int>(o / outw), n = static_cast<int>(o % outw);
+    const int gi = b / kMaxB, bl = b % kMaxB;
+    const int Bg = min(kMaxB, B - kMaxB * gi);
+    const int64_t ln = N;
+    const float *pg = part + static_cast<int64_t>(gi) * S * kMaxB * ln + bl * ln + n;
+    const int64_t step = static_cast<int64_t>(Bg) * ln;
+    float inv = 1.f;
+    if constexpr (KIND == 1) {
+        const float *sq = ssq_part + static_cast<int64_t>(gi) * S * kMaxB + bl;
+        float tot = 0.f;
+        for (int q = 0; q < S; ++q) tot += sq[q * kMaxB];
+        inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+    }
+    float sg = 0.f, su = 0.f;
+    for (int q = 0; q < S; ++q) {
+        sg += pg[q * step];
+        if (glu) su += pg[q * step + P];
+    }
+    if (glu) y[static_cast<int64_t>(b) * P + n] = act_mul<GELU>(sg * inv, su * inv);
+    else y[b * ln + n] = res ? sg * inv + res[b * ln + n] : sg * inv;
+}
+
 // ---------------------------------------------------------------- host side
 struct Plan {
     bool tiles;  // the tile kernel, else the shared-step kernel
+    bool kstat;  // the K-stationary streaming kernel (T = row tiles per workgroup)
+    int wv;      // its wavefronts per workgroup
     int T, rg, kc, S, spw;
     int NG, gx;  // batch groups; grid width (row ranges, padded to octets when NG > 1)
     size_t off_ssq, off_part, bytes;
@@ -822,33 +1182,83 @@ struct Plan {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// The tile kernel (each wavefront converts its own step's activations and
-// feeds four row tiles, two for Q8_0) when it yields kMinWGs workgroups;
-// otherwise the shared-step kernel (64 rows per workgroup, the four
+#ifndef Q4_MFMA_KSTAT
+#define Q4_MFMA_KSTAT 1  // 0: the tile / shared-step kernels only
+#endif
+constexpr int kKsTmaxQ4 = 12;  // row tiles per workgroup of the K-stationary kernel
+constexpr int kKsTargetWGs = 768;
+
+// The K-stationary kernel where it measured faster (see the plan below);
+// otherwise the tile kernel (each wavefront converts its own step's
+// activations and feeds four row tiles, two for Q8_0) when it yields kMinWGs
+// workgroups, else the shared-step kernel (64 rows per workgroup, the four
 // wavefronts share one step's operands), whose finer K split fills the chip
 // on small matrices.  K is split over at most kMaxS workgroups, and not at
 // all when the row ranges outnumber the tickets.
-Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt) {
+Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt, bool glu = false) {
     Plan p;
     p.NG = static_cast<int>((B + kMaxB - 1) / kMaxB);
     p.kc = static_cast<int>(K / (32 * kSeg));
-    p.tiles = true;
-    p.T = fmt == 1 ? 2 : 4;
-    p.rg = static_cast<int>((N + 16 * p.T - 1) / (16 * p.T));
     const int rounds = (p.kc + 3) / 4;
-    p.spw = static_cast<int64_t>(p.rg) * p.NG > kCounters ? rounds : (rounds + kMaxS - 1) / kMaxS;
-    p.S = (rounds + p.spw - 1) / p.spw;
-    if (static_cast<int64_t>(p.rg) * p.S * p.NG < kMinWGs) {
-        p.tiles = false;
-        p.T = 4;
-        p.rg = static_cast<int>((N + 63) / 64);
-        const int wgs = (kTargetWGs + p.NG - 1) / p.NG;
-        int want = std::max(1, std::min(std::min(p.kc, kMaxS), (wgs + p.rg - 1) / p.rg));
-        if (static_cast<int64_t>(p.rg) * p.NG > kCounters) want = 1;
-        p.spw = (p.kc + want - 1) / want;
-        p.S = (p.kc + p.spw - 1) / p.spw;
+    // K-stationary kernel, where it measured faster than the tile kernels
+    // (Q4_0 only; 5376 x 21504 and the Qwen3-4B projections at B = 8):
+    //  * K of at most 12 steps: one workgroup of WV = 4 ceil(steps / 4)
+    //    wavefronts covers the whole K (no split), when that still gives
+    //    at least 128 workgroups (16-wavefront workgroups, one per CU,
+    //    measured slower than the tile kernel);
+    //  * longer K: workgroups of 4 wavefronts over K ranges of 4 steps, the
+    //    ranges' partials added in order by a second launch, for matrices of
+    //    at least 512 row tiles.
+    // Elsewhere (few rows, Q8_0 tables) the tile / shared-step kernels below.
+    auto kstat_plan = [&](int wv) {
+        p.wv = wv;
+        p.S = (p.kc + wv - 1) / wv;
+        p.spw = 1;
+        p.tiles = true;
+        const int tmax = kKsTmaxQ4;
+        const int64_t units = glu ? (N / 2 + 15) / 16 : (N + 15) / 16;
+        const int permax = glu ? tmax / 2 : tmax;
+        const int64_t target = std::max<int64_t>(64, static_cast<int64_t>(kKsTargetWGs) * 4 / wv);
+        int per = static_cast<int>((units * p.S * p.NG + target - 1) / target);
+        per = std::max(1, std::min(per, permax));
+        p.rg = static_cast<int>((units + per - 1) / per);
+        p.T = glu ? 2 * per : per;
+        return units;
+    };
+    p.kstat = false;
+    if (Q4_MFMA_KSTAT && fmt == 0) {
+        if (p.kc <= 12) {
+            kstat_plan((p.kc + 3) / 4 * 4);
+            p.kstat = static_cast<int64_t>(p.rg) * p.NG >= 128;
+        } else if (p.kc <= 4 * kMaxS) {
+            p.kstat = kstat_plan(4) >= 512;
+        }
     }
-    p.gx = p.NG == 1 ? p.rg : (p.rg + 7) / 8 * 8 * p.NG;
+    if (!p.kstat) {
+        p.tiles = true;
+        p.T = fmt == 1 ? 2 : 4;
+        p.rg = static_cast<int>((N + 16 * p.T - 1) / (16 * p.T));
+        p.spw = static_cast<int64_t>(p.rg) * p.NG > kCounters ? rounds : (rounds + kMaxS - 1) / kMaxS;
+        p.S = (rounds + p.spw - 1) / p.spw;
+        if (static_cast<int64_t>(p.rg) * p.S * p.NG < kMinWGs) {
+            p.tiles = false;
+            p.T = 4;
+            p.rg = static_cast<int>((N + 63) / 64);
+            const int wgs = (kTargetWGs + p.NG - 1) / p.NG;
+            int want = std::max(1, std::min(std::min(p.kc, kMaxS), (wgs + p.rg - 1) / p.rg));
+            if (static_cast<int64_t>(p.rg) * p.NG > kCounters) want = 1;
+            p.spw = (p.kc + want - 1) / want;
+            p.S = (p.kc + p.spw - 1) / p.spw;
+        }
+    }
+#ifndef Q4_MFMA_XCD_PAD
+#define Q4_MFMA_XCD_PAD 1
+#endif
+    // Workgroups go to the 8 XCDs in turn (linear id mod 8).  With a grid
+    // width that is a multiple of 8, the K splits of a row range (same x,
+    // different y) run on one XCD and share its L2 for the cache lines their
+    // K ranges have in common; the padding workgroups exit at once.
+    p.gx = p.NG == 1 ? ((Q4_MFMA_XCD_PAD && p.S > 1) ? (p.rg + 7) / 8 * 8 : p.rg) : (p.rg + 7) / 8 * 8 * p.NG;
     // per group: S partial rows of its (up to 8) activation rows, and the
     // sums of squares of each row range and split
     const int64_t gB = p.NG == 1 ? B : kMaxB;
@@ -870,6 +1280,29 @@ void launch_act(const uint8_t *W, int N, int K, int B, const float *x, const flo
     float *ssq = reinterpret_cast<float *>(w8 + p.off_ssq);
     float *part = reinterpret_cast<float *>(w8 + p.off_part);
     const dim3 grid(p.gx, p.S);
+    if constexpr (FMT == 0) {  // (the plan takes it for Q4_0 only)
+    if (p.kstat) {
+        constexpr int TM = kKsTmaxQ4;
+        switch (p.wv) {
+#define Q4_KS_CASE(WVN)                                                                                        \
+    case WVN:                                                                                                  \
+        hipLaunchKernelGGL((mv_mfma_kstat_kernel<FMT, KIND, TM, GELU, WVN>), grid, dim3(64 * WVN), 0, s, W, N, K, \
+                           B, x, u, nw, ld, eps, y, res, ctr, ssq, part, p.S, p.T, glu, p.rg, p.NG);            \
+        break;
+            Q4_KS_CASE(4)
+            Q4_KS_CASE(8)
+            Q4_KS_CASE(12)
+            Q4_KS_CASE(16)
+#undef Q4_KS_CASE
+        }
+        if (p.S > 1) {
+            const int64_t outs = static_cast<int64_t>(B) * (glu ? N / 2 : N);
+            hipLaunchKernelGGL((mv_splitk_reduce_kernel<KIND, GELU>), dim3(static_cast<unsigned>((outs + kWG - 1) / kWG)),
+                               dim3(kWG), 0, s, N, K, B, p.S, glu, eps, part, ssq, y, res);
+        }
+        return;
+    }
+    }
     if (!p.tiles) {
         hipLaunchKernelGGL((mv_mfma_step_kernel<FMT, KIND, GELU>), grid, dim3(kWG), 0, s, W, N, K, B, x, u,
                            nw, ld, eps, y, res, ctr, ssq, part, p.S, p.spw, glu, p.rg, p.NG);
@@ -944,7 +1377,7 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
     const size_t ybytes = static_cast<size_t>(B * (out_op != Q4_OUT_PLAIN ? N / 2 : N)) * sizeof(float);
     Q4_CHECK(!overlaps(y, ybytes, x, xbytes) && (!x2 || !overlaps(y, ybytes, x2, xbytes)),
              Q4_ERR_INVALID_ARG, "%s: y must not overlap x or x2", name);
-    const Plan p = make_plan(N, K, B, FMT);
+    const Plan p = make_plan(N, K, B, FMT, out_op != Q4_OUT_PLAIN);
     hipStream_t s = q4::as_stream(stream);
     if (use_static) {
         Q4_CHECK(p.bytes <= kStaticScratchBytes, Q4_ERR_UNSUPPORTED,
@@ -975,7 +1408,10 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
 
 extern "C" size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B) {
     if (N < 1 || K < 256 || K % 256 != 0 || B < 1 || B > kMaxBatch) return 0;
-    return std::max(make_plan(N, K, B, 0).bytes, make_plan(N, K, B, 1).bytes);
+    size_t m = 0;
+    for (int fmt = 0; fmt < 2; ++fmt)
+        for (int glu = 0; glu < 2; ++glu) m = std::max(m, make_plan(N, K, B, fmt, glu != 0).bytes);
+    return m;
 }
 
 extern "C" q4_status q4_0_matvec_batched(const void *W, int64_t N, int64_t K, const float *x,

@@ -186,6 +186,12 @@ BATCHED_CASES = [
     ("q8", 8200, 2048, 20, "rms"), ("q8", 3001, 2560, 32, "plain"), ("q8", 140000, 256, 12, "rms"),
     # GeGLU input on both kernels
     ("q4", 300, 9728, 8, "geglu"), ("q4", 8192, 4096, 16, "geglu"), ("q4", 130, 21504, 3, "geglu"),
+    # the K-stationary kernel: whole K per workgroup (K <= 12 steps, idle
+    # wavefronts past the last step) and K ranges of 4 steps added by the
+    # second launch (13 steps: the last range has one live wavefront), ragged
+    # rows, one and several batch groups, every transform
+    ("q4", 4100, 2560, 8, "rms"), ("q4", 16390, 3328, 8, "rms"), ("q4", 16390, 3328, 12, "swiglu"),
+    ("q4", 8193, 5376, 1, "plain"), ("q4", 12000, 768, 20, "rms_unit"), ("q4", 8200, 5376, 6, "geglu"),
 ]
 
 
@@ -325,6 +331,8 @@ GLU_CASES = [
     ("batched", 2 * 33, 256, 1, "swiglu"),
     ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 16500, 1024, 4, "plain"),
     ("batched", 2 * 9728, 2560, 32, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
+    # K-stationary kernel with K ranges added by the second launch
+    ("batched", 2 * 8200, 5376, 8, "rms"), ("batched", 2 * 8210, 3328, 13, "plain"),
 ]
 
 
@@ -358,6 +366,7 @@ GEGLU_OUT_CASES = [
     ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 77, 2048, 3, "plain"),
     ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
+    ("batched", 2 * 8200, 5376, 3, "plain"),
 ]
 
 
