@@ -85,6 +85,8 @@ def lib():
         L.orc_decode_step.argtypes = [C.POINTER(_Model), C.c_int64, _i32_p, _i32_p, _dbl_p,
                                       _dbl_p]
         L.orc_num_threads.restype = C.c_int
+        L.orc_set_num_threads.argtypes = [C.c_int]
+        L.orc_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -105,6 +107,12 @@ def _u8(a):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later calls from this thread (results do not
+    depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def half_to_double(bits: int) -> float:

@@ -25,6 +25,17 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Thread count of later parallel regions started from the calling thread
+ * (n >= 1; ignored otherwise).  Results do not depend on it: threads only
+ * split independent outputs. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
  * Normal: (1 + f/1024) * 2^(e-15); subnormal (e = 0): f * 2^-24.
  * [GEM] Native Metal diagnostic: block scales are binary16. */

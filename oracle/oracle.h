@@ -126,6 +126,7 @@ void orc_decode_step(const orc_model *m, int64_t pos, const int32_t *tok, int32_
                      double *logits, double *margins);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

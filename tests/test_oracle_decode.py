@@ -29,6 +29,26 @@ def test_decode_deterministic(shape):
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+def test_decode_independent_of_thread_count():
+    """Threads split independent outputs only, so one thread and all threads
+    give the same step bit for bit (the CPU baseline times both)."""
+    shape = wl.TINY_GEMMA4
+    w = wl.model_weights(shape)
+    tok = wl.start_tokens(shape)
+    full = oracle.num_threads()
+    outs = []
+    try:
+        for n in (1, full):
+            oracle.set_num_threads(n)
+            assert oracle.num_threads() == n
+            model, _ = _fresh(shape, w)
+            outs.append(model.step(shape.start_pos, tok, want_logits=True)[:2])
+    finally:
+        oracle.set_num_threads(full)
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
 @pytest.mark.parametrize("shape", [wl.TINY_QWEN3, wl.TINY_GEMMA4], ids=lambda s: s.name)
 def test_decode_batch_rows_independent(shape):
     """A batch of B sequences equals B separate single-sequence steps, bit for bit."""
