@@ -888,16 +888,35 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int64_t seg = kSeg * kBytes;
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
+    // ---- loads first: this wavefront's step of the activations, then the
+    // first PF row tiles.  Loads return in order, so the conversion below
+    // waits for the activations only, while the weights are on their way.  A
+    // wavefront past the last step loads and converts the last step like the
+    // others (same control flow, no branch around loads) and then zeroes its
+    // operands and scales, so it adds exact zeros.
+    const int cs = min(c, kc - 1);
+    constexpr int NBUF = PF + 1;
+    const uint8_t *wbase = W + g * 2 * kBytes + static_cast<int64_t>(cs) * seg;
+    const int ntc = max(nt, 1);
+    auto fetch = [&](int i, uint32_t (&dst)[kDw]) {  // i-th live tile, clamped to the last
+        bool v;
+        const int r = tile_row(tile_of(min(i, ntc - 1)), v);
+        load_seg<kDw>(wbase + static_cast<int64_t>(v ? r : N - 1) * nb * kBytes, dst);
+    };
+    // ring of NBUF tiles: tile i lives in ring[i % NBUF]; every load is
+    // unconditional (clamped), so the outstanding-load count stays exact
+    uint32_t ring[NBUF][kDw];
+
     // ---- this wavefront's step: activations -> exact halves (MFMA operand order)
     half8_t af[kSeg];
     float fa = 0.f, fb = 0.f;
     float sqa = 0.f;  // RMSNorm: lane b < 8 holds batch row b's sum of squares over the step
-    if (active) {
+    {
         const int jl = lane >> 3, q8 = lane & 7;
         const int gl = FMT == 0 ? (q8 & 3) : (q8 >> 1);
         const int el = FMT == 0 ? (q8 >= 4 ? 4 : 0) : 4 * (q8 & 1);
         const float hscale = (FMT == 0 && q8 >= 4) ? 0.0625f : 1.0f;
-        const int64_t kx = static_cast<int64_t>(c) * (32 * kSeg) + 4 * lane;
+        const int64_t kx = static_cast<int64_t>(cs) * (32 * kSeg) + 4 * lane;
         f32x4_t xv[kMaxB], tv[kMaxB];
         f32x4_t gvv = {1.f, 1.f, 1.f, 1.f};
         if constexpr (KIND == 1) {
@@ -909,6 +928,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
             xv[b] = *reinterpret_cast<const f32x4_al16_t *>(x + bo);
             if constexpr (KIND == 2) tv[b] = *reinterpret_cast<const f32x4_al16_t *>(u + bo);
         }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) fetch(p, ring[p]);
         float ssq[kMaxB], mx[kMaxB];
 #pragma unroll
         for (int b = 0; b < kMaxB; ++b) {
@@ -977,6 +998,12 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
         fa = ldexpf(1.0f, -sa);
         fb = ldexpf(1.0f, -sb);
     }
+    if (!active) {  // past the last step: exact zeros (wave-uniform)
+#pragma unroll
+        for (int jj = 0; jj < kSeg; ++jj) af[jj] = half8_t{};
+        fa = fb = 0.f;
+        sqa = 0.f;
+    }
     __syncthreads();  // every wavefront holds its operands: the LDS region is free
 
     // ---- stream the row tiles past the step's operands; each tile's partial
@@ -985,18 +1012,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     // Every wavefront runs the same stream: one past the last step re-reads the
     // last step's weights (L2 hits) with zero operands and scales, so it adds
     // exact zeros to its slots.
-    if (!active) {
-#pragma unroll
-        for (int jj = 0; jj < kSeg; ++jj) af[jj] = half8_t{};
-    }
     if (nt > 0) {  // workgroup-uniform
-        constexpr int NBUF = PF + 1;
-        const uint8_t *wbase = W + g * 2 * kBytes + static_cast<int64_t>(min(c, kc - 1)) * seg;
-        auto fetch = [&](int i, uint32_t (&dst)[kDw]) {  // i-th live tile, clamped to the last
-            bool v;
-            const int r = tile_row(tile_of(min(i, nt - 1)), v);
-            load_seg<kDw>(wbase + static_cast<int64_t>(v ? r : N - 1) * nb * kBytes, dst);
-        };
         auto process = [&](int i, const uint32_t (&cur)[kDw]) {
             const uint32_t dp = __builtin_amdgcn_perm(cur[(kDw - 1) / 2], cur[0], 0x07060100u);
             uint32_t dps[4];
@@ -1031,11 +1047,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
             // result rows 4g..4g+3 are (batch 2g: hi, lo), (batch 2g+1: hi, lo)
             red[wv][tile_of(i)][lane] = make_float2(fa * (st[0] + st[1]), fb * (st[2] + st[3]));
         };
-        // ring of NBUF tiles: tile i lives in ring[i % NBUF]; every load is
-        // unconditional (clamped), so the outstanding-load count stays exact
-        uint32_t ring[NBUF][kDw];
-#pragma unroll
-        for (int p = 0; p < PF; ++p) fetch(p, ring[p]);
         int i0 = 0;
         for (; i0 + NBUF <= nt; i0 += NBUF) {
 #pragma unroll
@@ -1185,6 +1196,12 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 #ifndef Q4_MFMA_KSTAT
 #define Q4_MFMA_KSTAT 1  // 0: the tile / shared-step kernels only
 #endif
+#ifndef Q4_KS_WHOLE_MAX
+#define Q4_KS_WHOLE_MAX 12  // longest K (in steps) one K-stationary workgroup covers whole
+#endif
+#ifndef Q4_KS_MIN_UNITS
+#define Q4_KS_MIN_UNITS 512  // fewest row tiles for the K-split K-stationary kernel
+#endif
 constexpr int kKsTmaxQ4 = 12;  // row tiles per workgroup of the K-stationary kernel
 constexpr int kKsTargetWGs = 768;
 
@@ -1227,11 +1244,11 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt, bool glu = false) {
     };
     p.kstat = false;
     if (Q4_MFMA_KSTAT && fmt == 0) {
-        if (p.kc <= 12) {
+        if (p.kc <= Q4_KS_WHOLE_MAX) {
             kstat_plan((p.kc + 3) / 4 * 4);
             p.kstat = static_cast<int64_t>(p.rg) * p.NG >= 128;
         } else if (p.kc <= 4 * kMaxS) {
-            p.kstat = kstat_plan(4) >= 512;
+            p.kstat = kstat_plan(4) >= Q4_KS_MIN_UNITS;
         }
     }
     if (!p.kstat) {
