@@ -66,6 +66,11 @@ const char *q4dec_version(void);
  *   y         device fp32 [B][N]; may alias residual (in-place residual add)
  *   residual  device fp32 [B][N] or NULL
  * Accumulation is fp32; every weight-activation product is formed exactly.
+ * B > 1 runs the B = 1 vector kernel once per activation row (the rows run
+ * side by side in one launch), so W is read B times, from HBM or from the
+ * last-level cache: the time grows about linearly with B.  For 2 <= B the
+ * matrix-core entry q4_0_matvec_batched reads W once per call and is the
+ * fast path (it needs a workspace, which this call does not take).
  * Errors: Q4_ERR_INVALID_ARG (null / sizes), Q4_ERR_SHAPE (K % 32),
  *         Q4_ERR_ALIGNMENT, Q4_ERR_UNSUPPORTED (B > 8), Q4_ERR_HIP.
  */

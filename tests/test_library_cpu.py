@@ -189,3 +189,30 @@ def test_decode_model_variant_options_on_host():
     assert status(rope_dims=15) == "Q4_ERR_INVALID_ARG"
     assert status(rope_dims=66) == "Q4_ERR_INVALID_ARG"
     assert status(post=2) == "Q4_ERR_ALIGNMENT"
+
+
+def _no_gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu_visible(), reason="needs a machine without a GPU")
+def test_hip_runtime_error_is_reported_as_q4_err_hip():
+    """Valid, aligned arguments pass host validation and reach the HIP
+    runtime, which has no device here: the call returns Q4_ERR_HIP with the
+    runtime's message instead of crashing.  The buffers are host memory that
+    no kernel ever touches (the launch itself fails)."""
+    import numpy as np
+    L = q.lib()
+    W = np.zeros(64 * 8 * 18, np.uint8)
+    x = np.zeros((2, 256), np.float32)
+    y = np.zeros((2, 64), np.float32)
+    st, msg = _status(L.q4_0_matvec, W.ctypes.data, 64, 256, x.ctypes.data, 1, y.ctypes.data,
+                      None, None)
+    assert st == "Q4_ERR_HIP" and "device" in msg.lower()
+    st, msg = _status(L.q4_0_matvec_batched_noalloc, W.ctypes.data, 64, 256, x.ctypes.data, None,
+                      256, 2, 0, 0, None, 0.0, y.ctypes.data, None, None)
+    assert st == "Q4_ERR_HIP" and msg
