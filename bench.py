@@ -210,7 +210,7 @@ def bench_attention_stack(q, torch, batch, windows, reps=4, kv16=False):
                            qn=torch.from_numpy(qn).to(dev), kn=torch.from_numpy(kn).to(dev),
                            kc=kcd, vc=torch.from_numpy(vc).to(dev), kv=kv_layout_of(kcd)))
         del kc, vc
-    ws = torch.empty(q.gqa_decode_attn_workspace(layers[0]["kv"], hq, 0), dtype=torch.uint8,
+    ws = torch.zeros(q.gqa_decode_attn_workspace(layers[0]["kv"], hq, 0), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((batch, hq * hd), dtype=torch.float32, device=dev)
     scale = 1.0 / np.sqrt(hd)
@@ -807,7 +807,7 @@ def counter_run_attention(q, torch, batch):
         layers.append(dict(qkv=torch.from_numpy(np.ascontiguousarray(qkv)).to(dev),
                            qn=torch.from_numpy(qn).to(dev), kn=torch.from_numpy(kn).to(dev),
                            kc=kcd, vc=torch.from_numpy(vc).to(dev), kv=kv_layout_of(kcd)))
-    ws = torch.empty(q.gqa_decode_attn_workspace(layers[0]["kv"], hq, 0), dtype=torch.uint8,
+    ws = torch.zeros(q.gqa_decode_attn_workspace(layers[0]["kv"], hq, 0), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((batch, hq * hd), dtype=torch.float32, device=dev)
     ld = hq * hd + 2 * hkv * hd

@@ -114,9 +114,10 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 template <typename KT>
 __device__ __forceinline__ float4 load4(const KT *p) {
     if constexpr (sizeof(KT) == 4) {
-        return *reinterpret_cast<const float4 *>(p);
+        const f32x4_ev v = ld_kv(reinterpret_cast<const f32x4_ev *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
     } else {
-        const half4_t h = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(p));
+        const half4_t h = __builtin_bit_cast(half4_t, ld_kv(reinterpret_cast<const u32x2_ev *>(p)));
         return make_float4(static_cast<float>(h.x), static_cast<float>(h.y), static_cast<float>(h.z),
                            static_cast<float>(h.w));
     }

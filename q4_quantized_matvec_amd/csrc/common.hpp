@@ -51,6 +51,25 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+// KV-cache rows are read once per step: their loads carry the nontemporal
+// hint (Q4_NT_KV), measured 5-9 % faster attention.  (The weight windows of
+// the matvecs, 4-byte aligned 16-byte loads, measured slower with it and
+// stay plain.)  The pointee types fix the alignment: 16 bytes for fp32
+// rows, 8 for binary16 ones.
+#ifndef Q4_NT_KV
+#define Q4_NT_KV 1
+#endif
+typedef float f32x4_ev __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_ev __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4_ev ld_kv(const f32x4_ev *p) {
+    if constexpr (Q4_NT_KV) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+__device__ __forceinline__ u32x2_ev ld_kv(const u32x2_ev *p) {
+    if constexpr (Q4_NT_KV) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }

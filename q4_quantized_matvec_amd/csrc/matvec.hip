@@ -149,6 +149,15 @@ __host__ __device__ inline int ks_part_blocks(int nb, int ks) { return ((nb + ks
 #ifndef Q4_MV_KS_MIN
 #define Q4_MV_KS_MIN 1    // smallest K split (wavefronts per row) considered
 #endif
+#ifndef Q4_MV_KS_PER_CU
+#define Q4_MV_KS_PER_CU 1 // workgroups per CU when K is split over wavefronts
+#endif
+#ifndef Q4_MV_MIN_ROWS
+#define Q4_MV_MIN_ROWS 7  // rows per wavefront that amortise a workgroup's staging of x
+#endif
+#ifndef Q4_MV_MAX_JX
+#define Q4_MV_MAX_JX 4    // most block columns per lane before K is split over wavefronts
+#endif
 #ifndef Q4_MV_MIN_WAVES
 #define Q4_MV_MIN_WAVES 1 // occupancy hint (waves per SIMD) for the register allocator
 #endif
@@ -655,7 +664,7 @@ void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int
     // so a workgroup should own enough rows to amortise that (measured on
     // the 31B projections: about 7 rows per wavefront with the whole K in
     // one wavefront; one workgroup per CU when K is split over wavefronts).
-    int per_cu = KS > 1 ? 1 : std::max(1, std::min(3, N / (q4::device_cus() * RG * 7)));
+    int per_cu = KS > 1 ? Q4_MV_KS_PER_CU : std::max(1, std::min(3, N / (q4::device_cus() * RG * Q4_MV_MIN_ROWS)));
     if (Q4_MV_WG_PER_CU) per_cu = Q4_MV_WG_PER_CU;
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
     // GeGLU kernels exist for Q4_0 only (the gated projections)
@@ -768,7 +777,10 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
         (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0) {
         for (int cand : {1, 2, 4})
-            if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 256) { ks = cand; break; }
+            if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 64 * (cand == 4 ? 4 : Q4_MV_MAX_JX)) {
+                ks = cand;
+                break;
+            }
     }
     Q4_CHECK(!glu_out || ks == 1, Q4_ERR_UNSUPPORTED,
              "%s: a gated output needs K %% 256 == 0, K <= 8192, 16-byte aligned x", name);

@@ -101,7 +101,7 @@ def lockstep_step(q, oracle, m, weights, dmod, dev, say=print, caches_ids=None):
         check(qkv, r, 2e-4 * t + 1e-6, f"L{l} rmsnorm + qkv matvec", rep)
         raw = np_(qkv).copy()
         kv = kv_layout_of(L["k_cache"])
-        ws = torch.empty(q.gqa_decode_attn_workspace(kv, Hq, ly.window), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(q.gqa_decode_attn_workspace(kv, Hq, ly.window), dtype=torch.uint8, device=dev)
         att = torch.empty((B, nq), dtype=torch.float32, device=dev)
         # the step fuses QK-norm, RoPE and the KV append into the attention call
         q.gqa_decode_attn_rope(qkv, nqkv, Hq, L["q_norm"], L["k_norm"], kv, pos_d[0:1], ly.rope_theta,

@@ -149,7 +149,7 @@ def test_attention_stack_qwen3_1p7b(dev, batch, layers):
         q.qk_norm_rope(qd, hq * hd, kd, vd, hkv * hd, torch.from_numpy(qn).to(dev),
                        torch.from_numpy(kn).to(dev), hq, kv, pos_d[0:1], w.rope_theta, w.eps,
                        False, kcd, vcd)
-        ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
         out = torch.empty((batch, hq * hd), dtype=torch.float32, device=dev)
         q.gqa_decode_attn(qd, hq * hd, hq, kcd, vcd, kv, pos_d[1:2], 0, 1.0 / np.sqrt(hd), out,
                           hq * hd, ws)

@@ -165,7 +165,7 @@ def test_gqa_decode_attn_parity(dev, B, hq, hkv, hd, cap, n, window):
     scale = 1.0 / math.sqrt(hd) if window == 0 else 1.0
     kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
     kv = kv_layout_of(kc_d)
-    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
     out = torch.empty((B, hq * hd), dtype=torch.float32, device=dev)
     n_d = torch.tensor([n], dtype=torch.int64, device=dev)
     q.gqa_decode_attn(torch.from_numpy(qv).to(dev), hq * hd, hq, kc_d, vc_d, kv, n_d, window, scale,
@@ -189,7 +189,7 @@ def test_gqa_decode_attn_deterministic(dev, B, cap):
     kc = torch.randn(B, hkv, cap, hd, device=dev)
     vc = torch.randn(B, hkv, cap, hd, device=dev)
     kv = kv_layout_of(kc)
-    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, 0), dtype=torch.uint8, device=dev)
     n_d = torch.tensor([cap - 1], dtype=torch.int64, device=dev)
     outs = []
     for _ in range(3):
@@ -198,6 +198,44 @@ def test_gqa_decode_attn_deterministic(dev, B, cap):
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_gqa_decode_attn_shared_workspace_mixed_shapes(dev):
+    """One workspace shared by calls of different shapes, interleaved, as a
+    decode step's layers share it: every call of a shape gives the same bits
+    as its first call and as a call on a fresh workspace."""
+    shapes = {"A": (1, 4, 2, 128, 512, 500), "B": (2, 16, 8, 128, 4096, 4000),
+              "C": (1, 32, 4, 512, 1024, 1000)}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(207)
+    ins = {}
+    for key, (B, hq, hkv, hd, cap, n) in shapes.items():
+        qv = torch.randn((B, hq * hd), device=dev, generator=gen)
+        kc = torch.randn((B, hkv, cap, hd), device=dev, generator=gen)
+        vc = torch.randn((B, hkv, cap, hd), device=dev, generator=gen)
+        ins[key] = (qv, kc, vc, kv_layout_of(kc), torch.tensor([n], dtype=torch.int64, device=dev),
+                    hq, hd)
+    size = max(q.gqa_decode_attn_workspace(v[3], v[5], 0) for v in ins.values())
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+
+    def run(key, wsp):
+        qv, kc, vc, kv, n_d, hq, hd = ins[key]
+        out = torch.empty((qv.shape[0], hq * hd), device=dev)
+        q.gqa_decode_attn(qv, hq * hd, hq, kc, vc, kv, n_d, 0, 1.0 / math.sqrt(hd), out, hq * hd, wsp)
+        return out
+
+    first = {}
+    for key in "ABCACBA":
+        out = run(key, ws)
+        if key in first:
+            assert torch.equal(out, first[key]), f"shape {key} changed on a shared workspace"
+        else:
+            first[key] = out
+    for key in "ABC":
+        fresh = torch.zeros(q.gqa_decode_attn_workspace(ins[key][3], ins[key][5], 0), dtype=torch.uint8,
+                            device=dev)
+        assert torch.equal(run(key, fresh), first[key])
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "two_pass"])
@@ -255,7 +293,7 @@ def test_gqa_decode_attn_rope_parity(dev, B, hq, hkv, hd, cap, pos, window, v_fr
     scale = 1.0 / math.sqrt(hd) if not v_from_k else 1.0
     kc_d, vc_d = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
     kv = kv_layout_of(kc_d)
-    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
     out = torch.empty((B, nq), dtype=torch.float32, device=dev)
     pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
     q.gqa_decode_attn_rope(torch.from_numpy(rows).to(dev), ld, hq, torch.from_numpy(qn).to(dev),
@@ -341,7 +379,7 @@ def test_gqa_decode_attn_f16_cache_parity(dev, B, hq, hkv, hd, cap, n, window):
     kc_d, vc_d = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
     kv = kv_layout_of(kc_d)
     assert kv.dtype == 1
-    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
     out = torch.empty((B, hq * hd), dtype=torch.float32, device=dev)
     n_d = torch.tensor([n], dtype=torch.int64, device=dev)
     q.gqa_decode_attn(torch.from_numpy(qv).to(dev), hq * hd, hq, kc_d, vc_d, kv, n_d, window, scale,
@@ -377,7 +415,7 @@ def test_gqa_decode_attn_rope_f16_cache(dev, B, hq, hkv, hd, cap, pos, window, v
     scale = 1.0 / math.sqrt(hd) if not v_from_k else 1.0
     kc_d, vc_d = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
     kv = kv_layout_of(kc_d)
-    ws = torch.empty(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(q.gqa_decode_attn_workspace(kv, hq, window), dtype=torch.uint8, device=dev)
     out = torch.empty((B, nq), dtype=torch.float32, device=dev)
     pos_d = torch.tensor([pos], dtype=torch.int64, device=dev)
     q.gqa_decode_attn_rope(torch.from_numpy(rows).to(dev), ld, hq, torch.from_numpy(qn).to(dev),
