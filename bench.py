@@ -608,8 +608,8 @@ def main():
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the decode workloads (for profiler runs)")
     ap.add_argument("--counter-run", metavar="LEG",
-                    help="for a --pmc pass: run one leg (a decode workload, or attn_B1 / attn_B8) "
-                         "between two marker copies and exit")
+                    help="for a --pmc pass: run one leg (a decode workload, or attn_B1 / attn_B8, "
+                         "between two marker copies; or matvec_B1_B8) and exit")
     ap.add_argument("--pmc-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="store the headline matvec's counter bytes in profiles/traffic.json")
     ap.add_argument("--pmc-traffic-leg", nargs=3, metavar=("LEG", "FETCH_CSV", "WRITE_CSV"),
@@ -650,7 +650,9 @@ def main():
 
     if args.counter_run:
         leg = args.counter_run
-        if leg.startswith("attn_B"):
+        if leg == "matvec_B1_B8":
+            res = counter_run_matvec(q, torch)
+        elif leg.startswith("attn_B"):
             batch = int(leg[len("attn_B"):])
             res = counter_run_attention(q, torch, batch)
         else:
@@ -786,6 +788,27 @@ def main():
 
 
 COUNTER_UNITS = 4
+
+
+def counter_run_matvec(q, torch, launches=60, copies=12):
+    """The headline shape at B = 1 (q4_0_matvec, vector kernel) then at B = 8
+    (q4_0_matvec_batched, matrix cores), `launches` calls each over `copies`
+    weight copies, for per-kernel counter passes."""
+    from synth import workloads as wl
+    w = wl.MATVEC_5376x21504
+    dev = torch.device("cuda:0")
+    Ws = weight_copies(torch, w, copies, dev)
+    x1, y1 = activations(torch, w, 1, dev)
+    launch = matvec_launcher(q, torch, Ws, x1, y1)
+    for i in range(launches):
+        launch(i)
+    torch.cuda.synchronize()
+    x8, y8 = activations(torch, w, 8, dev)
+    launch = batched_launcher(q, torch, Ws, x8, y8, w.k, 8)
+    for i in range(launches):
+        launch(i)
+    torch.cuda.synchronize()
+    return {"launches": launches, "copies": copies}
 
 
 def counter_run_attention(q, torch, batch):

@@ -137,6 +137,9 @@ __host__ __device__ inline int ks_part_blocks(int nb, int ks) { return ((nb + ks
 #ifndef Q4_MV_PREFETCH
 #define Q4_MV_PREFETCH 2  // rows of loads in flight ahead of the row being reduced
 #endif
+#ifndef Q4_MV_PREFETCH_JX1
+#define Q4_MV_PREFETCH_JX1 4  // K <= 2048 (one block column per lane): 5.45 -> 4.98 us at 2048 x 6144
+#endif
 #ifndef Q4_MV_PREFETCH_Q8
 #define Q4_MV_PREFETCH_Q8 1
 #endif
@@ -154,6 +157,9 @@ __host__ __device__ inline int ks_part_blocks(int nb, int ks) { return ((nb + ks
 #endif
 #ifndef Q4_MV_MIN_ROWS
 #define Q4_MV_MIN_ROWS 7  // rows per wavefront that amortise a workgroup's staging of x
+#endif
+#ifndef Q4_MV_MIN_ROWS_JX1
+#define Q4_MV_MIN_ROWS_JX1 7
 #endif
 #ifndef Q4_MV_MAX_JX
 #define Q4_MV_MAX_JX 4    // most block columns per lane before K is split over wavefronts
@@ -657,14 +663,15 @@ __global__ __launch_bounds__(kWG) void q8_gather_kernel(const uint8_t *__restric
 template <int FMT, int JX, int KS>
 void launch_b1(const uint8_t *W, const float *x, float *y, const float *res, int N, int K,
                int B, const InOp &op, hipStream_t s) {
-    constexpr int PF = FMT == 0 ? Q4_MV_PREFETCH : Q4_MV_PREFETCH_Q8;
+    constexpr int PF = FMT == 0 ? (JX == 1 ? Q4_MV_PREFETCH_JX1 : Q4_MV_PREFETCH) : Q4_MV_PREFETCH_Q8;
     constexpr int RG = 4 / KS;
     const int want = (N + RG - 1) / RG;
     // Workgroups per CU: every workgroup stages the whole activation row once,
     // so a workgroup should own enough rows to amortise that (measured on
     // the 31B projections: about 7 rows per wavefront with the whole K in
     // one wavefront; one workgroup per CU when K is split over wavefronts).
-    int per_cu = KS > 1 ? Q4_MV_KS_PER_CU : std::max(1, std::min(3, N / (q4::device_cus() * RG * Q4_MV_MIN_ROWS)));
+    int per_cu = KS > 1 ? Q4_MV_KS_PER_CU
+                        : std::max(1, std::min(3, N / (q4::device_cus() * RG * (JX == 1 ? Q4_MV_MIN_ROWS_JX1 : Q4_MV_MIN_ROWS))));
     if (Q4_MV_WG_PER_CU) per_cu = Q4_MV_WG_PER_CU;
     const int nwg = std::max(1, std::min(want, per_cu * q4::device_cus()));
     // GeGLU kernels exist for Q4_0 only (the gated projections)

@@ -34,6 +34,8 @@ CASES_Q4 = [
     (67, 256, 1), (1, 256, 1), (5, 2048, 1), (1000, 2048, 1), (777, 5376, 1), (300, 8192, 1),
     (200, 16384, 1), (130, 21504, 1), (257, 2560, 1), (99, 9728, 1),
     (67, 32, 1), (67, 288, 3), (33, 256, 8), (100, 2560, 8), (64, 5376, 2), (50, 9728, 4),
+    # B > 1 on the vector kernel (one weight pass per batch row) at every K split
+    (300, 8192, 3), (129, 16384, 2), (1000, 2048, 5), (77, 5376, 7), (200, 21504, 6), (90, 256, 2),
 ]
 
 
@@ -136,6 +138,9 @@ FUSED_CASES = [
     ("q8", 1000, 5376, 1, "rms"), ("q8", 300, 2560, 8, "rms"), ("q4", 77, 2048, 1, "rms_unit"),
     # GeGLU input (tanh-form GELU gate): LDS-staged, split-K, B > 1
     ("q4", 257, 5376, 1, "geglu"), ("q4", 200, 21504, 1, "geglu"), ("q4", 64, 9728, 8, "geglu"),
+    # B > 1 on the vector kernel with each input transform
+    ("q4", 300, 5376, 3, "rms"), ("q4", 129, 8192, 2, "swiglu"), ("q4", 500, 2560, 4, "geglu"),
+    ("q8", 200, 5376, 6, "rms_unit"),
 ]
 
 
