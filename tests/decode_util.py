@@ -155,3 +155,161 @@ def lockstep_step(q, oracle, m, weights, dmod, dev, say=print, caches_ids=None):
     lg = np_(logits)
     assert nxt.cpu().numpy().tolist() == [oracle.argmax(lg[b])[0] for b in range(B)]
     return tok, nxt, logits, rep
+
+
+def _gated_ref(oracle, r, t, F, act):
+    """Reference and bound of a gated output (gate rows, then up rows of r)."""
+    g, u = r[:, :F], r[:, F:]
+    tg, tu = 2e-4 * t[:, :F] + 1e-6, 2e-4 * t[:, F:] + 1e-6
+    fn = oracle.geglu if act == "gelu_tanh" else oracle.swiglu
+    ref = np.stack([fn(g[b], u[b]) for b in range(r.shape[0])])
+    tol = 1.13 * tg * np.abs(u) + np.abs(np.stack([fn(g[b], np.ones_like(g[b])) for b in range(r.shape[0])])) \
+        * tu + 2e-4 * np.abs(ref) + 1e-6
+    return ref, tol
+
+
+def lockstep_step_variants(q, oracle, m, weights, dmod, dev, say=print):
+    """As lockstep_step for a model with the Gemma-4 block variants at B = 1
+    (where the library's step takes the vector kernels): the scaled embedding
+    gather; sandwich post-norms, each joining the residual stream inside the
+    next pre-normed projection (q4_0_matvec_post_norm, the stream alternating
+    between two buffers) and the last one by rmsnorm_add; p-RoPE layers
+    prepared by qk_norm_rope_partial and attended by gqa_decode_attn; GeGLU
+    or SwiGLU output of gate|up; the soft-capped logits.  Every call is
+    checked against the oracle fed the GPU's own inputs.  Returns (tokens,
+    next tokens, logits, worst err/tol per op)."""
+    import torch
+    from q4_quantized_matvec_amd._lib import kv_layout_of
+
+    B, D, Hq, F, eps = m.batch, m.d_model, m.n_q_heads, m.ffn, m.eps
+    assert B == 1 and D % 256 == 0 and D <= 8192, "the vector-kernel form of the step"
+    pos = m.start_pos
+    tok = torch.from_numpy(wl.start_tokens(m)).to(dev)
+    rep = {}
+    np_ = lambda t: t.detach().cpu().numpy().astype(np.float64)
+    gout = q.OUT_GEGLU if m.ffn_act == "gelu_tanh" else q.OUT_SWIGLU
+    pos_d = torch.tensor([pos, pos + 1], dtype=torch.int64, device=dev)
+
+    scale = float(np.float32(m.embed_scale)) if m.embed_scale and m.embed_scale != 1.0 else None
+    hc = q.q8_0_gather(dmod["embed"], tok, D, scale=scale)
+    ref = oracle.q8_0_gather(weights["embed"], m.vocab, D, tok.cpu().numpy()) * (scale or 1.0)
+    # one fp32 rounding of the exact (d q) s: at most half an ulp of the result
+    check(hc, ref, 2.0 ** -24 * (1.0 + 2.0 ** -20) * np.abs(ref) + 1e-30, "gather (scaled)", rep)
+    ha = torch.empty_like(hc)
+    tmp = torch.empty_like(hc)
+    pend = None  # (device gain, host gain) of a post-norm waiting in tmp
+
+    def normed_proj(Wd, Wh, N, gd, gh, out_op, what):
+        nonlocal hc, ha, pend
+        if pend is not None:
+            pwd, pwh = pend
+            y = q.q4_0_matvec_post_norm(Wd, hc, tmp, D, B, D, pwd, gd, eps, ha, n=N, out_op=out_op)
+            normed = oracle.rmsnorm(np_(tmp), pwh, eps)
+            ref_h = np_(hc) + normed
+            check(ha, ref_h, 2e-4 * np.abs(normed) + 2.0 ** -23 * np.abs(ref_h) + 1e-6,
+                  f"{what}: post-norm joins the stream", rep)
+            xin = oracle.rmsnorm(np_(ha), gh, eps)
+            hc, ha = ha, hc
+            pend = None
+        else:
+            y = q.q4_0_matvec_fused(Wd, hc, D, B, D, q.IN_RMSNORM, norm_w=gd, eps=eps, n=N, out_op=out_op)
+            xin = oracle.rmsnorm(np_(hc), gh, eps)
+        r, t = oracle.q4_0_matvec(Wh, N, D, xin)
+        if out_op == q.OUT_PLAIN:
+            check(y, r, 2e-4 * t + 1e-6, f"{what}: rmsnorm + matvec", rep)
+        else:
+            gref, gtol = _gated_ref(oracle, r, t, N // 2, m.ffn_act)
+            check(y, gref, gtol, f"{what}: rmsnorm + matvec + gated output", rep)
+        return y
+
+    for l, ly in enumerate(m.layers):
+        L, W = dmod["layers"][l], weights["layers"][l]
+        hd, hkv = ly.head_dim, ly.n_kv_heads
+        nq, nk, nv = wl.layer_rows(m, ly)
+        nqkv = nq + nk + nv
+        say(f"  lockstep layer {l}: hd {hd}, {hkv} kv heads, window {ly.window}, cap {ly.cap}, "
+            f"rotated dims {ly.rope_dims or hd}")
+        qkv = normed_proj(L["wqkv"], W["wqkv"], nqkv, L["attn_norm"], W["attn_norm"], q.OUT_PLAIN, f"L{l} qkv")
+        raw = np_(qkv).copy()
+        kv = kv_layout_of(L["k_cache"])
+        ws = torch.zeros(q.gqa_decode_attn_workspace(kv, Hq, ly.window), dtype=torch.uint8, device=dev)
+        att = torch.empty((B, nq), dtype=torch.float32, device=dev)
+        rot = ly.rope_dims if ly.rope_dims else hd
+        partial = rot != hd
+        if partial:
+            q.qk_norm_rope(qkv, nqkv, qkv[:, nq:], None if ly.v_from_k else qkv[:, nq + nk:], nqkv,
+                           L["q_norm"], L["k_norm"], Hq, kv, pos_d[0:1], ly.rope_theta, eps, ly.v_from_k,
+                           L["k_cache"], L["v_cache"], rot_dims=rot)
+            q.gqa_decode_attn(qkv, nqkv, Hq, L["k_cache"], L["v_cache"], kv, pos_d[1:2], ly.window,
+                              ly.attn_scale, att, nq, ws)
+        else:
+            q.gqa_decode_attn_rope(qkv, nqkv, Hq, L["q_norm"], L["k_norm"], kv, pos_d[0:1], ly.rope_theta,
+                                   eps, ly.v_from_k, L["k_cache"], L["v_cache"], ly.window,
+                                   ly.attn_scale, att, nq, ws)
+        slot = pos % ly.cap
+        n = pos + 1
+        lo = max(0, n - ly.window) if ly.window else 0
+        vis = np.arange(lo, n)
+        kc_t, vc_t = L["k_cache"], L["v_cache"]
+        for b in range(B):
+            kr = raw[b, nq:nq + nk].reshape(hkv, hd)
+            kref = oracle.rope_neox(oracle.rmsnorm(kr, W["k_norm"], eps), pos, ly.rope_theta,
+                                    rot if partial else 0)
+            check(np_(kc_t[b, :, slot]), kref, 2e-4 * np.abs(kref) + 2e-5, f"L{l} appended key", rep)
+            vref = (oracle.rmsnorm(kr, None, eps) if ly.v_from_k
+                    else raw[b, nq + nk:].reshape(hkv, hd))
+            check(np_(vc_t[b, :, slot]), vref, 2e-4 * np.abs(vref) + 1e-6, f"L{l} appended value", rep)
+            qh = oracle.rope_neox(oracle.rmsnorm(raw[b, :nq].reshape(Hq, hd), W["q_norm"], eps),
+                                  pos, ly.rope_theta, rot if partial else 0)
+            if partial:  # the prepared query is written back in place; attention reads it
+                check(np_(qkv[b, :nq]).reshape(Hq, hd), qh, 2e-4 * np.abs(qh) + 2e-5,
+                      f"L{l} p-RoPE query", rep)
+                qh = np_(qkv[b, :nq]).reshape(Hq, hd)
+            sl = torch.from_numpy(vis % ly.cap).to(dev)
+            keys = np.zeros((n, hkv, hd))
+            vals = np.zeros((n, hkv, hd))
+            keys[lo:] = np_(kc_t[b][:, sl].permute(1, 0, 2))
+            vals[lo:] = np_(vc_t[b][:, sl].permute(1, 0, 2))
+            o, bound = oracle.gqa_attention(qh, keys, vals, ly.window, ly.attn_scale)
+            check(att[b], o, 2e-4 * bound + 1e-6, f"L{l} attention", rep)
+        # O projection: with a post-norm its output waits in tmp
+        if W.get("post_attn_norm") is not None:
+            q.q4_0_matvec_fused(L["wo"], att, nq, B, nq, q.IN_PLAIN, y=tmp)
+            r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att))
+            check(tmp, r, 2e-4 * t + 1e-6, f"L{l} o-proj", rep)
+            pend = (L["post_attn_norm"], W["post_attn_norm"])
+        else:
+            xo = np_(hc)
+            q.q4_0_matvec_fused(L["wo"], att, nq, B, nq, q.IN_PLAIN, y=hc, residual=hc)
+            r, t = oracle.q4_0_matvec(W["wo"], D, nq, np_(att), res=xo)
+            check(hc, r, 2e-4 * t + 1e-6, f"L{l} o-proj + residual", rep)
+        h = normed_proj(L["wgu"], W["wgu"], 2 * F, L["ffn_norm"], W["ffn_norm"], gout, f"L{l} gate|up")
+        if W.get("post_ffn_norm") is not None:
+            q.q4_0_matvec_fused(L["wd"], h, F, B, F, q.IN_PLAIN, y=tmp)
+            r, t = oracle.q4_0_matvec(W["wd"], D, F, np_(h))
+            check(tmp, r, 2e-4 * t + 1e-6, f"L{l} down", rep)
+            pend = (L["post_ffn_norm"], W["post_ffn_norm"])
+        else:
+            xo = np_(hc)
+            q.q4_0_matvec_fused(L["wd"], h, F, B, F, q.IN_PLAIN, y=hc, residual=hc)
+            r, t = oracle.q4_0_matvec(W["wd"], D, F, np_(h), res=xo)
+            check(hc, r, 2e-4 * t + 1e-6, f"L{l} down + residual", rep)
+    if pend is not None:
+        x0 = np_(hc)
+        q.rmsnorm_add(tmp, pend[0], eps, hc)
+        normed = oracle.rmsnorm(np_(tmp), pend[1], eps)
+        ref_h = x0 + normed
+        check(hc, ref_h, 2e-4 * np.abs(normed) + 2.0 ** -23 * np.abs(ref_h) + 1e-6,
+              "last post-norm (rmsnorm_add)", rep)
+    logits = q.q8_0_matvec_fused(dmod["embed"], hc, D, B, D, q.IN_RMSNORM, norm_w=dmod["final_norm"], eps=eps)
+    r, t = oracle.q8_0_matvec(weights["embed"], m.vocab, D, oracle.rmsnorm(np_(hc), weights["final_norm"], eps))
+    check(logits, r, 2e-4 * t + 1e-6, "final rmsnorm + logits", rep)
+    if m.logit_softcap:
+        before = np_(logits)
+        q.softcap(logits, m.logit_softcap)
+        check(logits, oracle.softcap(before, m.logit_softcap), np.full(before.shape, 2e-6 * m.logit_softcap),
+              "soft cap", rep)
+    nxt = q.argmax_rows(logits)
+    lg = np_(logits)
+    assert nxt.cpu().numpy().tolist() == [oracle.argmax(lg[b])[0] for b in range(B)]
+    return tok, nxt, logits, rep

@@ -14,7 +14,8 @@ import oracle
 import q4_quantized_matvec_amd as q
 from synth import workloads as wl
 
-from decode_util import (gpu_model, lockstep_step, prefilled_caches, run_gpu, run_oracle,
+from decode_util import (gpu_model, lockstep_step, lockstep_step_variants, prefilled_caches, run_gpu,
+                         run_oracle,
                          upload_model)
 
 pytestmark = pytest.mark.gpu
@@ -107,6 +108,30 @@ def test_decode_lockstep_per_op(dev, shape):
     tok, nxt, logits, _ = lockstep_step(q, oracle, m, weights, dmod, dev, say=_say)
 
     # the library's own step runs the same kernels in the same order: bit-identical
+    fresh = upload_model(m, weights, dev)
+    dm = gpu_model(q, m, fresh)
+    dm.set_position(m.start_pos)
+    nxt2 = torch.empty_like(tok)
+    lg2 = torch.empty((m.batch, m.vocab), dtype=torch.float32, device=dev)
+    dm.step(tok, nxt2, lg2, eager=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lg2, logits) and torch.equal(nxt2, nxt)
+    for a, b2 in zip(dmod["layers"], fresh["layers"]):
+        assert torch.equal(a["k_cache"], b2["k_cache"]) and torch.equal(a["v_cache"], b2["v_cache"])
+    dm.close()
+
+
+def test_decode_lockstep_per_op_variants(dev):
+    """The Gemma-4 block variants at B = 1 (scaled gather, sandwich post-norms
+    fused into the next projection, p-RoPE layers, GeGLU, soft cap): every op
+    against the oracle fed the GPU's inputs, and the composition equal to
+    decode_step_eager bit for bit."""
+    m = wl.TINY_GEMMA4_EXACT_B1
+    _say(f"lockstep {m.name}")
+    weights = wl.model_weights(m)
+    dmod = upload_model(m, weights, dev)
+    tok, nxt, logits, rep = lockstep_step_variants(q, oracle, m, weights, dmod, dev, say=_say)
+    assert any("post-norm" in k for k in rep) and any("p-RoPE" in k for k in rep)
     fresh = upload_model(m, weights, dev)
     dm = gpu_model(q, m, fresh)
     dm.set_position(m.start_pos)

@@ -33,7 +33,8 @@ import q4_quantized_matvec_amd as q
 from q4_quantized_matvec_amd._lib import kv_layout_of
 from synth import workloads as wl
 
-from decode_util import gpu_model, lockstep_step, prefilled_caches, run_gpu, upload_model
+from decode_util import (gpu_model, lockstep_step, lockstep_step_variants, prefilled_caches, run_gpu,
+                         upload_model)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,6 +117,44 @@ def test_lockstep_fullsize(dev, shape, ids):
     for a, b2 in zip(dmod["layers"], fresh["layers"]):
         assert torch.equal(a["k_cache"], b2["k_cache"]) and torch.equal(a["v_cache"], b2["v_cache"])
     # and the captured graph of that step gives the same bits
+    dm.set_position(m.start_pos)
+    for a, b2 in zip(dmod["layers"], fresh["layers"]):
+        b2["k_cache"].copy_(a["k_cache"])
+        b2["v_cache"].copy_(a["v_cache"])
+    lg3 = torch.empty_like(lg2)
+    dm.step(tok, nxt2, lg3)
+    torch.cuda.synchronize()
+    assert torch.equal(lg3, logits)
+    dm.close()
+    del dmod, fresh
+    torch.cuda.empty_cache()
+
+
+def test_lockstep_fullsize_variants(dev):
+    """The 31B shape with the Gemma-4 block variants, layers 0 (sliding window,
+    1,024-slot ring at position 8,192) and 5 (full attention, p-RoPE over 128
+    of 512 dims, V from K): the scaled gather, the sandwich post-norms fused
+    into the next projection (K = 5,376 vector kernel, GeGLU output over
+    2 x 21,504 rows), the K-split down projection without a residual, the
+    last post-norm, the soft-capped 262,144 logits; each op against the
+    oracle fed the GPU's inputs, then the library's own eager step and its
+    graph on a fresh copy give the same bits."""
+    shape, ids = wl.GEMMA4_31B_EXACT, (0, 5)
+    m = wl.submodel(shape, ids)
+    _say(f"lockstep {m.name}: B={m.batch} at position {m.start_pos}, generating weights")
+    weights = wl.model_weights(shape, ids)
+    caches = prefilled_caches(shape, layer_ids=ids)
+    dmod = upload_model(m, weights, dev, caches=caches)
+    tok, nxt, logits, rep = lockstep_step_variants(q, oracle, m, weights, dmod, dev, say=_say)
+    _say("  worst err/tol per op: " + ", ".join(f"{k} {v:.2e}" for k, v in rep.items()))
+    fresh = upload_model(m, weights, dev, caches=caches)
+    dm = gpu_model(q, m, fresh)
+    dm.set_position(m.start_pos)
+    nxt2 = torch.empty_like(tok)
+    lg2 = torch.empty((m.batch, m.vocab), dtype=torch.float32, device=dev)
+    dm.step(tok, nxt2, lg2, eager=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lg2, logits) and torch.equal(nxt2, nxt)
     dm.set_position(m.start_pos)
     for a, b2 in zip(dmod["layers"], fresh["layers"]):
         b2["k_cache"].copy_(a["k_cache"])
