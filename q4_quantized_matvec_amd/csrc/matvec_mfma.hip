@@ -1203,7 +1203,10 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 #define Q4_KS_MIN_UNITS 512  // fewest row tiles for the K-split K-stationary kernel
 #endif
 constexpr int kKsTmaxQ4 = 12;  // row tiles per workgroup of the K-stationary kernel
-constexpr int kKsTargetWGs = 768;
+#ifndef Q4_KS_TARGET_WGS
+#define Q4_KS_TARGET_WGS 768
+#endif
+constexpr int kKsTargetWGs = Q4_KS_TARGET_WGS;
 
 // The K-stationary kernel where it measured faster (see the plan below);
 // otherwise the tile kernel (each wavefront converts its own step's

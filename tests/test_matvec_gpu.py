@@ -197,6 +197,10 @@ BATCHED_CASES = [
     # rows, one and several batch groups, every transform
     ("q4", 4100, 2560, 8, "rms"), ("q4", 16390, 3328, 8, "rms"), ("q4", 16390, 3328, 12, "swiglu"),
     ("q4", 8193, 5376, 1, "plain"), ("q4", 12000, 768, 20, "rms_unit"), ("q4", 8200, 5376, 6, "geglu"),
+    # ... with 2 to 4 batch groups: whole K with 12, 8 and 4 wavefronts, K
+    # ranges added by the second launch, a ragged last group, every transform
+    ("q4", 6144, 2560, 16, "rms"), ("q4", 5000, 2048, 29, "plain"), ("q4", 4100, 1024, 32, "rms"),
+    ("q4", 8200, 5376, 10, "plain"), ("q4", 8200, 3328, 16, "geglu"), ("q4", 16390, 3328, 27, "swiglu"),
 ]
 
 
@@ -338,6 +342,7 @@ GLU_CASES = [
     ("batched", 2 * 9728, 2560, 32, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
     # K-stationary kernel with K ranges added by the second launch
     ("batched", 2 * 8200, 5376, 8, "rms"), ("batched", 2 * 8210, 3328, 13, "plain"),
+    ("batched", 2 * 8200, 3328, 32, "rms"), ("batched", 2 * 4100, 2048, 16, "plain"),
 ]
 
 
@@ -371,7 +376,7 @@ GEGLU_OUT_CASES = [
     ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 77, 2048, 3, "plain"),
     ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
-    ("batched", 2 * 8200, 5376, 3, "plain"),
+    ("batched", 2 * 8200, 5376, 3, "plain"), ("batched", 2 * 4100, 1024, 32, "rms"),
 ]
 
 
