@@ -9,9 +9,10 @@ step streams its weights from HBM.  Inputs are resident in HBM before timing.
 Timing method (every GPU line): untimed dispatches until both `--warmup`
 dispatches and at least 50 ms of GPU work have run (the part's clocks take
 about 15 ms of sustained memory traffic to settle), then `--windows` timed
-windows of exactly `--steps` back-to-back dispatches each, HIP events on the
-stream the kernels run on; a line reports the median window (per dispatch)
-and the coefficient of variation over the windows.
+windows of exactly `--steps` back-to-back dispatches each, timing-only HIP
+events (no system-scope cache release at a window boundary) on the stream the
+kernels run on; a line reports the median window (per dispatch) and the
+coefficient of variation over the windows.
 
 Prints one JSON line (rank 0, N=1 only):
   value        = algorithmic bytes per dispatch / median dispatch time (GB/s)
@@ -57,6 +58,72 @@ def summarize(per_dispatch_ms):
             "windows": len(per_dispatch_ms)}
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+
+class TimingEvents:
+    """Timing-only HIP events on the launch stream.  A default event record
+    ends with a system-scope release (the caches are written back and
+    invalidated), which costs the work after it about a microsecond per
+    dispatch when windows are as short as 20 dispatches; these events are
+    created with hipEventDisableSystemFence, so a window boundary adds only
+    the timestamp.  They are read after a full device synchronisation.  The
+    HIP runtime is the one torch has loaded (the library links the same one)."""
+
+    _rt = None
+
+    @classmethod
+    def runtime(cls):
+        import ctypes
+        if cls._rt is None:
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    p = line.split()[-1]
+                    if "libamdhip64" in p and p.startswith("/"):
+                        path = p
+                        break
+            rt = ctypes.CDLL(path or "libamdhip64.so.7")
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self, torch, n):
+        import ctypes
+        self._c = ctypes
+        rt = self.runtime()
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = rt.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def record(self, i):
+        rc = self.runtime().hipEventRecord(self.ev[i], self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, i, j):
+        t = self._c.c_float()
+        rc = self.runtime().hipEventElapsedTime(self._c.byref(t), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(t.value)
+
+    def __del__(self):
+        try:
+            for e in self.ev:
+                self.runtime().hipEventDestroy(e)
+        except Exception:
+            pass
+
+
 def settle(torch, launch, warmup, ms=SETTLE_MS):
     """Untimed dispatches until `warmup` of them and `ms` of wall time with
     the GPU kept busy have passed (the host waits for each batch, so wall time
@@ -77,19 +144,18 @@ def time_windows(torch, launch, steps, warmup, windows):
     stream, so the GPU never idles between them; a few untimed dispatches
     before the first event keep the queue ahead of the GPU)."""
     i = settle(torch, launch, warmup)
-    stream = torch.cuda.current_stream()
     for _ in range(8):
         launch(i)
         i += 1
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(windows + 1)]
-    ev[0].record(stream)
+    ev = TimingEvents(torch, windows + 1)
+    ev.record(0)
     for w in range(windows):
         for _ in range(steps):
             launch(i)
             i += 1
-        ev[w + 1].record(stream)
+        ev.record(w + 1)
     torch.cuda.synchronize()
-    return summarize([ev[w].elapsed_time(ev[w + 1]) / steps for w in range(windows)])
+    return summarize([ev.ms(w, w + 1) / steps for w in range(windows)])
 
 
 def matvec_launcher(q, torch, Ws, x, y, check=True):
@@ -122,14 +188,13 @@ def time_graph(torch, make_launch, nodes, replays=5):
         for i in range(nodes):
             launch(i)
     settle(torch, lambda i: g.replay(), 3)
-    stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
-    ev[0].record(stream)
+    ev = TimingEvents(torch, replays + 1)
+    ev.record(0)
     for r in range(replays):
         g.replay()
-        ev[r + 1].record(stream)
+        ev.record(r + 1)
     torch.cuda.synchronize()
-    return summarize([ev[r].elapsed_time(ev[r + 1]) / nodes for r in range(replays)])
+    return summarize([ev.ms(r, r + 1) / nodes for r in range(replays)])
 
 
 def gbs(nbytes, ms):
@@ -330,7 +395,6 @@ def bench_decode(q, torch, m, reps=5, warmup=2, device_caches=False, kv16=False,
     dm = q.DecodeModel(**model_kwargs(m, dmod))
     a = torch.from_numpy(wl.start_tokens(m)).to(dev)
     b = torch.empty_like(a)
-    stream = torch.cuda.current_stream()
 
     def run(steps, eager=False):
         dm.set_position(m.start_pos)
@@ -351,14 +415,13 @@ def bench_decode(q, torch, m, reps=5, warmup=2, device_caches=False, kv16=False,
         run(m.steps)
     torch.cuda.synchronize()
     times = []
+    ev = TimingEvents(torch, 2)
     for _ in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        ev.record(0)
         run(m.steps)
-        e1.record(stream)
+        ev.record(1)
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / m.steps)
+        times.append(ev.ms(0, 1) / m.steps)
     t = summarize(times)
     ms = t["median_ms"]
     nbytes = sum(decode_algorithmic_bytes(m, s_, 2 if kv16 else 4) for s_ in range(m.steps)) / m.steps
