@@ -35,6 +35,23 @@ constexpr int kChunk = 64;  // positions per chunk (one per lane in the softmax 
 #define Q4_ATTN_SPLIT_TARGET 1024
 #endif
 constexpr int kSplitTarget = Q4_ATTN_SPLIT_TARGET;
+
+// Score products on the matrix cores for binary16 caches at hd 512 with 8
+// query heads per kv head (see attn_split_kernel).
+#ifndef Q4_ATTN_MFMA
+#define Q4_ATTN_MFMA 1
+#endif
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Power-of-two exponent that puts m (the largest magnitude of a query row) in
+// [2^11, 2^12); 0 for zero, infinite or NaN maxima.
+__device__ __forceinline__ int row_shift(float m) {
+    if (!(m > 0.f) || !(m <= 3.4e38f)) return 0;
+    int e;
+    (void)frexpf(m, &e);
+    return min(max(12 - e, -120), 120);
+}
 constexpr int kSplitFrom = 4 * kSplitTarget;
 
 struct AttnGeom {
@@ -271,6 +288,61 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[g][e] *= scale;
     }
+    // Matrix-core scores (binary16 keys, hd 512, 8 query heads): the scaled
+    // query rows go through LDS (the value-reduction buffer, unused until the
+    // end) into v_mfma_f32_16x16x32_f16 A operands.  A row 2h + t holds head
+    // h's part t of q_h * 2^e_h = hi + lo (hi = binary16 of the scaled row,
+    // lo = binary16 of the remainder; e_h puts the row's largest magnitude in
+    // [2^11, 2^12)), so hi + lo carries about 22 bits of every element and
+    // each product with a binary16 key is exact in the fp32 accumulation.
+    // Lane (i, g) holds A[i][8g .. 8g + 7] of each of the 16 steps of 32
+    // dimensions; the key operand of lane (n, g) is the 16 contiguous bytes
+    // of key n at the same dimensions.
+    constexpr bool kMfma = Q4_ATTN_MFMA && HD == 512 && GM == 8 && sizeof(KT) == 2;
+    constexpr int kQs = kMfma ? HD / 32 : 1;
+    [[maybe_unused]] half8_t qa[kQs];
+    __shared__ float qscale_s[kMfma ? GM : 1];
+    if constexpr (kMfma) {
+        float *qs = reinterpret_cast<float *>(red);  // [GM][HD]
+        static_assert(sizeof(red) >= sizeof(float) * GM * HD, "query staging");
+        if (wave == 0) {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                float *d = qs + g * HD;
+                *reinterpret_cast<float4 *>(d + 4 * sub) = make_float4(qv[g][0], qv[g][1], qv[g][2], qv[g][3]);
+                *reinterpret_cast<float4 *>(d + HD / 2 + 4 * sub) = make_float4(qv[g][4], qv[g][5], qv[g][6], qv[g][7]);
+            }
+        }
+        __syncthreads();
+        const int arow = lane & 15, ag = lane >> 4, ah = arow >> 1;
+        const float *qh = qs + ah * HD + 8 * ag;
+        float m = 0.f;
+#pragma unroll
+        for (int st_ = 0; st_ < kQs; ++st_) {
+            const float4 a = *reinterpret_cast<const float4 *>(qh + 32 * st_);
+            const float4 c = *reinterpret_cast<const float4 *>(qh + 32 * st_ + 4);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+        }
+        // the four lane groups of a row hold the row's four quarters
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const int sh = row_shift(m);
+        const float sc4 = ldexpf(1.0f, sh);
+        if (wave == 0 && ag == 0 && (arow & 1) == 0) qscale_s[ah] = ldexpf(1.0f, -sh);
+#pragma unroll
+        for (int st_ = 0; st_ < kQs; ++st_) {
+            half8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = qh[32 * st_ + e] * sc4;
+                const _Float16 hi = static_cast<_Float16>(xv);
+                v[e] = (arow & 1) ? static_cast<_Float16>(xv - static_cast<float>(hi)) : hi;
+            }
+            qa[st_] = v;
+        }
+        __syncthreads();  // qscale_s written; every wavefront has its operands
+    }
     // ---- value-pass roles and running state
     const int kg = threadIdx.x / TPK, d4 = threadIdx.x % TPK;
     constexpr int VG = VIT < 16 ? VIT : 16;  // keys per thread at a time
@@ -292,6 +364,29 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     const int64_t p0 = s0 + static_cast<int64_t>(ci) * kChunk;
     cnt = static_cast<int>(min(int64_t(kChunk), n - p0));
     sbase = static_cast<int>(p0 % cap);
+    if constexpr (kMfma) {
+        // wavefront w scores keys 16w .. 16w + 15 of the chunk: 16 steps of
+        // 32 dimensions, 8 key loads of 16 bytes in flight per lane
+        const int key = 16 * wave + (lane & 15);
+        const KT *kp = kb + slot(key) + 8 * (lane >> 4);
+        f32x4_t dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < kQs; s0 += 8) {
+            f32x4_ev kw[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kw[t] = ld_kv(reinterpret_cast<const f32x4_ev *>(kp + 32 * (s0 + t)));
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s0 + t], __builtin_bit_cast(half8_t, kw[t]), dacc,
+                                                              0, 0, 0);
+        }
+        // result rows 4g .. 4g + 3: (head 2g: hi, lo), (head 2g + 1: hi, lo)
+        const int h0 = 2 * (lane >> 4);
+        const float s_a = (dacc[0] + dacc[1]) * qscale_s[h0];
+        const float s_b = (dacc[2] + dacc[3]) * qscale_s[h0 + 1];
+        if (h0 < G) sc[key * GM + h0] = key < cnt ? s_a : -INFINITY;
+        if (h0 + 1 < G) sc[key * GM + h0 + 1] = key < cnt ? s_b : -INFINITY;
+    } else {
 #pragma unroll 1
     for (int i0 = 0; i0 < SIT; i0 += SG) {
         float kr[SG][8];
@@ -316,6 +411,7 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
                 if (sub == 0 && g < G) sc[jj * GM + g] = jj < cnt ? s : -INFINITY;
             }
         }
+    }
     }
     __syncthreads();
 

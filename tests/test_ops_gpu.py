@@ -365,6 +365,8 @@ F16_ATTN_CASES = [
     (8, 32, 8, 128, 2064, 2049, 0),      # Qwen3-4B-shaped, B = 8
     (1, 16, 8, 128, 40000, 33001, 0),    # multi-chunk splits, ragged
     (1, 32, 4, 512, 65552, 65536, 0),    # 31B full layer at 64K keys
+    (2, 28, 4, 512, 700, 650, 0),        # hd 512, 7:1 groups, B = 2, ragged tail
+    (1, 32, 4, 512, 1024, 3000, 1024),   # hd 512, sliding window, wrapped ring
 ]
 
 
@@ -400,6 +402,7 @@ def test_gqa_decode_attn_f16_cache_parity(dev, B, hq, hkv, hd, cap, n, window):
     (1, 32, 4, 512, 8208, 8192, 0, True, 1e6),
     (8, 32, 8, 128, 2064, 2048, 0, False, 1e6),
     (1, 32, 4, 512, 65552, 65536, 0, True, 1e6),
+    (2, 28, 4, 512, 700, 640, 0, False, 1e6),
 ])
 def test_gqa_decode_attn_rope_f16_cache(dev, B, hq, hkv, hd, cap, pos, window, v_from_k, theta):
     """Fused preparation, binary16 append and attention over binary16 caches."""
