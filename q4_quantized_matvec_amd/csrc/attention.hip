@@ -36,8 +36,8 @@ constexpr int kChunk = 64;  // positions per chunk (one per lane in the softmax 
 #endif
 constexpr int kSplitTarget = Q4_ATTN_SPLIT_TARGET;
 
-// Score products on the matrix cores for binary16 caches at hd 512 with 8
-// query heads per kv head (see attn_split_kernel).
+// Score products on the matrix cores for binary16 caches (see
+// attn_split_kernel).
 #ifndef Q4_ATTN_MFMA
 #define Q4_ATTN_MFMA 1
 #endif
@@ -288,20 +288,24 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[g][e] *= scale;
     }
-    // Matrix-core scores (binary16 keys, hd 512, 8 query heads): the scaled
-    // query rows go through LDS (the value-reduction buffer, unused until the
-    // end) into v_mfma_f32_16x16x32_f16 A operands.  A row 2h + t holds head
-    // h's part t of q_h * 2^e_h = hi + lo (hi = binary16 of the scaled row,
-    // lo = binary16 of the remainder; e_h puts the row's largest magnitude in
-    // [2^11, 2^12)), so hi + lo carries about 22 bits of every element and
-    // each product with a binary16 key is exact in the fp32 accumulation.
-    // Lane (i, g) holds A[i][8g .. 8g + 7] of each of the 16 steps of 32
-    // dimensions; the key operand of lane (n, g) is the 16 contiguous bytes
-    // of key n at the same dimensions.
-    constexpr bool kMfma = Q4_ATTN_MFMA && HD == 512 && GM == 8 && sizeof(KT) == 2;
+    // Matrix-core scores (binary16 keys): the scaled query rows go through
+    // LDS (the value-reduction buffer, unused until the end) into
+    // v_mfma_f32_16x16x32_f16 A operands.  A row 2h + t holds head h's part t
+    // of q_h * 2^e_h = hi + lo (hi = binary16 of the scaled row, lo = binary16
+    // of the remainder; e_h puts the row's largest magnitude in [2^11, 2^12)),
+    // so hi + lo carries about 22 bits of every element and each product with
+    // a binary16 key is exact in the fp32 accumulation; rows of heads >= GM
+    // are zero.  Lane (i, g) holds A[i][8g .. 8g + 7] of each of the HD / 32
+    // steps of 32 dimensions; the key operand of lane (n, g) is the 16
+    // contiguous bytes of key n at the same dimensions.
+    // Taken at hd 512 with 8 heads, where the vector ALUs bound the layer.
+    // At hd 128 and 256 (2 or 4 heads) it measured slower or level (the
+    // operands' registers cost occupancy and most MFMA rows are zero), and at
+    // hd 512 with fewer heads the operands would cost the same occupancy.
+    constexpr bool kMfma = Q4_ATTN_MFMA && sizeof(KT) == 2 && HD == 512 && GM == 8;
     constexpr int kQs = kMfma ? HD / 32 : 1;
     [[maybe_unused]] half8_t qa[kQs];
-    __shared__ float qscale_s[kMfma ? GM : 1];
+    __shared__ float qscale_s[8];
     if constexpr (kMfma) {
         float *qs = reinterpret_cast<float *>(red);  // [GM][HD]
         static_assert(sizeof(red) >= sizeof(float) * GM * HD, "query staging");
@@ -315,7 +319,8 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
         }
         __syncthreads();
         const int arow = lane & 15, ag = lane >> 4, ah = arow >> 1;
-        const float *qh = qs + ah * HD + 8 * ag;
+        const bool live = ah < GM;  // rows of heads past GM stay zero
+        const float *qh = qs + min(ah, GM - 1) * HD + 8 * ag;
         float m = 0.f;
 #pragma unroll
         for (int st_ = 0; st_ < kQs; ++st_) {
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
                 const _Float16 hi = static_cast<_Float16>(xv);
                 v[e] = (arow & 1) ? static_cast<_Float16>(xv - static_cast<float>(hi)) : hi;
             }
-            qa[st_] = v;
+            qa[st_] = live ? v : half8_t{};
         }
         __syncthreads();  // qscale_s written; every wavefront has its operands
     }
@@ -365,22 +370,24 @@ __global__ __launch_bounds__(kWG) void attn_split_kernel(
     cnt = static_cast<int>(min(int64_t(kChunk), n - p0));
     sbase = static_cast<int>(p0 % cap);
     if constexpr (kMfma) {
-        // wavefront w scores keys 16w .. 16w + 15 of the chunk: 16 steps of
-        // 32 dimensions, 8 key loads of 16 bytes in flight per lane
+        // wavefront w scores keys 16w .. 16w + 15 of the chunk: HD / 32 steps
+        // of 32 dimensions, up to 8 key loads of 16 bytes in flight per lane
+        constexpr int KB = kQs < 8 ? kQs : 8;
         const int key = 16 * wave + (lane & 15);
         const KT *kp = kb + slot(key) + 8 * (lane >> 4);
         f32x4_t dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s0 = 0; s0 < kQs; s0 += 8) {
-            f32x4_ev kw[8];
+        for (int s0 = 0; s0 < kQs; s0 += KB) {
+            f32x4_ev kw[KB];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) kw[t] = ld_kv(reinterpret_cast<const f32x4_ev *>(kp + 32 * (s0 + t)));
+            for (int t = 0; t < KB; ++t) kw[t] = ld_kv(reinterpret_cast<const f32x4_ev *>(kp + 32 * (s0 + t)));
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < KB; ++t)
                 dacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s0 + t], __builtin_bit_cast(half8_t, kw[t]), dacc,
                                                               0, 0, 0);
         }
-        // result rows 4g .. 4g + 3: (head 2g: hi, lo), (head 2g + 1: hi, lo)
+        // result rows 4g .. 4g + 3: (head 2g: hi, lo), (head 2g + 1: hi, lo);
+        // heads past G (hence past GM) are not read
         const int h0 = 2 * (lane >> 4);
         const float s_a = (dacc[0] + dacc[1]) * qscale_s[h0];
         const float s_b = (dacc[2] + dacc[3]) * qscale_s[h0 + 1];

@@ -367,6 +367,9 @@ F16_ATTN_CASES = [
     (1, 32, 4, 512, 65552, 65536, 0),    # 31B full layer at 64K keys
     (2, 28, 4, 512, 700, 650, 0),        # hd 512, 7:1 groups, B = 2, ragged tail
     (1, 32, 4, 512, 1024, 3000, 1024),   # hd 512, sliding window, wrapped ring
+    (1, 64, 8, 128, 600, 555, 0),        # hd 128, 8:1 groups
+    (2, 24, 8, 128, 500, 450, 0),        # hd 128, 3:1 groups (a zero operand row pair)
+    (1, 48, 16, 256, 900, 777, 0),       # hd 256, 3:1 groups
 ]
 
 
