@@ -26,8 +26,7 @@ fp32 N(0,1); norm gains fp32 U[0.8, 1.2]; start tokens uniform in [0, vocab).
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field, replace
-from typing import List
+from dataclasses import dataclass, replace
 
 import numpy as np
 

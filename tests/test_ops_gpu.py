@@ -9,7 +9,7 @@ import torch
 import oracle
 import q4_quantized_matvec_amd as q
 import synth
-from q4_quantized_matvec_amd._lib import KVLayout, kv_layout_of
+from q4_quantized_matvec_amd._lib import kv_layout_of
 
 pytestmark = pytest.mark.gpu
 
