@@ -156,6 +156,42 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __builtin_bit_cast(float, b[0]) + __builtin_bit_cast(float, opaque_copy(b[1]));
 }
 
+// Eight per-lane values v[b] (one per batch row) reduced over the 64 lanes at
+// once; on return lane l holds the result for b = l / 8.  Each exchange round
+// halves what a lane carries: lanes l and l ^ 32 (permlane32 swap) keep b < 4
+// in the low half and b >= 4 in the high half, lanes l and l ^ 16
+// (permlane16 swap) split those again, lanes l and l ^ 8 (row rotation by 8)
+// once more, and three DPP rounds finish over the 8 lanes of each half-row.
+// About 20 instructions, where eight separate wavefront reductions take
+// about 120 and their DPP hazards.
+template <bool MAX>
+__device__ __forceinline__ float red_op(float a, float b) {
+    return MAX ? fmaxf(a, b) : a + b;
+}
+template <bool MAX>
+__device__ __forceinline__ float reduce8_by_lane(const float (&v)[kMaxB]) {
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // lanes 0..31: b = j; lanes 32..63: b = j + 4
+        auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[j]),
+                                                  __builtin_bit_cast(uint32_t, v[j + 4]), false, false);
+        r[j] = red_op<MAX>(__builtin_bit_cast(float, s[0]), __builtin_bit_cast(float, opaque_copy(s[1])));
+    }
+    float t[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // 16-lane row q: b = j + 2 (q % 2) + 4 (q / 2)
+        auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, r[j]),
+                                                  __builtin_bit_cast(uint32_t, r[j + 2]), false, false);
+        t[j] = red_op<MAX>(__builtin_bit_cast(float, s[0]), __builtin_bit_cast(float, opaque_copy(s[1])));
+    }
+    const bool up = (threadIdx.x & 8) != 0;  // lanes with bit 3 set keep b odd
+    const float keep = up ? t[1] : t[0], send = up ? t[0] : t[1];
+    float w = red_op<MAX>(keep, dpp_keep<0x128>(send));  // row_ror:8 = lane ^ 8 within the row
+    w = red_op<MAX>(w, dpp_keep<0xB1>(w));                // quad_perm [1,0,3,2]
+    w = red_op<MAX>(w, dpp_keep<0x4E>(w));                // quad_perm [2,3,0,1]
+    return red_op<MAX>(w, dpp_keep<0x141>(w));            // row_half_mirror: the two quads
+}
+
 // Lane groups 0..3 hold v_t for t = 0..3; afterwards v_s at lane group g is
 // the old v_g of lane group s (a 4 x 4 transpose across the 16-lane rows).
 __device__ __forceinline__ void transpose4(uint32_t &v0, uint32_t &v1, uint32_t &v2, uint32_t &v3) {
@@ -693,10 +729,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
             xv[b] = t;
             mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
         }
+        const int shl = step_shift(reduce8_by_lane<true>(mx));  // batch row lane / 8
         int sh[kMaxB];
 #pragma unroll
-        for (int b = 0; b < kMaxB; ++b) sh[b] = step_shift(wave_max(mx[b]));
-                uint8_t *obase = reinterpret_cast<uint8_t *>(&opnd[wv][jl][16 * gl]) + 2 * el;
+        for (int b = 0; b < kMaxB; ++b) sh[b] = __builtin_amdgcn_readlane(shl, 8 * b);
+        uint8_t *obase = reinterpret_cast<uint8_t *>(&opnd[wv][jl][16 * gl]) + 2 * el;
 #pragma unroll
         for (int b = 0; b < kMaxB; ++b) {
             const float sc = ldexpf(hscale, sh[b]);
@@ -784,11 +821,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
     for (int t = 0; t < T; ++t) red[wv][t][lane] = acc[t];
     if constexpr (KIND == 1) {
         // sums of squares of this workgroup's K range per batch row
-#pragma unroll
-        for (int b = 0; b < kMaxB; ++b) {
-            const float t = wave_sum(ssq[b]);
-            if (lane == 0) ssq_w[wv][b] = t;
-        }
+        const float t = reduce8_by_lane<false>(ssq);
+        if ((lane & 7) == 0) ssq_w[wv][lane >> 3] = t;
     }
     __syncthreads();
     const int tw = wv < T ? wv : T - 1;  // this wavefront's tile (wavefronts >= T have none)
@@ -910,7 +944,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     // ---- this wavefront's step: activations -> exact halves (MFMA operand order)
     half8_t af[kSeg];
     float fa = 0.f, fb = 0.f;
-    float sqa = 0.f;  // RMSNorm: lane b < 8 holds batch row b's sum of squares over the step
+    float sqa = 0.f;  // RMSNorm: lane l holds batch row l / 8's sum of squares over the step
     {
         const int jl = lane >> 3, q8 = lane & 7;
         const int gl = FMT == 0 ? (q8 & 3) : (q8 >> 1);
@@ -952,9 +986,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
             xv[b] = t;
             mx[b] = fmaxf(fmaxf(fabsf(t[0]), fabsf(t[1])), fmaxf(fabsf(t[2]), fabsf(t[3])));
         }
+        const int shl = step_shift(reduce8_by_lane<true>(mx));  // batch row lane / 8
         int sh[kMaxB];
 #pragma unroll
-        for (int b = 0; b < kMaxB; ++b) sh[b] = step_shift(wave_max(mx[b]));
+        for (int b = 0; b < kMaxB; ++b) sh[b] = __builtin_amdgcn_readlane(shl, 8 * b);
         uint8_t *obase = reinterpret_cast<uint8_t *>(&opnd[wv][jl][16 * gl]) + 2 * el;
 #pragma unroll
         for (int b = 0; b < kMaxB; ++b) {
@@ -977,13 +1012,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
             *reinterpret_cast<uint2 *>(obase + 16 * (2 * b)) = hv;      // MFMA row 2b: hi
             *reinterpret_cast<uint2 *>(obase + 16 * (2 * b + 1)) = lv;  // MFMA row 2b + 1: lo
         }
-        if constexpr (KIND == 1) {
-#pragma unroll
-            for (int b = 0; b < kMaxB; ++b) {
-                const float t = wave_sum(ssq[b]);
-                if (lane == b) sqa = t;
-            }
-        }
+        if constexpr (KIND == 1) sqa = reduce8_by_lane<false>(ssq);  // batch row lane / 8
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wavefront reads back its own writes
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -1061,7 +1090,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
 
     if constexpr (KIND == 1) {
-        if (lane < kMaxB) ssq_w[wv][lane] = sqa;
+        if ((lane & 7) == 0) ssq_w[wv][lane >> 3] = sqa;
     }
     __syncthreads();
     // outputs of the workgroup: (live tile i, batch row b, row col) -> thread o
