@@ -686,9 +686,9 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
         if (c >= kc) break;                 // wave-uniform; steps only grow with r
         // ---- activations first (loads return in order), then the weights
         const int64_t kx = static_cast<int64_t>(c) * (32 * kSeg) + 4 * lane;
-        // (every load is unconditional, rows past B re-read the last one and
-        // are zeroed afterwards, so the compiler can wait for these loads
-        // alone and not for the weights behind them)
+        // (every load is unconditional, rows past B re-read the last one,
+        // whose sums are computed and never stored, so the compiler can wait
+        // for these loads alone and not for the weights behind them)
         f32x4_t xv[kMaxB], tv[kMaxB];
         f32x4_t gv = {1.f, 1.f, 1.f, 1.f};
         if constexpr (KIND == 1) {
@@ -701,12 +701,6 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(3))) void m
             xv[b] = *reinterpret_cast<const f32x4_al16_t *>(x + bo);
             if constexpr (KIND == 2) tv[b] = *reinterpret_cast<const f32x4_al16_t *>(u + bo);
         }
-#pragma unroll
-        for (int b = 0; b < kMaxB; ++b)
-            if (b >= B) {
-                xv[b] = zero;
-                if constexpr (KIND == 2) tv[b] = zero;
-            }
         uint32_t dw[T][kDw];
 #pragma unroll
         for (int t = 0; t < T; ++t) load_seg<kDw>(wrow[t] + c * seg, dw[t]);
@@ -895,7 +889,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
         B = gv_.Bg;
     }
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int nb = K / 32, kc = nb / kSeg;
     const int c = blockIdx.y * WV + wv;  // this wavefront's step
@@ -925,9 +919,11 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     // ---- loads first: this wavefront's step of the activations, then the
     // first PF row tiles.  Loads return in order, so the conversion below
     // waits for the activations only, while the weights are on their way.  A
-    // wavefront past the last step loads and converts the last step like the
-    // others (same control flow, no branch around loads) and then zeroes its
-    // operands and scales, so it adds exact zeros.
+    // wavefront past the last step skips the stream and adds zeros; in
+    // workgroups of 8 or 12 wavefronts it skips the conversion too.  (The
+    // branch around the conversion costs about 26 VGPRs: with 4 wavefronts
+    // that measured slower than converting the last step again, and with 16,
+    // at most 128 VGPRs, it spills.)
     const int cs = min(c, kc - 1);
     constexpr int NBUF = PF + 1;
     const uint8_t *wbase = W + g * 2 * kBytes + static_cast<int64_t>(cs) * seg;
@@ -945,7 +941,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     half8_t af[kSeg];
     float fa = 0.f, fb = 0.f;
     float sqa = 0.f;  // RMSNorm: lane l holds batch row l / 8's sum of squares over the step
-    {
+    constexpr bool kSkipIdleConversion = WV == 8 || WV == 12;
+    if (!kSkipIdleConversion || active) {
         const int jl = lane >> 3, q8 = lane & 7;
         const int gl = FMT == 0 ? (q8 & 3) : (q8 >> 1);
         const int el = FMT == 0 ? (q8 >= 4 ? 4 : 0) : 4 * (q8 & 1);
@@ -965,12 +962,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
         for (int p = 0; p < PF; ++p) fetch(p, ring[p]);
         float ssq[kMaxB], mx[kMaxB];
+        // rows past B repeat row B - 1: their sums are computed and never stored
 #pragma unroll
         for (int b = 0; b < kMaxB; ++b) {
-            if (b >= B) {
-                xv[b] = zero;
-                if constexpr (KIND == 2) tv[b] = zero;
-            }
             f32x4_t t = xv[b];
             ssq[b] = 0.f;
             if constexpr (KIND == 1) {
@@ -1027,21 +1021,15 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
         fa = ldexpf(1.0f, -sa);
         fb = ldexpf(1.0f, -sb);
     }
-    if (!active) {  // past the last step: exact zeros (wave-uniform)
-#pragma unroll
-        for (int jj = 0; jj < kSeg; ++jj) af[jj] = half8_t{};
-        fa = fb = 0.f;
-        sqa = 0.f;
-    }
     __syncthreads();  // every wavefront holds its operands: the LDS region is free
 
     // ---- stream the row tiles past the step's operands; each tile's partial
     // sums go to its LDS slot at once (live tile i -> slot tile_of(i): gate
     // tiles first, up tiles from slot tpw / 2; only live slots are read back)
-    // Every wavefront runs the same stream: one past the last step re-reads the
-    // last step's weights (L2 hits) with zero operands and scales, so it adds
-    // exact zeros to its slots.
-    if (nt > 0) {  // workgroup-uniform
+    // A wavefront past the last step writes zeros to its slots.
+    if (nt > 0 && !active) {
+        for (int i = 0; i < nt; ++i) red[wv][tile_of(i)][lane] = make_float2(0.f, 0.f);
+    } else if (nt > 0) {  // workgroup-uniform
         auto process = [&](int i, const uint32_t (&cur)[kDw]) {
             const uint32_t dp = __builtin_amdgcn_perm(cur[(kDw - 1) / 2], cur[0], 0x07060100u);
             uint32_t dps[4];
@@ -1090,7 +1078,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
 
     if constexpr (KIND == 1) {
-        if ((lane & 7) == 0) ssq_w[wv][lane >> 3] = sqa;
+        if ((lane & 7) == 0) ssq_w[wv][lane >> 3] = active ? sqa : 0.f;
     }
     __syncthreads();
     // outputs of the workgroup: (live tile i, batch row b, row col) -> thread o
