@@ -1214,7 +1214,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 #define Q4_MFMA_KSTAT 1  // 0: the tile / shared-step kernels only
 #endif
 #ifndef Q4_KS_WHOLE_MAX
-#define Q4_KS_WHOLE_MAX 12  // longest K (in steps) one K-stationary workgroup covers whole
+#define Q4_KS_WHOLE_MAX 16  // longest K (in steps) one K-stationary workgroup covers whole
 #endif
 #ifndef Q4_KS_MIN_UNITS
 #define Q4_KS_MIN_UNITS 512  // fewest row tiles for the K-split K-stationary kernel
@@ -1239,10 +1239,12 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt, bool glu = false) {
     const int rounds = (p.kc + 3) / 4;
     // K-stationary kernel, where it measured faster than the tile kernels
     // (Q4_0 only; 5376 x 21504 and the Qwen3-4B projections at B = 8):
-    //  * K of at most 12 steps: one workgroup of WV = 4 ceil(steps / 4)
+    //  * K of at most 16 steps: one workgroup of WV = 4 ceil(steps / 4)
     //    wavefronts covers the whole K (no split), when that still gives
-    //    at least 128 workgroups (16-wavefront workgroups, one per CU,
-    //    measured slower than the tile kernel);
+    //    at least 128 workgroups; with 16 wavefronts (1,024 threads, one
+    //    workgroup per CU) only for 144..384 of them and B <= 16: with 128
+    //    (a gated output of 4,096 rows) and at B = 32 the other kernels
+    //    measured faster;
     //  * longer K: workgroups of 4 wavefronts over K ranges of 4 steps, the
     //    ranges' partials added in order by a second launch, for matrices of
     //    at least 512 row tiles.
@@ -1266,10 +1268,10 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int fmt, bool glu = false) {
     if (Q4_MFMA_KSTAT && fmt == 0) {
         if (p.kc <= Q4_KS_WHOLE_MAX) {
             kstat_plan((p.kc + 3) / 4 * 4);
-            p.kstat = static_cast<int64_t>(p.rg) * p.NG >= 128;
-        } else if (p.kc <= 4 * kMaxS) {
-            p.kstat = kstat_plan(4) >= Q4_KS_MIN_UNITS;
+            const int64_t wgs = static_cast<int64_t>(p.rg) * p.NG;
+            p.kstat = p.wv <= 12 ? wgs >= 128 : (wgs >= 144 && wgs <= 384 && p.NG <= 2);
         }
+        if (!p.kstat && p.kc > 12 && p.kc <= 4 * kMaxS) p.kstat = kstat_plan(4) >= Q4_KS_MIN_UNITS;
     }
     if (!p.kstat) {
         p.tiles = true;
