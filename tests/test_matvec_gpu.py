@@ -201,6 +201,11 @@ BATCHED_CASES = [
     # ranges added by the second launch, a ragged last group, every transform
     ("q4", 6144, 2560, 16, "rms"), ("q4", 5000, 2048, 29, "plain"), ("q4", 4100, 1024, 32, "rms"),
     ("q4", 8200, 5376, 10, "plain"), ("q4", 8200, 3328, 16, "geglu"), ("q4", 16390, 3328, 27, "swiglu"),
+    # fewer than 8 rows in a group on the K-stationary paths (the rows past B
+    # repeat the last one and are never stored): whole K with 12 wavefronts,
+    # two of them past the last step; whole K with 16; K ranges + reduce
+    ("q4", 6144, 2560, 5, "rms"), ("q4", 2560, 4096, 3, "plain"), ("q4", 21504, 5376, 5, "plain"),
+    ("q4", 19456, 2560, 7, "swiglu"),
 ]
 
 
