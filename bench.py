@@ -782,16 +782,19 @@ def main():
     if args.copy_calibration:
         marker_copy(torch, reps=4)
     if not args.headline_only:
-        # B = 2..8 through the plain entry point (vector kernel, W re-read per
-        # row from the caches) and through the matrix-core entry point
+        # B = 2..8 through the workspace-free entry point (at B = 2 the vector
+        # kernel once per row, W re-read from the caches; from B = 3 on this
+        # shape the matrix-core tile kernel without a K split) and through the
+        # matrix-core entry point with a workspace
         for bb in (2, 4, 8, 16, 32):
             xb, yb = activations(torch, w, bb, dev)
             nb = matvec_bytes(w.n, w.k, bb)
             if bb <= 8:
-                log(f"timing B={bb} (q4_0_matvec, vector kernel)")
-                out[f"matvec_B{bb}_vector"] = line(
+                kern = "vector kernel per row" if bb < 3 else "matrix-core tiles, whole K"
+                log(f"timing B={bb} (q4_0_matvec, {kern})")
+                out[f"matvec_B{bb}_plain_entry"] = line(
                     nb, time_windows(torch, matvec_launcher(q, torch, Ws, xb, yb), args.steps,
-                                     args.warmup, args.windows), path="q4_0_matvec")
+                                     args.warmup, args.windows), path=f"q4_0_matvec ({kern})")
             log(f"timing B={bb} (q4_0_matvec_batched, matrix cores)")
             out[f"matvec_B{bb}"] = line(
                 nb, time_windows(torch, batched_launcher(q, torch, Ws, xb, yb, w.k, bb), args.steps,

@@ -65,12 +65,17 @@ const char *q4dec_version(void);
  *   x         device fp32 [B][K], 4-byte aligned
  *   y         device fp32 [B][N]; may alias residual (in-place residual add)
  *   residual  device fp32 [B][N] or NULL
- * Accumulation is fp32; every weight-activation product is formed exactly.
- * B > 1 runs the B = 1 vector kernel once per activation row (the rows run
- * side by side in one launch), so W is read B times, from HBM or from the
- * last-level cache: the time grows about linearly with B.  For 2 <= B the
- * matrix-core entry q4_0_matvec_batched reads W once per call and is the
- * fast path (it needs a workspace, which this call does not take).
+ * Accumulation is fp32; every weight-activation product is formed exactly
+ * (on the matrix cores: activations as two binary16 halves with a power-of-two
+ * scale per 256 elements, about 22 significant bits).
+ * B > 1 without a workspace: from B = 3, when K % 256 == 0, W and x are
+ * 16-byte aligned, y does not overlap x and the matrix has many rows
+ * (N >= 16384, or N >= 4096 at B >= 6), the matrix-core tile kernel with every
+ * workgroup walking the whole K reads W once per call; otherwise the B = 1
+ * vector kernel runs once per activation row (the rows side by side in one
+ * launch) and W is read B times, from HBM or from the last-level cache.  The
+ * matrix-core entry q4_0_matvec_batched, which splits K and takes a
+ * workspace, is faster on most shapes from B = 2 on.
  * Errors: Q4_ERR_INVALID_ARG (null / sizes), Q4_ERR_SHAPE (K % 32),
  *         Q4_ERR_ALIGNMENT, Q4_ERR_UNSUPPORTED (B > 8), Q4_ERR_HIP.
  */

@@ -26,6 +26,15 @@ size_t argmax_scratch_bytes(int64_t B);
 q4_status argmax_rows_scratch(const float *logits, int64_t B, int64_t V, int32_t *out,
                               void *scratch, hipStream_t s);
 
+// The matrix-core matvec without a K split, so without a workspace: every
+// workgroup of the tile kernel walks the whole K for its 64 (Q4_0) or 32
+// (Q8_0) rows.  For the workspace-free matvec entry points at 3 <= B <= 8;
+// the caller has checked K % 256 == 0, 16-byte aligned W, x, x2 and norm_w,
+// ld_x % 4 == 0 and y disjoint from x and x2.  fmt: 0 = Q4_0, 1 = Q8_0.
+void matvec_mfma_whole_k(int fmt, const void *W, int N, int K, const float *x, const float *x2,
+                         const float *norm_w, int64_t ldx, int B, int op_kind, int out_op, float eps,
+                         float *y, const float *res, hipStream_t s);
+
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -741,6 +741,11 @@ void launch_generic(int B, const uint8_t *W, const float *x, float *y, const flo
 #undef Q4_CASE
 }
 
+bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
+}
+
 template <int FMT>
 q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, const float *x,
                        const float *x2, int64_t ldx, int64_t B, int op_kind, int out_op,
@@ -780,9 +785,10 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     InOp op{gated_in ? 2 : op_kind, gated_in ? x2 : nullptr, op_kind == Q4_IN_RMSNORM ? norm_w : nullptr,
             eps, ldx, out_op == Q4_OUT_SWIGLU ? 1 : out_op == Q4_OUT_GEGLU ? 2 : 0,
             op_kind == Q4_IN_GEGLU ? 1 : 0};
+    const bool x16 = K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
+                     (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0;
     int ks = 0;
-    if (K % 256 == 0 && q4::aligned(x, 16) && (!op.u || q4::aligned(op.u, 16)) &&
-        (!op.w || q4::aligned(op.w, 16)) && ldx % 4 == 0) {
+    if (x16) {
         for (int cand : {1, 2, 4})
             if (cand >= Q4_MV_KS_MIN && ks_part_blocks(nb, cand) <= 64 * (cand == 4 ? 4 : Q4_MV_MAX_JX)) {
                 ks = cand;
@@ -791,6 +797,20 @@ q4_status matvec_entry(const char *name, const void *Wv, int64_t N, int64_t K, c
     }
     Q4_CHECK(!glu_out || ks == 1, Q4_ERR_UNSUPPORTED,
              "%s: a gated output needs K %% 256 == 0, K <= 8192, 16-byte aligned x", name);
+    // 3 <= B <= 8 rows: the matrix-core tile kernel without a K split reads W
+    // once per call and needs no workspace.  It is faster than the vector
+    // kernel once per row where the rows give it enough workgroups (measured:
+    // 21504 x 5376 at B = 3, 4, 8 in 28.5, 28.6, 29.0 us against 34.4, 43.9,
+    // 80.8 us; 6144 x 2560 at B = 8 10.8 against 17.7 us; 2560 x 9728 slower
+    // at every B, 27.0 against 11.3-32.0 us).
+    const size_t xbytes = static_cast<size_t>((B - 1) * ldx + K) * sizeof(float);
+    const size_t ybytes = static_cast<size_t>(B * (glu_out ? N / 2 : N)) * sizeof(float);
+    if (x16 && q4::aligned(Wv, 16) && B >= 3 && (N >= 16384 || (B >= 6 && N >= 4096)) &&
+        !ranges_overlap(y, ybytes, x, xbytes) && (!op.u || !ranges_overlap(y, ybytes, op.u, xbytes))) {
+        q4::matvec_mfma_whole_k(FMT, Wv, n, k, x, op.u, op.w, ldx, static_cast<int>(B), op_kind, out_op, eps,
+                                y, res, s);
+        return q4::launch_status(name);
+    }
     if (ks) {
         const int jx = (ks_part_blocks(nb, ks) + 63) / 64;
         const int b = static_cast<int>(B);

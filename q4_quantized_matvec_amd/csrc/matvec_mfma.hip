@@ -45,6 +45,7 @@
 // weights come from HBM once and the later groups read them from that XCD's
 // L2.
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -1314,10 +1315,11 @@ template <int FMT, int KIND, bool GELU>
 void launch_act(const uint8_t *W, int N, int K, int B, const float *x, const float *u, const float *nw,
                 int64_t ld, float eps, float *y, const float *res, void *ws, const Plan &p, int glu,
                 hipStream_t s) {
+    // (no workspace when K is not split: the kernels touch it only for S > 1)
     uint8_t *w8 = static_cast<uint8_t *>(ws);
-    int *ctr = reinterpret_cast<int *>(w8);
-    float *ssq = reinterpret_cast<float *>(w8 + p.off_ssq);
-    float *part = reinterpret_cast<float *>(w8 + p.off_part);
+    int *ctr = w8 ? reinterpret_cast<int *>(w8) : nullptr;
+    float *ssq = w8 ? reinterpret_cast<float *>(w8 + p.off_ssq) : nullptr;
+    float *part = w8 ? reinterpret_cast<float *>(w8 + p.off_part) : nullptr;
     const dim3 grid(p.gx, p.S);
     if constexpr (FMT == 0) {  // (the plan takes it for Q4_0 only)
     if (p.kstat) {
@@ -1444,6 +1446,41 @@ q4_status batched_entry(const char *name, const void *Wv, int64_t N, int64_t K, 
 }
 
 }  // namespace
+
+namespace q4 {
+
+void matvec_mfma_whole_k(int fmt, const void *Wv, int N, int K, const float *x, const float *x2,
+                         const float *norm_w, int64_t ldx, int B, int op_kind, int out_op, float eps,
+                         float *y, const float *res, hipStream_t s) {
+    Plan p{};
+    p.NG = 1;
+    p.kc = K / (32 * kSeg);
+    p.kstat = false;
+    p.tiles = true;
+    p.wv = 4;
+    p.T = fmt == 1 ? 2 : 4;
+    p.rg = (N + 16 * p.T - 1) / (16 * p.T);
+    p.spw = (p.kc + 3) / 4;  // every round of 4 steps in one workgroup
+    p.S = 1;
+    p.gx = p.rg;
+    const uint8_t *W = static_cast<const uint8_t *>(Wv);
+    const int glu = out_op == Q4_OUT_PLAIN ? 0 : 1;
+    const bool gelu = op_kind == Q4_IN_GEGLU || out_op == Q4_OUT_GEGLU;
+    const bool gated_in = op_kind == Q4_IN_SWIGLU || op_kind == Q4_IN_GEGLU;
+    auto go = [&](auto fmt_tag) {
+        constexpr int F = decltype(fmt_tag)::value;
+        if (op_kind == Q4_IN_RMSNORM)
+            launch<F, 1>(W, N, K, B, x, nullptr, norm_w, ldx, eps, y, res, nullptr, p, glu, gelu, s);
+        else if (gated_in)
+            launch<F, 2>(W, N, K, B, x, x2, nullptr, ldx, eps, y, res, nullptr, p, glu, gelu, s);
+        else
+            launch<F, 0>(W, N, K, B, x, nullptr, nullptr, ldx, eps, y, res, nullptr, p, glu, gelu, s);
+    };
+    if (fmt == 0) go(std::integral_constant<int, 0>{});
+    else go(std::integral_constant<int, 1>{});
+}
+
+}  // namespace q4
 
 extern "C" size_t matvec_batched_workspace(int64_t N, int64_t K, int64_t B) {
     if (N < 1 || K < 256 || K % 256 != 0 || B < 1 || B > kMaxBatch) return 0;

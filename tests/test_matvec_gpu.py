@@ -36,6 +36,9 @@ CASES_Q4 = [
     (67, 32, 1), (67, 288, 3), (33, 256, 8), (100, 2560, 8), (64, 5376, 2), (50, 9728, 4),
     # B > 1 on the vector kernel (one weight pass per batch row) at every K split
     (300, 8192, 3), (129, 16384, 2), (1000, 2048, 5), (77, 5376, 7), (200, 21504, 6), (90, 256, 2),
+    # 3 <= B <= 8 with many rows: the matrix-core tile kernel over the whole K
+    # (no workspace), ragged row tails
+    (16390, 2560, 3), (4100, 1024, 6), (5000, 2048, 8), (16400, 256, 4),
 ]
 
 
@@ -51,7 +54,8 @@ def test_q4_0_matvec_parity(dev, n, k, b):
 
 
 @pytest.mark.parametrize("n,k,b", [(67, 256, 1), (1000, 2560, 1), (500, 5376, 1),
-                                   (100, 2560, 8), (31, 32, 1), (300, 21504, 1), (40, 288, 5)])
+                                   (100, 2560, 8), (31, 32, 1), (300, 21504, 1), (40, 288, 5),
+                                   (16400, 2560, 4), (4099, 1024, 7)])
 def test_q8_0_matvec_parity(dev, n, k, b):
     _say(f"q8_0_matvec N={n} K={k} B={b}")
     W = synth.q8_0_matrix(102, f"t.q8.{n}.{k}", n, k)
@@ -63,10 +67,10 @@ def test_q8_0_matvec_parity(dev, n, k, b):
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
-@pytest.mark.parametrize("b", [1, 3])
-def test_matvec_residual_in_place(dev, fmt, b):
-    _say(f"{fmt} residual in place B={b}")
-    n, k = 513, 2048
+@pytest.mark.parametrize("b,n", [(1, 513), (3, 513), (3, 16400)])
+def test_matvec_residual_in_place(dev, fmt, b, n):
+    _say(f"{fmt} residual in place B={b} N={n}")
+    k = 2048
     gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
     orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
     fn = q.q4_0_matvec if fmt == "q4" else q.q8_0_matvec
@@ -141,6 +145,9 @@ FUSED_CASES = [
     # B > 1 on the vector kernel with each input transform
     ("q4", 300, 5376, 3, "rms"), ("q4", 129, 8192, 2, "swiglu"), ("q4", 500, 2560, 4, "geglu"),
     ("q8", 200, 5376, 6, "rms_unit"),
+    # ... and on the matrix-core tile kernel over the whole K (many rows)
+    ("q4", 16390, 2560, 4, "rms"), ("q4", 8200, 2048, 7, "swiglu"), ("q4", 4100, 1024, 6, "geglu"),
+    ("q8", 16400, 2560, 3, "rms"), ("q4", 5000, 2048, 8, "rms_unit"),
 ]
 
 
@@ -337,9 +344,13 @@ def test_matvec_batched_spikes(dev):
 
 
 GLU_CASES = [
-    # (path, N, K, B, op): merged gate|up with the SwiGLU output; N = 2F
-    ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 300, 5376, 1, "rms"),
-    ("vector", 2 * 77, 2048, 3, "plain"), ("vector", 2 * 33, 256, 8, "rms_unit"),
+    # (path, N, K, B, op): merged gate|up with the SwiGLU output; N = 2F.
+    # fused: the workspace-free q4_0_matvec_fused (the vector kernel, or from
+    # B = 3 with many rows the matrix-core tile kernel over the whole K);
+    # batched: q4_0_matvec_batched
+    ("fused", 2 * 9728, 2560, 1, "rms"), ("fused", 2 * 300, 5376, 1, "rms"),
+    ("fused", 2 * 77, 2048, 3, "plain"), ("fused", 2 * 33, 256, 8, "rms_unit"),
+    ("fused", 2 * 8200, 2560, 4, "rms"), ("fused", 2 * 2050, 1024, 8, "plain"),
     ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 300, 2560, 8, "rms"),
     ("batched", 2 * 77, 9728, 5, "plain"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 33, 256, 1, "swiglu"),
@@ -378,7 +389,8 @@ def test_matvec_swiglu_output(dev, path, n, k, b, op):
 
 GEGLU_OUT_CASES = [
     # (path, N, K, B, op): merged gate|up with the GeGLU output (tanh-form GELU gate)
-    ("vector", 2 * 9728, 2560, 1, "rms"), ("vector", 2 * 77, 2048, 3, "plain"),
+    ("fused", 2 * 9728, 2560, 1, "rms"), ("fused", 2 * 77, 2048, 3, "plain"),
+    ("fused", 2 * 8200, 2560, 5, "rms"),
     ("batched", 2 * 9728, 2560, 8, "rms"), ("batched", 2 * 1000, 5376, 2, "rms"),
     ("batched", 2 * 16384, 2048, 8, "rms"), ("batched", 2 * 300, 2560, 11, "plain"),
     ("batched", 2 * 8200, 5376, 3, "plain"), ("batched", 2 * 4100, 1024, 32, "rms"),
