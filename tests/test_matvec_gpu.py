@@ -148,6 +148,9 @@ FUSED_CASES = [
     # ... and on the matrix-core tile kernel over the whole K (many rows)
     ("q4", 16390, 2560, 4, "rms"), ("q4", 8200, 2048, 7, "swiglu"), ("q4", 4100, 1024, 6, "geglu"),
     ("q8", 16400, 2560, 3, "rms"), ("q4", 5000, 2048, 8, "rms_unit"),
+    # activation rows with a stride past K
+    ("q4", 16390, 2560, 4, "rms_strided"), ("q4", 300, 5376, 1, "rms_strided"),
+    ("q4", 5000, 2048, 7, "plain_strided"), ("q4", 200, 21504, 2, "plain_strided"),
 ]
 
 
@@ -158,7 +161,7 @@ def test_matvec_fused_input_parity(dev, fmt, n, k, b, op):
     orc = oracle.q4_0_matvec if fmt == "q4" else oracle.q8_0_matvec
     fn = q.q4_0_matvec_fused if fmt == "q4" else q.q8_0_matvec_fused
     W = gen(106, f"t.fused.{fmt}.{n}.{k}", n, k)
-    ld = 2 * k if op in ("swiglu", "geglu") else k
+    ld = 2 * k if op in ("swiglu", "geglu") else k + 64 if op.endswith("_strided") else k
     xa = synth.normal_f32(106, f"t.fused.x.{k}.{b}", (b, ld)) * 2.0
     w = synth.uniform_f32(106, f"t.fused.w.{k}", (k,), 0.8, 1.2)
     r = synth.normal_f32(106, f"t.fused.r.{n}.{b}", (b, n))
@@ -166,15 +169,18 @@ def test_matvec_fused_input_parity(dev, fmt, n, k, b, op):
         xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
     elif op == "geglu":
         xin = np.stack([oracle.geglu(xa[i, :k], xa[i, k:]) for i in range(b)])
+    elif op == "plain_strided":
+        xin = xa[:, :k].astype(np.float64)
     else:
         xin = oracle.rmsnorm(xa[:, :k], None if op == "rms_unit" else w, 1e-6)
     ref, terms = orc(W, n, k, xin, res=r)
     xd = torch.from_numpy(xa).to(dev)
     yr = torch.from_numpy(r).to(dev)
-    kind = {"swiglu": q.IN_SWIGLU, "geglu": q.IN_GEGLU}.get(op, q.IN_RMSNORM)
+    kind = {"swiglu": q.IN_SWIGLU, "geglu": q.IN_GEGLU, "plain_strided": q.IN_PLAIN}.get(op, q.IN_RMSNORM)
     fn(torch.from_numpy(W).to(dev), xd, k, b, ld, kind,
        x2=xd[:, k:] if op in ("swiglu", "geglu") else None,
-       norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6, y=yr, residual=yr)
+       norm_w=torch.from_numpy(w).to(dev) if op in ("rms", "rms_strided") else None, eps=1e-6, y=yr,
+       residual=yr)
     torch.cuda.synchronize()
     _check(yr, ref, terms, f"{fmt} fused {op} {n}x{k} B={b}")
 
@@ -213,13 +219,17 @@ BATCHED_CASES = [
     # two of them past the last step; whole K with 16; K ranges + reduce
     ("q4", 6144, 2560, 5, "rms"), ("q4", 2560, 4096, 3, "plain"), ("q4", 21504, 5376, 5, "plain"),
     ("q4", 19456, 2560, 7, "swiglu"),
+    # activation rows with a stride past K (ld_x = K + 64) on each kernel
+    ("q4", 6144, 2560, 8, "rms_strided"), ("q4", 21504, 5376, 8, "plain_strided"),
+    ("q4", 2560, 4096, 8, "plain_strided"), ("q4", 2560, 9728, 8, "rms_strided"),
+    ("q8", 1000, 2560, 8, "plain_strided"), ("q4", 4100, 1024, 20, "rms_strided"),
 ]
 
 
 def _fused_inputs(fmt, n, k, b, op, seed):
     gen = synth.q4_0_matrix if fmt == "q4" else synth.q8_0_matrix
     W = gen(seed, f"t.batched.{fmt}.{n}.{k}", n, k)
-    ld = 2 * k if op in ("swiglu", "geglu") else k
+    ld = 2 * k if op in ("swiglu", "geglu") else k + 64 if op.endswith("_strided") else k
     xa = synth.normal_f32(seed, f"t.batched.x.{k}.{b}", (b, ld)) * 2.0
     w = synth.uniform_f32(seed, f"t.batched.w.{k}", (k,), 0.8, 1.2)
     r = synth.normal_f32(seed, f"t.batched.r.{n}.{b}", (b, n))
@@ -227,7 +237,7 @@ def _fused_inputs(fmt, n, k, b, op, seed):
         xin = np.stack([oracle.swiglu(xa[i, :k], xa[i, k:]) for i in range(b)])
     elif op == "geglu":
         xin = np.stack([oracle.geglu(xa[i, :k], xa[i, k:]) for i in range(b)])
-    elif op == "plain":
+    elif op in ("plain", "plain_strided"):
         xin = xa[:, :k].astype(np.float64)
     else:
         xin = oracle.rmsnorm(xa[:, :k], None if op == "rms_unit" else w, 1e-6)
@@ -235,7 +245,7 @@ def _fused_inputs(fmt, n, k, b, op, seed):
 
 
 _KIND = {"plain": q.IN_PLAIN, "rms": q.IN_RMSNORM, "rms_unit": q.IN_RMSNORM, "swiglu": q.IN_SWIGLU,
-         "geglu": q.IN_GEGLU}
+         "geglu": q.IN_GEGLU, "plain_strided": q.IN_PLAIN, "rms_strided": q.IN_RMSNORM}
 
 
 @pytest.mark.parametrize("fmt,n,k,b,op", BATCHED_CASES)
@@ -249,7 +259,7 @@ def test_matvec_batched_parity(dev, fmt, n, k, b, op):
     yr = torch.from_numpy(r).to(dev)
     Wd = torch.from_numpy(W).to(dev)
     kw = dict(x2=xd[:, k:] if op in ("swiglu", "geglu") else None,
-              norm_w=torch.from_numpy(w).to(dev) if op == "rms" else None, eps=1e-6)
+              norm_w=torch.from_numpy(w).to(dev) if op in ("rms", "rms_strided") else None, eps=1e-6)
     y0 = fn(Wd, xd, k, b, ld, _KIND[op], **kw)
     fn(Wd, xd, k, b, ld, _KIND[op], y=yr, residual=yr, **kw)
     torch.cuda.synchronize()
